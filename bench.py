@@ -1,0 +1,172 @@
+"""Benchmark of one MoE layer step on one MI355X.
+
+A step is one moe_layer_forward over one batch of synthetic tokens: router GEMM,
+top-k, routing tables, gate/up grouped GEMM with SwiGLU, down grouped GEMM,
+shared expert and combine. Inputs are resident in HBM before the timed region.
+
+Prints one JSON line (see the contract in the design doc): value = tokens/s of the
+layer, roofline = the gate/up grouped GEMM (the dominant kernel) against the
+bf16 dense MFMA peak, cpu_baseline = the fp64 oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer prefill tokens/s @T=4096 (+% MFMA peak); decode-step HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def layer_flops(T, H, I, E, k):
+    return T * (2 * H * E + (k + 1) * 2 * H * 3 * I)
+
+
+def gateup_flops(T, H, I, k):
+    # real (token, expert) rows of the gate/up GEMM: T*k routed + T shared
+    return (T * k + T) * 2 * H * (2 * I)
+
+
+def q4_bytes(N, K):
+    return N * K // 2 + 4 * N * (K // 64)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="prefill4096")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(inp):
+    """Time the fp64 oracle (as it stands) on the whole workload once."""
+    import oracle.moe_oracle as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    om.moe_layer(inp)
+    dt = time.perf_counter() - t0
+    return {"value": inp.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full layer pass, T={inp.T} tokens (all of the timed workload), {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library runs on a "
+              "single GPU; see DESIGN.md for how the layer would shard)", file=sys.stderr)
+        sys.exit(2)
+    import ctypes
+
+    import torch
+
+    from int4_expert_routing_amd import _lib, ops
+    from synth import CONFIGS, make_config
+
+    lib = _lib.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.config]
+    inp = make_config(args.config, seed=args.seed)
+    T, H, I, E, k = inp.T, inp.H, inp.I, inp.E, inp.k
+    w = ops.MoEWeights.from_host(inp, dev)
+    x = ops.bf16_from_bits(inp.x, dev)
+    layer = ops.MoELayer(w, k, T)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    structs = [s.c_struct() for s in (w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)]
+    dims = _lib.MoeDims(T, H, I, E, k, 0)
+    nev = _lib.MOE_LAYER_STAGE_EVENTS
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        evp = None
+        n = 0
+        if events is not None:
+            evp = (ctypes.c_void_p * nev)(*[e.cuda_event for e in events])
+            n = nev
+        st = lib.moe_layer_forward_timed(
+            ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.router_w.data_ptr()),
+            ctypes.c_void_p(w.logit_bias.data_ptr()) if w.logit_bias is not None else None,
+            *[ctypes.byref(s) for s in structs], ctypes.byref(dims), ctypes.c_void_p(y.data_ptr()), None, None,
+            None, ctypes.c_void_p(layer.workspace.data_ptr()), layer.workspace.numel(),
+            ctypes.c_void_p(stream.cuda_stream), evp, n)
+        _lib.check(st, "moe_layer_forward_timed")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for e in evs:            # create the HIP events before the timed region
+        for ev in e:
+            ev.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = np.zeros(nev - 1)
+    step_ms = []
+    for e in evs:
+        for i in range(nev - 1):
+            stage_ms[i] += e[i].elapsed_time(e[i + 1])
+        step_ms.append(e[0].elapsed_time(e[nev - 1]))
+    stage_ms /= args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms = float(np.mean(step_ms))
+    names = ["prep", "route", "gate_up_gemm", "down_gemm", "combine"]
+    flops = layer_flops(T, H, I, E, k)
+    gu_flops = gateup_flops(T, H, I, k)
+    gu_ms = float(stage_ms[2])
+    achieved_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
+    weight_bytes = E * 3 * q4_bytes(I, H) + 3 * q4_bytes(I, H) + E * H * 2
+    out = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: MoE layer T={T} H={H} I={I} E={E} top-{k} + 1 shared expert, "
+                               "int4 g64 affine weights (bf16 scale/bias), bf16 activations",
+                   "T": T, "H": H, "I": I, "E": E, "k": k, "seed": args.seed,
+                   "logit_bias": "zipf1.2" if cfg.get("zipf") else None},
+        "layer_pct_mfma_peak": 100.0 * flops / (ms_per_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "layer_gpu_ms_events": gpu_ms,
+        "stage_ms": {n: float(v) for n, v in zip(names, stage_ms)},
+        "roofline": {"kernel": "gemm_q4_kernel<SwiGLU> (gate/up grouped GEMM)", "bound": "mfma",
+                     "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": gu_flops},
+        "weight_bytes": weight_bytes,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

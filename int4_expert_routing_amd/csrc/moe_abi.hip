@@ -1,0 +1,381 @@
+// extern "C" entry points of the library: argument validation, workspace
+// layout, and the launch sequence of each call (all on the caller's stream,
+// no host synchronisation).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+// Workspace of one layer call. Offsets in bytes from the workspace base.
+struct LayerLayout {
+  size_t logits, ids, w, block_counts, block_base, rank, counts, offsets, sorted_rows, row_of_pair,
+      tile_map, num_tiles, x_perm, x_aux, h, h_aux, Y, total;
+};
+
+int64_t max_tiles_of(int64_t T, int64_t E, int64_t k, int64_t bm) {
+  const int64_t pairs = T * k;
+  return pairs / bm + (E < pairs ? E : pairs);
+}
+
+LayerLayout layer_layout(const moe_dims& d) {
+  const size_t T = size_t(d.T), E = size_t(d.E), k = size_t(d.k), H = size_t(d.H), I = size_t(d.I);
+  const size_t nblk = size_t(ceil_div(d.T, kRouteTokens));
+  const size_t rows = T * k + T;
+  const int bm = d.block_rows > 0 ? d.block_rows : kBlockRows;
+  Carve c;
+  LayerLayout L;
+  L.logits = c.take(T * E * 4);
+  L.ids = c.take(T * k * 4);
+  L.w = c.take(T * k * 4);
+  L.block_counts = c.take(nblk * E * 4);
+  L.block_base = c.take(nblk * E * 4);
+  L.rank = c.take(T * k * 4);
+  L.counts = c.take(E * 4);
+  L.offsets = c.take((E + 1) * 4);
+  L.sorted_rows = c.take(T * k * 4);
+  L.row_of_pair = c.take(T * k * 4);
+  L.tile_map = c.take(size_t(max_tiles_of(d.T, d.E, d.k, bm)) * 8);
+  L.num_tiles = c.take(4);
+  L.x_perm = c.take(T * H * 2);
+  L.x_aux = c.take(T * size_t(aux_cols(d.H)) * 2);
+  L.h = c.take(rows * I * 2);
+  L.h_aux = c.take(rows * size_t(aux_cols(d.I)) * 2);
+  L.Y = c.take(rows * H * 4);
+  L.total = c.off;
+  return L;
+}
+
+int check_route_dims(const moe_dims* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->T < 0 || d->E < 1 || d->E > kMaxExperts || d->k < 1 || d->k > d->E || d->k > kMaxTopk)
+    return MOE_ERR_SHAPE;
+  if (d->block_rows < 0) return MOE_ERR_SHAPE;
+  // T*k*(rows) must stay within int32 indexing.
+  if (int64_t(d->T) * (d->k + 1) > (int64_t(1) << 30)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int check_layer_dims(const moe_dims* d) {
+  const int st = check_route_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->H < 128 || d->I < 64 || d->H % 128 != 0 || d->I % 64 != 0) return MOE_ERR_SHAPE;
+  if (d->H > kMaxK || d->I > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (d->block_rows != 0 && d->block_rows != kBlockRows) return MOE_ERR_UNSUPPORTED;
+  if (int64_t(d->T) * (d->k + 1) * d->H > (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int check_weights(const moe_q4_weights* w, int n, int N, int K) {
+  if (!w) return MOE_ERR_NULL;
+  if (!w->q || !w->s || !w->b) return MOE_ERR_NULL;
+  if (w->n_experts != n || w->N != N || w->K != K) return MOE_ERR_SHAPE;
+  if (!aligned16(w->q)) return MOE_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(w->s) & 1u) || (reinterpret_cast<uintptr_t>(w->b) & 1u)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+QStack stack_of(const moe_q4_weights* w) { return QStack{w->q, w->s, w->b}; }
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a pointer is not suitably aligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: not implemented for these sizes";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_check_dims(const moe_dims* dims) { return check_layer_dims(dims); }
+
+int32_t moe_max_tiles(const moe_dims* d) {
+  if (check_route_dims(d) != MOE_OK) return 0;
+  const int bm = d->block_rows > 0 ? d->block_rows : kBlockRows;
+  return int32_t(max_tiles_of(d->T, d->E, d->k, bm));
+}
+
+size_t moe_workspace_bytes(const moe_dims* d) {
+  if (check_route_dims(d) != MOE_OK || d->T == 0) return 0;
+  moe_dims dd = *d;
+  if (dd.H < 0 || dd.I < 0) return 0;
+  return layer_layout(dd).total;
+}
+
+int moe_route(const float* logits, const float* logit_bias, const moe_dims* dims, int32_t* topk_ids,
+              float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_rows, int32_t* row_of_pair,
+              int32_t* tile_map, int32_t* num_tiles, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_route_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->block_rows < 1) return MOE_ERR_SHAPE;
+  if (dims->T == 0) return MOE_OK;   // nothing to do; other arguments are not examined
+  if (!logits || !topk_ids || !topk_w || !counts || !offsets || !sorted_rows || !row_of_pair || !tile_map ||
+      !num_tiles)
+    return MOE_ERR_NULL;
+  if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_w) || !aligned4(counts) || !aligned4(offsets) ||
+      !aligned4(sorted_rows) || !aligned4(row_of_pair) || !aligned4(tile_map) || !aligned4(num_tiles) ||
+      (logit_bias && !aligned4(logit_bias)))
+    return MOE_ERR_ALIGN;
+  if (dims->T == 0) return MOE_OK;
+  moe_dims d = *dims;
+  d.H = 0;
+  d.I = 0;
+  const LayerLayout L = layer_layout(d);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const int nblk = ceil_div(d.T, kRouteTokens);
+  RouteArgs ra{};
+  ra.logits_in = logits;
+  ra.bias = logit_bias;
+  ra.topk_ids = topk_ids;
+  ra.topk_w = topk_w;
+  ra.block_counts = at<int32_t>(workspace, L.block_counts);
+  ra.rank_in_block = at<int32_t>(workspace, L.rank);
+  ra.T = d.T;
+  ra.E = d.E;
+  ra.k = d.k;
+  ScanArgs sa{ra.block_counts, at<int32_t>(workspace, L.block_base), counts, offsets, tile_map, num_tiles,
+              nblk, d.E, d.block_rows};
+  ScatterArgs ca{topk_ids, sa.block_base, ra.rank_in_block, sorted_rows, row_of_pair, d.T, d.E, d.k};
+  const hipError_t err = launch_route(ra, sa, ca, false, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+size_t moe_gemm_workspace_bytes(int32_t a_rows, int32_t K) {
+  if (a_rows < 0 || K <= 0 || K % kGroup) return 0;
+  Carve c;
+  c.take(size_t(a_rows) * K * 2);
+  c.take(size_t(a_rows) * aux_cols(K) * 2);
+  return c.off;
+}
+
+int moe_grouped_gemm_q4(const uint16_t* A, int32_t a_rows, const int32_t* sorted_rows, int32_t row_div,
+                        const moe_q4_weights* W0, const moe_q4_weights* W1, const int32_t* offsets,
+                        const int32_t* tile_map, const int32_t* num_tiles, int32_t max_tiles, int32_t epilogue,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!A || !W0 || !offsets || !tile_map || !num_tiles || !out) return MOE_ERR_NULL;
+  if (epilogue != MOE_EPI_STORE_F32 && epilogue != MOE_EPI_SWIGLU_BF16) return MOE_ERR_SHAPE;
+  if (a_rows < 0 || max_tiles < 0) return MOE_ERR_SHAPE;
+  if (sorted_rows && row_div < 1) return MOE_ERR_SHAPE;
+  const int n = W0->n_experts, N = W0->N, K = W0->K;
+  if (n < 1 || N < 1 || K < kGroup || K % kGroup) return MOE_ERR_SHAPE;
+  if (K > kMaxK) return MOE_ERR_UNSUPPORTED;
+  int st = check_weights(W0, n, N, K);
+  if (st != MOE_OK) return st;
+  if (epilogue == MOE_EPI_SWIGLU_BF16) {
+    st = check_weights(W1, n, N, K);
+    if (st != MOE_OK) return st;
+    if (N % 64) return MOE_ERR_UNSUPPORTED;
+  } else if (N % 128) {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(A) || !aligned16(out)) return MOE_ERR_ALIGN;
+  if (a_rows == 0 || max_tiles == 0) return MOE_OK;
+  const size_t need = moe_gemm_workspace_bytes(a_rows, K);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  Carve c;
+  uint16_t* a_perm = at<uint16_t>(workspace, c.take(size_t(a_rows) * K * 2));
+  uint16_t* a_aux = at<uint16_t>(workspace, c.take(size_t(a_rows) * aux_cols(K) * 2));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_prep_rows(A, a_rows, K, a_perm, a_aux, s) != hipSuccess) return MOE_ERR_HIP;
+  GemmArgs ga{};
+  ga.A = a_perm;
+  ga.Aaux = a_aux;
+  ga.sorted_rows = sorted_rows;
+  ga.row_div = sorted_rows ? row_div : 1;
+  ga.routed_rows = 0x7FFFFFFF;   // every tile is a routed tile
+  ga.shared_src_base = 0;
+  ga.w0[0] = ga.w0[1] = stack_of(W0);
+  ga.w1[0] = ga.w1[1] = epilogue == MOE_EPI_SWIGLU_BF16 ? stack_of(W1) : stack_of(W0);
+  ga.E = -1;                     // no shared-expert tiles
+  ga.offsets = offsets;
+  ga.tile_map = tile_map;
+  ga.num_tiles = num_tiles;
+  ga.n_shared_tiles = 0;
+  ga.shared_rows = 0;
+  ga.N = N;
+  ga.K = K;
+  ga.out = out;
+  int epi;
+  if (epilogue == MOE_EPI_STORE_F32) {
+    ga.NT = N / 128;
+    epi = kEpiF32;
+  } else {
+    ga.NT = N / 64;
+    epi = kEpiSwigluNatural;
+  }
+  return launch_gemm(ga, epi, max_tiles, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
+                              const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,
+                              const moe_q4_weights* sh_gate, const moe_q4_weights* sh_up,
+                              const moe_q4_weights* sh_down, const moe_dims* dims, uint16_t* y, float* logits_out,
+                              int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int n_events) {
+  int st = check_layer_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims d = *dims;
+  if (d.T == 0) return MOE_OK;   // nothing to do; other arguments are not examined
+  if (!x || !router_w || !y) return MOE_ERR_NULL;
+  if ((st = check_weights(gate, d.E, d.I, d.H)) != MOE_OK) return st;
+  if ((st = check_weights(up, d.E, d.I, d.H)) != MOE_OK) return st;
+  if ((st = check_weights(down, d.E, d.H, d.I)) != MOE_OK) return st;
+  if ((st = check_weights(sh_gate, 1, d.I, d.H)) != MOE_OK) return st;
+  if ((st = check_weights(sh_up, 1, d.I, d.H)) != MOE_OK) return st;
+  if ((st = check_weights(sh_down, 1, d.H, d.I)) != MOE_OK) return st;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(y)) return MOE_ERR_ALIGN;
+  if ((logit_bias && !aligned4(logit_bias)) || (logits_out && !aligned4(logits_out)) ||
+      (topk_ids_out && !aligned4(topk_ids_out)) || (topk_w_out && !aligned4(topk_w_out)))
+    return MOE_ERR_ALIGN;
+  if (n_events < 0 || (n_events > 0 && !events)) return MOE_ERR_NULL;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return MOE_ERR_NULL;
+  if (d.T == 0) return MOE_OK;
+  const LayerLayout L = layer_layout(d);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  // stage boundary i records events[i] when the caller asked for timing
+  auto mark = [&](int i) -> bool {
+    return i >= n_events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+  };
+  if (!mark(0)) return MOE_ERR_HIP;
+  const int T = d.T, E = d.E, k = d.k, H = d.H, I = d.I;
+  const int nblk = ceil_div(T, kRouteTokens);
+  const int bm = kBlockRows;
+
+  // 1. activations: permuted chunk order + group sums
+  uint16_t* x_perm = at<uint16_t>(ws, L.x_perm);
+  uint16_t* x_aux = at<uint16_t>(ws, L.x_aux);
+  if (launch_prep_rows(x, T, H, x_perm, x_aux, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
+
+  // 2-4. router GEMM, top-k, histogram, scan, scatter, block map
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  RouteArgs ra{};
+  ra.x = x;
+  ra.wr = router_w;
+  ra.bias = logit_bias;
+  ra.logits_out = logits_out;
+  ra.topk_ids = ids;
+  ra.topk_w = wts;
+  ra.block_counts = at<int32_t>(ws, L.block_counts);
+  ra.rank_in_block = at<int32_t>(ws, L.rank);
+  ra.T = T;
+  ra.H = H;
+  ra.E = E;
+  ra.k = k;
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* tile_map = at<int32_t>(ws, L.tile_map);
+  int32_t* num_tiles = at<int32_t>(ws, L.num_tiles);
+  int32_t* sorted_rows = at<int32_t>(ws, L.sorted_rows);
+  int32_t* row_of_pair = at<int32_t>(ws, L.row_of_pair);
+  ScanArgs sa{ra.block_counts, at<int32_t>(ws, L.block_base), at<int32_t>(ws, L.counts), offsets, tile_map,
+              num_tiles, nblk, E, bm};
+  ScatterArgs ca{ids, sa.block_base, ra.rank_in_block, sorted_rows, row_of_pair, T, E, k};
+  if (launch_route(ra, sa, ca, true, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
+
+  // 5. gate/up grouped GEMM with SwiGLU, routed tiles + shared-expert tiles
+  const int routed_rows = T * k;
+  const int n_sh = ceil_div(T, bm);
+  const int max_routed = int(max_tiles_of(T, E, k, bm));
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  uint16_t* h_aux = at<uint16_t>(ws, L.h_aux);
+  GemmArgs g1{};
+  g1.A = x_perm;
+  g1.Aaux = x_aux;
+  g1.sorted_rows = sorted_rows;
+  g1.row_div = k;
+  g1.routed_rows = routed_rows;
+  g1.shared_src_base = routed_rows;
+  g1.w0[0] = stack_of(gate);
+  g1.w0[1] = stack_of(sh_gate);
+  g1.w1[0] = stack_of(up);
+  g1.w1[1] = stack_of(sh_up);
+  g1.E = E;
+  g1.offsets = offsets;
+  g1.tile_map = tile_map;
+  g1.num_tiles = num_tiles;
+  g1.n_shared_tiles = n_sh;
+  g1.shared_rows = T;
+  g1.N = I;
+  g1.K = H;
+  g1.NT = I / 64;
+  g1.out = h;
+  g1.out_aux = h_aux;
+  if (launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+
+  // 6. down grouped GEMM (fp32 rows)
+  float* Y = at<float>(ws, L.Y);
+  GemmArgs g2 = g1;
+  g2.A = h;
+  g2.Aaux = h_aux;
+  g2.sorted_rows = nullptr;
+  g2.row_div = 1;
+  g2.shared_src_base = 0;
+  g2.w0[0] = stack_of(down);
+  g2.w0[1] = stack_of(sh_down);
+  g2.w1[0] = g2.w0[0];
+  g2.w1[1] = g2.w0[1];
+  g2.N = H;
+  g2.K = I;
+  g2.NT = H / 128;
+  g2.out = Y;
+  g2.out_aux = nullptr;
+  if (launch_gemm(g2, kEpiF32, n_sh + max_routed, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+
+  // 7. weighted combine + shared expert, bf16 output
+  if (launch_combine(Y, wts, row_of_pair, T, k, H, routed_rows, y, s) != hipSuccess || !mark(5)) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_layer_forward(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
+                      const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,
+                      const moe_q4_weights* sh_gate, const moe_q4_weights* sh_up, const moe_q4_weights* sh_down,
+                      const moe_dims* dims, uint16_t* y, float* logits_out, int32_t* topk_ids_out,
+                      float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_forward_impl(x, router_w, logit_bias, gate, up, down, sh_gate, sh_up, sh_down, dims, y, logits_out,
+                            topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+int moe_layer_forward_timed(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
+                            const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,
+                            const moe_q4_weights* sh_gate, const moe_q4_weights* sh_up,
+                            const moe_q4_weights* sh_down, const moe_dims* dims, uint16_t* y, float* logits_out,
+                            int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* events, int32_t n_events) {
+  return layer_forward_impl(x, router_w, logit_bias, gate, up, down, sh_gate, sh_up, sh_down, dims, y, logits_out,
+                            topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, events, n_events);
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the routing and GEMM kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 64;        // weights per quantisation group along K
+constexpr int kBlockRows = 64;    // rows per GEMM tile
+constexpr int kRouteTokens = 32;  // tokens per routing workgroup
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bf16, round to nearest, ties to even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_from_order_key(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = __shfl_xor(uint32_t(v), mask, kWave);
+  uint32_t hi = __shfl_xor(uint32_t(v >> 32), mask, kWave);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Within each 8-element (16-byte) chunk of bf16 values, the GEMM kernels keep
+// activations in the order [0,4,1,5,2,6,3,7]: the order in which one 32-bit
+// word of eight 4-bit codes unpacks into four bf16 pairs (see gemm_q4.hip).
+// in: natural chunk as 4 words (x1:x0, x3:x2, x5:x4, x7:x6); out: permuted.
+__device__ __forceinline__ u32x4 permute_chunk(u32x4 v) {
+  u32x4 o;
+  o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // (x4 : x0)
+  o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // (x5 : x1)
+  o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (x6 : x2)
+  o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (x7 : x3)
+  return o;
+}
+// Inverse of permute_chunk.
+__device__ __forceinline__ u32x4 unpermute_chunk(u32x4 v) {
+  u32x4 o;
+  o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (x1 : x0)
+  o.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (x3 : x2)
+  o.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x5 : x4)
+  o.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (x7 : x6)
+  return o;
+}
+
+// Sum of the 8 bf16 values of a chunk (order irrelevant), in fp32.
+__device__ __forceinline__ float chunk_sum(u32x4 v) {
+  float a = bf16_lo_to_f32(v.x) + bf16_hi_to_f32(v.x);
+  float b = bf16_lo_to_f32(v.y) + bf16_hi_to_f32(v.y);
+  float c = bf16_lo_to_f32(v.z) + bf16_hi_to_f32(v.z);
+  float d = bf16_lo_to_f32(v.w) + bf16_hi_to_f32(v.w);
+  return (a + b) + (c + d);
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Number of bf16 entries per row of the group-sum side table: three per
+// 64-wide group (hi, lo, hi of the group sum), padded to whole MFMA K steps.
+__host__ __device__ constexpr int aux_cols(int K) { return ceil_div(3 * (K / kGroup), 16) * 16; }
+
+}  // namespace moe

@@ -1,0 +1,246 @@
+// GPU-resident MoE routing for gfx950: router GEMM + top-k + softmax, per-block
+// histogram, prefix scan, stable scatter and block map, with no host
+// synchronisation between the steps (page "Perplexity Open Sources Lily ..."
+// Technical Details, Model bullet: the router picks 8 of 256 experts; prefill
+// bullet: routing histogram, prefix scan, scatter and block map stay on the GPU).
+//
+// Three launches on one stream:
+//   1. route_topk_kernel  - one workgroup per 32 tokens: logits (bf16 MFMA with
+//      fp32 accumulation, or read from memory), top-k by the key (logit desc,
+//      expert asc), softmax over the chosen k, the block's expert histogram and
+//      each pair's rank among the block's pairs of the same expert.
+//   2. route_scan_kernel  - one workgroup: per-expert scan over blocks, exclusive
+//      scan over experts (offsets), and the tile list of the block map.
+//   3. route_scatter_kernel - one workgroup per 32 tokens: final row of each
+//      pair = block base of its expert + its in-block rank.
+// Ranks count only earlier pairs, so the sort is stable and the result does not
+// depend on thread timing: repeated runs give identical tables.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kRouteThreads = 256;
+constexpr int kMaxKeysPerLane = kMaxExperts / kWave;  // 8
+
+template <bool FROM_X>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) {
+  extern __shared__ float lds_f[];
+  float* lg = lds_f;                                          // [32][E]
+  int32_t* ids_s = reinterpret_cast<int32_t*>(lg + kRouteTokens * a.E);  // [32*k]
+  int32_t* hist = ids_s + kRouteTokens * a.k;                 // [E]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int blk = blockIdx.x;
+  const int t0 = blk * kRouteTokens;
+  const int nt = min(kRouteTokens, a.T - t0);
+  const int E = a.E, k = a.k;
+
+  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+
+  if constexpr (FROM_X) {
+    // Router GEMM: 32 tokens x E experts, K = H. Wave w owns expert blocks
+    // w, w+4, ... of 32 experts; MFMA 32x32x16 bf16 with fp32 accumulation.
+    const int nblkE = ceil_div(E, 32);
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    const int m = lane & 31;
+    const int half = lane >> 5;
+    const bool row_ok = m < nt;
+    const uint16_t* xrow = a.x + size_t(t0 + (row_ok ? m : 0)) * a.H + 8 * half;
+    for (int k0 = 0; k0 < a.H; k0 += 16) {
+      u32x4 av = row_ok ? *reinterpret_cast<const u32x4*>(xrow + k0) : u32x4{0, 0, 0, 0};
+      bf16x8 af = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = wave + 4 * i;
+        if (b < nblkE) {
+          const int n = b * 32 + m;
+          u32x4 bv = n < E ? *reinterpret_cast<const u32x4*>(a.wr + size_t(n) * a.H + 8 * half + k0)
+                           : u32x4{0, 0, 0, 0};
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = wave + 4 * i;
+      if (b >= nblkE) continue;
+      const int n = b * 32 + (lane & 31);
+      if (n >= E) continue;
+      const float beta = a.bias ? a.bias[n] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int mm = 8 * (r >> 2) + 4 * half + (r & 3);
+        float v = (acc[i][r] + beta) + 0.0f;   // + 0.0f turns -0 into +0
+        lg[mm * E + n] = v;
+        if (a.logits_out && mm < nt) a.logits_out[size_t(t0 + mm) * E + n] = v;
+      }
+    }
+  } else {
+    for (int i = tid; i < nt * E; i += kRouteThreads) {
+      const int n = i % E;
+      float v = a.logits_in[size_t(t0) * E + i];
+      if (a.bias) v = v + a.bias[n];
+      lg[i] = v + 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // Top-k per token: one wave per token; each lane holds experts lane + 64 i.
+  for (int m = wave; m < nt; m += kRouteThreads / kWave) {
+    uint64_t key[kMaxKeysPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      const int e = lane + 64 * i;
+      key[i] = e < E ? (uint64_t(float_order_key(lg[m * E + e])) << 32) | uint32_t(0xFFFFFFFFu - e) : 0ull;
+    }
+    int my_e = 0;
+    float my_l = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int i = 1; i < kMaxKeysPerLane; ++i) best = key[i] > best ? key[i] : best;
+      best = wave_max_u64(best);
+      const int ej = int(0xFFFFFFFFu - uint32_t(best));
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i)
+        if (lane + 64 * i == ej) key[i] = 0ull;
+      if (lane == j) {
+        my_e = ej;
+        my_l = float_from_order_key(uint32_t(best >> 32));
+      }
+    }
+    const float l0 = __shfl(my_l, 0, kWave);
+    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
+    const float sum = wave_sum_f32(ex);
+    if (lane < k) {
+      const size_t f = size_t(t0 + m) * k + lane;
+      a.topk_ids[f] = my_e;
+      a.topk_w[f] = ex / sum;
+      ids_s[m * k + lane] = my_e;
+    }
+  }
+  __syncthreads();
+
+  const int npairs = nt * k;
+  for (int p = tid; p < npairs; p += kRouteThreads) atomicAdd(&hist[ids_s[p]], 1);
+  // Rank of each pair among the earlier pairs of this block with the same
+  // expert (pair order f = t*k + j), which makes the scatter stable.
+  for (int p = tid; p < npairs; p += kRouteThreads) {
+    const int e = ids_s[p];
+    int r = 0;
+    for (int q = 0; q < p; ++q) r += ids_s[q] == e;
+    a.rank_in_block[size_t(t0) * k + p] = r;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) a.block_counts[size_t(blk) * E + e] = hist[e];
+}
+
+// Inclusive scan of v over n <= 1024 entries held in LDS (one per thread).
+__device__ void block_inclusive_scan(int32_t* v, int32_t* tmp, int n) {
+  const int tid = threadIdx.x;
+  for (int d = 1; d < n; d <<= 1) {
+    int32_t x = 0;
+    if (tid < n) x = v[tid] + (tid >= d ? v[tid - d] : 0);
+    __syncthreads();
+    if (tid < n) v[tid] = x;
+    __syncthreads();
+  }
+  (void)tmp;
+}
+
+__global__ __launch_bounds__(1024) void route_scan_kernel(ScanArgs a) {
+  __shared__ int32_t psum[1024];
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t off[kMaxExperts];
+  __shared__ int32_t ntl[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  const int parts = 1024 / E;
+  const int chunk = ceil_div(a.nblk, parts);
+  const int e = tid % E;
+  const int part = tid / E;
+  const bool active = part < parts;
+  const int b0 = part * chunk;
+  const int b1 = min(a.nblk, b0 + chunk);
+
+  if (active) {
+    int32_t s = 0;
+    for (int b = b0; b < b1; ++b) s += a.block_counts[size_t(b) * E + e];
+    psum[part * E + e] = s;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int32_t run = 0;
+    for (int p = 0; p < parts; ++p) {
+      const int32_t v = psum[p * E + tid];
+      psum[p * E + tid] = run;
+      run += v;
+    }
+    cnt[tid] = run;
+    off[tid] = run;
+    ntl[tid] = ceil_div(run, a.block_rows);
+  }
+  __syncthreads();
+  block_inclusive_scan(off, nullptr, E);   // inclusive scan of counts
+  block_inclusive_scan(ntl, nullptr, E);   // inclusive scan of tiles per expert
+  if (active) {
+    int32_t run = off[e] - cnt[e] + psum[part * E + e];
+    for (int b = b0; b < b1; ++b) {
+      a.block_base[size_t(b) * E + e] = run;
+      run += a.block_counts[size_t(b) * E + e];
+    }
+  }
+  if (tid < E) {
+    const int32_t c = cnt[tid];
+    const int32_t o = off[tid] - c;
+    a.counts[tid] = c;
+    a.offsets[tid] = o;
+    const int nt_e = ceil_div(c, a.block_rows);
+    const int t_first = ntl[tid] - nt_e;
+    for (int i = 0; i < nt_e; ++i) {
+      a.tile_map[2 * (t_first + i)] = tid;
+      a.tile_map[2 * (t_first + i) + 1] = o + i * a.block_rows;
+    }
+    if (tid == E - 1) {
+      a.offsets[E] = off[tid];
+      *a.num_tiles = ntl[tid];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArgs a) {
+  const int blk = blockIdx.x;
+  const int t0 = blk * kRouteTokens;
+  const int nt = min(kRouteTokens, a.T - t0);
+  const int npairs = nt * a.k;
+  for (int p = threadIdx.x; p < npairs; p += kRouteThreads) {
+    const size_t f = size_t(t0) * a.k + p;
+    const int e = a.topk_ids[f];
+    const int pos = a.block_base[size_t(blk) * a.E + e] + a.rank_in_block[f];
+    a.sorted_rows[pos] = int32_t(f);
+    a.row_of_pair[f] = pos;
+  }
+}
+
+hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,
+                        hipStream_t stream) {
+  const int nblk = ceil_div(ra.T, kRouteTokens);
+  const size_t lds = sizeof(float) * kRouteTokens * ra.E + sizeof(int32_t) * (kRouteTokens * ra.k + ra.E);
+  if (from_x)
+    hipLaunchKernelGGL(route_topk_kernel<true>, dim3(nblk), dim3(kRouteThreads), lds, stream, ra);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<false>, dim3(nblk), dim3(kRouteThreads), lds, stream, ra);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, sa);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kRouteThreads), 0, stream, ca);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,116 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before launching anything (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from int4_expert_routing_amd import _lib
+from int4_expert_routing_amd._lib import MoeDims, MoeQ4Weights
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_q4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for must in ("moe_route", "moe_grouped_gemm_q4", "moe_layer_forward", "moe_workspace_bytes",
+                 "moe_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in moe_q4.h but not exported"
+    assert set(declared_functions()) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings(lib):
+    for st in range(0, -7, -1):
+        assert lib.moe_status_string(st).decode().startswith("MOE_")
+    assert b"unknown" in lib.moe_status_string(5)
+
+
+def test_check_dims_and_workspace(lib):
+    good = MoeDims(4096, 2048, 512, 256, 8, 0)
+    assert lib.moe_check_dims(ctypes.byref(good)) == _lib.MOE_OK
+    ws = lib.moe_workspace_bytes(ctypes.byref(good))
+    # the fp32 per-row outputs dominate: (T*k + T) rows * H * 4 bytes
+    assert ws >= (4096 * 9) * 2048 * 4
+    assert lib.moe_workspace_bytes(ctypes.byref(MoeDims(0, 2048, 512, 256, 8, 0))) == 0
+    cases = {
+        (4096, 2048, 512, 256, 0, 0): _lib.MOE_ERR_SHAPE,        # k = 0
+        (4096, 2048, 512, 8, 9, 0): _lib.MOE_ERR_SHAPE,          # k > E
+        (4096, 2048, 512, 257, 8, 0): _lib.MOE_ERR_SHAPE,        # E too large
+        (4096, 2000, 512, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # H not a multiple of 128
+        (4096, 2048, 500, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # I not a multiple of 64
+        (-1, 2048, 512, 256, 8, 0): _lib.MOE_ERR_SHAPE,          # negative T
+        (4096, 2048, 512, 256, 8, 32): _lib.MOE_ERR_UNSUPPORTED,  # other tile height
+        (16, 8192, 512, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,    # K beyond the GEMM limit
+    }
+    for dims, want in cases.items():
+        assert lib.moe_check_dims(ctypes.byref(MoeDims(*dims))) == want, dims
+    assert lib.moe_check_dims(None) == _lib.MOE_ERR_NULL
+
+
+def test_max_tiles_bound(lib):
+    assert lib.moe_max_tiles(ctypes.byref(MoeDims(4096, 0, 0, 256, 8, 64))) == 4096 * 8 // 64 + 256
+    assert lib.moe_max_tiles(ctypes.byref(MoeDims(1, 0, 0, 256, 8, 64))) == 0 + 8
+
+
+def test_calls_reject_bad_arguments_before_launching(lib):
+    # every call below fails validation, so nothing reaches the GPU runtime
+    d = MoeDims(64, 256, 128, 16, 2, 64)
+    null = None
+    st = lib.moe_route(null, null, ctypes.byref(d), *([null] * 8), null, 0, null)
+    assert st == _lib.MOE_ERR_NULL
+    bad = MoeDims(64, 256, 128, 16, 0, 64)
+    assert lib.moe_route(null, null, ctypes.byref(bad), *([null] * 8), null, 0, null) == _lib.MOE_ERR_SHAPE
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+    st = lib.moe_route(fake, null, ctypes.byref(d), *([fake] * 8), null, 0, null)
+    assert st == _lib.MOE_ERR_WORKSPACE
+    w = MoeQ4Weights(0x1000, 0x2000, 0x3000, 16, 128, 256)
+    st = lib.moe_layer_forward(null, null, null, *([ctypes.byref(w)] * 6), ctypes.byref(d), null, null, null,
+                               null, null, 0, null)
+    assert st == _lib.MOE_ERR_NULL
+    # wrong weight shapes
+    st = lib.moe_layer_forward(fake, fake, null, *([ctypes.byref(w)] * 6), ctypes.byref(d), fake, null, null,
+                               null, null, 0, null)
+    assert st == _lib.MOE_ERR_SHAPE
+    # misaligned activations
+    d2 = MoeDims(64, 256, 128, 16, 2, 0)
+    ws = [MoeQ4Weights(0x1000, 0x2000, 0x3000, n, N, K)
+          for n, N, K in ((16, 128, 256), (16, 128, 256), (16, 256, 128), (1, 128, 256), (1, 128, 256),
+                          (1, 256, 128))]
+    st = lib.moe_layer_forward(ctypes.c_void_p(0x1002), fake, null, *[ctypes.byref(x) for x in ws],
+                               ctypes.byref(d2), fake, null, null, null, null, 0, null)
+    assert st == _lib.MOE_ERR_ALIGN
+    # workspace too small
+    st = lib.moe_layer_forward(fake, fake, null, *[ctypes.byref(x) for x in ws], ctypes.byref(d2), fake, null,
+                               null, null, fake, 16, null)
+    assert st == _lib.MOE_ERR_WORKSPACE
+    # T = 0 is a no-op
+    d0 = MoeDims(0, 256, 128, 16, 2, 0)
+    st = lib.moe_layer_forward(fake, fake, null, *[ctypes.byref(x) for x in ws], ctypes.byref(d0), fake, null,
+                               null, null, null, 0, null)
+    assert st == _lib.MOE_OK
+    # grouped GEMM: unsupported width, bad epilogue
+    w0 = MoeQ4Weights(0x1000, 0x2000, 0x3000, 4, 96, 256)
+    st = lib.moe_grouped_gemm_q4(fake, 8, null, 1, ctypes.byref(w0), null, fake, fake, fake, 4, 0, fake, null, 0,
+                                 null)
+    assert st == _lib.MOE_ERR_UNSUPPORTED
+    st = lib.moe_grouped_gemm_q4(fake, 8, null, 1, ctypes.byref(w0), null, fake, fake, fake, 4, 7, fake, null, 0,
+                                 null)
+    assert st == _lib.MOE_ERR_SHAPE

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Routing tables are compared bit for bit given the same fp32 logits; bf16 layer
+outputs must be within relative L2 <= 1e-3 and max-abs <= 2e-2 * max|ref| of
+the oracle (which rounds only h and y to bf16); logits within 1e-4 of the
+oracle's own; routing weights within 1e-6.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as om
+from int4_expert_routing_amd import _lib, ops
+from synth import Q4Weights, make_config, make_layer
+from tests.helpers import (LOGIT_ABS_TOL, WEIGHT_ABS_TOL, assert_close_bf16, rel_l2, max_abs_frac,
+                           tiny_layer)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    _lib.load()   # raises when the library has not been built
+    return torch.device("cuda:0")
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+
+def _logits(kind, T, E, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "zeros":
+        return np.zeros((T, E), np.float32)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    if kind == "ties":
+        l = (np.round(l * 2) / 2).astype(np.float32)
+    return l
+
+
+ROUTE_CASES = [
+    (4096, 256, 8, 64, "gauss"), (4096, 256, 8, 64, "zipf"), (37, 16, 2, 64, "gauss"),
+    (64, 16, 2, 3, "ties"), (1, 256, 8, 64, "gauss"), (200, 8, 8, 16, "gauss"),
+    (100, 32, 4, 64, "zeros"), (513, 256, 8, 64, "ties"), (32768, 256, 8, 64, "gauss"),
+    (33, 256, 32, 1, "ties"), (257, 5, 3, 7, "gauss"),
+]
+
+
+@pytest.mark.parametrize("T,E,k,bm,kind", ROUTE_CASES)
+def test_route_matches_oracle_bit_exact(dev, T, E, k, bm, kind):
+    print(f"route case T={T} E={E} k={k} bm={bm} {kind}", flush=True)
+    l = _logits(kind, T, E, seed=T + E)
+    bias = None
+    if kind == "zipf":
+        bias = (-1.2 * np.log(np.arange(1, E + 1))).astype(np.float32)
+    out = ops.moe_route(torch.from_numpy(l).to(dev), k, bm,
+                        logit_bias=None if bias is None else torch.from_numpy(bias).to(dev))
+    torch.cuda.synchronize()
+    lb = l if bias is None else (l + bias[None, :]).astype(np.float32)
+    ids, w = om.select_topk(lb, k)
+    tab = om.routing_tables(ids, E, bm)
+    assert np.array_equal(_np(out["topk_ids"]), ids)
+    assert np.max(np.abs(_np(out["topk_w"]) - w)) <= WEIGHT_ABS_TOL
+    for name in ("counts", "offsets", "sorted_rows", "row_of_pair"):
+        assert np.array_equal(_np(out[name]), tab[name]), name
+    n = int(_np(out["num_tiles"])[0])
+    assert n == int(tab["num_tiles"])
+    assert np.array_equal(_np(out["tile_map"])[:n], tab["tile_map"])
+
+
+def test_route_is_deterministic(dev):
+    l = torch.from_numpy(_logits("ties", 4096, 256, 3)).to(dev)
+    a = ops.moe_route(l, 8, 64)
+    b = ops.moe_route(l, 8, 64)
+    torch.cuda.synchronize()
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
+
+
+# ----------------------------------------------------------------------------
+# grouped GEMM (public entry point)
+# ----------------------------------------------------------------------------
+
+def _route_for(dev, T, E, k, seed):
+    l = torch.from_numpy(_logits("gauss", T, E, seed)).to(dev)
+    return ops.moe_route(l, k, ops.BLOCK_ROWS)
+
+
+def test_gemm_integer_case_is_exact(dev):
+    # s = 1, b = 0 and integer activations: every partial sum is an integer below
+    # 2**24, so the fp32 result must equal the int64 product exactly
+    T, E, k, N, K = 150, 4, 2, 256, 512
+    rng = np.random.default_rng(1)
+    xi = rng.integers(-16, 17, size=(T, K)).astype(np.float32)
+    A = torch.from_numpy(xi).to(torch.bfloat16).to(dev)
+    q = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32)
+    one = np.full((E, N, K // 64), 0x3F80, np.uint16)
+    zero = np.zeros((E, N, K // 64), np.uint16)
+    W = ops.Q4Stack.from_host(Q4Weights(q, one, zero), dev)
+    r = _route_for(dev, T, E, k, 5)
+    out = ops.moe_grouped_gemm_q4(A, W, r["offsets"], r["tile_map"], r["num_tiles"], ops.MOE_EPI_STORE_F32,
+                                  T * k, sorted_rows=r["sorted_rows"], row_div=k)
+    torch.cuda.synchronize()
+    got = _np(out).astype(np.float64)
+    srt = _np(r["sorted_rows"])
+    offs = _np(r["offsets"])
+    qn = om.unpack_q4(q).astype(np.int64)
+    want = np.zeros((T * k, N), np.int64)
+    for e in range(E):
+        rows = np.arange(offs[e], offs[e + 1])
+        want[rows] = xi[srt[rows] // k].astype(np.int64) @ qn[e].T
+    assert np.array_equal(got, want.astype(np.float64))
+
+
+@pytest.mark.parametrize("bias_mode", ["sym", "random"])
+def test_gemm_f32_matches_oracle(dev, bias_mode):
+    T, E, k, N, K = 300, 8, 2, 256, 512
+    inp = make_layer(T, K, N, E, k, seed=7, bias_mode=bias_mode)
+    A = ops.bf16_from_bits(inp.x, dev)
+    W = ops.Q4Stack.from_host(inp.gate, dev)   # gate is [E][N=I][K=H]: here N=256, K=512
+    r = _route_for(dev, T, E, k, 9)
+    out = ops.moe_grouped_gemm_q4(A, W, r["offsets"], r["tile_map"], r["num_tiles"], ops.MOE_EPI_STORE_F32,
+                                  T * k, sorted_rows=r["sorted_rows"], row_div=k)
+    torch.cuda.synchronize()
+    got = _np(out).astype(np.float64)
+    srt = _np(r["sorted_rows"])
+    offs = _np(r["offsets"])
+    x = om.bf16_bits_to_f64(inp.x)
+    want = np.zeros((T * k, N))
+    for e in range(E):
+        rows = np.arange(offs[e], offs[e + 1])
+        want[rows] = x[srt[rows] // k] @ om.expert_weights(inp.gate, e).T
+    assert rel_l2(got, want) < 1e-5, rel_l2(got, want)
+    assert max_abs_frac(got, want) < 1e-4
+
+
+def test_gemm_swiglu_matches_oracle(dev):
+    T, E, k, I, H = 200, 8, 2, 128, 512
+    inp = make_layer(T, H, I, E, k, seed=11, bias_mode="random")
+    A = ops.bf16_from_bits(inp.x, dev)
+    Wg = ops.Q4Stack.from_host(inp.gate, dev)
+    Wu = ops.Q4Stack.from_host(inp.up, dev)
+    r = _route_for(dev, T, E, k, 13)
+    out = ops.moe_grouped_gemm_q4(A, Wg, r["offsets"], r["tile_map"], r["num_tiles"], ops.MOE_EPI_SWIGLU_BF16,
+                                  T * k, W1=Wu, sorted_rows=r["sorted_rows"], row_div=k)
+    torch.cuda.synchronize()
+    got = ops.bits_from_bf16(out)
+    srt = _np(r["sorted_rows"])
+    offs = _np(r["offsets"])
+    x = om.bf16_bits_to_f64(inp.x)
+    want = np.zeros((T * k, I))
+    for e in range(E):
+        rows = np.arange(offs[e], offs[e + 1])
+        xs = x[srt[rows] // k]
+        g = xs @ om.expert_weights(inp.gate, e).T
+        u = xs @ om.expert_weights(inp.up, e).T
+        want[rows] = om.round_bf16(om.silu(g) * u)
+    gotf = om.bf16_bits_to_f64(got)
+    assert_close_bf16(gotf, want, "SwiGLU h")
+    # nearly every element rounds to the same bf16 value as the exact reference
+    assert np.mean(gotf == want) > 0.98
+
+
+# ----------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------
+
+def run_layer(dev, inp):
+    w = ops.MoEWeights.from_host(inp, dev)
+    x = ops.bf16_from_bits(inp.x, dev)
+    logits = torch.empty(inp.T, inp.E, dtype=torch.float32, device=dev)
+    ids = torch.empty(inp.T, inp.k, dtype=torch.int32, device=dev)
+    wts = torch.empty(inp.T, inp.k, dtype=torch.float32, device=dev)
+    y = ops.moe_layer_forward(x, w, inp.k, logits_out=logits, topk_ids_out=ids, topk_w_out=wts)
+    torch.cuda.synchronize()
+    return dict(y=om.bf16_bits_to_f64(ops.bits_from_bf16(y)), logits=_np(logits), ids=_np(ids), w=_np(wts))
+
+
+def check_layer(inp, g, tokens=None):
+    """Compare a GPU layer run with the oracle (routing from the GPU's own logits)."""
+    own = om.router_logits(inp.x, inp.router_w, inp.logit_bias)
+    assert np.max(np.abs(g["logits"].astype(np.float64) - own)) <= LOGIT_ABS_TOL
+    ids, w = om.select_topk(g["logits"], inp.k)
+    assert np.array_equal(g["ids"], ids), "top-k ids differ from the oracle on the same logits"
+    assert np.max(np.abs(g["w"] - w)) <= WEIGHT_ABS_TOL
+    if tokens is None:
+        ref = om.moe_layer(inp, logits=g["logits"])["y"]
+        got = g["y"]
+    else:
+        ref = om.round_bf16(om.moe_layer_tokens(inp, tokens, g["logits"]))
+        got = g["y"][tokens]
+    return assert_close_bf16(got, ref, "layer y")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("bias_mode", ["sym", "random"])
+def test_layer_tiny(dev, seed, bias_mode):
+    print(f"layer tiny seed={seed} bias={bias_mode}", flush=True)
+    inp = tiny_layer(seed, bias_mode)
+    g = run_layer(dev, inp)
+    check_layer(inp, g)
+    # with the close calls resampled the GPU routes exactly like the fp64 logits
+    ids_own, _ = om.select_topk(om.router_logits(inp.x, inp.router_w), inp.k)
+    assert np.array_equal(g["ids"], ids_own)
+
+
+def test_layer_tiny_zipf(dev):
+    inp = tiny_layer(3, "random", zipf=1.2)
+    check_layer(inp, run_layer(dev, inp))
+
+
+@pytest.mark.parametrize("T", [1, 31, 33, 65, 100, 257])
+def test_layer_ragged_token_counts(dev, T):
+    print(f"layer ragged T={T}", flush=True)
+    inp = make_layer(T, 256, 128, 16, 2, seed=T, bias_mode="random")
+    check_layer(inp, run_layer(dev, inp))
+
+
+def test_layer_k_equals_E(dev):
+    inp = make_layer(40, 256, 128, 4, 4, seed=4, bias_mode="random")
+    check_layer(inp, run_layer(dev, inp))
+
+
+def test_layer_zero_tokens_is_a_noop(dev):
+    inp = make_layer(3, 256, 128, 16, 2, seed=0)
+    w = ops.MoEWeights.from_host(inp, dev)
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device=dev)
+    y = ops.moe_layer_forward(x, w, 2)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)
+
+
+def test_layer_is_deterministic(dev):
+    inp = make_layer(300, 256, 128, 16, 2, seed=5, bias_mode="random")
+    a = run_layer(dev, inp)
+    b = run_layer(dev, inp)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode8"])
+def test_layer_full_shape_decode(dev, name):
+    print(f"layer {name}", flush=True)
+    inp = make_config(name, seed=0, bias_mode="random")
+    g = run_layer(dev, inp)
+    check_layer(inp, g, tokens=list(range(inp.T)))
+
+
+def test_layer_full_shape_prefill512_all_tokens(dev):
+    print("layer prefill512", flush=True)
+    inp = make_config("prefill512", seed=1)
+    check_layer(inp, run_layer(dev, inp))
+
+
+@pytest.mark.parametrize("name", ["prefill4096", "prefill4096_zipf"])
+def test_layer_full_shape_prefill4096_sampled(dev, name):
+    print(f"layer {name}", flush=True)
+    inp = make_config(name, seed=0)
+    g = run_layer(dev, inp)
+    rng = np.random.default_rng(0)
+    toks = sorted(set(rng.choice(inp.T, 24, replace=False).tolist()) | {0, inp.T - 1})
+    check_layer(inp, g, tokens=toks)
+
+
+def test_layer_full_shape_prefill32768_sampled(dev):
+    print("layer prefill32768", flush=True)
+    inp = make_config("prefill32768", seed=0)
+    g = run_layer(dev, inp)
+    toks = [0, 1, 4095, 4096, 20000, 32767]
+    check_layer(inp, g, tokens=toks)
