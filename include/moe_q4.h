@@ -147,7 +147,7 @@ int32_t moe_max_tiles(const moe_dims* dims);
  *
  *   A           device bf16 [a_rows][K]
  *   W0, W1      host structs; W1 only for SWIGLU (same n_experts, N, K as W0),
- *               K % 64 == 0; N % 64 == 0 (SWIGLU) or N % 128 == 0 (STORE_F32)
+ *               K % 64 == 0, K <= 2048; N % 64 == 0 (SWIGLU) or N % 128 == 0 (STORE_F32)
  *   offsets, tile_map, num_tiles  device, as produced by moe_route with
  *               block_rows = MOE_GEMM_BLOCK_ROWS; max_tiles bounds *num_tiles
  *   workspace   device, at least moe_gemm_workspace_bytes(a_rows, K) bytes
@@ -177,7 +177,8 @@ size_t moe_gemm_workspace_bytes(int32_t a_rows, int32_t K);
  *   gate, up     host structs, n_experts = E, N = I, K = H
  *   down         host struct,  n_experts = E, N = H, K = I
  *   sh_gate, sh_up, sh_down  the shared expert, n_experts = 1, same shapes
- *   dims         host; H % 128 == 0, I % 64 == 0, block_rows = 0 or MOE_GEMM_BLOCK_ROWS
+ *   dims         host; H % 128 == 0, I % 64 == 0, H and I <= 2048,
+ *                block_rows = 0 or MOE_GEMM_BLOCK_ROWS
  *   y            device bf16 [T][H]
  *   logits_out   device float [T][E] or NULL: the logits routing used (biased)
  *   topk_ids_out device int32 [T][k] or NULL

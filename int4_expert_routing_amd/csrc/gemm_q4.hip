@@ -11,15 +11,14 @@
 // s*q+b to bf16 before a bf16 MFMA would add ~2^-9 relative error per weight.
 // Instead the MFMA operand is the exact value 128+q, whose bf16 bit pattern is
 // 0x4300 | q, so one AND/OR turns two packed codes into two operands. For each
-// 64-wide group g of K the MFMA accumulates the exact-product partial
-//     P_g = sum_{k in g} x_k (128 + q_k)            (fp32)
-// and the kernel folds it as acc += s_g * P_g (one FMA per output per group).
-// What is left, sum_g (b_g - 128 s_g) X_g with X_g = sum_{k in g} x_k, is a
-// contraction over groups; it runs on the MFMA too, as 3 extra K columns per
-// group: activations (X_hi, X_lo, X_hi) against weights (b'_hi, b'_hi, b'_lo),
-// where hi/lo split a float into two bf16 values (b' = b - 128 s). X_g is
-// computed once per activation row (prep kernel, or the SwiGLU epilogue that
-// writes h) and stored in a side table.
+// 64-wide group g of K, with X_g = sum_{k in g} x_k, the MFMA chain of the group
+// starts from the accumulator value -128*X_g (exact fp32, from a side table)
+// and adds sum x_k (128 + q_k), leaving
+//     P_g = sum_{k in g} x_k q_k                      (fp32, no cancellation)
+// which the kernel folds as acc += s_g * P_g (one FMA per output per group).
+// The bias term sum_g b_g X_g runs on the MFMA as 3 extra K columns per group:
+// activations (X_hi, X_mid, X_lo), an exact three-part bf16 split of X_g,
+// against (b_g, b_g, b_g).
 //
 // Operand order. One 32-bit word holds codes k..k+7 (nibble i = code k+i); the
 // AND/OR unpack yields the bf16 pairs (k, k+4), (k+1, k+5), (k+2, k+6),
@@ -47,6 +46,7 @@ constexpr int kGemmThreads = 128;
 constexpr int kRing = 4;            // groups of weight codes in flight per wave
 constexpr uint32_t kMagic = 0x43004300u;  // two bf16 128.0
 constexpr uint32_t kNib = 0x000F000Fu;
+constexpr int kAbufBytes = 8192;    // one A buffer: 64 rows x 64 bf16
 
 struct TileInfo {
   int e, r0, r1;
@@ -84,10 +84,20 @@ __device__ __forceinline__ bf16x8 unpack_word(uint32_t w) {
 // LDS byte offset of 16-byte chunk c (0..7) of row m in one A buffer.
 __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ (m & 7))) * 16; }
 
-__device__ __forceinline__ uint32_t split_hi(float v) { return f32_to_bf16_rne(v); }
-__device__ __forceinline__ uint32_t split_lo(float v) {
-  const uint32_t h = f32_to_bf16_rne(v);
-  return f32_to_bf16_rne(v - __uint_as_float(h << 16));
+// Starting accumulator of a group's chain for row block rb: lane holds rows
+// rb*32 + 8j + 4*half + i (j, i = 0..3), the 32x32 MFMA output layout.
+__device__ __forceinline__ f32x16 chain_init(const float* xneg_g, int rb, int half) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(xneg_g + rb * 32 + 4 * half);
+  const f32x4 a = p[0], b = p[2], c = p[4], d = p[6];
+  return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
+}
+
+size_t gemm_lds_bytes(int K) {
+  const int G = K / kGroup;
+  return 2 * kAbufBytes                           // A double buffer
+         + size_t(G) * kBlockRows * 4              // -128 X_g  [G][64]
+         + size_t(kBlockRows) * xpart_cols(K) * 2  // X_g parts [64][xpart_cols]
+         + size_t(G) * 128 * 2;                    // scales    [G][128]
 }
 
 template <int EPI>
@@ -95,10 +105,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K;
   const int G = K / kGroup;
-  const int KPa = aux_cols(K);
-  uint8_t* abuf = smem;                                        // 2 x 8 KiB
-  uint16_t* aux_s = reinterpret_cast<uint16_t*>(smem + 2 * 8192);  // [64][KPa]
-  uint16_t* s_st = aux_s + kBlockRows * KPa;                  // [G][128]
+  const int KPx = xpart_cols(K);
+  const int KNx = xneg_cols(K);
+  uint8_t* abuf = smem;
+  float* xneg_s = reinterpret_cast<float*>(smem + 2 * kAbufBytes);        // [G][64]
+  uint16_t* xpart_s = reinterpret_cast<uint16_t*>(xneg_s + G * kBlockRows);  // [64][KPx]
+  uint16_t* s_st = xpart_s + kBlockRows * KPx;                             // [G][128]
 
   const int nt = blockIdx.x % a.NT;
   const int tile = blockIdx.x / a.NT;
@@ -115,7 +127,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
 
   // ---- weight rows owned by this wave: cb = 0, 1 --------------------------
   const size_t qrow = size_t(K / 8);
-  const uint32_t* qp[2];
   const QStack& m0 = a.w0[stack];
   const QStack& m1 = (EPI == kEpiF32) ? a.w0[stack] : a.w1[stack];
   int ncol[2];
@@ -126,37 +137,42 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
     ncol[0] = nt * 64 + wave * 32 + l32;
     ncol[1] = ncol[0];
   }
+  const uint32_t* qp[2];
   qp[0] = m0.q + (size_t(el) * a.N + ncol[0]) * qrow + 4 * half;
   qp[1] = m1.q + (size_t(el) * a.N + ncol[1]) * qrow + 4 * half;
 
-  // ---- prologue: stage scales of the workgroup's 128 weight rows ----------
+  // thread t <-> weight row (wave t/64, cb (t/32)%2, lane t%32) of the workgroup
+  const QStack* st_row;
+  int n_row;
   {
-    // thread t <-> weight row (wave t/64, cb (t/32)%2, lane t%32)
     const int w_ = tid >> 6, cb_ = (tid >> 5) & 1, j_ = tid & 31;
-    int n_;
-    const QStack* st;
     if constexpr (EPI == kEpiF32) {
-      n_ = nt * 128 + w_ * 64 + cb_ * 32 + j_;
-      st = &a.w0[stack];
+      n_row = nt * 128 + w_ * 64 + cb_ * 32 + j_;
+      st_row = &a.w0[stack];
     } else {
-      n_ = nt * 64 + w_ * 32 + j_;
-      st = cb_ ? &a.w1[stack] : &a.w0[stack];
+      n_row = nt * 64 + w_ * 32 + j_;
+      st_row = cb_ ? &a.w1[stack] : &a.w0[stack];
     }
-    const uint16_t* sp = st->s + (size_t(el) * a.N + n_) * G;
+  }
+  {
+    const uint16_t* sp = st_row->s + (size_t(el) * a.N + n_row) * G;
     for (int g = 0; g < G; ++g) s_st[g * 128 + tid] = sp[g];
   }
 
-  // ---- prologue: A side table and first A tile ----------------------------
+  // ---- prologue: side tables and the first A tile -------------------------
   const int srow = tid >> 1;          // staging row 0..63
   const int shalf = tid & 1;          // which 32-element half of a group
   const int sr = ti.r0 + srow;
   const bool svalid = sr < ti.r1;
-  const uint16_t* arow = a.A + size_t(svalid ? src_row(a, sr) : 0) * K + shalf * 32;
+  const int src = svalid ? src_row(a, sr) : 0;
+  const uint16_t* arow = a.A + size_t(src) * K + shalf * 32;
   {
-    const uint16_t* auxrow = a.Aaux + size_t(svalid ? src_row(a, sr) : 0) * KPa;
-    for (int c = shalf; c < KPa / 8; c += 2) {
-      u32x4 v = svalid ? *reinterpret_cast<const u32x4*>(auxrow + 8 * c) : u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(aux_s + srow * KPa + 8 * c) = v;
+    const float* xn = a.Axneg + size_t(src) * KNx;
+    for (int g = shalf; g < G; g += 2) xneg_s[g * kBlockRows + srow] = svalid ? xn[g] : 0.0f;
+    const uint16_t* xp = a.Apart + size_t(src) * KPx;
+    for (int c = shalf; c < KPx / 8; c += 2) {
+      u32x4 v = svalid ? *reinterpret_cast<const u32x4*>(xp + 8 * c) : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(xpart_s + srow * KPx + 8 * c) = v;
     }
   }
   u32x4 stage[4];
@@ -191,7 +207,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
     for (int u = 0; u < kRing; ++u) {
       const int g = g0 + u;
       if (g < G) {
-        const uint8_t* cur = abuf + (g & 1) * 8192;
+        const uint8_t* cur = abuf + (g & 1) * kAbufBytes;
         // next A tile into registers
         const bool more = g + 1 < G;
         if (more) {
@@ -222,12 +238,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         bf16x8 bf0[4], bf1[4];
         bf0[0] = unpack_word(w0.x); bf0[1] = unpack_word(w0.y); bf0[2] = unpack_word(w0.z); bf0[3] = unpack_word(w0.w);
         bf1[0] = unpack_word(w1.x); bf1[1] = unpack_word(w1.y); bf1[2] = unpack_word(w1.z); bf1[3] = unpack_word(w1.w);
+        const float* xg = xneg_s + g * kBlockRows;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][0], bf0[0], f32x16{}, 0, 0, 0);
-          f32x16 p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][0], bf1[0], f32x16{}, 0, 0, 0);
+          f32x16 p0 = chain_init(xg, rb, half);
+          f32x16 p1 = chain_init(xg, rb, half);
 #pragma unroll
-          for (int j = 1; j < 4; ++j) {
+          for (int j = 0; j < 4; ++j) {
             p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][j], bf0[j], p0, 0, 0, 0);
             p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][j], bf1[j], p1, 0, 0, 0);
           }
@@ -238,7 +255,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
           }
         }
         if (more) {
-          uint8_t* nxt = abuf + ((g + 1) & 1) * 8192;
+          uint8_t* nxt = abuf + ((g + 1) & 1) * kAbufBytes;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             *reinterpret_cast<u32x4*>(nxt + a_chunk_off(srow, shalf * 4 + i)) = stage[i];
@@ -248,46 +265,27 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
     }
   }
 
-  // ---- bias and offset correction: 3 extra K columns per group ------------
+  // ---- bias term: 3 extra K columns per group ------------------------------
   // Stage the biases of the 128 weight rows into the (now free) A buffers.
   uint16_t* b_st = reinterpret_cast<uint16_t*>(abuf);   // [G][128], G*256 B <= 16 KiB
   {
-    const int w_ = tid >> 6, cb_ = (tid >> 5) & 1, j_ = tid & 31;
-    int n_;
-    const QStack* st;
-    if constexpr (EPI == kEpiF32) {
-      n_ = nt * 128 + w_ * 64 + cb_ * 32 + j_;
-      st = &a.w0[stack];
-    } else {
-      n_ = nt * 64 + w_ * 32 + j_;
-      st = cb_ ? &a.w1[stack] : &a.w0[stack];
-    }
-    const uint16_t* bp = st->b + (size_t(el) * a.N + n_) * G;
+    const uint16_t* bp = st_row->b + (size_t(el) * a.N + n_row) * G;
     for (int g = 0; g < G; ++g) b_st[g * 128 + tid] = bp[g];
   }
   __syncthreads();
-  for (int st = 0; st < KPa / 16; ++st) {
+  for (int st = 0; st < KPx / 16; ++st) {
     bf16x8 a2[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
-      a2[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(aux_s + (rb * 32 + l32) * KPa + 16 * st + 8 * half));
+      a2[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xpart_s + (rb * 32 + l32) * KPx + 16 * st + 8 * half));
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int scol = cb ? scol1 : scol0;
       uint32_t v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int kk = 16 * st + 8 * half + i;
-        const int g = kk / 3;
-        const int t = kk - 3 * g;
-        uint32_t bits = 0;
-        if (g < G) {
-          const float s = bf16_to_f32(s_st[g * 128 + scol]);
-          const float b = bf16_to_f32(b_st[g * 128 + scol]);
-          const float bp = b - 128.0f * s;
-          bits = t == 2 ? split_lo(bp) : split_hi(bp);
-        }
-        v[i] = bits;
+        const int g = (16 * st + 8 * half + i) / 3;
+        v[i] = g < G ? uint32_t(b_st[g * 128 + scol]) : 0u;
       }
       u32x4 pk;
       pk.x = v[0] | (v[1] << 16);
@@ -332,27 +330,31 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
     const int row = ti.r0 + srow;
     u32x4 ch[4];
-    float part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ch[i] = *reinterpret_cast<const u32x4*>(hs + srow * 64 + shalf * 32 + 8 * i);
-      part += chunk_sum(ch[i]);
-    }
+    for (int i = 0; i < 4; ++i) ch[i] = *reinterpret_cast<const u32x4*>(hs + srow * 64 + shalf * 32 + 8 * i);
     if constexpr (EPI == kEpiSwigluInternal) {
-      const float X = part + __shfl_xor(part, 1, kWave);
+      double part = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part += chunk_sum_f64(ch[i]);
+      const float X = float(part + __shfl_xor(part, 1, kWave));
       if (row < ti.r1) {
         uint16_t* dst = out + size_t(row) * a.N + nt * 64 + shalf * 32;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = permute_chunk(ch[i]);
-        const int KPo = aux_cols(a.N);
-        uint16_t* ax = a.out_aux + size_t(row) * KPo;
+        const int Go = a.N / kGroup;
+        const int KPo = xpart_cols(a.N);
+        uint16_t* xp = a.out_part + size_t(row) * KPo;
+        float* xn = a.out_xneg + size_t(row) * xneg_cols(a.N);
         if (shalf == 0) {
-          const uint16_t hi = uint16_t(split_hi(X));
-          ax[3 * nt + 0] = hi;
-          ax[3 * nt + 1] = uint16_t(split_lo(X));
-          ax[3 * nt + 2] = hi;
+          uint16_t h, m, l;
+          split3_bf16(X, h, m, l);
+          xp[3 * nt + 0] = h;
+          xp[3 * nt + 1] = m;
+          xp[3 * nt + 2] = l;
+          xn[nt] = -128.0f * X;
         } else if (nt == 0) {
-          for (int c = 3 * (a.N / kGroup); c < KPo; ++c) ax[c] = 0;
+          for (int c = 3 * Go; c < KPo; ++c) xp[c] = 0;
+          for (int c = Go; c < xneg_cols(a.N); ++c) xn[c] = 0.0f;
         }
       }
     } else {
@@ -363,11 +365,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
       }
     }
   }
-}
-
-size_t gemm_lds_bytes(int K) {
-  const int G = K / kGroup;
-  return 2 * 8192 + size_t(kBlockRows) * aux_cols(K) * 2 + size_t(G) * 128 * 2;
 }
 
 hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream) {
@@ -389,13 +386,13 @@ hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipS
 }
 
 // ---------------------------------------------------------------------------
-// Activation preparation: permuted chunk order plus the group-sum side table
-// (hi, lo, hi of each 64-wide group's fp32 sum; zero padding).
-// 8 lanes per group, one 16-byte chunk each.
+// Activation preparation: permuted chunk order plus the group-sum tables.
+// 8 lanes per group, one 16-byte chunk each; group sums in fp64, rounded once.
 __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* A, int rows, int K, uint16_t* a_perm,
-                                                        uint16_t* a_aux) {
+                                                        float* a_xneg, uint16_t* a_part) {
   const int G = K / kGroup;
-  const int KP = aux_cols(K);
+  const int KPx = xpart_cols(K);
+  const int KNx = xneg_cols(K);
   const long gid = long(blockIdx.x) * blockDim.x + threadIdx.x;
   const long team = gid >> 3;
   const int sub = int(gid & 7);
@@ -405,29 +402,35 @@ __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* A, int r
   const int g = ok ? int(team % G) : 0;
   u32x4 v = u32x4{0, 0, 0, 0};
   if (ok) v = *reinterpret_cast<const u32x4*>(A + size_t(row) * K + g * kGroup + 8 * sub);
-  float s = chunk_sum(v);
+  double s = chunk_sum_f64(v);
   s += __shfl_xor(s, 1, kWave);
   s += __shfl_xor(s, 2, kWave);
   s += __shfl_xor(s, 4, kWave);
   if (!ok) return;
   *reinterpret_cast<u32x4*>(a_perm + size_t(row) * K + g * kGroup + 8 * sub) = permute_chunk(v);
-  uint16_t* ax = a_aux + size_t(row) * KP;
+  uint16_t* xp = a_part + size_t(row) * KPx;
+  float* xn = a_xneg + size_t(row) * KNx;
   if (sub == 0) {
-    const uint16_t hi = uint16_t(split_hi(s));
-    ax[3 * g] = hi;
-    ax[3 * g + 1] = uint16_t(split_lo(s));
-    ax[3 * g + 2] = hi;
+    const float X = float(s);
+    uint16_t h, m, l;
+    split3_bf16(X, h, m, l);
+    xp[3 * g] = h;
+    xp[3 * g + 1] = m;
+    xp[3 * g + 2] = l;
+    xn[g] = -128.0f * X;
   }
-  if (g == G - 1 && sub == 1)
-    for (int c = 3 * G; c < KP; ++c) ax[c] = 0;
+  if (g == G - 1 && sub == 1) {
+    for (int c = 3 * G; c < KPx; ++c) xp[c] = 0;
+    for (int c = G; c < KNx; ++c) xn[c] = 0.0f;
+  }
 }
 
-hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_aux,
-                            hipStream_t stream) {
+hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, float* a_xneg,
+                            uint16_t* a_part, hipStream_t stream) {
   const long threads = long(rows) * (K / kGroup) * 8;
   if (threads == 0) return hipSuccess;
   const unsigned blocks = unsigned((threads + 255) / 256);
-  hipLaunchKernelGGL(prep_rows_kernel, dim3(blocks), dim3(256), 0, stream, A, rows, K, a_perm, a_aux);
+  hipLaunchKernelGGL(prep_rows_kernel, dim3(blocks), dim3(256), 0, stream, A, rows, K, a_perm, a_xneg, a_part);
   return hipGetLastError();
 }
 

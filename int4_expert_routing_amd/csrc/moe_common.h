@@ -89,10 +89,37 @@ __device__ __forceinline__ float chunk_sum(u32x4 v) {
   return (a + b) + (c + d);
 }
 
+// Same sum in fp64 (exact for the 8 values: bf16 products of a sum stay far
+// inside fp64's 53-bit significand).
+__device__ __forceinline__ double chunk_sum_f64(u32x4 v) {
+  double a = double(bf16_lo_to_f32(v.x)) + double(bf16_hi_to_f32(v.x));
+  double b = double(bf16_lo_to_f32(v.y)) + double(bf16_hi_to_f32(v.y));
+  double c = double(bf16_lo_to_f32(v.z)) + double(bf16_hi_to_f32(v.z));
+  double d = double(bf16_lo_to_f32(v.w)) + double(bf16_hi_to_f32(v.w));
+  return (a + b) + (c + d);
+}
+
+// Split a float into three bf16 values whose exact sum is the float
+// (each step's remainder is exact in fp32).
+__device__ __forceinline__ void split3_bf16(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  const uint32_t h = f32_to_bf16_rne(v);
+  const float r1 = v - __uint_as_float(h << 16);
+  const uint32_t m = f32_to_bf16_rne(r1);
+  const float r2 = r1 - __uint_as_float(m << 16);
+  hi = uint16_t(h);
+  mid = uint16_t(m);
+  lo = uint16_t(f32_to_bf16_rne(r2));
+}
+
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Number of bf16 entries per row of the group-sum side table: three per
-// 64-wide group (hi, lo, hi of the group sum), padded to whole MFMA K steps.
-__host__ __device__ constexpr int aux_cols(int K) { return ceil_div(3 * (K / kGroup), 16) * 16; }
+// Per activation row the GEMM needs each 64-wide group's sum X_g twice:
+//   * as float -128*X_g (the starting value of that group's MFMA chain), in a
+//     table of xneg_cols(K) floats per row (groups padded to a multiple of 4);
+//   * split exactly into three bf16 parts (hi, mid, lo) for the bias term
+//     sum_g b_g X_g, in a table of xpart_cols(K) bf16 per row (3 per group,
+//     padded to whole MFMA K steps).
+__host__ __device__ constexpr int xneg_cols(int K) { return ceil_div(K / kGroup, 4) * 4; }
+__host__ __device__ constexpr int xpart_cols(int K) { return ceil_div(3 * (K / kGroup), 16) * 16; }
 
 }  // namespace moe

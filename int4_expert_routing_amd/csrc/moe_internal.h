@@ -8,7 +8,7 @@ namespace moe {
 
 constexpr int kMaxExperts = MOE_MAX_EXPERTS;
 constexpr int kMaxTopk = MOE_MAX_TOPK;
-constexpr int kMaxK = 4096;  // largest reduction size of the grouped GEMM
+constexpr int kMaxK = 2048;  // largest reduction size of the grouped GEMM (LDS budget)
 
 struct RouteArgs {
   const uint16_t* x;        // bf16 [T][H] (router GEMM input) or null
@@ -56,7 +56,8 @@ enum GemmEpilogue { kEpiF32 = 0, kEpiSwigluNatural = 1, kEpiSwigluInternal = 2 }
 
 struct GemmArgs {
   const uint16_t* A;        // activations in the permuted chunk order [a_rows][K]
-  const uint16_t* Aaux;     // group-sum side table [a_rows][aux_cols(K)]
+  const float* Axneg;       // -128 * group sums [a_rows][xneg_cols(K)]
+  const uint16_t* Apart;    // group sums split in three bf16 parts [a_rows][xpart_cols(K)]
   const int32_t* sorted_rows;  // gather for routed rows: src = sorted_rows[r] / row_div; null = identity
   int row_div;
   int routed_rows;          // rows [0, routed_rows) belong to routed tiles
@@ -71,13 +72,14 @@ struct GemmArgs {
   int shared_rows;
   int N, K, NT;             // NT = column tiles per row tile
   void* out;                // f32 [rows][N], or bf16 [rows][N]
-  uint16_t* out_aux;        // group-sum table of the bf16 output (internal SwiGLU only)
+  float* out_xneg;          // group-sum tables of the bf16 output (internal SwiGLU only)
+  uint16_t* out_part;
 };
 
 hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream);
 
-hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_aux,
-                            hipStream_t stream);
+hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, float* a_xneg,
+                            uint16_t* a_part, hipStream_t stream);
 
 hipError_t launch_combine(const float* Y, const float* w, const int32_t* row_of_pair, int T, int k, int H,
                           int shared_row0, uint16_t* y, hipStream_t stream);

@@ -58,7 +58,7 @@ def test_check_dims_and_workspace(lib):
         (4096, 2048, 500, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # I not a multiple of 64
         (-1, 2048, 512, 256, 8, 0): _lib.MOE_ERR_SHAPE,          # negative T
         (4096, 2048, 512, 256, 8, 32): _lib.MOE_ERR_UNSUPPORTED,  # other tile height
-        (16, 8192, 512, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,    # K beyond the GEMM limit
+        (16, 4096, 512, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,    # K beyond the GEMM limit
     }
     for dims, want in cases.items():
         assert lib.moe_check_dims(ctypes.byref(MoeDims(*dims))) == want, dims
