@@ -41,7 +41,7 @@ extern "C" {
 #define MOE_Q4_GROUP 64
 /* Rows per GEMM tile; tile maps passed to moe_grouped_gemm_q4 and built for
  * moe_layer_forward use this block size. */
-#define MOE_GEMM_BLOCK_ROWS 64
+#define MOE_GEMM_BLOCK_ROWS 128
 /* Largest supported expert count and top-k. */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
@@ -147,7 +147,8 @@ int32_t moe_max_tiles(const moe_dims* dims);
  *
  *   A           device bf16 [a_rows][K]
  *   W0, W1      host structs; W1 only for SWIGLU (same n_experts, N, K as W0),
- *               K % 64 == 0, K <= 2048; N % 64 == 0 (SWIGLU) or N % 128 == 0 (STORE_F32)
+ *               K % 128 == 0, K <= 2048; N % 64 == 0 (SWIGLU) or N % 128 == 0 (STORE_F32);
+ *               q 16-byte aligned, s and b 4-byte aligned
  *   offsets, tile_map, num_tiles  device, as produced by moe_route with
  *               block_rows = MOE_GEMM_BLOCK_ROWS; max_tiles bounds *num_tiles
  *   workspace   device, at least moe_gemm_workspace_bytes(a_rows, K) bytes
@@ -177,7 +178,7 @@ size_t moe_gemm_workspace_bytes(int32_t a_rows, int32_t K);
  *   gate, up     host structs, n_experts = E, N = I, K = H
  *   down         host struct,  n_experts = E, N = H, K = I
  *   sh_gate, sh_up, sh_down  the shared expert, n_experts = 1, same shapes
- *   dims         host; H % 128 == 0, I % 64 == 0, H and I <= 2048,
+ *   dims         host; H % 128 == 0, I % 128 == 0, H and I <= 2048,
  *                block_rows = 0 or MOE_GEMM_BLOCK_ROWS
  *   y            device bf16 [T][H]
  *   logits_out   device float [T][E] or NULL: the logits routing used (biased)

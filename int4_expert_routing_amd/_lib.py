@@ -24,7 +24,7 @@ MOE_EPI_STORE_F32 = 0
 MOE_EPI_SWIGLU_BF16 = 1
 
 MOE_Q4_GROUP = 64
-MOE_GEMM_BLOCK_ROWS = 64
+MOE_GEMM_BLOCK_ROWS = 128
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
 

@@ -26,27 +26,44 @@
 // the order [0,4,1,5,2,6,3,7] (prep kernel / SwiGLU epilogue), so both MFMA
 // operands list the same K indices in the same slots.
 //
-// Tiling (one workgroup = 2 wave64s = 128 threads):
-//   rows: 64 per tile (two 32-row MFMA blocks per wave);
-//   cols: SwiGLU: 64 gate + 64 up columns (wave w: gate and up columns
-//         32w..32w+31, so the SwiGLU pairs sit in the same lane and register);
-//         STORE_F32: 128 columns (wave w: 64w..64w+63).
-//   MFMA v_mfma_f32_32x32x16_bf16; per 64-wide group each wave issues 16 MFMAs.
-//   A tiles go global -> registers -> LDS (double buffered, XOR-swizzled 16-byte
-//   chunks); weight codes go global -> registers directly (each wave reads only
-//   its own columns), 4 groups in flight.
+// Tiling (one workgroup = 4 wave64s = 256 threads, tile = up to 128 rows):
+//   each wave owns 32 output columns of one weight matrix and all rows of the
+//   tile, as up to four 32-row MFMA blocks; only blocks that hold real rows are
+//   computed (the kernel is instantiated per live-block count), so MFMA work
+//   follows the real row count at 32-row granularity.
+//   SwiGLU: waves 0,1 = gate columns 0-31, 32-63; waves 2,3 = up columns
+//           0-31, 32-63 of the workgroup's 64 (gate and up meet in LDS at the end);
+//   STORE_F32: waves 0..3 = columns 0-31, ..., 96-127.
+//   MFMA v_mfma_f32_32x32x16_bf16: per 64-wide group a wave issues one chain
+//   of 4 MFMAs per row block; one group's weight codes are unpacked once and
+//   reused by every row block.
+// Streaming: per group, the activation tile (128 rows x 64 bf16, 16-byte chunks
+//   XOR-swizzled by row), the weight codes of the 128 columns and the 128 rows'
+//   -128*X_g land in a 3-slot LDS ring through buffer loads that write LDS
+//   directly (no registers, one scalar offset per group), issued two groups
+//   ahead; one s_waitcnt + s_barrier per group.
 // Work mapping: blockIdx.x = tile * NT + column_tile; column tiles are the fast
-// index so the 8 column tiles of a row tile land on the 8 XCDs and every XCD
-// keeps its own 1/8 of each expert's weights in its L2.
+// index so the column tiles of a row tile spread over the 8 XCDs and each XCD
+// keeps its own slice of every expert's weights in its L2.
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kGemmThreads = 128;
-constexpr int kRing = 4;            // groups of weight codes in flight per wave
+constexpr int kGemmThreads = 256;
+constexpr int kRing = 3;                 // LDS ring slots
 constexpr uint32_t kMagic = 0x43004300u;  // two bf16 128.0
 constexpr uint32_t kNib = 0x000F000Fu;
-constexpr int kAbufBytes = 8192;    // one A buffer: 64 rows x 64 bf16
+constexpr int kSlotA = 0;                // 128 rows x 128 B
+constexpr int kSlotB = 16384;            // 4 waves x 64 lanes x 16 B of weight codes
+constexpr int kSlotX = 20480;            // 128 floats: -128 * X_g
+constexpr int kSlotBytes = 20992;
+constexpr int kOpsPerGroup = 6;          // buffer->LDS loads per wave per group
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
+// s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm6 = 0x0F76;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct TileInfo {
   int e, r0, r1;
@@ -81,23 +98,83 @@ __device__ __forceinline__ bf16x8 unpack_word(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// LDS byte offset of 16-byte chunk c (0..7) of row m in one A buffer.
+// LDS byte offset of 16-byte chunk c (0..7) of row m in one activation tile.
 __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ (m & 7))) * 16; }
 
-// Starting accumulator of a group's chain for row block rb: lane holds rows
-// rb*32 + 8j + 4*half + i (j, i = 0..3), the 32x32 MFMA output layout.
-__device__ __forceinline__ f32x16 chain_init(const float* xneg_g, int rb, int half) {
-  const f32x4* p = reinterpret_cast<const f32x4*>(xneg_g + rb * 32 + 4 * half);
-  const f32x4 a = p[0], b = p[2], c = p[4], d = p[6];
-  return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
-}
+__device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
 
 size_t gemm_lds_bytes(int K) {
   const int G = K / kGroup;
-  return 2 * kAbufBytes                           // A double buffer
-         + size_t(G) * kBlockRows * 4              // -128 X_g  [G][64]
-         + size_t(kBlockRows) * xpart_cols(K) * 2  // X_g parts [64][xpart_cols]
-         + size_t(G) * 128 * 2;                    // scales    [G][128]
+  return size_t(kRing) * kSlotBytes + size_t(kBlockRows) * G * 2;
+}
+
+// Per-wave streaming state: buffer descriptors, per-lane byte offsets.
+struct Stream {
+  __amdgpu_buffer_rsrc_t ra, rb, rx;
+  uint32_t va[4];    // activation chunk offsets (4 instructions)
+  uint32_t vb;       // weight-code offset
+  uint32_t vx;       // -128*X_g offset (lanes 0..31)
+};
+
+__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int g, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + wave * 4096 + i * 1024), 16, st.va[i],
+                                             g * (kGroup * 2), 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb, lds(slot + kSlotB + wave * 1024), 16, st.vb, g * 32, 0, 0);
+  if (lane < 32)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rx, lds(slot + kSlotX + wave * 128), 4, st.vx, g * 4, 0, 0);
+}
+
+// One 64-wide group: unpack the wave's weight codes, then per live row block a
+// chain of 4 MFMAs started at -128*X_g, folded into acc with the group scale.
+template <int NRB>
+__device__ __forceinline__ void group_compute(const uint8_t* slot, float sc, int wave, int lane, f32x16 (&acc)[4]) {
+  const int l32 = lane & 31, half = lane >> 5;
+  const u32x4 w = *reinterpret_cast<const u32x4*>(slot + kSlotB + wave * 1024 + lane * 16);
+  const bf16x8 b0 = unpack_word(w.x), b1 = unpack_word(w.y), b2 = unpack_word(w.z), b3 = unpack_word(w.w);
+  const float* xg = reinterpret_cast<const float*>(slot + kSlotX);
+  f32x16 p[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int m = rb * 32 + l32;
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 0)));
+    const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 1)));
+    const bf16x8 a2 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 2)));
+    const bf16x8 a3 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 3)));
+    // the lane's accumulator rows: rb*32 + 8j + 4*half + i
+    const f32x4* xp = reinterpret_cast<const f32x4*>(xg + rb * 32 + 4 * half);
+    const f32x4 c0 = xp[0], c1 = xp[2], c2 = xp[4], c3 = xp[6];
+    f32x16 q = f32x16{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                      c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, q, 0, 0, 0);
+    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, q, 0, 0, 0);
+    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2, q, 0, 0, 0);
+    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b3, q, 0, 0, 0);
+    p[rb] = q;
+  }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[rb][r] = __builtin_fmaf(sc, p[rb][r], acc[rb][r]);
+}
+
+template <int NRB>
+__device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, const uint16_t* s_wave, int G, int wave,
+                                          int lane, f32x16 (&acc)[4]) {
+  const int l32 = lane & 31;
+  for (int g = 0; g < G; ++g) {
+    // group g landed for this wave; the barrier makes it so for every wave and
+    // frees slot (g+2)%3, last read in iteration g-1
+    if (g + 1 < G)
+      __builtin_amdgcn_s_waitcnt(kWaitVm6);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_barrier();
+    if (g + 2 < G) issue_group(st, ring + ((g + 2) % kRing) * kSlotBytes, g + 2, wave, lane);
+    const float sc = bf16_to_f32(s_wave[l32 * G + g]);
+    group_compute<NRB>(ring + (g % kRing) * kSlotBytes, sc, wave, lane, acc);
+  }
 }
 
 template <int EPI>
@@ -107,10 +184,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   const int G = K / kGroup;
   const int KPx = xpart_cols(K);
   const int KNx = xneg_cols(K);
-  uint8_t* abuf = smem;
-  float* xneg_s = reinterpret_cast<float*>(smem + 2 * kAbufBytes);        // [G][64]
-  uint16_t* xpart_s = reinterpret_cast<uint16_t*>(xneg_s + G * kBlockRows);  // [64][KPx]
-  uint16_t* s_st = xpart_s + kBlockRows * KPx;                             // [G][128]
+  uint8_t* ring = smem;
+  uint16_t* s_st = reinterpret_cast<uint16_t*>(smem + kRing * kSlotBytes);   // [128 weight rows][G]
 
   const int nt = blockIdx.x % a.NT;
   const int tile = blockIdx.x / a.NT;
@@ -118,184 +193,106 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   if (!tile_info(a, tile, ti)) return;
   const int stack = ti.e == a.E ? 1 : 0;
   const int el = stack ? 0 : ti.e;
+  const int nrows = ti.r1 - ti.r0;
+  const int nrb = (nrows + 31) >> 5;     // 32-row blocks holding real rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // ---- weight rows owned by this wave: cb = 0, 1 --------------------------
-  const size_t qrow = size_t(K / 8);
-  const QStack& m0 = a.w0[stack];
-  const QStack& m1 = (EPI == kEpiF32) ? a.w0[stack] : a.w1[stack];
-  int ncol[2];
+  // ---- this wave's weight matrix and its 32 columns ------------------------
+  int col0;
+  const QStack* mat;
   if constexpr (EPI == kEpiF32) {
-    ncol[0] = nt * 128 + wave * 64 + l32;
-    ncol[1] = ncol[0] + 32;
+    col0 = nt * 128 + wave * 32;
+    mat = &a.w0[stack];
   } else {
-    ncol[0] = nt * 64 + wave * 32 + l32;
-    ncol[1] = ncol[0];
+    col0 = nt * 64 + (wave & 1) * 32;
+    mat = (wave >> 1) ? &a.w1[stack] : &a.w0[stack];
   }
-  const uint32_t* qp[2];
-  qp[0] = m0.q + (size_t(el) * a.N + ncol[0]) * qrow + 4 * half;
-  qp[1] = m1.q + (size_t(el) * a.N + ncol[1]) * qrow + 4 * half;
+  const size_t wrow0 = size_t(el) * a.N + col0;
+  const uint32_t* q_wave = mat->q + wrow0 * size_t(K / 8);
+  const uint16_t* s_glob = mat->s + wrow0 * size_t(G);
+  const uint16_t* b_glob = mat->b + wrow0 * size_t(G);
+  const int ncol = col0 + l32;
 
-  // thread t <-> weight row (wave t/64, cb (t/32)%2, lane t%32) of the workgroup
-  const QStack* st_row;
-  int n_row;
+  // ---- streaming descriptors and per-lane offsets -------------------------
+  Stream st;
+  st.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.A), 0, 0x7FFFFFFF, kRsrcWord3);
+  st.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q_wave), 0, 0x7FFFFFFF, kRsrcWord3);
+  st.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.Axneg), 0, 0x7FFFFFFF, kRsrcWord3);
   {
-    const int w_ = tid >> 6, cb_ = (tid >> 5) & 1, j_ = tid & 31;
-    if constexpr (EPI == kEpiF32) {
-      n_row = nt * 128 + w_ * 64 + cb_ * 32 + j_;
-      st_row = &a.w0[stack];
-    } else {
-      n_row = nt * 64 + w_ * 32 + j_;
-      st_row = cb_ ? &a.w1[stack] : &a.w0[stack];
+    // activation DMA i of this wave fills chunk positions wave*256 + i*64 + lane:
+    // row m = wave*32 + i*8 + lane/8, swizzled chunk lane%8 = logical chunk cidx
+    const int cidx = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wave * 32 + i * 8 + (lane >> 3);
+      const int r = ti.r0 + min(m, nrows - 1);     // padding rows re-read the last real row
+      st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
     }
+    st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
+    const int mx = wave * 32 + l32;
+    st.vx = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KNx * 4);
   }
+
+  // ---- prologue: scales of the wave's 32 weight rows (contiguous), groups 0, 1
   {
-    const uint16_t* sp = st_row->s + (size_t(el) * a.N + n_row) * G;
-    for (int g = 0; g < G; ++g) s_st[g * 128 + tid] = sp[g];
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s_glob), 0, 0x7FFFFFFF, kRsrcWord3);
+    const int dwords = 16 * G;            // 32 rows x G bf16
+    for (int p0 = 0; p0 < dwords; p0 += 64)
+      if (p0 + lane < dwords)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(s_st + wave * 32 * G + 2 * p0), 4, uint32_t((p0 + lane) * 4),
+                                                 0, 0, 0);
   }
+  issue_group(st, ring, 0, wave, lane);
+  if (G > 1) issue_group(st, ring + kSlotBytes, 1, wave, lane);
 
-  // ---- prologue: side tables and the first A tile -------------------------
-  const int srow = tid >> 1;          // staging row 0..63
-  const int shalf = tid & 1;          // which 32-element half of a group
-  const int sr = ti.r0 + srow;
-  const bool svalid = sr < ti.r1;
-  const int src = svalid ? src_row(a, sr) : 0;
-  const uint16_t* arow = a.A + size_t(src) * K + shalf * 32;
-  {
-    const float* xn = a.Axneg + size_t(src) * KNx;
-    for (int g = shalf; g < G; g += 2) xneg_s[g * kBlockRows + srow] = svalid ? xn[g] : 0.0f;
-    const uint16_t* xp = a.Apart + size_t(src) * KPx;
-    for (int c = shalf; c < KPx / 8; c += 2) {
-      u32x4 v = svalid ? *reinterpret_cast<const u32x4*>(xp + 8 * c) : u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(xpart_s + srow * KPx + 8 * c) = v;
-    }
+  f32x16 acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x16{};
+  const uint16_t* s_wave = s_st + wave * 32 * G;
+  switch (nrb) {
+    case 1: main_loop<1>(st, ring, s_wave, G, wave, lane, acc); break;
+    case 2: main_loop<2>(st, ring, s_wave, G, wave, lane, acc); break;
+    case 3: main_loop<3>(st, ring, s_wave, G, wave, lane, acc); break;
+    default: main_loop<4>(st, ring, s_wave, G, wave, lane, acc); break;
   }
-  u32x4 stage[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    stage[i] = svalid ? *reinterpret_cast<const u32x4*>(arow + 8 * i) : u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<u32x4*>(abuf + a_chunk_off(srow, shalf * 4 + i)) = stage[i];
-
-  // weight-code ring: slot u holds group g with g % kRing == u
-  u32x4 ring[kRing][2];
-#pragma unroll
-  for (int u = 0; u < kRing; ++u) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-      ring[u][cb] = u < G ? *reinterpret_cast<const u32x4*>(qp[cb] + u * 8) : u32x4{0, 0, 0, 0};
-  }
-  __syncthreads();
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16{};
-
-  const int scol0 = (wave * 2 + 0) * 32 + l32;
-  const int scol1 = (wave * 2 + 1) * 32 + l32;
-
-  for (int g0 = 0; g0 < G; g0 += kRing) {
-#pragma unroll
-    for (int u = 0; u < kRing; ++u) {
-      const int g = g0 + u;
-      if (g < G) {
-        const uint8_t* cur = abuf + (g & 1) * kAbufBytes;
-        // next A tile into registers
-        const bool more = g + 1 < G;
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            stage[i] = svalid ? *reinterpret_cast<const u32x4*>(arow + (g + 1) * kGroup + 8 * i)
-                              : u32x4{0, 0, 0, 0};
-        }
-        // A fragments of this group
-        bf16x8 af[2][4];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const int m = rb * 32 + l32;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            af[rb][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + a_chunk_off(m, 4 * half + j)));
-        }
-        const float s0 = bf16_to_f32(s_st[g * 128 + scol0]);
-        const float s1 = bf16_to_f32(s_st[g * 128 + scol1]);
-        const u32x4 w0 = ring[u][0];
-        const u32x4 w1 = ring[u][1];
-        // refill this ring slot with group g + kRing
-        if (g + kRing < G) {
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            ring[u][cb] = *reinterpret_cast<const u32x4*>(qp[cb] + (g + kRing) * 8);
-        }
-        bf16x8 bf0[4], bf1[4];
-        bf0[0] = unpack_word(w0.x); bf0[1] = unpack_word(w0.y); bf0[2] = unpack_word(w0.z); bf0[3] = unpack_word(w0.w);
-        bf1[0] = unpack_word(w1.x); bf1[1] = unpack_word(w1.y); bf1[2] = unpack_word(w1.z); bf1[3] = unpack_word(w1.w);
-        const float* xg = xneg_s + g * kBlockRows;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          f32x16 p0 = chain_init(xg, rb, half);
-          f32x16 p1 = chain_init(xg, rb, half);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][j], bf0[j], p0, 0, 0, 0);
-            p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][j], bf1[j], p1, 0, 0, 0);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc[rb][0][r] = __builtin_fmaf(s0, p0[r], acc[rb][0][r]);
-            acc[rb][1][r] = __builtin_fmaf(s1, p1[r], acc[rb][1][r]);
-          }
-        }
-        if (more) {
-          uint8_t* nxt = abuf + ((g + 1) & 1) * kAbufBytes;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4*>(nxt + a_chunk_off(srow, shalf * 4 + i)) = stage[i];
-        }
-        __syncthreads();
-      }
-    }
-  }
+  __syncthreads();   // every wave is done with the ring
 
   // ---- bias term: 3 extra K columns per group ------------------------------
-  // Stage the biases of the 128 weight rows into the (now free) A buffers.
-  uint16_t* b_st = reinterpret_cast<uint16_t*>(abuf);   // [G][128], G*256 B <= 16 KiB
-  {
-    const uint16_t* bp = st_row->b + (size_t(el) * a.N + n_row) * G;
-    for (int g = 0; g < G; ++g) b_st[g * 128 + tid] = bp[g];
+  uint16_t* xpart_s = reinterpret_cast<uint16_t*>(ring);   // [128][KPx]
+  for (int i = tid; i < kBlockRows * (KPx / 8); i += kGemmThreads) {
+    const int m = i / (KPx / 8), c = i % (KPx / 8);
+    const int r = ti.r0 + min(m, nrows - 1);
+    *reinterpret_cast<u32x4*>(xpart_s + m * KPx + 8 * c) =
+        *reinterpret_cast<const u32x4*>(a.Apart + size_t(src_row(a, r)) * KPx + 8 * c);
   }
   __syncthreads();
-  for (int st = 0; st < KPx / 16; ++st) {
-    bf16x8 a2[2];
+  const uint16_t* bp = b_glob + size_t(l32) * G;
+  for (int sk = 0; sk < KPx / 16; ++sk) {
+    uint32_t v[8];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      a2[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xpart_s + (rb * 32 + l32) * KPx + 16 * st + 8 * half));
+    for (int i = 0; i < 8; ++i) {
+      const int g = (16 * sk + 8 * half + i) / 3;
+      v[i] = g < G ? uint32_t(bp[g]) : 0u;
+    }
+    u32x4 pk;
+    pk.x = v[0] | (v[1] << 16);
+    pk.y = v[2] | (v[3] << 16);
+    pk.z = v[4] | (v[5] << 16);
+    pk.w = v[6] | (v[7] << 16);
+    const bf16x8 bb = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int scol = cb ? scol1 : scol0;
-      uint32_t v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int g = (16 * st + 8 * half + i) / 3;
-        v[i] = g < G ? uint32_t(b_st[g * 128 + scol]) : 0u;
+    for (int rb = 0; rb < 4; ++rb) {
+      if (rb < nrb) {
+        const bf16x8 xa =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xpart_s + (rb * 32 + l32) * KPx + 16 * sk + 8 * half));
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bb, acc[rb], 0, 0, 0);
       }
-      u32x4 pk;
-      pk.x = v[0] | (v[1] << 16);
-      pk.y = v[2] | (v[3] << 16);
-      pk.z = v[4] | (v[5] << 16);
-      pk.w = v[6] | (v[7] << 16);
-      const bf16x8 b2 = __builtin_bit_cast(bf16x8, pk);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[rb], b2, acc[rb][cb], 0, 0, 0);
     }
   }
 
@@ -303,31 +300,42 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   if constexpr (EPI == kEpiF32) {
     float* out = reinterpret_cast<float*>(a.out);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int row = ti.r0 + m;
-        if (row < ti.r1) {
-          out[size_t(row) * a.N + ncol[0]] = acc[rb][0][r];
-          out[size_t(row) * a.N + ncol[1]] = acc[rb][1][r];
-        }
+        if (m < nrows) out[size_t(ti.r0 + m) * a.N + ncol] = acc[rb][r];
       }
   } else {
-    __syncthreads();   // everyone is done with b_st / abuf
-    uint16_t* hs = reinterpret_cast<uint16_t*>(abuf);   // [64][64] bf16, natural order
+    __syncthreads();   // everyone is done with xpart_s
+    float* gate_s = reinterpret_cast<float*>(ring);                          // [128][64] fp32
+    uint16_t* hs = reinterpret_cast<uint16_t*>(ring + kBlockRows * 64 * 4);  // [128][64] bf16
+    const int col = (wave & 1) * 32 + l32;
+    if (wave < 2) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const float gv = acc[rb][0][r];
-        const float uv = acc[rb][1][r];
-        const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        hs[m * 64 + wave * 32 + l32] = uint16_t(f32_to_bf16_rne(hv));
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          gate_s[m * 64 + col] = acc[rb][r];
+        }
+    }
+    __syncthreads();
+    if (wave >= 2) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float gv = gate_s[m * 64 + col];
+          const float uv = acc[rb][r];
+          const float hv = gv / (1.0f + __expf(-gv)) * uv;
+          hs[m * 64 + col] = uint16_t(f32_to_bf16_rne(hv));
+        }
+    }
     __syncthreads();
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    const int srow = tid >> 1, shalf = tid & 1;
     const int row = ti.r0 + srow;
     u32x4 ch[4];
 #pragma unroll
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) part += chunk_sum_f64(ch[i]);
       const float X = float(part + __shfl_xor(part, 1, kWave));
-      if (row < ti.r1) {
+      if (srow < nrows) {
         uint16_t* dst = out + size_t(row) * a.N + nt * 64 + shalf * 32;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = permute_chunk(ch[i]);
@@ -358,7 +366,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         }
       }
     } else {
-      if (row < ti.r1) {
+      if (srow < nrows) {
         uint16_t* dst = out + size_t(row) * a.N + nt * 64 + shalf * 32;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = ch[i];

@@ -76,7 +76,7 @@ int check_route_dims(const moe_dims* d) {
 int check_layer_dims(const moe_dims* d) {
   const int st = check_route_dims(d);
   if (st != MOE_OK) return st;
-  if (d->H < 128 || d->I < 64 || d->H % 128 != 0 || d->I % 64 != 0) return MOE_ERR_SHAPE;
+  if (d->H < 128 || d->I < 128 || d->H % 128 != 0 || d->I % 128 != 0) return MOE_ERR_SHAPE;
   if (d->H > kMaxK || d->I > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (d->block_rows != 0 && d->block_rows != kBlockRows) return MOE_ERR_UNSUPPORTED;
   if (int64_t(d->T) * (d->k + 1) * d->H > (int64_t(1) << 40)) return MOE_ERR_SHAPE;
@@ -88,7 +88,7 @@ int check_weights(const moe_q4_weights* w, int n, int N, int K) {
   if (!w->q || !w->s || !w->b) return MOE_ERR_NULL;
   if (w->n_experts != n || w->N != N || w->K != K) return MOE_ERR_SHAPE;
   if (!aligned16(w->q)) return MOE_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(w->s) & 1u) || (reinterpret_cast<uintptr_t>(w->b) & 1u)) return MOE_ERR_ALIGN;
+  if (!aligned4(w->s) || !aligned4(w->b)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -190,7 +190,7 @@ int moe_grouped_gemm_q4(const uint16_t* A, int32_t a_rows, const int32_t* sorted
   if (a_rows < 0 || max_tiles < 0) return MOE_ERR_SHAPE;
   if (sorted_rows && row_div < 1) return MOE_ERR_SHAPE;
   const int n = W0->n_experts, N = W0->N, K = W0->K;
-  if (n < 1 || N < 1 || K < kGroup || K % kGroup) return MOE_ERR_SHAPE;
+  if (n < 1 || N < 1 || K < 2 * kGroup || K % (2 * kGroup)) return MOE_ERR_SHAPE;
   if (K > kMaxK) return MOE_ERR_UNSUPPORTED;
   int st = check_weights(W0, n, N, K);
   if (st != MOE_OK) return st;
@@ -292,7 +292,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   ra.x = x;
   ra.wr = router_w;
   ra.bias = logit_bias;
-  ra.logits_out = logits_out;
+  ra.logits_out = logits_out ? logits_out : at<float>(ws, L.logits);
   ra.topk_ids = ids;
   ra.topk_w = wts;
   ra.block_counts = at<int32_t>(ws, L.block_counts);

@@ -7,7 +7,7 @@
 namespace moe {
 
 constexpr int kGroup = 64;        // weights per quantisation group along K
-constexpr int kBlockRows = 64;    // rows per GEMM tile
+constexpr int kBlockRows = 128;   // rows per GEMM tile
 constexpr int kRouteTokens = 32;  // tokens per routing workgroup
 constexpr int kWave = 64;
 

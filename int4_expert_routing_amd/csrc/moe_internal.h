@@ -15,7 +15,7 @@ struct RouteArgs {
   const uint16_t* wr;       // bf16 [E][H]
   const float* logits_in;   // float [T][E] when logits are given
   const float* bias;        // float [E] or null
-  float* logits_out;        // float [T][E] or null
+  float* logits_out;        // float [T][E]: router GEMM output (layer path)
   int32_t* topk_ids;        // [T][k]
   float* topk_w;            // [T][k]
   int32_t* block_counts;    // [nblk][E]

@@ -4,11 +4,12 @@
 // Technical Details, Model bullet: the router picks 8 of 256 experts; prefill
 // bullet: routing histogram, prefix scan, scatter and block map stay on the GPU).
 //
-// Three launches on one stream:
-//   1. route_topk_kernel  - one workgroup per 32 tokens: logits (bf16 MFMA with
-//      fp32 accumulation, or read from memory), top-k by the key (logit desc,
-//      expert asc), softmax over the chosen k, the block's expert histogram and
-//      each pair's rank among the block's pairs of the same expert.
+// Launches on one stream:
+//   0. router_logits_kernel (layer path only) - logits = x W_r^T (+ bias) with
+//      bf16 MFMA and fp32 accumulation, 32 tokens x 64 experts per workgroup.
+//   1. route_topk_kernel  - one workgroup per 32 tokens: top-k by the key
+//      (logit desc, expert asc), softmax over the chosen k, the block's expert
+//      histogram and each pair's rank among the block's pairs of the same expert.
 //   2. route_scan_kernel  - one workgroup: per-expert scan over blocks, exclusive
 //      scan over experts (offsets), and the tile list of the block map.
 //   3. route_scatter_kernel - one workgroup per 32 tokens: final row of each
@@ -20,9 +21,78 @@
 namespace moe {
 
 constexpr int kRouteThreads = 256;
-constexpr int kMaxKeysPerLane = kMaxExperts / kWave;  // 8
+constexpr int kMaxKeysPerLane = kMaxExperts / kWave;
 
-template <bool FROM_X>
+// Router GEMM: logits[t][e] = fp32(sum_h x[t][h] W_r[e][h]) + bias[e] for a
+// 32-token x 64-expert tile per workgroup. The four waves split K in 64-wide
+// chunks (wave w takes chunks w, w+4, ...), accumulate two 32x32 blocks each
+// with bf16 MFMA, prefetch the next chunk while multiplying the current one,
+// and reduce their partial sums through LDS.
+__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ wr,
+                                                                     const float* __restrict__ bias, int T, int H,
+                                                                     int E, float* __restrict__ logits) {
+  __shared__ float red[4][2][16][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int t0 = blockIdx.x * kRouteTokens;
+  const int e0 = blockIdx.y * 64;
+  const int nt = min(kRouteTokens, T - t0);
+  const bool row_ok = l32 < nt;
+  const int n0 = e0 + l32, n1 = e0 + 32 + l32;
+  const bool ok0 = n0 < E, ok1 = n1 < E;
+  const uint16_t* xr = x + size_t(t0 + (row_ok ? l32 : 0)) * H + 32 * half;
+  const uint16_t* w0 = wr + size_t(ok0 ? n0 : 0) * H + 32 * half;
+  const uint16_t* w1 = wr + size_t(ok1 ? n1 : 0) * H + 32 * half;
+  const int nchunks = H / 64;
+  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  u32x4 ca[4], cb0[4], cb1[4];
+  auto load = [&](int c, u32x4 (&A)[4], u32x4 (&B0)[4], u32x4 (&B1)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      A[j] = row_ok ? *reinterpret_cast<const u32x4*>(xr + c * 64 + 8 * j) : u32x4{0, 0, 0, 0};
+      B0[j] = ok0 ? *reinterpret_cast<const u32x4*>(w0 + c * 64 + 8 * j) : u32x4{0, 0, 0, 0};
+      B1[j] = ok1 ? *reinterpret_cast<const u32x4*>(w1 + c * 64 + 8 * j) : u32x4{0, 0, 0, 0};
+    }
+  };
+  int c = wave;
+  if (c < nchunks) load(c, ca, cb0, cb1);
+  while (c < nchunks) {
+    u32x4 na[4], nb0[4], nb1[4];
+    const int cn = c + 4;
+    if (cn < nchunks) load(cn, na, nb0, nb1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, ca[j]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, cb0[j]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, cb1[j]), acc1, 0, 0, 0);
+    }
+    if (cn < nchunks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ca[j] = na[j];
+        cb0[j] = nb0[j];
+        cb1[j] = nb1[j];
+      }
+    }
+    c = cn;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    red[wave][0][r][lane] = acc0[r];
+    red[wave][1][r][lane] = acc1[r];
+  }
+  __syncthreads();
+  // output element (eb, r, lane): token 8(r/4) + 4*half + r%4, expert e0 + 32 eb + lane%32
+  for (int i = tid; i < 2 * 16 * 64; i += kRouteThreads) {
+    const int ln = i & 63, r = (i >> 6) & 15, eb = i >> 10;
+    const float v = red[0][eb][r][ln] + red[1][eb][r][ln] + red[2][eb][r][ln] + red[3][eb][r][ln];
+    const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+    const int n = e0 + 32 * eb + (ln & 31);
+    if (m < nt && n < E) logits[size_t(t0 + m) * E + n] = (v + (bias ? bias[n] : 0.0f)) + 0.0f;
+  }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) {
   extern __shared__ float lds_f[];
   float* lg = lds_f;                                          // [32][E]
@@ -39,53 +109,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) 
 
   for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
 
-  if constexpr (FROM_X) {
-    // Router GEMM: 32 tokens x E experts, K = H. Wave w owns expert blocks
-    // w, w+4, ... of 32 experts; MFMA 32x32x16 bf16 with fp32 accumulation.
-    const int nblkE = ceil_div(E, 32);
-    f32x16 acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-    const int m = lane & 31;
-    const int half = lane >> 5;
-    const bool row_ok = m < nt;
-    const uint16_t* xrow = a.x + size_t(t0 + (row_ok ? m : 0)) * a.H + 8 * half;
-    for (int k0 = 0; k0 < a.H; k0 += 16) {
-      u32x4 av = row_ok ? *reinterpret_cast<const u32x4*>(xrow + k0) : u32x4{0, 0, 0, 0};
-      bf16x8 af = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int b = wave + 4 * i;
-        if (b < nblkE) {
-          const int n = b * 32 + m;
-          u32x4 bv = n < E ? *reinterpret_cast<const u32x4*>(a.wr + size_t(n) * a.H + 8 * half + k0)
-                           : u32x4{0, 0, 0, 0};
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = wave + 4 * i;
-      if (b >= nblkE) continue;
-      const int n = b * 32 + (lane & 31);
-      if (n >= E) continue;
-      const float beta = a.bias ? a.bias[n] : 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mm = 8 * (r >> 2) + 4 * half + (r & 3);
-        float v = (acc[i][r] + beta) + 0.0f;   // + 0.0f turns -0 into +0
-        lg[mm * E + n] = v;
-        if (a.logits_out && mm < nt) a.logits_out[size_t(t0 + mm) * E + n] = v;
-      }
-    }
-  } else {
-    for (int i = tid; i < nt * E; i += kRouteThreads) {
-      const int n = i % E;
-      float v = a.logits_in[size_t(t0) * E + i];
-      if (a.bias) v = v + a.bias[n];
-      lg[i] = v + 0.0f;
-    }
+  for (int i = tid; i < nt * E; i += kRouteThreads) {
+    const int n = i % E;
+    float v = a.logits_in[size_t(t0) * E + i];
+    if (a.bias) v = v + a.bias[n];
+    lg[i] = v + 0.0f;   // + 0.0f turns -0 into +0
   }
   __syncthreads();
 
@@ -169,7 +197,15 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(ScanArgs a) {
 
   if (active) {
     int32_t s = 0;
-    for (int b = b0; b < b1; ++b) s += a.block_counts[size_t(b) * E + e];
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = a.block_counts[size_t(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; b < b1; ++b) s += a.block_counts[size_t(b) * E + e];
     psum[part * E + e] = s;
   }
   __syncthreads();
@@ -189,7 +225,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(ScanArgs a) {
   block_inclusive_scan(ntl, nullptr, E);   // inclusive scan of tiles per expert
   if (active) {
     int32_t run = off[e] - cnt[e] + psum[part * E + e];
-    for (int b = b0; b < b1; ++b) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = a.block_counts[size_t(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        a.block_base[size_t(b + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (; b < b1; ++b) {
       a.block_base[size_t(b) * E + e] = run;
       run += a.block_counts[size_t(b) * E + e];
     }
@@ -230,10 +277,20 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
                         hipStream_t stream) {
   const int nblk = ceil_div(ra.T, kRouteTokens);
   const size_t lds = sizeof(float) * kRouteTokens * ra.E + sizeof(int32_t) * (kRouteTokens * ra.k + ra.E);
-  if (from_x)
-    hipLaunchKernelGGL(route_topk_kernel<true>, dim3(nblk), dim3(kRouteThreads), lds, stream, ra);
-  else
-    hipLaunchKernelGGL(route_topk_kernel<false>, dim3(nblk), dim3(kRouteThreads), lds, stream, ra);
+  if (from_x) {
+    // logits (biased) into logits_out, then top-k from them without the bias
+    hipLaunchKernelGGL(router_logits_kernel, dim3(nblk, ceil_div(ra.E, 64)), dim3(kRouteThreads), 0, stream, ra.x,
+                       ra.wr, ra.bias, ra.T, ra.H, ra.E, ra.logits_out);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    RouteArgs rb = ra;
+    rb.logits_in = ra.logits_out;
+    rb.bias = nullptr;
+    rb.logits_out = nullptr;
+    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kRouteThreads), lds, stream, rb);
+  } else {
+    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kRouteThreads), lds, stream, ra);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, sa);

@@ -55,9 +55,9 @@ def test_check_dims_and_workspace(lib):
         (4096, 2048, 512, 8, 9, 0): _lib.MOE_ERR_SHAPE,          # k > E
         (4096, 2048, 512, 257, 8, 0): _lib.MOE_ERR_SHAPE,        # E too large
         (4096, 2000, 512, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # H not a multiple of 128
-        (4096, 2048, 500, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # I not a multiple of 64
+        (4096, 2048, 576, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # I not a multiple of 128
         (-1, 2048, 512, 256, 8, 0): _lib.MOE_ERR_SHAPE,          # negative T
-        (4096, 2048, 512, 256, 8, 32): _lib.MOE_ERR_UNSUPPORTED,  # other tile height
+        (4096, 2048, 512, 256, 8, 64): _lib.MOE_ERR_UNSUPPORTED,  # other tile height
         (16, 4096, 512, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,    # K beyond the GEMM limit
     }
     for dims, want in cases.items():
@@ -66,7 +66,7 @@ def test_check_dims_and_workspace(lib):
 
 
 def test_max_tiles_bound(lib):
-    assert lib.moe_max_tiles(ctypes.byref(MoeDims(4096, 0, 0, 256, 8, 64))) == 4096 * 8 // 64 + 256
+    assert lib.moe_max_tiles(ctypes.byref(MoeDims(4096, 0, 0, 256, 8, 128))) == 4096 * 8 // 128 + 256
     assert lib.moe_max_tiles(ctypes.byref(MoeDims(1, 0, 0, 256, 8, 64))) == 0 + 8
 
 
@@ -82,11 +82,12 @@ def test_calls_reject_bad_arguments_before_launching(lib):
     st = lib.moe_route(fake, null, ctypes.byref(d), *([fake] * 8), null, 0, null)
     assert st == _lib.MOE_ERR_WORKSPACE
     w = MoeQ4Weights(0x1000, 0x2000, 0x3000, 16, 128, 256)
-    st = lib.moe_layer_forward(null, null, null, *([ctypes.byref(w)] * 6), ctypes.byref(d), null, null, null,
+    dl = MoeDims(64, 256, 128, 16, 2, 0)
+    st = lib.moe_layer_forward(null, null, null, *([ctypes.byref(w)] * 6), ctypes.byref(dl), null, null, null,
                                null, null, 0, null)
     assert st == _lib.MOE_ERR_NULL
     # wrong weight shapes
-    st = lib.moe_layer_forward(fake, fake, null, *([ctypes.byref(w)] * 6), ctypes.byref(d), fake, null, null,
+    st = lib.moe_layer_forward(fake, fake, null, *([ctypes.byref(w)] * 6), ctypes.byref(dl), fake, null, null,
                                null, null, 0, null)
     assert st == _lib.MOE_ERR_SHAPE
     # misaligned activations
