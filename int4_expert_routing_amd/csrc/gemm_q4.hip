@@ -42,9 +42,9 @@
 //   -128*X_g land in a 3-slot LDS ring through buffer loads that write LDS
 //   directly (no registers, one scalar offset per group), issued two groups
 //   ahead; one s_waitcnt + s_barrier per group.
-// Work mapping: blockIdx.x = tile * NT + column_tile; column tiles are the fast
-// index so the column tiles of a row tile spread over the 8 XCDs and each XCD
-// keeps its own slice of every expert's weights in its L2.
+// Work mapping: each XCD takes a contiguous chunk of the tile list and runs
+// all column slices of its tiles (see the kernel), so activation rows and
+// expert weights are fetched into one XCD's L2 rather than into all eight.
 #include "moe_internal.h"
 
 namespace moe {
@@ -187,8 +187,19 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   uint8_t* ring = smem;
   uint16_t* s_st = reinterpret_cast<uint16_t*>(smem + kRing * kSlotBytes);   // [128 weight rows][G]
 
-  const int nt = blockIdx.x % a.NT;
-  const int tile = blockIdx.x / a.NT;
+  // XCD-aware work mapping: workgroups are dispatched round-robin over the 8
+  // XCDs (blockIdx % 8). The tile list (shared tiles, then routed tiles in
+  // expert order) is cut into 8 contiguous chunks, chunk x runs on XCD x, and
+  // within a chunk the column slices of a tile are consecutive. So every
+  // column slice of a row tile reads the activation rows from the same L2, and
+  // consecutive tiles of one expert share its weights in that L2.
+  const int ntot = a.n_shared_tiles + *a.num_tiles;
+  const int chunk = (ntot + 7) >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int j = blockIdx.x >> 3;
+  const int nt = j % a.NT;
+  const int tile = xcd * chunk + j / a.NT;
+  if (j / a.NT >= chunk || tile >= ntot) return;
   TileInfo ti;
   if (!tile_info(a, tile, ti)) return;
   const int stack = ti.e == a.E ? 1 : 0;
@@ -376,7 +387,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
 }
 
 hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream) {
-  const dim3 grid(unsigned(max_row_tiles) * unsigned(ga.NT));
+  // 8 chunks of at most ceil(max_row_tiles / 8) tiles, NT column slices each
+  const dim3 grid(8u * unsigned(ceil_div(max_row_tiles, 8)) * unsigned(ga.NT));
   if (grid.x == 0) return hipSuccess;
   const size_t lds = gemm_lds_bytes(ga.K);
   switch (epilogue) {

@@ -117,38 +117,78 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) 
   }
   __syncthreads();
 
-  // Top-k per token: one wave per token; each lane holds experts lane + 64 i.
-  for (int m = wave; m < nt; m += kRouteThreads / kWave) {
-    uint64_t key[kMaxKeysPerLane];
+  // Top-k: each wave selects for 8 tokens at once (lane holds experts lane +
+  // 64 i of every token), so the 8 tokens' cross-lane max reductions are
+  // independent and their shuffle latencies overlap.
+  {
+    constexpr int TPW = kRouteTokens / (kRouteThreads / kWave);   // tokens per wave
+    const int mbase = wave * TPW;
+    uint64_t key[TPW][kMaxKeysPerLane];
 #pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-      const int e = lane + 64 * i;
-      key[i] = e < E ? (uint64_t(float_order_key(lg[m * E + e])) << 32) | uint32_t(0xFFFFFFFFu - e) : 0ull;
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i) {
+        const int e = lane + 64 * i;
+        const int m = mbase + tt;
+        key[tt][i] = (e < E && m < nt) ? (uint64_t(float_order_key(lg[m * E + e])) << 32) | uint32_t(0xFFFFFFFFu - e)
+                                       : 0ull;
+      }
+    int my_e[TPW];
+    float my_l[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      my_e[tt] = 0;
+      my_l[tt] = 0.0f;
     }
-    int my_e = 0;
-    float my_l = 0.0f;
     for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
+      uint64_t best[TPW];
 #pragma unroll
-      for (int i = 1; i < kMaxKeysPerLane; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-      const int ej = int(0xFFFFFFFFu - uint32_t(best));
+      for (int tt = 0; tt < TPW; ++tt) {
+        best[tt] = key[tt][0];
 #pragma unroll
-      for (int i = 0; i < kMaxKeysPerLane; ++i)
-        if (lane + 64 * i == ej) key[i] = 0ull;
-      if (lane == j) {
-        my_e = ej;
-        my_l = float_from_order_key(uint32_t(best >> 32));
+        for (int i = 1; i < kMaxKeysPerLane; ++i) best[tt] = key[tt][i] > best[tt] ? key[tt][i] : best[tt];
+      }
+#pragma unroll
+      for (int msk = 32; msk >= 1; msk >>= 1)
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const uint64_t o = shfl_xor_u64(best[tt], msk);
+          best[tt] = o > best[tt] ? o : best[tt];
+        }
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int ej = int(0xFFFFFFFFu - uint32_t(best[tt]));
+#pragma unroll
+        for (int i = 0; i < kMaxKeysPerLane; ++i)
+          if (lane + 64 * i == ej) key[tt][i] = 0ull;
+        if (lane == j) {
+          my_e[tt] = ej;
+          my_l[tt] = float_from_order_key(uint32_t(best[tt] >> 32));
+        }
       }
     }
-    const float l0 = __shfl(my_l, 0, kWave);
-    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
-    const float sum = wave_sum_f32(ex);
-    if (lane < k) {
-      const size_t f = size_t(t0 + m) * k + lane;
-      a.topk_ids[f] = my_e;
-      a.topk_w[f] = ex / sum;
-      ids_s[m * k + lane] = my_e;
+    float ex[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const float l0 = __shfl(my_l[tt], 0, kWave);
+      ex[tt] = lane < k ? expf(my_l[tt] - l0) : 0.0f;
+    }
+    float sum[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) sum[tt] = ex[tt];
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1)
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) sum[tt] += __shfl_xor(sum[tt], msk, kWave);
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int m = mbase + tt;
+      if (lane < k && m < nt) {
+        const size_t f = size_t(t0 + m) * k + lane;
+        a.topk_ids[f] = my_e[tt];
+        a.topk_w[f] = ex[tt] / sum[tt];
+        ids_s[m * k + lane] = my_e[tt];
+      }
     }
   }
   __syncthreads();
