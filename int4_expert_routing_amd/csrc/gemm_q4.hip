@@ -56,12 +56,13 @@ constexpr uint32_t kNib = 0x000F000Fu;
 constexpr int kSlotA = 0;                // 128 rows x 128 B
 constexpr int kSlotB = 16384;            // 4 waves x 64 lanes x 16 B of weight codes
 constexpr int kSlotX = 20480;            // 128 floats: -128 * X_g
-constexpr int kSlotBytes = 20992;
-constexpr int kOpsPerGroup = 6;          // buffer->LDS loads per wave per group
+constexpr int kSlotS = 20992;            // 4 waves x 32 dwords: scale pairs (groups g&~1, g|1)
+constexpr int kSlotBytes = 21504;
+constexpr int kOpsPerGroup = 7;          // buffer->LDS loads per wave per group
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 // s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm6 = 0x0F76;
+constexpr int kWaitVmGroup = 0x0F70 | kOpsPerGroup;   // one group's loads may stay in flight
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -89,31 +90,45 @@ __device__ __forceinline__ int src_row(const GemmArgs& a, int r) {
   return a.sorted_rows ? a.sorted_rows[r] / a.row_div : r;
 }
 
-__device__ __forceinline__ bf16x8 unpack_word(uint32_t w) {
+// (a & m) | c in one VALU op. The VOP3 encoding takes no literal constants, so
+// the mask and the magic value are passed in registers.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(c));
+  return d;
+}
+
+__device__ __forceinline__ bf16x8 unpack_word(uint32_t w, uint32_t nib, uint32_t magic) {
   u32x4 r;
-  r.x = (w & kNib) | kMagic;
-  r.y = ((w >> 4) & kNib) | kMagic;
-  r.z = ((w >> 8) & kNib) | kMagic;
-  r.w = ((w >> 12) & kNib) | kMagic;
+  r.x = and_or(w, nib, magic);
+  r.y = and_or(w >> 4, nib, magic);
+  r.z = and_or(w >> 8, nib, magic);
+  r.w = and_or(w >> 12, nib, magic);
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// LDS byte offset of 16-byte chunk c (0..7) of row m in one activation tile.
-__device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ (m & 7))) * 16; }
+// Row m of an activation tile holds its 8 16-byte chunks permuted by
+// c -> c ^ swz(m). Within any 16 consecutive rows, (m & 1, chunk slot) never
+// repeats for a fixed c, and within any 8 consecutive rows the slots are all
+// distinct, so a 16-lane (64-bank) or 8-lane (32-bank) group of one fragment
+// read touches every bank once.
+__device__ __forceinline__ int swz(int m) { return (m & 7) ^ ((m >> 3) & 1); }
+__device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ swz(m))) * 16; }
 
 __device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
 
 size_t gemm_lds_bytes(int K) {
-  const int G = K / kGroup;
-  return size_t(kRing) * kSlotBytes + size_t(kBlockRows) * G * 2;
+  (void)K;
+  return size_t(kRing) * kSlotBytes;
 }
 
 // Per-wave streaming state: buffer descriptors, per-lane byte offsets.
 struct Stream {
-  __amdgpu_buffer_rsrc_t ra, rb, rx;
+  __amdgpu_buffer_rsrc_t ra, rb, rx, rs;
   uint32_t va[4];    // activation chunk offsets (4 instructions)
   uint32_t vb;       // weight-code offset
   uint32_t vx;       // -128*X_g offset (lanes 0..31)
+  uint32_t vs;       // scale offset (lanes 0..31)
 };
 
 __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int g, int wave, int lane) {
@@ -122,17 +137,23 @@ __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int
     __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + wave * 4096 + i * 1024), 16, st.va[i],
                                              g * (kGroup * 2), 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb, lds(slot + kSlotB + wave * 1024), 16, st.vb, g * 32, 0, 0);
-  if (lane < 32)
+  if (lane < 32) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rx, lds(slot + kSlotX + wave * 128), 4, st.vx, g * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rs, lds(slot + kSlotS + wave * 128), 4, st.vs, (g & ~1) * 2, 0, 0);
+  }
 }
 
 // One 64-wide group: unpack the wave's weight codes, then per live row block a
 // chain of 4 MFMAs started at -128*X_g, folded into acc with the group scale.
 template <int NRB>
-__device__ __forceinline__ void group_compute(const uint8_t* slot, float sc, int wave, int lane, f32x16 (&acc)[4]) {
+__device__ __forceinline__ void group_compute(const uint8_t* slot, int godd, int wave, int lane, f32x16 (&acc)[4]) {
   const int l32 = lane & 31, half = lane >> 5;
+  const uint32_t nib = kNib, magic = kMagic;
   const u32x4 w = *reinterpret_cast<const u32x4*>(slot + kSlotB + wave * 1024 + lane * 16);
-  const bf16x8 b0 = unpack_word(w.x), b1 = unpack_word(w.y), b2 = unpack_word(w.z), b3 = unpack_word(w.w);
+  const uint16_t sbits = reinterpret_cast<const uint16_t*>(slot + kSlotS + wave * 128)[2 * l32 + godd];
+  const float sc = bf16_to_f32(sbits);
+  const bf16x8 b0 = unpack_word(w.x, nib, magic), b1 = unpack_word(w.y, nib, magic),
+               b2 = unpack_word(w.z, nib, magic), b3 = unpack_word(w.w, nib, magic);
   const float* xg = reinterpret_cast<const float*>(slot + kSlotX);
   f32x16 p[NRB];
 #pragma unroll
@@ -159,21 +180,28 @@ __device__ __forceinline__ void group_compute(const uint8_t* slot, float sc, int
     for (int r = 0; r < 16; ++r) acc[rb][r] = __builtin_fmaf(sc, p[rb][r], acc[rb][r]);
 }
 
+template <int NRB, int S>
+__device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g, int G, int wave, int lane,
+                                          f32x16 (&acc)[4]) {
+  // group g landed for this wave; the barrier makes it so for every wave and
+  // frees slot (S+2)%3, last read in the previous step
+  if (g + 1 < G)
+    __builtin_amdgcn_s_waitcnt(kWaitVmGroup);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_barrier();
+  if (g + 2 < G) issue_group(st, ring + ((S + 2) % kRing) * kSlotBytes, g + 2, wave, lane);
+  group_compute<NRB>(ring + S * kSlotBytes, g & 1, wave, lane, acc);
+}
+
 template <int NRB>
-__device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, const uint16_t* s_wave, int G, int wave,
-                                          int lane, f32x16 (&acc)[4]) {
-  const int l32 = lane & 31;
-  for (int g = 0; g < G; ++g) {
-    // group g landed for this wave; the barrier makes it so for every wave and
-    // frees slot (g+2)%3, last read in iteration g-1
-    if (g + 1 < G)
-      __builtin_amdgcn_s_waitcnt(kWaitVm6);
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __builtin_amdgcn_s_barrier();
-    if (g + 2 < G) issue_group(st, ring + ((g + 2) % kRing) * kSlotBytes, g + 2, wave, lane);
-    const float sc = bf16_to_f32(s_wave[l32 * G + g]);
-    group_compute<NRB>(ring + (g % kRing) * kSlotBytes, sc, wave, lane, acc);
+__device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, int G, int wave, int lane,
+                                          f32x16 (&acc)[4]) {
+  // unrolled by the ring size so every slot offset is a constant
+  for (int g = 0; g < G; g += kRing) {
+    loop_step<NRB, 0>(st, ring, g, G, wave, lane, acc);
+    if (g + 1 < G) loop_step<NRB, 1>(st, ring, g + 1, G, wave, lane, acc);
+    if (g + 2 < G) loop_step<NRB, 2>(st, ring, g + 2, G, wave, lane, acc);
   }
 }
 
@@ -185,7 +213,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   const int KPx = xpart_cols(K);
   const int KNx = xneg_cols(K);
   uint8_t* ring = smem;
-  uint16_t* s_st = reinterpret_cast<uint16_t*>(smem + kRing * kSlotBytes);   // [128 weight rows][G]
 
   // XCD-aware work mapping: workgroups are dispatched round-robin over the 8
   // XCDs (blockIdx % 8). The tile list (shared tiles, then routed tiles in
@@ -225,7 +252,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   }
   const size_t wrow0 = size_t(el) * a.N + col0;
   const uint32_t* q_wave = mat->q + wrow0 * size_t(K / 8);
-  const uint16_t* s_glob = mat->s + wrow0 * size_t(G);
+  const uint16_t* s_glob = mat->s + wrow0 * size_t(G);     // 4-byte aligned: G is even
   const uint16_t* b_glob = mat->b + wrow0 * size_t(G);
   const int ncol = col0 + l32;
 
@@ -234,43 +261,36 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   st.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.A), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q_wave), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.Axneg), 0, 0x7FFFFFFF, kRsrcWord3);
+  st.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s_glob), 0, 0x7FFFFFFF, kRsrcWord3);
   {
     // activation DMA i of this wave fills chunk positions wave*256 + i*64 + lane:
-    // row m = wave*32 + i*8 + lane/8, swizzled chunk lane%8 = logical chunk cidx
-    const int cidx = (lane & 7) ^ (lane >> 3);
+    // row m = wave*32 + i*8 + lane/8 and chunk slot lane%8, which holds logical
+    // chunk (lane%8) ^ swz(m) = (lane%8) ^ (lane/8) ^ (i%2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = wave * 32 + i * 8 + (lane >> 3);
+      const int cidx = (lane & 7) ^ swz(m);
       const int r = ti.r0 + min(m, nrows - 1);     // padding rows re-read the last real row
       st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
     }
     st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
     const int mx = wave * 32 + l32;
     st.vx = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KNx * 4);
+    st.vs = uint32_t(l32 * G * 2);   // scale row of column l32; + (g & ~1) * 2 per group
   }
 
-  // ---- prologue: scales of the wave's 32 weight rows (contiguous), groups 0, 1
-  {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s_glob), 0, 0x7FFFFFFF, kRsrcWord3);
-    const int dwords = 16 * G;            // 32 rows x G bf16
-    for (int p0 = 0; p0 < dwords; p0 += 64)
-      if (p0 + lane < dwords)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(s_st + wave * 32 * G + 2 * p0), 4, uint32_t((p0 + lane) * 4),
-                                                 0, 0, 0);
-  }
+  // ---- prologue: groups 0 and 1 ---------------------------------------------
   issue_group(st, ring, 0, wave, lane);
   if (G > 1) issue_group(st, ring + kSlotBytes, 1, wave, lane);
 
   f32x16 acc[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x16{};
-  const uint16_t* s_wave = s_st + wave * 32 * G;
   switch (nrb) {
-    case 1: main_loop<1>(st, ring, s_wave, G, wave, lane, acc); break;
-    case 2: main_loop<2>(st, ring, s_wave, G, wave, lane, acc); break;
-    case 3: main_loop<3>(st, ring, s_wave, G, wave, lane, acc); break;
-    default: main_loop<4>(st, ring, s_wave, G, wave, lane, acc); break;
+    case 1: main_loop<1>(st, ring, G, wave, lane, acc); break;
+    case 2: main_loop<2>(st, ring, G, wave, lane, acc); break;
+    case 3: main_loop<3>(st, ring, G, wave, lane, acc); break;
+    default: main_loop<4>(st, ring, G, wave, lane, acc); break;
   }
   __syncthreads();   // every wave is done with the ring
 
