@@ -9,16 +9,15 @@
 //
 // Exactness. A weight is W = s*q + b with q in 0..15 and s, b bf16. Rounding
 // s*q+b to bf16 before a bf16 MFMA would add ~2^-9 relative error per weight.
-// Instead the MFMA operand is the exact value 128+q, whose bf16 bit pattern is
-// 0x4300 | q, so one AND/OR turns two packed codes into two operands. For each
-// 64-wide group g of K, with X_g = sum_{k in g} x_k, the MFMA chain of the group
-// starts from the accumulator value -128*X_g (exact fp32, from a side table)
-// and adds sum x_k (128 + q_k), leaving
-//     P_g = sum_{k in g} x_k q_k                      (fp32, no cancellation)
-// which the kernel folds as acc += s_g * P_g (one FMA per output per group).
-// The bias term sum_g b_g X_g runs on the MFMA as 3 extra K columns per group:
-// activations (X_hi, X_mid, X_lo), an exact three-part bf16 split of X_g,
-// against (b_g, b_g, b_g).
+// Instead the MFMA operand is the exact value 1 + q/16, whose bf16 bit pattern
+// is 0x3F80 | (q << 3), so a shift and one AND/OR turn two packed codes into
+// two operands. With W = 16s * (1 + q/16) + (b - 16s), for each 64-wide group g
+// of K the MFMA chain of the group accumulates
+//     P_g = sum_{k in g} x_k (1 + q_k/16)             (fp32)
+// which the kernel folds as acc += 16 s_g * P_g (one FMA per output per group;
+// 16 s_g is exact). The remaining sum_g (b_g - 16 s_g) X_g, X_g = sum_{k in g}
+// x_k, runs on the MFMA as 6 extra K columns per group: an exact three-part
+// bf16 split of X_g (from a side table) against b_g and against -16 s_g.
 //
 // Operand order. One 32-bit word holds codes k..k+7 (nibble i = code k+i); the
 // AND/OR unpack yields the bf16 pairs (k, k+4), (k+1, k+5), (k+2, k+6),
@@ -38,10 +37,10 @@
 //   of 4 MFMAs per row block; one group's weight codes are unpacked once and
 //   reused by every row block.
 // Streaming: per group, the activation tile (128 rows x 64 bf16, 16-byte chunks
-//   XOR-swizzled by row), the weight codes of the 128 columns and the 128 rows'
-//   -128*X_g land in a 3-slot LDS ring through buffer loads that write LDS
-//   directly (no registers, one scalar offset per group), issued two groups
-//   ahead; one s_waitcnt + s_barrier per group.
+//   XOR-swizzled by row) and the weight codes and scales of the 128 columns
+//   land in a 3-slot LDS ring through buffer loads that write LDS directly (no
+//   registers, one scalar offset per group), issued two groups ahead; one
+//   s_waitcnt + s_barrier per group.
 // Work mapping: each XCD takes a contiguous chunk of the tile list and runs
 // all column slices of its tiles (see the kernel), so activation rows and
 // expert weights are fetched into one XCD's L2 rather than into all eight.
@@ -51,14 +50,13 @@ namespace moe {
 
 constexpr int kGemmThreads = 256;
 constexpr int kRing = 3;                 // LDS ring slots
-constexpr uint32_t kMagic = 0x43004300u;  // two bf16 128.0
-constexpr uint32_t kNib = 0x000F000Fu;
+constexpr uint32_t kMagic = 0x3F803F80u;  // two bf16 1.0
+constexpr uint32_t kNib = 0x00780078u;    // a code shifted to mantissa bits 3..6 of each half
 constexpr int kSlotA = 0;                // 128 rows x 128 B
 constexpr int kSlotB = 16384;            // 4 waves x 64 lanes x 16 B of weight codes
-constexpr int kSlotX = 20480;            // 128 floats: -128 * X_g
-constexpr int kSlotS = 20992;            // 4 waves x 32 dwords: scale pairs (groups g&~1, g|1)
-constexpr int kSlotBytes = 21504;
-constexpr int kOpsPerGroup = 7;          // buffer->LDS loads per wave per group
+constexpr int kSlotS = 20480;            // 4 waves x 32 dwords: scale pairs (groups g&~1, g|1)
+constexpr int kSlotBytes = 20992;
+constexpr int kOpsPerGroup = 6;          // buffer->LDS loads per wave per group
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 // s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
@@ -98,12 +96,15 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return d;
 }
 
+// Word w holds codes k..k+7 (nibble i = code k+i). Register pair i gets codes
+// (k+i, k+i+4), which sit at bits 4i and 4i+16; each is moved to mantissa bits
+// 3..6 of its half (shift by 3 - 4i) and ORed into bf16 1.0.
 __device__ __forceinline__ bf16x8 unpack_word(uint32_t w, uint32_t nib, uint32_t magic) {
   u32x4 r;
-  r.x = and_or(w, nib, magic);
-  r.y = and_or(w >> 4, nib, magic);
-  r.z = and_or(w >> 8, nib, magic);
-  r.w = and_or(w >> 12, nib, magic);
+  r.x = and_or(w << 3, nib, magic);
+  r.y = and_or(w >> 1, nib, magic);
+  r.z = and_or(w >> 5, nib, magic);
+  r.w = and_or(w >> 9, nib, magic);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -124,10 +125,9 @@ size_t gemm_lds_bytes(int K) {
 
 // Per-wave streaming state: buffer descriptors, per-lane byte offsets.
 struct Stream {
-  __amdgpu_buffer_rsrc_t ra, rb, rx, rs;
+  __amdgpu_buffer_rsrc_t ra, rb, rs;
   uint32_t va[4];    // activation chunk offsets (4 instructions)
   uint32_t vb;       // weight-code offset
-  uint32_t vx;       // -128*X_g offset (lanes 0..31)
   uint32_t vs;       // scale offset (lanes 0..31)
 };
 
@@ -137,24 +137,21 @@ __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int
     __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + wave * 4096 + i * 1024), 16, st.va[i],
                                              g * (kGroup * 2), 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb, lds(slot + kSlotB + wave * 1024), 16, st.vb, g * 32, 0, 0);
-  if (lane < 32) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rx, lds(slot + kSlotX + wave * 128), 4, st.vx, g * 4, 0, 0);
+  if (lane < 32)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rs, lds(slot + kSlotS + wave * 128), 4, st.vs, (g & ~1) * 2, 0, 0);
-  }
 }
 
 // One 64-wide group: unpack the wave's weight codes, then per live row block a
-// chain of 4 MFMAs started at -128*X_g, folded into acc with the group scale.
+// chain of 4 MFMAs, folded into acc with 16 times the group scale.
 template <int NRB>
 __device__ __forceinline__ void group_compute(const uint8_t* slot, int godd, int wave, int lane, f32x16 (&acc)[4]) {
   const int l32 = lane & 31, half = lane >> 5;
   const uint32_t nib = kNib, magic = kMagic;
   const u32x4 w = *reinterpret_cast<const u32x4*>(slot + kSlotB + wave * 1024 + lane * 16);
   const uint16_t sbits = reinterpret_cast<const uint16_t*>(slot + kSlotS + wave * 128)[2 * l32 + godd];
-  const float sc = bf16_to_f32(sbits);
+  const float sc = 16.0f * bf16_to_f32(sbits);
   const bf16x8 b0 = unpack_word(w.x, nib, magic), b1 = unpack_word(w.y, nib, magic),
                b2 = unpack_word(w.z, nib, magic), b3 = unpack_word(w.w, nib, magic);
-  const float* xg = reinterpret_cast<const float*>(slot + kSlotX);
   f32x16 p[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -163,12 +160,7 @@ __device__ __forceinline__ void group_compute(const uint8_t* slot, int godd, int
     const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 1)));
     const bf16x8 a2 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 2)));
     const bf16x8 a3 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 3)));
-    // the lane's accumulator rows: rb*32 + 8j + 4*half + i
-    const f32x4* xp = reinterpret_cast<const f32x4*>(xg + rb * 32 + 4 * half);
-    const f32x4 c0 = xp[0], c1 = xp[2], c2 = xp[4], c3 = xp[6];
-    f32x16 q = f32x16{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
-                      c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
-    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, q, 0, 0, 0);
+    f32x16 q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, f32x16{}, 0, 0, 0);
     q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, q, 0, 0, 0);
     q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2, q, 0, 0, 0);
     q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b3, q, 0, 0, 0);
@@ -211,7 +203,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   const int K = a.K;
   const int G = K / kGroup;
   const int KPx = xpart_cols(K);
-  const int KNx = xneg_cols(K);
   uint8_t* ring = smem;
 
   // XCD-aware work mapping: workgroups are dispatched round-robin over the 8
@@ -260,7 +251,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   Stream st;
   st.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.A), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q_wave), 0, 0x7FFFFFFF, kRsrcWord3);
-  st.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.Axneg), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s_glob), 0, 0x7FFFFFFF, kRsrcWord3);
   {
     // activation DMA i of this wave fills chunk positions wave*256 + i*64 + lane:
@@ -274,8 +264,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
       st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
     }
     st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
-    const int mx = wave * 32 + l32;
-    st.vx = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KNx * 4);
     st.vs = uint32_t(l32 * G * 2);   // scale row of column l32; + (g & ~1) * 2 per group
   }
 
@@ -294,7 +282,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   }
   __syncthreads();   // every wave is done with the ring
 
-  // ---- bias term: 3 extra K columns per group ------------------------------
+  // ---- bias term: 6 extra K columns per group: (X parts) x (b, -16 s) ------
   uint16_t* xpart_s = reinterpret_cast<uint16_t*>(ring);   // [128][KPx]
   for (int i = tid; i < kBlockRows * (KPx / 8); i += kGemmThreads) {
     const int m = i / (KPx / 8), c = i % (KPx / 8);
@@ -304,12 +292,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   }
   __syncthreads();
   const uint16_t* bp = b_glob + size_t(l32) * G;
+  const uint16_t* spp = s_glob + size_t(l32) * G;
   for (int sk = 0; sk < KPx / 16; ++sk) {
     uint32_t v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int g = (16 * sk + 8 * half + i) / 3;
-      v[i] = g < G ? uint32_t(bp[g]) : 0u;
+      const int kk = 16 * sk + 8 * half + i;
+      const int g = kk / 6;
+      uint32_t bits = 0u;
+      if (g < G) bits = (kk - 6 * g) < 3 ? uint32_t(bp[g]) : f32_to_bf16_rne(-16.0f * bf16_to_f32(spp[g]));
+      v[i] = bits;
     }
     u32x4 pk;
     pk.x = v[0] | (v[1] << 16);
@@ -383,17 +375,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         const int Go = a.N / kGroup;
         const int KPo = xpart_cols(a.N);
         uint16_t* xp = a.out_part + size_t(row) * KPo;
-        float* xn = a.out_xneg + size_t(row) * xneg_cols(a.N);
         if (shalf == 0) {
           uint16_t h, m, l;
           split3_bf16(X, h, m, l);
-          xp[3 * nt + 0] = h;
-          xp[3 * nt + 1] = m;
-          xp[3 * nt + 2] = l;
-          xn[nt] = -128.0f * X;
+          xp[6 * nt + 0] = h;
+          xp[6 * nt + 1] = m;
+          xp[6 * nt + 2] = l;
+          xp[6 * nt + 3] = h;
+          xp[6 * nt + 4] = m;
+          xp[6 * nt + 5] = l;
         } else if (nt == 0) {
-          for (int c = 3 * Go; c < KPo; ++c) xp[c] = 0;
-          for (int c = Go; c < xneg_cols(a.N); ++c) xn[c] = 0.0f;
+          for (int c = 6 * Go; c < KPo; ++c) xp[c] = 0;
         }
       }
     } else {
@@ -426,13 +418,12 @@ hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipS
 }
 
 // ---------------------------------------------------------------------------
-// Activation preparation: permuted chunk order plus the group-sum tables.
+// Activation preparation: permuted chunk order plus the group-sum table.
 // 8 lanes per group, one 16-byte chunk each; group sums in fp64, rounded once.
 __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* A, int rows, int K, uint16_t* a_perm,
-                                                        float* a_xneg, uint16_t* a_part) {
+                                                        uint16_t* a_part) {
   const int G = K / kGroup;
   const int KPx = xpart_cols(K);
-  const int KNx = xneg_cols(K);
   const long gid = long(blockIdx.x) * blockDim.x + threadIdx.x;
   const long team = gid >> 3;
   const int sub = int(gid & 7);
@@ -449,28 +440,22 @@ __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* A, int r
   if (!ok) return;
   *reinterpret_cast<u32x4*>(a_perm + size_t(row) * K + g * kGroup + 8 * sub) = permute_chunk(v);
   uint16_t* xp = a_part + size_t(row) * KPx;
-  float* xn = a_xneg + size_t(row) * KNx;
-  if (sub == 0) {
-    const float X = float(s);
+  if (sub < 6) {
     uint16_t h, m, l;
-    split3_bf16(X, h, m, l);
-    xp[3 * g] = h;
-    xp[3 * g + 1] = m;
-    xp[3 * g + 2] = l;
-    xn[g] = -128.0f * X;
+    split3_bf16(float(s), h, m, l);
+    const int which = sub % 3;
+    xp[6 * g + sub] = which == 0 ? h : (which == 1 ? m : l);
   }
-  if (g == G - 1 && sub == 1) {
-    for (int c = 3 * G; c < KPx; ++c) xp[c] = 0;
-    for (int c = G; c < KNx; ++c) xn[c] = 0.0f;
-  }
+  if (g == G - 1 && sub == 7)
+    for (int c = 6 * G; c < KPx; ++c) xp[c] = 0;
 }
 
-hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, float* a_xneg,
-                            uint16_t* a_part, hipStream_t stream) {
+hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
+                            hipStream_t stream) {
   const long threads = long(rows) * (K / kGroup) * 8;
   if (threads == 0) return hipSuccess;
   const unsigned blocks = unsigned((threads + 255) / 256);
-  hipLaunchKernelGGL(prep_rows_kernel, dim3(blocks), dim3(256), 0, stream, A, rows, K, a_perm, a_xneg, a_part);
+  hipLaunchKernelGGL(prep_rows_kernel, dim3(blocks), dim3(256), 0, stream, A, rows, K, a_perm, a_part);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ struct Carve {
 // Workspace of one layer call. Offsets in bytes from the workspace base.
 struct LayerLayout {
   size_t logits, ids, w, block_counts, block_base, rank, counts, offsets, sorted_rows, row_of_pair,
-      tile_map, num_tiles, x_perm, x_xneg, x_part, h, h_xneg, h_part, Y, total;
+      tile_map, num_tiles, x_perm, x_part, h, h_part, Y, total;
 };
 
 int64_t max_tiles_of(int64_t T, int64_t E, int64_t k, int64_t bm) {
@@ -53,10 +53,8 @@ LayerLayout layer_layout(const moe_dims& d) {
   L.tile_map = c.take(size_t(max_tiles_of(d.T, d.E, d.k, bm)) * 8);
   L.num_tiles = c.take(4);
   L.x_perm = c.take(T * H * 2);
-  L.x_xneg = c.take(T * size_t(xneg_cols(d.H)) * 4);
   L.x_part = c.take(T * size_t(xpart_cols(d.H)) * 2);
   L.h = c.take(rows * I * 2);
-  L.h_xneg = c.take(rows * size_t(xneg_cols(d.I)) * 4);
   L.h_part = c.take(rows * size_t(xpart_cols(d.I)) * 2);
   L.Y = c.take(rows * H * 4);
   L.total = c.off;
@@ -176,7 +174,6 @@ size_t moe_gemm_workspace_bytes(int32_t a_rows, int32_t K) {
   if (a_rows < 0 || K <= 0 || K % kGroup) return 0;
   Carve c;
   c.take(size_t(a_rows) * K * 2);
-  c.take(size_t(a_rows) * xneg_cols(K) * 4);
   c.take(size_t(a_rows) * xpart_cols(K) * 2);
   return c.off;
 }
@@ -207,13 +204,11 @@ int moe_grouped_gemm_q4(const uint16_t* A, int32_t a_rows, const int32_t* sorted
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   Carve c;
   uint16_t* a_perm = at<uint16_t>(workspace, c.take(size_t(a_rows) * K * 2));
-  float* a_xneg = at<float>(workspace, c.take(size_t(a_rows) * xneg_cols(K) * 4));
   uint16_t* a_part = at<uint16_t>(workspace, c.take(size_t(a_rows) * xpart_cols(K) * 2));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_prep_rows(A, a_rows, K, a_perm, a_xneg, a_part, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_prep_rows(A, a_rows, K, a_perm, a_part, s) != hipSuccess) return MOE_ERR_HIP;
   GemmArgs ga{};
   ga.A = a_perm;
-  ga.Axneg = a_xneg;
   ga.Apart = a_part;
   ga.sorted_rows = sorted_rows;
   ga.row_div = sorted_rows ? row_div : 1;
@@ -281,9 +276,8 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
 
   // 1. activations: permuted chunk order + group sums
   uint16_t* x_perm = at<uint16_t>(ws, L.x_perm);
-  float* x_xneg = at<float>(ws, L.x_xneg);
   uint16_t* x_part = at<uint16_t>(ws, L.x_part);
-  if (launch_prep_rows(x, T, H, x_perm, x_xneg, x_part, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
+  if (launch_prep_rows(x, T, H, x_perm, x_part, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
 
   // 2-4. router GEMM, top-k, histogram, scan, scatter, block map
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
@@ -316,11 +310,9 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   const int n_sh = ceil_div(T, bm);
   const int max_routed = int(max_tiles_of(T, E, k, bm));
   uint16_t* h = at<uint16_t>(ws, L.h);
-  float* h_xneg = at<float>(ws, L.h_xneg);
   uint16_t* h_part = at<uint16_t>(ws, L.h_part);
   GemmArgs g1{};
   g1.A = x_perm;
-  g1.Axneg = x_xneg;
   g1.Apart = x_part;
   g1.sorted_rows = sorted_rows;
   g1.row_div = k;
@@ -340,7 +332,6 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.K = H;
   g1.NT = I / 64;
   g1.out = h;
-  g1.out_xneg = h_xneg;
   g1.out_part = h_part;
   if (launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
@@ -348,7 +339,6 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   float* Y = at<float>(ws, L.Y);
   GemmArgs g2 = g1;
   g2.A = h;
-  g2.Axneg = h_xneg;
   g2.Apart = h_part;
   g2.sorted_rows = nullptr;
   g2.row_div = 1;
@@ -361,7 +351,6 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g2.K = I;
   g2.NT = H / 128;
   g2.out = Y;
-  g2.out_xneg = nullptr;
   g2.out_part = nullptr;
   if (launch_gemm(g2, kEpiF32, n_sh + max_routed, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
 

@@ -113,13 +113,11 @@ __device__ __forceinline__ void split3_bf16(float v, uint16_t& hi, uint16_t& mid
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Per activation row the GEMM needs each 64-wide group's sum X_g twice:
-//   * as float -128*X_g (the starting value of that group's MFMA chain), in a
-//     table of xneg_cols(K) floats per row (groups padded to a multiple of 4);
-//   * split exactly into three bf16 parts (hi, mid, lo) for the bias term
-//     sum_g b_g X_g, in a table of xpart_cols(K) bf16 per row (3 per group,
-//     padded to whole MFMA K steps).
-__host__ __device__ constexpr int xneg_cols(int K) { return ceil_div(K / kGroup, 4) * 4; }
-__host__ __device__ constexpr int xpart_cols(int K) { return ceil_div(3 * (K / kGroup), 16) * 16; }
+// Per activation row the GEMM needs each 64-wide group's sum X_g, split
+// exactly into three bf16 parts (hi, mid, lo); the side table stores them twice
+// per group, [hi, mid, lo, hi, mid, lo], because the bias correction pairs the
+// three parts with two weight-side values. xpart_cols(K) bf16 per row (6 per
+// group, padded to whole MFMA K steps).
+__host__ __device__ constexpr int xpart_cols(int K) { return ceil_div(6 * (K / kGroup), 16) * 16; }
 
 }  // namespace moe

@@ -56,7 +56,6 @@ enum GemmEpilogue { kEpiF32 = 0, kEpiSwigluNatural = 1, kEpiSwigluInternal = 2 }
 
 struct GemmArgs {
   const uint16_t* A;        // activations in the permuted chunk order [a_rows][K]
-  const float* Axneg;       // -128 * group sums [a_rows][xneg_cols(K)]
   const uint16_t* Apart;    // group sums split in three bf16 parts [a_rows][xpart_cols(K)]
   const int32_t* sorted_rows;  // gather for routed rows: src = sorted_rows[r] / row_div; null = identity
   int row_div;
@@ -72,14 +71,13 @@ struct GemmArgs {
   int shared_rows;
   int N, K, NT;             // NT = column tiles per row tile
   void* out;                // f32 [rows][N], or bf16 [rows][N]
-  float* out_xneg;          // group-sum tables of the bf16 output (internal SwiGLU only)
-  uint16_t* out_part;
+  uint16_t* out_part;       // group-sum table of the bf16 output (internal SwiGLU only)
 };
 
 hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream);
 
-hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, float* a_xneg,
-                            uint16_t* a_part, hipStream_t stream);
+hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
+                            hipStream_t stream);
 
 hipError_t launch_combine(const float* Y, const float* w, const int32_t* row_of_pair, int T, int k, int H,
                           int shared_row0, uint16_t* y, hipStream_t stream);
