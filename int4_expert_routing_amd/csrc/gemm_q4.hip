@@ -16,8 +16,9 @@
 //     P_g = sum_{k in g} x_k (1 + q_k/16)             (fp32)
 // which the kernel folds as acc += 16 s_g * P_g (one FMA per output per group;
 // 16 s_g is exact). The remaining sum_g (b_g - 16 s_g) X_g, X_g = sum_{k in g}
-// x_k, runs on the MFMA as 6 extra K columns per group: an exact three-part
-// bf16 split of X_g (from a side table) against b_g and against -16 s_g.
+// x_k, runs on the MFMA as 8 extra K columns per group: an exact three-part
+// bf16 split of X_g (from a side table) against b_g, again against -16 s_g,
+// and two zero columns, so that each 8-wide operand slice is one group.
 //
 // Operand order. One 32-bit word holds codes k..k+7 (nibble i = code k+i); the
 // AND/OR unpack yields the bf16 pairs (k, k+4), (k+1, k+5), (k+2, k+6),
@@ -118,9 +119,14 @@ __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ 
 
 __device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
 
+// LDS of one workgroup: the ring during the K loop; afterwards the same memory
+// holds the tile's group-sum table (128 x xpart_cols bf16) and, for SwiGLU, the
+// gate tile (128 x 64 fp32) plus the h tile (128 x 64 bf16).
 size_t gemm_lds_bytes(int K) {
-  (void)K;
-  return size_t(kRing) * kSlotBytes;
+  const size_t ring = size_t(kRing) * kSlotBytes;
+  const size_t xpart = size_t(kBlockRows) * xpart_cols(K) * 2;
+  const size_t swiglu = size_t(kBlockRows) * 64 * 4 + size_t(kBlockRows) * 64 * 2;
+  return ring > xpart ? (ring > swiglu ? ring : swiglu) : (xpart > swiglu ? xpart : swiglu);
 }
 
 // Per-wave streaming state: buffer descriptors, per-lane byte offsets.
@@ -282,7 +288,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   }
   __syncthreads();   // every wave is done with the ring
 
-  // ---- bias term: 6 extra K columns per group: (X parts) x (b, -16 s) ------
+  // ---- bias term: 8 extra K columns per group: (X parts) x (b, -16 s) ------
+  // This lane supplies, in K step sk, the operand slice of group 2 sk + half:
+  // its column's b and s of every group are loaded at once (G <= 32).
+  constexpr int kMaxPairs = kMaxK / kGroup / 2;       // 16 dword pairs of groups
+  uint32_t bpair[kMaxPairs], spair[kMaxPairs];
+  {
+    const uint32_t* bq = reinterpret_cast<const uint32_t*>(b_glob + size_t(l32) * G);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(s_glob + size_t(l32) * G);
+#pragma unroll
+    for (int d = 0; d < kMaxPairs; ++d) {
+      bpair[d] = d < G / 2 ? bq[d] : 0u;
+      spair[d] = d < G / 2 ? sq[d] : 0u;
+    }
+  }
   uint16_t* xpart_s = reinterpret_cast<uint16_t*>(ring);   // [128][KPx]
   for (int i = tid; i < kBlockRows * (KPx / 8); i += kGemmThreads) {
     const int m = i / (KPx / 8), c = i % (KPx / 8);
@@ -291,30 +310,22 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         *reinterpret_cast<const u32x4*>(a.Apart + size_t(src_row(a, r)) * KPx + 8 * c);
   }
   __syncthreads();
-  const uint16_t* bp = b_glob + size_t(l32) * G;
-  const uint16_t* spp = s_glob + size_t(l32) * G;
-  for (int sk = 0; sk < KPx / 16; ++sk) {
-    uint32_t v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kk = 16 * sk + 8 * half + i;
-      const int g = kk / 6;
-      uint32_t bits = 0u;
-      if (g < G) bits = (kk - 6 * g) < 3 ? uint32_t(bp[g]) : f32_to_bf16_rne(-16.0f * bf16_to_f32(spp[g]));
-      v[i] = bits;
-    }
-    u32x4 pk;
-    pk.x = v[0] | (v[1] << 16);
-    pk.y = v[2] | (v[3] << 16);
-    pk.z = v[4] | (v[5] << 16);
-    pk.w = v[6] | (v[7] << 16);
-    const bf16x8 bb = __builtin_bit_cast(bf16x8, pk);
+  for (int d = 0; d < kMaxPairs; ++d) {
+    if (d < G / 2) {
+      // groups 2d (lanes 0..31) and 2d+1 (lanes 32..63)
+      const uint32_t bb = half ? (bpair[d] >> 16) : (bpair[d] & 0xFFFFu);
+      const uint32_t sb = half ? (spair[d] >> 16) : (spair[d] & 0xFFFFu);
+      const uint32_t ns = f32_to_bf16_rne(-16.0f * bf16_to_f32(uint16_t(sb)));
+      const u32x4 pk = {bb | (bb << 16), bb | (ns << 16), ns | (ns << 16), 0u};
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if (rb < nrb) {
-        const bf16x8 xa =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xpart_s + (rb * 32 + l32) * KPx + 16 * sk + 8 * half));
-        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bb, acc[rb], 0, 0, 0);
+      for (int rb = 0; rb < 4; ++rb) {
+        if (rb < nrb) {
+          const bf16x8 xa = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(xpart_s + (rb * 32 + l32) * KPx + 16 * d + 8 * half));
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv, acc[rb], 0, 0, 0);
+        }
       }
     }
   }
@@ -372,20 +383,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         uint16_t* dst = out + size_t(row) * a.N + nt * 64 + shalf * 32;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = permute_chunk(ch[i]);
-        const int Go = a.N / kGroup;
         const int KPo = xpart_cols(a.N);
         uint16_t* xp = a.out_part + size_t(row) * KPo;
         if (shalf == 0) {
           uint16_t h, m, l;
           split3_bf16(X, h, m, l);
-          xp[6 * nt + 0] = h;
-          xp[6 * nt + 1] = m;
-          xp[6 * nt + 2] = l;
-          xp[6 * nt + 3] = h;
-          xp[6 * nt + 4] = m;
-          xp[6 * nt + 5] = l;
-        } else if (nt == 0) {
-          for (int c = 6 * Go; c < KPo; ++c) xp[c] = 0;
+          const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
+                           uint32_t(m) | (uint32_t(l) << 16), 0u};
+          *reinterpret_cast<u32x4*>(xp + 8 * nt) = e;
         }
       }
     } else {
@@ -440,14 +445,13 @@ __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* A, int r
   if (!ok) return;
   *reinterpret_cast<u32x4*>(a_perm + size_t(row) * K + g * kGroup + 8 * sub) = permute_chunk(v);
   uint16_t* xp = a_part + size_t(row) * KPx;
-  if (sub < 6) {
+  if (sub == 0) {
     uint16_t h, m, l;
     split3_bf16(float(s), h, m, l);
-    const int which = sub % 3;
-    xp[6 * g + sub] = which == 0 ? h : (which == 1 ? m : l);
+    const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
+                     uint32_t(m) | (uint32_t(l) << 16), 0u};
+    *reinterpret_cast<u32x4*>(xp + 8 * g) = e;
   }
-  if (g == G - 1 && sub == 7)
-    for (int c = 6 * G; c < KPx; ++c) xp[c] = 0;
 }
 
 hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,

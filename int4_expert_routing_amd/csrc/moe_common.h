@@ -114,10 +114,10 @@ __device__ __forceinline__ void split3_bf16(float v, uint16_t& hi, uint16_t& mid
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Per activation row the GEMM needs each 64-wide group's sum X_g, split
-// exactly into three bf16 parts (hi, mid, lo); the side table stores them twice
-// per group, [hi, mid, lo, hi, mid, lo], because the bias correction pairs the
-// three parts with two weight-side values. xpart_cols(K) bf16 per row (6 per
-// group, padded to whole MFMA K steps).
-__host__ __device__ constexpr int xpart_cols(int K) { return ceil_div(6 * (K / kGroup), 16) * 16; }
+// exactly into three bf16 parts (hi, mid, lo). The side table stores 8 bf16 per
+// group, [hi, mid, lo, hi, mid, lo, 0, 0], so that one 8-element MFMA operand
+// slice covers exactly one group: the bias correction pairs the first three
+// with b_g and the next three with -16 s_g. xpart_cols(K) = 8 * K/64.
+__host__ __device__ constexpr int xpart_cols(int K) { return 8 * (K / kGroup); }
 
 }  // namespace moe
