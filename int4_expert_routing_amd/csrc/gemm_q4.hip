@@ -273,6 +273,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
     st.vs = uint32_t(l32 * G * 2);   // scale row of column l32; + (g & ~1) * 2 per group
   }
 
+  // source row of the group-sum table row this thread stages after the K loop
+  const int xpart_src = src_row(a, ti.r0 + min(tid >> 1, nrows - 1));
+
   // ---- prologue: groups 0 and 1 ---------------------------------------------
   issue_group(st, ring, 0, wave, lane);
   if (G > 1) issue_group(st, ring + kSlotBytes, 1, wave, lane);
@@ -302,12 +305,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
       spair[d] = d < G / 2 ? sq[d] : 0u;
     }
   }
+  // group-sum table of the tile: thread t copies half of row t/2 (independent
+  // 16-byte loads from one source row, resolved before the K loop)
   uint16_t* xpart_s = reinterpret_cast<uint16_t*>(ring);   // [128][KPx]
-  for (int i = tid; i < kBlockRows * (KPx / 8); i += kGemmThreads) {
-    const int m = i / (KPx / 8), c = i % (KPx / 8);
-    const int r = ti.r0 + min(m, nrows - 1);
-    *reinterpret_cast<u32x4*>(xpart_s + m * KPx + 8 * c) =
-        *reinterpret_cast<const u32x4*>(a.Apart + size_t(src_row(a, r)) * KPx + 8 * c);
+  {
+    const uint16_t* srcp = a.Apart + size_t(xpart_src) * KPx + (tid & 1) * (KPx / 2);
+    uint16_t* dstp = xpart_s + (tid >> 1) * KPx + (tid & 1) * (KPx / 2);
+    constexpr int kMaxChunks = kMaxK / kGroup * 8 / 8 / 2;   // 16-byte chunks per half row, at most
+    u32x4 v[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < KPx / 16) v[c] = *reinterpret_cast<const u32x4*>(srcp + 8 * c);
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < KPx / 16) *reinterpret_cast<u32x4*>(dstp + 8 * c) = v[c];
   }
   __syncthreads();
 #pragma unroll
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
           const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
           const float gv = gate_s[m * 64 + col];
           const float uv = acc[rb][r];
-          const float hv = gv / (1.0f + __expf(-gv)) * uv;
+          const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           hs[m * 64 + col] = uint16_t(f32_to_bf16_rne(hv));
         }
     }
