@@ -18,7 +18,8 @@
 // 16 s_g is exact). The remaining sum_g (b_g - 16 s_g) X_g, X_g = sum_{k in g}
 // x_k, runs on the MFMA as 8 extra K columns per group: an exact three-part
 // bf16 split of X_g (from a side table) against b_g, again against -16 s_g,
-// and two zero columns, so that each 8-wide operand slice is one group.
+// and two zero columns, so that each 8-wide operand slice is one group; every
+// second group one such MFMA per row block covers the last two groups.
 //
 // Operand order. One 32-bit word holds codes k..k+7 (nibble i = code k+i); the
 // AND/OR unpack yields the bf16 pairs (k, k+4), (k+1, k+5), (k+2, k+6),
@@ -39,7 +40,8 @@
 //   reused by every row block.
 // Streaming: per group, the activation tile (128 rows x 64 bf16, 16-byte chunks
 //   XOR-swizzled by row) and the weight codes and scales of the 128 columns
-//   land in a 3-slot LDS ring through buffer loads that write LDS directly (no
+//   (plus the rows' side-table entries and the columns' biases) land in a
+//   3-slot LDS ring through buffer loads that write LDS directly (no
 //   registers, one scalar offset per group), issued two groups ahead; one
 //   s_waitcnt + s_barrier per group.
 // Work mapping: each XCD takes a contiguous chunk of the tile list and runs
@@ -56,8 +58,10 @@ constexpr uint32_t kNib = 0x00780078u;    // a code shifted to mantissa bits 3..
 constexpr int kSlotA = 0;                // 128 rows x 128 B
 constexpr int kSlotB = 16384;            // 4 waves x 64 lanes x 16 B of weight codes
 constexpr int kSlotS = 20480;            // 4 waves x 32 dwords: scale pairs (groups g&~1, g|1)
-constexpr int kSlotBytes = 20992;
-constexpr int kOpsPerGroup = 6;          // buffer->LDS loads per wave per group
+constexpr int kSlotBias = 20992;         // 4 waves x 32 dwords: bias pairs (groups g&~1, g|1)
+constexpr int kSlotXP = 21504;           // 128 rows x 16 B: the group's 8 side-table entries
+constexpr int kSlotBytes = 23552;
+constexpr int kOpsPerGroup = 8;          // buffer->LDS loads per wave per group
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 // s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
@@ -120,21 +124,21 @@ __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ 
 __device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
 
 // LDS of one workgroup: the ring during the K loop; afterwards the same memory
-// holds the tile's group-sum table (128 x xpart_cols bf16) and, for SwiGLU, the
-// gate tile (128 x 64 fp32) plus the h tile (128 x 64 bf16).
+// holds, for SwiGLU, the gate tile (128 x 64 fp32) plus the h tile (128 x 64 bf16).
 size_t gemm_lds_bytes(int K) {
+  (void)K;
   const size_t ring = size_t(kRing) * kSlotBytes;
-  const size_t xpart = size_t(kBlockRows) * xpart_cols(K) * 2;
   const size_t swiglu = size_t(kBlockRows) * 64 * 4 + size_t(kBlockRows) * 64 * 2;
-  return ring > xpart ? (ring > swiglu ? ring : swiglu) : (xpart > swiglu ? xpart : swiglu);
+  return ring > swiglu ? ring : swiglu;
 }
 
 // Per-wave streaming state: buffer descriptors, per-lane byte offsets.
 struct Stream {
-  __amdgpu_buffer_rsrc_t ra, rb, rs;
+  __amdgpu_buffer_rsrc_t ra, rb, rs, rbias, rxp;
   uint32_t va[4];    // activation chunk offsets (4 instructions)
   uint32_t vb;       // weight-code offset
-  uint32_t vs;       // scale offset (lanes 0..31)
+  uint32_t vs;       // scale / bias row offset of column lane%32 (lanes 0..31)
+  uint32_t vxp;      // side-table row offset of row wave*32 + lane (lanes 0..31)
 };
 
 __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int g, int wave, int lane) {
@@ -143,8 +147,34 @@ __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int
     __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + wave * 4096 + i * 1024), 16, st.va[i],
                                              g * (kGroup * 2), 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb, lds(slot + kSlotB + wave * 1024), 16, st.vb, g * 32, 0, 0);
-  if (lane < 32)
+  if (lane < 32) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rs, lds(slot + kSlotS + wave * 128), 4, st.vs, (g & ~1) * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rbias, lds(slot + kSlotBias + wave * 128), 4, st.vs, (g & ~1) * 2, 0,
+                                             0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rxp, lds(slot + kSlotXP + wave * 512), 16, st.vxp, g * 16, 0, 0);
+  }
+}
+
+// Bias term of groups g-1 (lanes 0..31) and g (lanes 32..63), g odd: one MFMA
+// per live row block with the rows' 8 side-table entries of each group against
+// (b, b, b, -16 s, -16 s, -16 s, 0, 0) of the lane's column.
+template <int NRB>
+__device__ __forceinline__ void bias_pair(const uint8_t* slot_even, const uint8_t* slot_odd, int wave, int lane,
+                                          f32x16 (&acc)[4]) {
+  const int l32 = lane & 31, half = lane >> 5;
+  const uint32_t sp = reinterpret_cast<const uint32_t*>(slot_odd + kSlotS + wave * 128)[l32];
+  const uint32_t bp = reinterpret_cast<const uint32_t*>(slot_odd + kSlotBias + wave * 128)[l32];
+  const uint32_t bb = half ? (bp >> 16) : (bp & 0xFFFFu);
+  const uint32_t sb = half ? (sp >> 16) : (sp & 0xFFFFu);
+  const uint32_t ns = f32_to_bf16_rne(-16.0f * bf16_to_f32(uint16_t(sb)));
+  const u32x4 pk = {bb | (bb << 16), bb | (ns << 16), ns | (ns << 16), 0u};
+  const bf16x8 bv = __builtin_bit_cast(bf16x8, pk);
+  const uint8_t* xp = (half ? slot_odd : slot_even) + kSlotXP;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const bf16x8 xa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xp + (rb * 32 + l32) * 16));
+    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv, acc[rb], 0, 0, 0);
+  }
 }
 
 // One 64-wide group: unpack the wave's weight codes, then per live row block a
@@ -188,6 +218,12 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
   else
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();
+  if (g & 1) {
+    // groups g-1 and g; slot (S+2)%3 still holds group g-1 until the loads
+    // below overwrite it, so its reads must have returned first
+    bias_pair<NRB>(ring + ((S + 2) % kRing) * kSlotBytes, ring + S * kSlotBytes, wave, lane, acc);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  }
   if (g + 2 < G) issue_group(st, ring + ((S + 2) % kRing) * kSlotBytes, g + 2, wave, lane);
   group_compute<NRB>(ring + S * kSlotBytes, g & 1, wave, lane, acc);
 }
@@ -258,6 +294,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   st.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.A), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q_wave), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s_glob), 0, 0x7FFFFFFF, kRsrcWord3);
+  st.rbias = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b_glob), 0, 0x7FFFFFFF, kRsrcWord3);
+  st.rxp = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Apart), 0, 0x7FFFFFFF, kRsrcWord3);
   {
     // activation DMA i of this wave fills chunk positions wave*256 + i*64 + lane:
     // row m = wave*32 + i*8 + lane/8 and chunk slot lane%8, which holds logical
@@ -270,11 +308,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
       st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
     }
     st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
-    st.vs = uint32_t(l32 * G * 2);   // scale row of column l32; + (g & ~1) * 2 per group
+    st.vs = uint32_t(l32 * G * 2);   // scale/bias row of column l32; + (g & ~1) * 2 per group
+    const int mx = wave * 32 + l32;
+    st.vxp = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KPx * 2);
   }
-
-  // source row of the group-sum table row this thread stages after the K loop
-  const int xpart_src = src_row(a, ti.r0 + min(tid >> 1, nrows - 1));
 
   // ---- prologue: groups 0 and 1 ---------------------------------------------
   issue_group(st, ring, 0, wave, lane);
@@ -291,56 +328,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   }
   __syncthreads();   // every wave is done with the ring
 
-  // ---- bias term: 8 extra K columns per group: (X parts) x (b, -16 s) ------
-  // This lane supplies, in K step sk, the operand slice of group 2 sk + half:
-  // its column's b and s of every group are loaded at once (G <= 32).
-  constexpr int kMaxPairs = kMaxK / kGroup / 2;       // 16 dword pairs of groups
-  uint32_t bpair[kMaxPairs], spair[kMaxPairs];
-  {
-    const uint32_t* bq = reinterpret_cast<const uint32_t*>(b_glob + size_t(l32) * G);
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(s_glob + size_t(l32) * G);
-#pragma unroll
-    for (int d = 0; d < kMaxPairs; ++d) {
-      bpair[d] = d < G / 2 ? bq[d] : 0u;
-      spair[d] = d < G / 2 ? sq[d] : 0u;
-    }
-  }
-  // group-sum table of the tile: thread t copies half of row t/2 (independent
-  // 16-byte loads from one source row, resolved before the K loop)
-  uint16_t* xpart_s = reinterpret_cast<uint16_t*>(ring);   // [128][KPx]
-  {
-    const uint16_t* srcp = a.Apart + size_t(xpart_src) * KPx + (tid & 1) * (KPx / 2);
-    uint16_t* dstp = xpart_s + (tid >> 1) * KPx + (tid & 1) * (KPx / 2);
-    constexpr int kMaxChunks = kMaxK / kGroup * 8 / 8 / 2;   // 16-byte chunks per half row, at most
-    u32x4 v[kMaxChunks];
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < KPx / 16) v[c] = *reinterpret_cast<const u32x4*>(srcp + 8 * c);
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < KPx / 16) *reinterpret_cast<u32x4*>(dstp + 8 * c) = v[c];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int d = 0; d < kMaxPairs; ++d) {
-    if (d < G / 2) {
-      // groups 2d (lanes 0..31) and 2d+1 (lanes 32..63)
-      const uint32_t bb = half ? (bpair[d] >> 16) : (bpair[d] & 0xFFFFu);
-      const uint32_t sb = half ? (spair[d] >> 16) : (spair[d] & 0xFFFFu);
-      const uint32_t ns = f32_to_bf16_rne(-16.0f * bf16_to_f32(uint16_t(sb)));
-      const u32x4 pk = {bb | (bb << 16), bb | (ns << 16), ns | (ns << 16), 0u};
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, pk);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (rb < nrb) {
-          const bf16x8 xa = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(xpart_s + (rb * 32 + l32) * KPx + 16 * d + 8 * half));
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv, acc[rb], 0, 0, 0);
-        }
-      }
-    }
-  }
-
   // ---- epilogues ------------------------------------------------------------
   if constexpr (EPI == kEpiF32) {
     float* out = reinterpret_cast<float*>(a.out);
@@ -352,7 +339,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         if (m < nrows) out[size_t(ti.r0 + m) * a.N + ncol] = acc[rb][r];
       }
   } else {
-    __syncthreads();   // everyone is done with xpart_s
     float* gate_s = reinterpret_cast<float*>(ring);                          // [128][64] fp32
     uint16_t* hs = reinterpret_cast<uint16_t*>(ring + kBlockRows * 64 * 4);  // [128][64] bf16
     const int col = (wave & 1) * 32 + l32;
