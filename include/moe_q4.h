@@ -148,7 +148,7 @@ int32_t moe_max_tiles(const moe_dims* dims);
  *   A           device bf16 [a_rows][K]
  *   W0, W1      host structs; W1 only for SWIGLU (same n_experts, N, K as W0),
  *               K % 128 == 0, K <= 2048; N % 64 == 0 (SWIGLU) or N % 128 == 0 (STORE_F32);
- *               q 16-byte aligned, s and b 4-byte aligned
+ *               q, s and b 16-byte aligned
  *   offsets, tile_map, num_tiles  device, as produced by moe_route with
  *               block_rows = MOE_GEMM_BLOCK_ROWS; max_tiles bounds *num_tiles
  *   workspace   device, at least moe_gemm_workspace_bytes(a_rows, K) bytes

@@ -27,23 +27,25 @@
 // the order [0,4,1,5,2,6,3,7] (prep kernel / SwiGLU epilogue), so both MFMA
 // operands list the same K indices in the same slots.
 //
-// Tiling (one workgroup = 4 wave64s = 256 threads, tile = up to 128 rows):
+// Tiling (one workgroup = 8 wave64s = 512 threads, tile = up to 128 rows):
 //   each wave owns 32 output columns of one weight matrix and all rows of the
 //   tile, as up to four 32-row MFMA blocks; only blocks that hold real rows are
 //   computed (the kernel is instantiated per live-block count), so MFMA work
 //   follows the real row count at 32-row granularity.
-//   SwiGLU: waves 0,1 = gate columns 0-31, 32-63; waves 2,3 = up columns
-//           0-31, 32-63 of the workgroup's 64 (gate and up meet in LDS at the end);
-//   STORE_F32: waves 0..3 = columns 0-31, ..., 96-127.
+//   SwiGLU: waves 0-3 = gate columns 0-127, waves 4-7 = up columns 0-127 of
+//           the workgroup's 128 (gate and up meet in LDS at the end);
+//   STORE_F32: waves 0-7 = columns 0-255.
 //   MFMA v_mfma_f32_32x32x16_bf16: per 64-wide group a wave issues one chain
 //   of 4 MFMAs per row block; one group's weight codes are unpacked once and
 //   reused by every row block.
 // Streaming: per group, the activation tile (128 rows x 64 bf16, 16-byte chunks
-//   XOR-swizzled by row) and the weight codes and scales of the 128 columns
-//   (plus the rows' side-table entries and the columns' biases) land in a
-//   3-slot LDS ring through buffer loads that write LDS directly (no
-//   registers, one scalar offset per group), issued two groups ahead; one
-//   s_waitcnt + s_barrier per group.
+//   XOR-swizzled by row), the 256 columns' weight codes and the rows'
+//   side-table entries land in a 3-slot LDS ring through buffer loads that
+//   write LDS directly (no registers, one scalar offset per group), issued two
+//   groups ahead; one s_waitcnt + s_barrier per group. Scales and biases of the
+//   256 columns are staged once per tile. Every vector-memory instruction moves
+//   16 bytes per lane: the per-CU load path, not the MFMA, limits this kernel
+//   when instructions move less.
 // Work mapping: each XCD takes a contiguous chunk of the tile list and runs
 // all column slices of its tiles (see the kernel), so activation rows and
 // expert weights are fetched into one XCD's L2 rather than into all eight.
@@ -51,21 +53,18 @@
 
 namespace moe {
 
-constexpr int kGemmThreads = 256;
-constexpr int kRing = 3;                 // LDS ring slots
+constexpr int kGemmWaves = 8;
+constexpr int kGemmThreads = kGemmWaves * 64;
+constexpr int kRing = 4;                 // LDS ring slots: group g lives in slot g % 4
 constexpr uint32_t kMagic = 0x3F803F80u;  // two bf16 1.0
 constexpr uint32_t kNib = 0x00780078u;    // a code shifted to mantissa bits 3..6 of each half
-constexpr int kSlotA = 0;                // 128 rows x 128 B
-constexpr int kSlotB = 16384;            // 4 waves x 64 lanes x 16 B of weight codes
-constexpr int kSlotS = 20480;            // 4 waves x 32 dwords: scale pairs (groups g&~1, g|1)
-constexpr int kSlotBias = 20992;         // 4 waves x 32 dwords: bias pairs (groups g&~1, g|1)
-constexpr int kSlotXP = 21504;           // 128 rows x 16 B: the group's 8 side-table entries
-constexpr int kSlotBytes = 23552;
-constexpr int kOpsPerGroup = 8;          // buffer->LDS loads per wave per group
+constexpr int kSlotA = 0;                // 128 rows x 128 B of activations
+constexpr int kSlotB = 16384;            // 8 waves x 64 lanes x 16 B of weight codes
+constexpr int kSlotXP = 24576;           // odd groups: 128 rows x 32 B, side-table entries of groups g-1, g
+constexpr int kSlotBytes = 28672;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 // s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVmGroup = 0x0F70 | kOpsPerGroup;   // one group's loads may stay in flight
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -123,129 +122,174 @@ __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ 
 
 __device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
 
-// LDS of one workgroup: the ring during the K loop; afterwards the same memory
-// holds, for SwiGLU, the gate tile (128 x 64 fp32) plus the h tile (128 x 64 bf16).
+// Scales and biases of a wave's 32 columns, staged at tile start as
+// [pair j][column][2 groups] (4 bytes per column and group pair), so that the
+// 32 lanes of one column read hit 32 consecutive LDS words.
+__host__ __device__ constexpr int staged_words(int G) { return 32 * (G / 2); }
+
+// LDS of one workgroup: the ring plus the staged scales and biases of the 256
+// columns during the K loop; afterwards, for SwiGLU, the gate tile (128 x 128
+// fp32) and the h tile (128 x 128 bf16).
 size_t gemm_lds_bytes(int K) {
-  (void)K;
-  const size_t ring = size_t(kRing) * kSlotBytes;
-  const size_t swiglu = size_t(kBlockRows) * 64 * 4 + size_t(kBlockRows) * 64 * 2;
-  return ring > swiglu ? ring : swiglu;
+  const int G = K / kGroup;
+  const size_t loop = size_t(kRing) * kSlotBytes + size_t(2) * kGemmWaves * staged_words(G) * 4;
+  const size_t swiglu = size_t(kBlockRows) * 128 * 4 + size_t(kBlockRows) * 128 * 2;
+  return loop > swiglu ? loop : swiglu;
 }
 
 // Per-wave streaming state: buffer descriptors, per-lane byte offsets.
 struct Stream {
-  __amdgpu_buffer_rsrc_t ra, rb, rs, rbias, rxp;
-  uint32_t va[4];    // activation chunk offsets (4 instructions)
+  __amdgpu_buffer_rsrc_t ra, rb, rxp;
+  uint32_t va[2];    // activation chunk offsets (2 instructions)
   uint32_t vb;       // weight-code offset
-  uint32_t vs;       // scale / bias row offset of column lane%32 (lanes 0..31)
-  uint32_t vxp;      // side-table row offset of row wave*32 + lane (lanes 0..31)
+  uint32_t vxp;      // side-table offset of (row, half) (waves 0..3, odd groups)
 };
 
-__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int g, int wave, int lane) {
+// Loads of group g into its slot: 2 activation + 1 weight-code instruction per
+// wave; for odd g, waves 0..3 also load the side-table entries of groups g-1
+// and g (32 contiguous bytes per row).
+template <int ODD>
+__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int g, int wave) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + wave * 4096 + i * 1024), 16, st.va[i],
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + wave * 2048 + i * 1024), 16, st.va[i],
                                              g * (kGroup * 2), 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb, lds(slot + kSlotB + wave * 1024), 16, st.vb, g * 32, 0, 0);
-  if (lane < 32) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rs, lds(slot + kSlotS + wave * 128), 4, st.vs, (g & ~1) * 2, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rbias, lds(slot + kSlotBias + wave * 128), 4, st.vs, (g & ~1) * 2, 0,
+  if (ODD && wave < 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rxp, lds(slot + kSlotXP + wave * 1024), 16, st.vxp, (g - 1) * 16, 0,
                                              0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rxp, lds(slot + kSlotXP + wave * 512), 16, st.vxp, g * 16, 0, 0);
-  }
 }
 
-// Bias term of groups g-1 (lanes 0..31) and g (lanes 32..63), g odd: one MFMA
-// per live row block with the rows' 8 side-table entries of each group against
-// (b, b, b, -16 s, -16 s, -16 s, 0, 0) of the lane's column.
-template <int NRB>
-__device__ __forceinline__ void bias_pair(const uint8_t* slot_even, const uint8_t* slot_odd, int wave, int lane,
-                                          f32x16 (&acc)[4]) {
-  const int l32 = lane & 31, half = lane >> 5;
-  const uint32_t sp = reinterpret_cast<const uint32_t*>(slot_odd + kSlotS + wave * 128)[l32];
-  const uint32_t bp = reinterpret_cast<const uint32_t*>(slot_odd + kSlotBias + wave * 128)[l32];
-  const uint32_t bb = half ? (bp >> 16) : (bp & 0xFFFFu);
-  const uint32_t sb = half ? (sp >> 16) : (sp & 0xFFFFu);
-  const uint32_t ns = f32_to_bf16_rne(-16.0f * bf16_to_f32(uint16_t(sb)));
-  const u32x4 pk = {bb | (bb << 16), bb | (ns << 16), ns | (ns << 16), 0u};
-  const bf16x8 bv = __builtin_bit_cast(bf16x8, pk);
-  const uint8_t* xp = (half ? slot_odd : slot_even) + kSlotXP;
+// Wait until at most N of this wave's buffer loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(kWaitVm0 | N);
+}
+
+__device__ __forceinline__ void read_frags(const uint8_t* slot, int m, int half, bf16x8 (&f)[4]) {
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const bf16x8 xa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xp + (rb * 32 + l32) * 16));
-    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv, acc[rb], 0, 0, 0);
-  }
+  for (int c = 0; c < 4; ++c)
+    f[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + c)));
 }
 
-// One 64-wide group: unpack the wave's weight codes, then per live row block a
-// chain of 4 MFMAs, folded into acc with 16 times the group scale.
-template <int NRB>
-__device__ __forceinline__ void group_compute(const uint8_t* slot, int godd, int wave, int lane, f32x16 (&acc)[4]) {
+__device__ __forceinline__ void fold(const f32x16& p, float sc, f32x16& acc) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(sc, p[r], acc[r]);
+}
+
+// Step g of the K loop (S = g % 4, a compile-time slot). Group g is in slot S;
+// groups g+1, g+2 may still be landing; group g+3 is issued into slot
+// (S+3)%4, which held group g-1.
+//
+// Per live row block rb: a chain of 4 MFMAs over the group's 64 K values
+// gives P_g, folded as acc += 16 s_g P_g. The fold of a block runs while the
+// next block's chain is in the matrix pipe; the last block's fold is carried
+// into the next step (pend, pend_sc). For odd g one more MFMA per block adds
+// the bias term of groups g-1 and g (lanes 0..31: group g-1, 32..63: group g)
+// from the rows' 8 side-table entries per group against
+// (b, b, b, -16 s, -16 s, -16 s, 0, 0) of the lane's column.
+template <int NRB, int S>
+__device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, const uint32_t* s_pairs,
+                                          const uint32_t* b_pairs, int g, int G, int wave, int lane, uint32_t& s_pair,
+                                          uint32_t& b_pair, f32x16& pend, float& pend_sc, f32x16 (&acc)[4]) {
+  constexpr int ODD = S & 1;
   const int l32 = lane & 31, half = lane >> 5;
-  const uint32_t nib = kNib, magic = kMagic;
+  // this wave's loads of group g have landed once at most those of g+1 and
+  // g+2 are outstanding; the barrier makes it so for every wave, and orders
+  // every wave's reads of slot (S+3)%4 (previous step) before its refill
+  // (a wave issues 3 loads per group, waves 0..3 one more for odd groups)
+  if (g + 2 < G) {
+    if (wave < 4)
+      wait_vm<7>();
+    else
+      wait_vm<6>();
+  } else if (g + 1 < G) {
+    if (!ODD && wave < 4)
+      wait_vm<4>();
+    else
+      wait_vm<3>();
+  } else {
+    wait_vm<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  if (g + 3 < G) issue_group<!ODD>(st, ring + ((S + 3) % kRing) * kSlotBytes, g + 3, wave);
+  const uint8_t* slot = ring + S * kSlotBytes;
+
   const u32x4 w = *reinterpret_cast<const u32x4*>(slot + kSlotB + wave * 1024 + lane * 16);
-  const uint16_t sbits = reinterpret_cast<const uint16_t*>(slot + kSlotS + wave * 128)[2 * l32 + godd];
-  const float sc = 16.0f * bf16_to_f32(sbits);
+  bf16x8 fa[2][4];
+  read_frags(slot, l32, half, fa[0]);
+  if (!ODD) {
+    s_pair = s_pairs[(g >> 1) * 32];
+    b_pair = b_pairs[(g >> 1) * 32];
+  }
+  const uint32_t nib = kNib, magic = kMagic;
   const bf16x8 b0 = unpack_word(w.x, nib, magic), b1 = unpack_word(w.y, nib, magic),
                b2 = unpack_word(w.z, nib, magic), b3 = unpack_word(w.w, nib, magic);
-  f32x16 p[NRB];
+  const float sc = 16.0f * __uint_as_float(ODD ? (s_pair & 0xFFFF0000u) : (s_pair << 16));
+  bf16x8 bv;
+  if (ODD) {
+    const int sh = half << 4;
+    const uint32_t sb = (s_pair >> sh) & 0xFFFFu, bb = (b_pair >> sh) & 0xFFFFu;
+    // -16 s is exact in bf16 (a power-of-two multiple), so truncating the
+    // fp32 product is the rounding
+    const uint32_t ns = __float_as_uint(-16.0f * __uint_as_float(sb << 16)) >> 16;
+    const u32x4 pk = {bb | (bb << 16), bb | (ns << 16), ns | (ns << 16), 0u};
+    bv = __builtin_bit_cast(bf16x8, pk);
+  }
+  f32x16 last;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const int m = rb * 32 + l32;
-    const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 0)));
-    const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 1)));
-    const bf16x8 a2 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 2)));
-    const bf16x8 a3 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + 3)));
-    f32x16 q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, f32x16{}, 0, 0, 0);
-    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, q, 0, 0, 0);
-    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2, q, 0, 0, 0);
-    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b3, q, 0, 0, 0);
-    p[rb] = q;
+    if (rb + 1 < NRB) read_frags(slot, (rb + 1) * 32 + l32, half, fa[(rb + 1) & 1]);
+    bf16x8 xa;
+    if (ODD)
+      xa = __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4*>(slot + kSlotXP + (rb * 32 + l32) * 32 + half * 16));
+    const bf16x8(&f)[4] = fa[rb & 1];
+    f32x16 q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], b0, f32x16{}, 0, 0, 0);
+    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[1], b1, q, 0, 0, 0);
+    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[2], b2, q, 0, 0, 0);
+    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[3], b3, q, 0, 0, 0);
+    if (rb == 0)
+      fold(pend, pend_sc, acc[NRB - 1]);
+    else
+      fold(last, sc, acc[rb - 1]);
+    if (ODD) acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv, acc[rb], 0, 0, 0);
+    last = q;
   }
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[rb][r] = __builtin_fmaf(sc, p[rb][r], acc[rb][r]);
+  pend = last;
+  pend_sc = sc;
 }
 
-template <int NRB, int S>
-__device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g, int G, int wave, int lane,
-                                          f32x16 (&acc)[4]) {
-  // group g landed for this wave; the barrier makes it so for every wave and
-  // frees slot (S+2)%3, last read in the previous step
-  if (g + 1 < G)
-    __builtin_amdgcn_s_waitcnt(kWaitVmGroup);
-  else
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __builtin_amdgcn_s_barrier();
-  if (g & 1) {
-    // groups g-1 and g; slot (S+2)%3 still holds group g-1 until the loads
-    // below overwrite it, so its reads must have returned first
-    bias_pair<NRB>(ring + ((S + 2) % kRing) * kSlotBytes, ring + S * kSlotBytes, wave, lane, acc);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  }
-  if (g + 2 < G) issue_group(st, ring + ((S + 2) % kRing) * kSlotBytes, g + 2, wave, lane);
-  group_compute<NRB>(ring + S * kSlotBytes, g & 1, wave, lane, acc);
-}
-
+// G is even (K is a multiple of 128).
 template <int NRB>
-__device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, int G, int wave, int lane,
-                                          f32x16 (&acc)[4]) {
-  // unrolled by the ring size so every slot offset is a constant
+__device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, const uint32_t* s_pairs,
+                                          const uint32_t* b_pairs, int G, int wave, int lane, f32x16 (&acc)[4]) {
+  uint32_t s_pair = 0, b_pair = 0;
+  f32x16 pend = f32x16{};
+  float pend_sc = 0.0f;
+  // unrolled by the ring size so every slot offset and group parity is a constant
   for (int g = 0; g < G; g += kRing) {
-    loop_step<NRB, 0>(st, ring, g, G, wave, lane, acc);
-    if (g + 1 < G) loop_step<NRB, 1>(st, ring, g + 1, G, wave, lane, acc);
-    if (g + 2 < G) loop_step<NRB, 2>(st, ring, g + 2, G, wave, lane, acc);
+    loop_step<NRB, 0>(st, ring, s_pairs, b_pairs, g, G, wave, lane, s_pair, b_pair, pend, pend_sc, acc);
+    loop_step<NRB, 1>(st, ring, s_pairs, b_pairs, g + 1, G, wave, lane, s_pair, b_pair, pend, pend_sc, acc);
+    if (g + 2 < G) {
+      loop_step<NRB, 2>(st, ring, s_pairs, b_pairs, g + 2, G, wave, lane, s_pair, b_pair, pend, pend_sc, acc);
+      loop_step<NRB, 3>(st, ring, s_pairs, b_pairs, g + 3, G, wave, lane, s_pair, b_pair, pend, pend_sc, acc);
+    }
   }
+  fold(pend, pend_sc, acc[NRB - 1]);
 }
 
 template <int EPI>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_q4_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K;
   const int G = K / kGroup;
   const int KPx = xpart_cols(K);
   uint8_t* ring = smem;
+  const int SW = staged_words(G);
+  uint32_t* s_st = reinterpret_cast<uint32_t*>(smem + kRing * kSlotBytes);   // [8 waves][SW]
+  uint32_t* b_st = s_st + kGemmWaves * SW;                                    // [8 waves][SW]
 
   // XCD-aware work mapping: workgroups are dispatched round-robin over the 8
   // XCDs (blockIdx % 8). The tile list (shared tiles, then routed tiles in
@@ -274,18 +318,22 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   const int half = lane >> 5;
 
   // ---- this wave's weight matrix and its 32 columns ------------------------
+  // A wave past the last column (N not a multiple of the workgroup's width)
+  // streams the last 32 columns again and stores nothing.
   int col0;
   const QStack* mat;
   if constexpr (EPI == kEpiF32) {
-    col0 = nt * 128 + wave * 32;
+    col0 = nt * 256 + wave * 32;
     mat = &a.w0[stack];
   } else {
-    col0 = nt * 64 + (wave & 1) * 32;
-    mat = (wave >> 1) ? &a.w1[stack] : &a.w0[stack];
+    col0 = nt * 128 + (wave & 3) * 32;
+    mat = (wave >> 2) ? &a.w1[stack] : &a.w0[stack];
   }
+  const bool live = col0 < a.N;
+  col0 = live ? col0 : a.N - 32;
   const size_t wrow0 = size_t(el) * a.N + col0;
   const uint32_t* q_wave = mat->q + wrow0 * size_t(K / 8);
-  const uint16_t* s_glob = mat->s + wrow0 * size_t(G);     // 4-byte aligned: G is even
+  const uint16_t* s_glob = mat->s + wrow0 * size_t(G);     // 32 contiguous rows of G scales
   const uint16_t* b_glob = mat->b + wrow0 * size_t(G);
   const int ncol = col0 + l32;
 
@@ -293,38 +341,55 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   Stream st;
   st.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.A), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q_wave), 0, 0x7FFFFFFF, kRsrcWord3);
-  st.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s_glob), 0, 0x7FFFFFFF, kRsrcWord3);
-  st.rbias = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b_glob), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rxp = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Apart), 0, 0x7FFFFFFF, kRsrcWord3);
   {
-    // activation DMA i of this wave fills chunk positions wave*256 + i*64 + lane:
-    // row m = wave*32 + i*8 + lane/8 and chunk slot lane%8, which holds logical
-    // chunk (lane%8) ^ swz(m) = (lane%8) ^ (lane/8) ^ (i%2)
+    // activation load i of wave w fills chunk positions w*128 + i*64 + lane:
+    // row m = w*16 + i*8 + lane/8 and chunk slot lane%8, which holds logical
+    // chunk (lane%8) ^ swz(m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wave * 32 + i * 8 + (lane >> 3);
+    for (int i = 0; i < 2; ++i) {
+      const int m = wave * 16 + i * 8 + (lane >> 3);
       const int cidx = (lane & 7) ^ swz(m);
       const int r = ti.r0 + min(m, nrows - 1);     // padding rows re-read the last real row
       st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
     }
     st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
-    st.vs = uint32_t(l32 * G * 2);   // scale/bias row of column l32; + (g & ~1) * 2 per group
-    const int mx = wave * 32 + l32;
-    st.vxp = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KPx * 2);
+    // side-table load of wave w (0..3): row w*32 + lane/2, 16-byte half lane%2
+    const int mx = (wave & 3) * 32 + (lane >> 1);
+    st.vxp = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KPx * 2) + uint32_t((lane & 1) * 16);
   }
 
-  // ---- prologue: groups 0 and 1 ---------------------------------------------
-  issue_group(st, ring, 0, wave, lane);
-  if (G > 1) issue_group(st, ring + kSlotBytes, 1, wave, lane);
+  // ---- prologue: scales and biases of the wave's 32 columns, groups 0..2 ----
+  {
+    // word p = j*32 + c of the wave's staging area holds column c's values of
+    // groups 2j, 2j+1, i.e. 4 bytes at (c*G + 2j)*2 of the column block
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s_glob), 0, 0x7FFFFFFF, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rbias =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b_glob), 0, 0x7FFFFFFF, kRsrcWord3);
+    for (int p0 = 0; p0 < SW; p0 += 64) {
+      const int p = p0 + lane;
+      if (p < SW) {
+        const uint32_t off = uint32_t(((p & 31) * G + 2 * (p >> 5)) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(s_st + wave * SW + p0), 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds(b_st + wave * SW + p0), 4, off, 0, 0, 0);
+      }
+    }
+  }
+  issue_group<0>(st, ring, 0, wave);
+  issue_group<1>(st, ring + kSlotBytes, 1, wave);
+  if (G > 2) issue_group<0>(st, ring + 2 * kSlotBytes, 2, wave);
 
   f32x16 acc[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x16{};
+  const uint32_t* s_pairs = s_st + wave * SW + l32;
+  const uint32_t* b_pairs = b_st + wave * SW + l32;
   switch (nrb) {
-    case 1: main_loop<1>(st, ring, G, wave, lane, acc); break;
-    case 2: main_loop<2>(st, ring, G, wave, lane, acc); break;
-    case 3: main_loop<3>(st, ring, G, wave, lane, acc); break;
-    default: main_loop<4>(st, ring, G, wave, lane, acc); break;
+    case 1: main_loop<1>(st, ring, s_pairs, b_pairs, G, wave, lane, acc); break;
+    case 2: main_loop<2>(st, ring, s_pairs, b_pairs, G, wave, lane, acc); break;
+    case 3: main_loop<3>(st, ring, s_pairs, b_pairs, G, wave, lane, acc); break;
+    default: main_loop<4>(st, ring, s_pairs, b_pairs, G, wave, lane, acc); break;
   }
   __syncthreads();   // every wave is done with the ring
 
@@ -336,63 +401,64 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (m < nrows) out[size_t(ti.r0 + m) * a.N + ncol] = acc[rb][r];
+        if (live && m < nrows) out[size_t(ti.r0 + m) * a.N + ncol] = acc[rb][r];
       }
   } else {
-    float* gate_s = reinterpret_cast<float*>(ring);                          // [128][64] fp32
-    uint16_t* hs = reinterpret_cast<uint16_t*>(ring + kBlockRows * 64 * 4);  // [128][64] bf16
-    const int col = (wave & 1) * 32 + l32;
-    if (wave < 2) {
+    float* gate_s = reinterpret_cast<float*>(ring);                           // [128][128] fp32
+    uint16_t* hs = reinterpret_cast<uint16_t*>(ring + kBlockRows * 128 * 4);  // [128][128] bf16
+    const int col = (wave & 3) * 32 + l32;
+    if (wave < 4) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          gate_s[m * 64 + col] = acc[rb][r];
+          gate_s[m * 128 + col] = acc[rb][r];
         }
     }
     __syncthreads();
-    if (wave >= 2) {
+    if (wave >= 4) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float gv = gate_s[m * 64 + col];
+          const float gv = gate_s[m * 128 + col];
           const float uv = acc[rb][r];
           const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-          hs[m * 64 + col] = uint16_t(f32_to_bf16_rne(hv));
+          hs[m * 128 + col] = uint16_t(f32_to_bf16_rne(hv));
         }
     }
     __syncthreads();
+    // thread t: row t/4, quarter t%4 = 32 columns; quarters (0,1) and (2,3)
+    // are the two 64-wide groups of h this workgroup produced
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-    const int srow = tid >> 1, shalf = tid & 1;
+    const int srow = tid >> 2, sq = tid & 3;
     const int row = ti.r0 + srow;
     u32x4 ch[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ch[i] = *reinterpret_cast<const u32x4*>(hs + srow * 64 + shalf * 32 + 8 * i);
+    for (int i = 0; i < 4; ++i) ch[i] = *reinterpret_cast<const u32x4*>(hs + srow * 128 + sq * 32 + 8 * i);
     if constexpr (EPI == kEpiSwigluInternal) {
       double part = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) part += chunk_sum_f64(ch[i]);
       const float X = float(part + __shfl_xor(part, 1, kWave));
       if (srow < nrows) {
-        uint16_t* dst = out + size_t(row) * a.N + nt * 64 + shalf * 32;
+        uint16_t* dst = out + size_t(row) * a.N + nt * 128 + sq * 32;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = permute_chunk(ch[i]);
-        const int KPo = xpart_cols(a.N);
-        uint16_t* xp = a.out_part + size_t(row) * KPo;
-        if (shalf == 0) {
+        if ((sq & 1) == 0) {
+          const int go = 2 * nt + (sq >> 1);   // group of h this pair of quarters covers
           uint16_t h, m, l;
           split3_bf16(X, h, m, l);
           const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
                            uint32_t(m) | (uint32_t(l) << 16), 0u};
-          *reinterpret_cast<u32x4*>(xp + 8 * nt) = e;
+          *reinterpret_cast<u32x4*>(a.out_part + size_t(row) * xpart_cols(a.N) + 8 * go) = e;
         }
       }
     } else {
-      if (srow < nrows) {
-        uint16_t* dst = out + size_t(row) * a.N + nt * 64 + shalf * 32;
+      if (srow < nrows && nt * 128 + sq * 32 < a.N) {
+        uint16_t* dst = out + size_t(row) * a.N + nt * 128 + sq * 32;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = ch[i];
       }

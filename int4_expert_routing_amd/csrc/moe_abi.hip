@@ -86,7 +86,7 @@ int check_weights(const moe_q4_weights* w, int n, int N, int K) {
   if (!w->q || !w->s || !w->b) return MOE_ERR_NULL;
   if (w->n_experts != n || w->N != N || w->K != K) return MOE_ERR_SHAPE;
   if (!aligned16(w->q)) return MOE_ERR_ALIGN;
-  if (!aligned4(w->s) || !aligned4(w->b)) return MOE_ERR_ALIGN;
+  if (!aligned16(w->s) || !aligned16(w->b)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -227,10 +227,10 @@ int moe_grouped_gemm_q4(const uint16_t* A, int32_t a_rows, const int32_t* sorted
   ga.out = out;
   int epi;
   if (epilogue == MOE_EPI_STORE_F32) {
-    ga.NT = N / 128;
+    ga.NT = ceil_div(N, 256);
     epi = kEpiF32;
   } else {
-    ga.NT = N / 64;
+    ga.NT = ceil_div(N, 128);
     epi = kEpiSwigluNatural;
   }
   return launch_gemm(ga, epi, max_tiles, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -330,7 +330,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.shared_rows = T;
   g1.N = I;
   g1.K = H;
-  g1.NT = I / 64;
+  g1.NT = I / 128;
   g1.out = h;
   g1.out_part = h_part;
   if (launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
@@ -349,7 +349,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g2.w1[1] = g2.w0[1];
   g2.N = H;
   g2.K = I;
-  g2.NT = H / 128;
+  g2.NT = ceil_div(H, 256);
   g2.out = Y;
   g2.out_part = nullptr;
   if (launch_gemm(g2, kEpiF32, n_sh + max_routed, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
