@@ -49,15 +49,13 @@
 // Work mapping: each XCD takes a contiguous chunk of the tile list and runs
 // all column slices of its tiles (see the kernel), so activation rows and
 // expert weights are fetched into one XCD's L2 rather than into all eight.
-#include "moe_internal.h"
+#include "gemm_tiles.h"
 
 namespace moe {
 
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kRing = 4;                 // LDS ring slots: group g lives in slot g % 4
-constexpr uint32_t kMagic = 0x3F803F80u;  // two bf16 1.0
-constexpr uint32_t kNib = 0x00780078u;    // a code shifted to mantissa bits 3..6 of each half
 constexpr int kSlotA = 0;                // 128 rows x 128 B of activations
 constexpr int kSlotB = 16384;            // 8 waves x 64 lanes x 16 B of weight codes
 constexpr int kSlotXP = 24576;           // odd groups: 128 rows x 32 B, side-table entries of groups g-1, g
@@ -67,50 +65,6 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (g
 constexpr int kWaitVm0 = 0x0F70;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-struct TileInfo {
-  int e, r0, r1;
-};
-
-__device__ __forceinline__ bool tile_info(const GemmArgs& a, int tile, TileInfo& ti) {
-  if (tile < a.n_shared_tiles) {
-    ti.e = a.E;
-    ti.r0 = a.routed_rows + tile * kBlockRows;
-    ti.r1 = min(ti.r0 + kBlockRows, a.routed_rows + a.shared_rows);
-    return true;
-  }
-  const int i = tile - a.n_shared_tiles;
-  if (i >= *a.num_tiles) return false;
-  ti.e = a.tile_map[2 * i];
-  ti.r0 = a.tile_map[2 * i + 1];
-  ti.r1 = min(ti.r0 + kBlockRows, a.offsets[ti.e + 1]);
-  return true;
-}
-
-__device__ __forceinline__ int src_row(const GemmArgs& a, int r) {
-  if (r >= a.routed_rows) return r - a.shared_src_base;
-  return a.sorted_rows ? a.sorted_rows[r] / a.row_div : r;
-}
-
-// (a & m) | c in one VALU op. The VOP3 encoding takes no literal constants, so
-// the mask and the magic value are passed in registers.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(c));
-  return d;
-}
-
-// Word w holds codes k..k+7 (nibble i = code k+i). Register pair i gets codes
-// (k+i, k+i+4), which sit at bits 4i and 4i+16; each is moved to mantissa bits
-// 3..6 of its half (shift by 3 - 4i) and ORed into bf16 1.0.
-__device__ __forceinline__ bf16x8 unpack_word(uint32_t w, uint32_t nib, uint32_t magic) {
-  u32x4 r;
-  r.x = and_or(w << 3, nib, magic);
-  r.y = and_or(w >> 1, nib, magic);
-  r.z = and_or(w >> 5, nib, magic);
-  r.w = and_or(w >> 9, nib, magic);
-  return __builtin_bit_cast(bf16x8, r);
-}
 
 // Row m of an activation tile holds its 8 16-byte chunks permuted by
 // c -> c ^ swz(m). Within any 16 consecutive rows, (m & 1, chunk slot) never

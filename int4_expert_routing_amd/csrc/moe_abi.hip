@@ -330,10 +330,16 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.shared_rows = T;
   g1.N = I;
   g1.K = H;
-  g1.NT = I / 128;
+  // few tokens: every tile has at most kDecodeMaxRows rows, and the weight
+  // stream, not the MFMA, bounds the layer
+  const bool decode = T <= kDecodeMaxRows && decode_supported(I, H, kEpiSwigluInternal) &&
+                      decode_supported(H, I, kEpiF32);
+  g1.NT = decode ? I / 64 : I / 128;
   g1.out = h;
   g1.out_part = h_part;
-  if (launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s) != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+  const hipError_t e1 = decode ? launch_decode(g1, kEpiSwigluInternal, n_sh + max_routed, s)
+                               : launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s);
+  if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
   // 6. down grouped GEMM (fp32 rows)
   float* Y = at<float>(ws, L.Y);
@@ -349,10 +355,12 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g2.w1[1] = g2.w0[1];
   g2.N = H;
   g2.K = I;
-  g2.NT = ceil_div(H, 256);
+  g2.NT = decode ? H / 128 : ceil_div(H, 256);
   g2.out = Y;
   g2.out_part = nullptr;
-  if (launch_gemm(g2, kEpiF32, n_sh + max_routed, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+  const hipError_t e2 = decode ? launch_decode(g2, kEpiF32, n_sh + max_routed, s)
+                               : launch_gemm(g2, kEpiF32, n_sh + max_routed, s);
+  if (e2 != hipSuccess || !mark(4)) return MOE_ERR_HIP;
 
   // 7. weighted combine + shared expert, bf16 output
   if (launch_combine(Y, wts, row_of_pair, T, k, H, routed_rows, y, s) != hipSuccess || !mark(5)) return MOE_ERR_HIP;

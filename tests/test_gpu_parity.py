@@ -13,7 +13,7 @@ import oracle.moe_oracle as om
 from int4_expert_routing_amd import _lib, ops
 from synth import Q4Weights, make_config, make_layer
 from tests.helpers import (LOGIT_ABS_TOL, WEIGHT_ABS_TOL, assert_close_bf16, rel_l2, max_abs_frac,
-                           tiny_layer)
+                           resample_close_calls, tiny_layer)
 
 pytestmark = pytest.mark.gpu
 
@@ -250,6 +250,33 @@ def test_layer_full_shape_decode(dev, name):
     inp = make_config(name, seed=0, bias_mode="random")
     g = run_layer(dev, inp)
     check_layer(inp, g, tokens=list(range(inp.T)))
+
+
+# Few-token calls (T <= 8) run the decode-shaped kernels; these shapes cover each
+# of their reduction lengths (K = 256, 512, 1024, 2048) and every row count 1..8
+# of a tile, with the general path just above the threshold (T = 9) beside them.
+@pytest.mark.parametrize("T,H,I,E,k,bias_mode,seed", [
+    (1, 256, 256, 16, 2, "random", 0),
+    (2, 256, 256, 16, 2, "sym", 1),
+    (3, 256, 256, 16, 2, "random", 2),
+    (5, 1024, 512, 16, 4, "random", 3),
+    (8, 256, 256, 16, 2, "random", 4),
+    (8, 256, 256, 16, 16, "random", 5),      # k = E: every expert gets all 8 rows
+    (7, 512, 1024, 32, 8, "sym", 6),
+    (9, 256, 256, 16, 2, "random", 7),       # above the threshold: grouped GEMM path
+])
+def test_layer_few_tokens(dev, T, H, I, E, k, bias_mode, seed):
+    print(f"layer few tokens T={T} H={H} I={I} E={E} k={k} {bias_mode} seed={seed}", flush=True)
+    inp = resample_close_calls(make_layer(T=T, H=H, I=I, E=E, k=k, seed=seed, bias_mode=bias_mode))
+    g = run_layer(dev, inp)
+    check_layer(inp, g)
+
+
+def test_layer_decode8_zipf_seeds(dev):
+    print("layer decode8 zipf seeds 1, 2", flush=True)
+    for seed in (1, 2):
+        inp = make_config("decode8", seed=seed, bias_mode="random", zipf=1.2)
+        check_layer(inp, run_layer(dev, inp), tokens=list(range(inp.T)))
 
 
 def test_layer_full_shape_prefill512_all_tokens(dev):
