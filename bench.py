@@ -4,14 +4,17 @@ A step is one moe_layer_forward over one batch of synthetic tokens: router GEMM,
 top-k, routing tables, gate/up grouped GEMM with SwiGLU, down grouped GEMM,
 shared expert and combine. Inputs are resident in HBM before the timed region.
 
-Prints one JSON line (see the contract in the design doc): value = tokens/s of the
-layer, roofline = the gate/up grouped GEMM (the dominant kernel) against the
-bf16 dense MFMA peak, cpu_baseline = the fp64 oracle on the host cores.
+Prints one JSON line: value = tokens/s of the T=4096 layer, roofline = the
+gate/up grouped GEMM (the dominant kernel) against the bf16 dense MFMA peak,
+cpu_baseline = the fp64 oracle on the host cores, decode = the T=1 and T=8
+layer as HBM bytes per second (weights rotated over 8 device-resident layer
+sets so that the 256 MB last-level cache cannot hold the working set).
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -39,6 +42,87 @@ def q4_bytes(N, K):
     return N * K // 2 + 4 * N * (K // 64)
 
 
+PER_EXPERT_BYTES = 3 * q4_bytes(512, 2048)    # gate, up, down of one expert at H=2048, I=512
+
+
+def random_weights(ops, torch, dev, E, H, I, seed):
+    """A layer of random weights drawn on the device (same distributions as the
+    synthetic host generator: uniform codes, s = |N(0,1)|*0.02, b = -8s)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+
+    def stack(n, N, K):
+        q = torch.randint(-2**31, 2**31 - 1, (n, N, K // 8), dtype=torch.int32, device=dev, generator=g)
+        sc = (torch.randn(n, N, K // 64, device=dev, generator=g).abs() * 0.02).to(torch.bfloat16)
+        b = (sc.float() * -8.0).to(torch.bfloat16)
+        return ops.Q4Stack(q, sc, b)
+
+    rw = (torch.randn(E, H, device=dev, generator=g) / math.sqrt(H)).to(torch.bfloat16)
+    return ops.MoEWeights(router_w=rw, gate=stack(E, I, H), up=stack(E, I, H), down=stack(E, H, I),
+                          sh_gate=stack(1, I, H), sh_up=stack(1, I, H), sh_down=stack(1, H, I))
+
+
+def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, reps=25):
+    """Layer calls at T tokens, captured as one HIP graph of `calls` calls that
+    cycle over n_sets weight sets and `calls` fresh inputs, replayed `reps`
+    times; bytes per call = the distinct experts the call routes to, plus the
+    shared expert, the router matrix, x and y."""
+    import ctypes
+    E, H, I = w0.E, w0.H, w0.I
+    sets = [w0] + [random_weights(ops, torch, dev, E, H, I, 1000 + i) for i in range(n_sets - 1)]
+    structs = [[s.c_struct() for s in (w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)] for w in sets]
+    gx = torch.Generator(device=dev)
+    gx.manual_seed(77)
+    xs = [torch.randn(T, H, device=dev, generator=gx).to(torch.bfloat16) for _ in range(calls)]
+    ys = [torch.empty(T, H, dtype=torch.bfloat16, device=dev) for _ in range(calls)]
+    ids = [torch.empty(T, k, dtype=torch.int32, device=dev) for _ in range(calls)]
+    dims = _lib.MoeDims(T, H, I, E, k, 0)
+    ws = torch.empty(int(lib.moe_workspace_bytes(ctypes.byref(dims))), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        w = sets[i % n_sets]
+        st = lib.moe_layer_forward(
+            ctypes.c_void_p(xs[i].data_ptr()), ctypes.c_void_p(w.router_w.data_ptr()), None,
+            *[ctypes.byref(s) for s in structs[i % n_sets]], ctypes.byref(dims), ctypes.c_void_p(ys[i].data_ptr()),
+            None, ctypes.c_void_p(ids[i].data_ptr()), None, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        _lib.check(st, "moe_layer_forward")
+
+    for i in range(calls):
+        call(i)
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    t0 = time.perf_counter()
+    for i in range(calls):
+        call(i)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) * 1e6 / calls
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(calls):
+            call(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+    same = all(torch.equal(a, b) for a, b in zip(eager, ys))
+    distinct = [len(set(t.flatten().tolist())) for t in ids]
+    bytes_per_call = [(d + 1) * PER_EXPERT_BYTES + E * H * 2 + 2 * T * H * 2 for d in distinct]
+    avg_bytes = float(np.mean(bytes_per_call))
+    gbs = avg_bytes / (us * 1e-6) / 1e9
+    return {"T": T, "us_per_layer": us, "GB_per_s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+            "bytes_per_layer": avg_bytes, "distinct_experts_avg": float(np.mean(distinct)),
+            "eager_us_per_layer": eager_us, "graph_replay_matches_eager": bool(same),
+            "method": f"HIP graph of {calls} layer calls over {n_sets} weight sets and {calls} inputs, "
+                      f"{reps} replays timed with events"}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -47,6 +131,7 @@ def parse():
     p.add_argument("--config", default="prefill4096")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
     return p.parse_args()
 
 
@@ -163,6 +248,13 @@ def main():
                      "algorithmic_flops_per_launch": gu_flops},
         "weight_bytes": weight_bytes,
     }
+    if not args.no_decode:
+        out["decode"] = {}
+        for dname in ("decode1", "decode8"):
+            dinp = make_config(dname, seed=args.seed)
+            dw = ops.MoEWeights.from_host(dinp, dev)
+            out["decode"][dname] = decode_measure(lib, _lib, ops, torch, dev, dw, dinp.T, dinp.k)
+            del dw
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

@@ -274,10 +274,16 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   const int nblk = ceil_div(T, kRouteTokens);
   const int bm = kBlockRows;
 
+  // few tokens: every tile has at most kDecodeMaxRows rows, and the weight
+  // stream, not the MFMA, bounds the layer (decode-shaped kernels, which read x
+  // in natural order and need no group-sum tables)
+  const bool decode = T <= kDecodeMaxRows && decode_supported(I, H, kEpiSwigluInternal) &&
+                      decode_supported(H, I, kEpiF32);
+
   // 1. activations: permuted chunk order + group sums
   uint16_t* x_perm = at<uint16_t>(ws, L.x_perm);
   uint16_t* x_part = at<uint16_t>(ws, L.x_part);
-  if (launch_prep_rows(x, T, H, x_perm, x_part, s) != hipSuccess || !mark(1)) return MOE_ERR_HIP;
+  if ((!decode && launch_prep_rows(x, T, H, x_perm, x_part, s) != hipSuccess) || !mark(1)) return MOE_ERR_HIP;
 
   // 2-4. router GEMM, top-k, histogram, scan, scatter, block map
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
@@ -330,14 +336,11 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.shared_rows = T;
   g1.N = I;
   g1.K = H;
-  // few tokens: every tile has at most kDecodeMaxRows rows, and the weight
-  // stream, not the MFMA, bounds the layer
-  const bool decode = T <= kDecodeMaxRows && decode_supported(I, H, kEpiSwigluInternal) &&
-                      decode_supported(H, I, kEpiF32);
-  g1.NT = decode ? I / 64 : I / 128;
+  if (decode) g1.A = x;
+  g1.NT = decode ? I / 16 : I / 128;
   g1.out = h;
   g1.out_part = h_part;
-  const hipError_t e1 = decode ? launch_decode(g1, kEpiSwigluInternal, n_sh + max_routed, s)
+  const hipError_t e1 = decode ? launch_decode(g1, kEpiSwigluInternal, true, n_sh + max_routed, s)
                                : launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s);
   if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
@@ -355,10 +358,10 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g2.w1[1] = g2.w0[1];
   g2.N = H;
   g2.K = I;
-  g2.NT = decode ? H / 128 : ceil_div(H, 256);
+  g2.NT = decode ? H / 32 : ceil_div(H, 256);
   g2.out = Y;
   g2.out_part = nullptr;
-  const hipError_t e2 = decode ? launch_decode(g2, kEpiF32, n_sh + max_routed, s)
+  const hipError_t e2 = decode ? launch_decode(g2, kEpiF32, false, n_sh + max_routed, s)
                                : launch_gemm(g2, kEpiF32, n_sh + max_routed, s);
   if (e2 != hipSuccess || !mark(4)) return MOE_ERR_HIP;
 

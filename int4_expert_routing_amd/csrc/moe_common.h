@@ -8,7 +8,7 @@ namespace moe {
 
 constexpr int kGroup = 64;        // weights per quantisation group along K
 constexpr int kBlockRows = 128;   // rows per GEMM tile
-constexpr int kRouteTokens = 32;  // tokens per routing workgroup
+constexpr int kRouteTokens = 16;  // tokens per routing block (top-k, histogram, scatter)
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -80,8 +80,11 @@ hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipS
 // of a layer call with T <= kDecodeMaxRows tokens).
 constexpr int kDecodeMaxRows = 8;
 bool decode_supported(int N, int K, int epilogue);
-// ga.NT = N/64 column blocks (SwiGLU, internal epilogue) or N/128 (STORE_F32).
-hipError_t launch_decode(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream);
+// ga.NT = N/16 column blocks (SwiGLU, internal epilogue: h in the operand chunk
+// order, no group-sum table) or N/32 (STORE_F32). natural_rows: ga.A holds rows
+// in natural element order (the kernel reorders them while staging).
+hipError_t launch_decode(const GemmArgs& ga, int epilogue, bool natural_rows, int max_row_tiles,
+                         hipStream_t stream);
 
 hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
                             hipStream_t stream);

@@ -7,12 +7,13 @@
 // Launches on one stream:
 //   0. router_logits_kernel (layer path only) - logits = x W_r^T (+ bias) with
 //      bf16 MFMA and fp32 accumulation, 32 tokens x 64 experts per workgroup.
-//   1. route_topk_kernel  - one workgroup per 32 tokens: top-k by the key
-//      (logit desc, expert asc), softmax over the chosen k, the block's expert
-//      histogram and each pair's rank among the block's pairs of the same expert.
+//   1. route_topk_kernel  - one workgroup per 16 tokens, one wave per token:
+//      top-k by the key (logit desc, expert asc) through a ballot radix
+//      select, softmax over the chosen k, the block's expert histogram and
+//      each pair's rank among the block's pairs of the same expert.
 //   2. route_scan_kernel  - one workgroup: per-expert scan over blocks, exclusive
 //      scan over experts (offsets), and the tile list of the block map.
-//   3. route_scatter_kernel - one workgroup per 32 tokens: final row of each
+//   3. route_scatter_kernel - one workgroup per 16 tokens: final row of each
 //      pair = block base of its expert + its in-block rank.
 // Ranks count only earlier pairs, so the sort is stable and the result does not
 // depend on thread timing: repeated runs give identical tables.
@@ -21,6 +22,8 @@
 namespace moe {
 
 constexpr int kRouteThreads = 256;
+constexpr int kRouterRows = 32;                          // tokens per router-GEMM workgroup (one MFMA block)
+constexpr int kTopkThreads = kRouteTokens * kWave;       // top-k: one wave per token
 constexpr int kMaxKeysPerLane = kMaxExperts / kWave;
 
 // Router GEMM: logits[t][e] = fp32(sum_h x[t][h] W_r[e][h]) + bias[e] for a
@@ -35,9 +38,9 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(const uint
   __shared__ float red[4][2][16][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int t0 = blockIdx.x * kRouteTokens;
+  const int t0 = blockIdx.x * kRouterRows;
   const int e0 = blockIdx.y * 64;
-  const int nt = min(kRouteTokens, T - t0);
+  const int nt = min(kRouterRows, T - t0);
   const bool row_ok = l32 < nt;
   const int n0 = e0 + l32, n1 = e0 + 32 + l32;
   const bool ok0 = n0 < E, ok1 = n1 < E;
@@ -93,11 +96,29 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(const uint
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) {
-  extern __shared__ float lds_f[];
-  float* lg = lds_f;                                          // [32][E]
-  int32_t* ids_s = reinterpret_cast<int32_t*>(lg + kRouteTokens * a.E);  // [32*k]
-  int32_t* hist = ids_s + kRouteTokens * a.k;                 // [E]
+// Top-k of one token held by one wave: lane l holds the order keys of experts
+// l, l+64, l+128, l+192 (0 for experts >= E, below every finite logit's key).
+// The k-th largest key tau is found by a most-significant-bit-first radix
+// select whose counts are wave ballots; the chosen set is every key > tau plus
+// the lowest-index experts with key == tau, which is the set the key
+// (logit desc, expert asc) orders first.
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&u)[kMaxKeysPerLane], int k) {
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) cnt += __popcll(__ballot(u[i] >= cand));
+    tau = cnt >= k ? cand : tau;
+  }
+  return tau;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
+  __shared__ uint32_t sel_key[kRouteTokens][kMaxTopk];
+  __shared__ int32_t sel_e[kRouteTokens][kMaxTopk];
+  __shared__ int32_t ids_s[kRouteTokens * kMaxTopk];
+  __shared__ int32_t hist[kMaxExperts];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,105 +127,116 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) 
   const int t0 = blk * kRouteTokens;
   const int nt = min(kRouteTokens, a.T - t0);
   const int E = a.E, k = a.k;
+  const uint64_t below = (1ull << lane) - 1ull;
 
-  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+  for (int e = tid; e < E; e += kTopkThreads) hist[e] = 0;
 
-  for (int i = tid; i < nt * E; i += kRouteThreads) {
-    const int n = i % E;
-    float v = a.logits_in[size_t(t0) * E + i];
-    if (a.bias) v = v + a.bias[n];
-    lg[i] = v + 0.0f;   // + 0.0f turns -0 into +0
-  }
-  __syncthreads();
-
-  // Top-k: each wave selects for 8 tokens at once (lane holds experts lane +
-  // 64 i of every token), so the 8 tokens' cross-lane max reductions are
-  // independent and their shuffle latencies overlap.
-  {
-    constexpr int TPW = kRouteTokens / (kRouteThreads / kWave);   // tokens per wave
-    const int mbase = wave * TPW;
-    uint64_t key[TPW][kMaxKeysPerLane];
+  const int m = wave;                                            // this wave's token
+  if (m < nt) {
+    uint32_t u[kMaxKeysPerLane];
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-      for (int i = 0; i < kMaxKeysPerLane; ++i) {
-        const int e = lane + 64 * i;
-        const int m = mbase + tt;
-        key[tt][i] = (e < E && m < nt) ? (uint64_t(float_order_key(lg[m * E + e])) << 32) | uint32_t(0xFFFFFFFFu - e)
-                                       : 0ull;
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      const int e = lane + 64 * i;
+      uint32_t key = 0u;
+      if (e < E) {
+        float v = a.logits_in[size_t(t0 + m) * E + e];
+        if (a.bias) v = v + a.bias[e];
+        key = float_order_key(v + 0.0f);                         // + 0.0f turns -0 into +0
       }
-    int my_e[TPW];
-    float my_l[TPW];
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      my_e[tt] = 0;
-      my_l[tt] = 0.0f;
+      u[i] = key;
     }
-    for (int j = 0; j < k; ++j) {
-      uint64_t best[TPW];
+    const uint32_t tau = kth_largest(u, k);
+    int n_gt = 0;
+    uint64_t tie[kMaxKeysPerLane];
 #pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        best[tt] = key[tt][0];
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      n_gt += __popcll(__ballot(u[i] > tau));
+      tie[i] = __ballot(u[i] == tau);
+    }
+    // ties at tau are taken in expert order: expert lane + 64 i ranks after
+    // every tie of a lower i and after the lower lanes' ties of the same i
+    const int need = k - n_gt;
+    int ties_before = 0;
+    int slot_base = 0;
 #pragma unroll
-        for (int i = 1; i < kMaxKeysPerLane; ++i) best[tt] = key[tt][i] > best[tt] ? key[tt][i] : best[tt];
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      const bool is_tie = (tie[i] >> lane) & 1ull;
+      const int tie_rank = ties_before + __popcll(tie[i] & below);
+      const bool chosen = u[i] > tau || (is_tie && tie_rank < need);
+      const uint64_t cm = __ballot(chosen);
+      if (chosen) {
+        const int slot = slot_base + __popcll(cm & below);
+        sel_key[m][slot] = u[i];
+        sel_e[m][slot] = lane + 64 * i;
       }
-#pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1)
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-          const uint64_t o = shfl_xor_u64(best[tt], msk);
-          best[tt] = o > best[tt] ? o : best[tt];
-        }
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        const int ej = int(0xFFFFFFFFu - uint32_t(best[tt]));
-#pragma unroll
-        for (int i = 0; i < kMaxKeysPerLane; ++i)
-          if (lane + 64 * i == ej) key[tt][i] = 0ull;
-        if (lane == j) {
-          my_e[tt] = ej;
-          my_l[tt] = float_from_order_key(uint32_t(best[tt] >> 32));
-        }
+      ties_before += __popcll(tie[i]);
+      slot_base += __popcll(cm);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane j < k: its chosen element's position in (logit desc, expert asc) order
+    int pos = 0;
+    uint32_t my_key = 0;
+    int my_e = 0;
+    if (lane < k) {
+      my_key = sel_key[m][lane];
+      my_e = sel_e[m][lane];
+      for (int q = 0; q < k; ++q) {
+        const uint32_t kq = sel_key[m][q];
+        const int eq = sel_e[m][q];
+        pos += (kq > my_key || (kq == my_key && eq < my_e)) ? 1 : 0;
       }
     }
-    float ex[TPW];
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      const float l0 = __shfl(my_l[tt], 0, kWave);
-      ex[tt] = lane < k ? expf(my_l[tt] - l0) : 0.0f;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) {
+      sel_key[m][pos] = my_key;
+      sel_e[m][pos] = my_e;
     }
-    float sum[TPW];
+    __builtin_amdgcn_wave_barrier();
+    float my_l = 0.0f;
+    if (lane < k) {
+      my_e = sel_e[m][lane];
+      my_l = float_from_order_key(sel_key[m][lane]);
+    }
+    const float l0 = float_from_order_key(sel_key[m][0]);
+    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
+    float sum = ex;
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) sum[tt] = ex[tt];
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1)
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) sum[tt] += __shfl_xor(sum[tt], msk, kWave);
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      const int m = mbase + tt;
-      if (lane < k && m < nt) {
-        const size_t f = size_t(t0 + m) * k + lane;
-        a.topk_ids[f] = my_e[tt];
-        a.topk_w[f] = ex[tt] / sum[tt];
-        ids_s[m * k + lane] = my_e[tt];
-      }
+    for (int msk = 32; msk >= 1; msk >>= 1) sum += __shfl_xor(sum, msk, kWave);
+    if (lane < k) {
+      const size_t f = size_t(t0 + m) * k + lane;
+      a.topk_ids[f] = my_e;
+      a.topk_w[f] = ex / sum;
+      ids_s[m * k + lane] = my_e;
     }
   }
   __syncthreads();
 
-  const int npairs = nt * k;
-  for (int p = tid; p < npairs; p += kRouteThreads) atomicAdd(&hist[ids_s[p]], 1);
-  // Rank of each pair among the earlier pairs of this block with the same
-  // expert (pair order f = t*k + j), which makes the scatter stable.
-  for (int p = tid; p < npairs; p += kRouteThreads) {
-    const int e = ids_s[p];
-    int r = 0;
-    for (int q = 0; q < p; ++q) r += ids_s[q] == e;
-    a.rank_in_block[size_t(t0) * k + p] = r;
+  // Histogram of the block's pairs and each pair's rank among the earlier pairs
+  // of the same expert (pair order f = t*k + j), which makes the scatter
+  // stable. Wave 0 walks the pairs 64 at a time; lanes with the same expert
+  // find each other through one ballot per expert-index bit.
+  if (wave == 0) {
+    const int npairs = nt * k;
+    for (int c0 = 0; c0 < npairs; c0 += kWave) {
+      const int p = c0 + lane;
+      const int e = p < npairs ? ids_s[p] : kMaxExperts;   // past the end: a value no expert has
+      uint64_t same = ~0ull;
+#pragma unroll
+      for (int bit = 0; bit < 9; ++bit) {
+        const uint64_t bb = __ballot((e >> bit) & 1);
+        same &= ((e >> bit) & 1) ? bb : ~bb;
+      }
+      if (p < npairs) {
+        const int base = hist[e];
+        const int before = __popcll(same & below);
+        a.rank_in_block[size_t(t0) * k + p] = base + before;
+        if (before == 0) hist[e] = base + __popcll(same);   // every lane of the group has read hist[e]
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads) a.block_counts[size_t(blk) * E + e] = hist[e];
+  for (int e = tid; e < E; e += kTopkThreads) a.block_counts[size_t(blk) * E + e] = hist[e];
 }
 
 // Inclusive scan of v over n <= 1024 entries held in LDS (one per thread).
@@ -316,10 +348,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArg
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,
                         hipStream_t stream) {
   const int nblk = ceil_div(ra.T, kRouteTokens);
-  const size_t lds = sizeof(float) * kRouteTokens * ra.E + sizeof(int32_t) * (kRouteTokens * ra.k + ra.E);
+  const int nrb = ceil_div(ra.T, kRouterRows);
   if (from_x) {
     // logits (biased) into logits_out, then top-k from them without the bias
-    hipLaunchKernelGGL(router_logits_kernel, dim3(nblk, ceil_div(ra.E, 64)), dim3(kRouteThreads), 0, stream, ra.x,
+    hipLaunchKernelGGL(router_logits_kernel, dim3(nrb, ceil_div(ra.E, 64)), dim3(kRouteThreads), 0, stream, ra.x,
                        ra.wr, ra.bias, ra.T, ra.H, ra.E, ra.logits_out);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -327,9 +359,9 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
     rb.logits_in = ra.logits_out;
     rb.bias = nullptr;
     rb.logits_out = nullptr;
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kRouteThreads), lds, stream, rb);
+    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, rb);
   } else {
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kRouteThreads), lds, stream, ra);
+    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, ra);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
