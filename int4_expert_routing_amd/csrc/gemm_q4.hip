@@ -121,12 +121,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(kWaitVm0 | N);
 }
 
-__device__ __forceinline__ void read_frags(const uint8_t* slot, int m, int half, bf16x8 (&f)[4]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    f[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(m, 4 * half + c)));
-}
-
 __device__ __forceinline__ void fold(const f32x16& p, float sc, f32x16& acc) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(sc, p[r], acc[r]);
@@ -137,16 +131,18 @@ __device__ __forceinline__ void fold(const f32x16& p, float sc, f32x16& acc) {
 // (S+3)%4, which held group g-1.
 //
 // Per live row block rb: a chain of 4 MFMAs over the group's 64 K values
-// gives P_g, folded as acc += 16 s_g P_g. The fold of a block runs while the
-// next block's chain is in the matrix pipe; the last block's fold is carried
-// into the next step (pend, pend_sc). For odd g one more MFMA per block adds
-// the bias term of groups g-1 and g (lanes 0..31: group g-1, 32..63: group g)
-// from the rows' 8 side-table entries per group against
-// (b, b, b, -16 s, -16 s, -16 s, 0, 0) of the lane's column.
+// gives P_g. The NRB chains are issued level by level (level l = the l-th
+// 16-wide slice of the group), so consecutive MFMAs never depend on each
+// other. Chain rb's P_g is folded as acc += 16 s_g P_g just before the
+// chain's first MFMA of the next step, when the matrix pipe has long
+// finished it. For odd g one more MFMA per block adds the bias term of groups
+// g-1 and g (lanes 0..31: group g-1, 32..63: group g) from the rows' 8
+// side-table entries per group against (b, b, b, -16 s, -16 s, -16 s, 0, 0)
+// of the lane's column.
 template <int NRB, int S>
 __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, const uint32_t* s_pairs,
                                           const uint32_t* b_pairs, int g, int G, int wave, int lane, uint32_t& s_pair,
-                                          uint32_t& b_pair, f32x16& pend, float& pend_sc, f32x16 (&acc)[4]) {
+                                          uint32_t& b_pair, float& sc_prev, f32x16 (&q)[4], f32x16 (&acc)[4]) {
   constexpr int ODD = S & 1;
   const int l32 = lane & 31, half = lane >> 5;
   // this wave's loads of group g have landed once at most those of g+1 and
@@ -171,17 +167,35 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, const
   const uint8_t* slot = ring + S * kSlotBytes;
 
   const u32x4 w = *reinterpret_cast<const u32x4*>(slot + kSlotB + wave * 1024 + lane * 16);
-  bf16x8 fa[2][4];
-  read_frags(slot, l32, half, fa[0]);
   if (!ODD) {
     s_pair = s_pairs[(g >> 1) * 32];
     b_pair = b_pairs[(g >> 1) * 32];
   }
+  bf16x8 fa[2][4];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+    fa[0][rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(rb * 32 + l32, 4 * half)));
   const uint32_t nib = kNib, magic = kMagic;
-  const bf16x8 b0 = unpack_word(w.x, nib, magic), b1 = unpack_word(w.y, nib, magic),
-               b2 = unpack_word(w.z, nib, magic), b3 = unpack_word(w.w, nib, magic);
-  const float sc = 16.0f * __uint_as_float(ODD ? (s_pair & 0xFFFF0000u) : (s_pair << 16));
-  bf16x8 bv;
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    if (l + 1 < 4) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        fa[(l + 1) & 1][rb] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(rb * 32 + l32, 4 * half + l + 1)));
+    }
+    const bf16x8 bq = unpack_word(w[l], nib, magic);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (l == 0) {
+        fold(q[rb], sc_prev, acc[rb]);
+        q[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][rb], bq, f32x16{}, 0, 0, 0);
+      } else {
+        q[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[l & 1][rb], bq, q[rb], 0, 0, 0);
+      }
+    }
+  }
+  sc_prev = 16.0f * __uint_as_float(ODD ? (s_pair & 0xFFFF0000u) : (s_pair << 16));
   if (ODD) {
     const int sh = half << 4;
     const uint32_t sb = (s_pair >> sh) & 0xFFFFu, bb = (b_pair >> sh) & 0xFFFFu;
@@ -189,30 +203,14 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, const
     // fp32 product is the rounding
     const uint32_t ns = __float_as_uint(-16.0f * __uint_as_float(sb << 16)) >> 16;
     const u32x4 pk = {bb | (bb << 16), bb | (ns << 16), ns | (ns << 16), 0u};
-    bv = __builtin_bit_cast(bf16x8, pk);
-  }
-  f32x16 last;
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    if (rb + 1 < NRB) read_frags(slot, (rb + 1) * 32 + l32, half, fa[(rb + 1) & 1]);
-    bf16x8 xa;
-    if (ODD)
-      xa = __builtin_bit_cast(bf16x8,
-                              *reinterpret_cast<const u32x4*>(slot + kSlotXP + (rb * 32 + l32) * 32 + half * 16));
-    const bf16x8(&f)[4] = fa[rb & 1];
-    f32x16 q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], b0, f32x16{}, 0, 0, 0);
-    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[1], b1, q, 0, 0, 0);
-    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[2], b2, q, 0, 0, 0);
-    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[3], b3, q, 0, 0, 0);
-    if (rb == 0)
-      fold(pend, pend_sc, acc[NRB - 1]);
-    else
-      fold(last, sc, acc[rb - 1]);
-    if (ODD) acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv, acc[rb], 0, 0, 0);
-    last = q;
+    for (int rb = 0; rb < NRB; ++rb) {
+      const bf16x8 xa =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + kSlotXP + (rb * 32 + l32) * 32 + half * 16));
+      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv, acc[rb], 0, 0, 0);
+    }
   }
-  pend = last;
-  pend_sc = sc;
 }
 
 // G is even (K is a multiple of 128).
@@ -220,18 +218,21 @@ template <int NRB>
 __device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, const uint32_t* s_pairs,
                                           const uint32_t* b_pairs, int G, int wave, int lane, f32x16 (&acc)[4]) {
   uint32_t s_pair = 0, b_pair = 0;
-  f32x16 pend = f32x16{};
-  float pend_sc = 0.0f;
+  float sc_prev = 0.0f;
+  f32x16 q[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) q[rb] = f32x16{};
   // unrolled by the ring size so every slot offset and group parity is a constant
   for (int g = 0; g < G; g += kRing) {
-    loop_step<NRB, 0>(st, ring, s_pairs, b_pairs, g, G, wave, lane, s_pair, b_pair, pend, pend_sc, acc);
-    loop_step<NRB, 1>(st, ring, s_pairs, b_pairs, g + 1, G, wave, lane, s_pair, b_pair, pend, pend_sc, acc);
+    loop_step<NRB, 0>(st, ring, s_pairs, b_pairs, g, G, wave, lane, s_pair, b_pair, sc_prev, q, acc);
+    loop_step<NRB, 1>(st, ring, s_pairs, b_pairs, g + 1, G, wave, lane, s_pair, b_pair, sc_prev, q, acc);
     if (g + 2 < G) {
-      loop_step<NRB, 2>(st, ring, s_pairs, b_pairs, g + 2, G, wave, lane, s_pair, b_pair, pend, pend_sc, acc);
-      loop_step<NRB, 3>(st, ring, s_pairs, b_pairs, g + 3, G, wave, lane, s_pair, b_pair, pend, pend_sc, acc);
+      loop_step<NRB, 2>(st, ring, s_pairs, b_pairs, g + 2, G, wave, lane, s_pair, b_pair, sc_prev, q, acc);
+      loop_step<NRB, 3>(st, ring, s_pairs, b_pairs, g + 3, G, wave, lane, s_pair, b_pair, sc_prev, q, acc);
     }
   }
-  fold(pend, pend_sc, acc[NRB - 1]);
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) fold(q[rb], sc_prev, acc[rb]);
 }
 
 template <int EPI>
