@@ -24,7 +24,7 @@ struct Carve {
 
 // Workspace of one layer call. Offsets in bytes from the workspace base.
 struct LayerLayout {
-  size_t logits, ids, w, block_counts, block_base, rank, counts, offsets, sorted_rows, row_of_pair,
+  size_t logits, logit_parts, ids, w, block_counts, block_base, rank, counts, offsets, sorted_rows, row_of_pair,
       tile_map, num_tiles, x_perm, x_part, h, h_part, Y, total;
 };
 
@@ -41,6 +41,7 @@ LayerLayout layer_layout(const moe_dims& d) {
   Carve c;
   LayerLayout L;
   L.logits = c.take(T * E * 4);
+  L.logit_parts = c.take(size_t(router_splits(d.T, d.H) > 1 ? kRouterSplits : 0) * T * E * 4);
   L.ids = c.take(T * k * 4);
   L.w = c.take(T * k * 4);
   L.block_counts = c.take(nblk * E * 4);
@@ -293,6 +294,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   ra.wr = router_w;
   ra.bias = logit_bias;
   ra.logits_out = logits_out ? logits_out : at<float>(ws, L.logits);
+  ra.logit_parts = at<float>(ws, L.logit_parts);
   ra.topk_ids = ids;
   ra.topk_w = wts;
   ra.block_counts = at<int32_t>(ws, L.block_counts);

@@ -13,7 +13,9 @@ constexpr int kMaxK = 2048;  // largest reduction size of the grouped GEMM (LDS 
 struct RouteArgs {
   const uint16_t* x;        // bf16 [T][H] (router GEMM input) or null
   const uint16_t* wr;       // bf16 [E][H]
-  const float* logits_in;   // float [T][E] when logits are given
+  const float* logits_in;   // float [T][E] when logits are given, or [n_parts][T][E] partial sums
+  int n_parts;              // number of partial-sum planes in logits_in (1 = plain logits)
+  float* logit_parts;       // workspace for the router's K-range partials [kRouterSplits][T][E]
   const float* bias;        // float [E] or null
   float* logits_out;        // float [T][E]: router GEMM output (layer path)
   int32_t* topk_ids;        // [T][k]
@@ -41,6 +43,11 @@ struct ScatterArgs {
   int32_t* row_of_pair;
   int T, E, k;
 };
+
+// Few-token layer calls split the router GEMM's K range in kRouterSplits.
+constexpr int kRouterSplits = 8;
+constexpr int kRouterSplitMaxT = 256;
+int router_splits(int T, int H);
 
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,
                         hipStream_t stream);

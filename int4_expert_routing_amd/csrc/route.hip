@@ -6,7 +6,8 @@
 //
 // Launches on one stream:
 //   0. router_logits_kernel (layer path only) - logits = x W_r^T (+ bias) with
-//      bf16 MFMA and fp32 accumulation, 32 tokens x 64 experts per workgroup.
+//      bf16 MFMA and fp32 accumulation, 32 tokens x 64 experts (x a K range
+//      for few tokens) per single-wave workgroup.
 //   1. route_topk_kernel  - one workgroup per 16 tokens, one wave per token:
 //      top-k by the key (logit desc, expert asc) through a ballot radix
 //      select, softmax over the chosen k, the block's expert histogram and
@@ -26,73 +27,104 @@ constexpr int kRouterRows = 32;                          // tokens per router-GE
 constexpr int kTopkThreads = kRouteTokens * kWave;       // top-k: one wave per token
 constexpr int kMaxKeysPerLane = kMaxExperts / kWave;
 
-// Router GEMM: logits[t][e] = fp32(sum_h x[t][h] W_r[e][h]) + bias[e] for a
-// 32-token x 64-expert tile per workgroup. The four waves split K in 64-wide
-// chunks (wave w takes chunks w, w+4, ...), accumulate two 32x32 blocks each
-// with bf16 MFMA, prefetch the next chunk while multiplying the current one,
-// and reduce their partial sums through LDS.
-__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                                     const uint16_t* __restrict__ wr,
-                                                                     const float* __restrict__ bias, int T, int H,
-                                                                     int E, float* __restrict__ logits) {
-  __shared__ float red[4][2][16][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Router GEMM: logits[t][e] = fp32(sum_h x[t][h] W_r[e][h]) + bias[e].
+// One wave per workgroup computes a 32-token x 64-expert tile over one K
+// range (blockIdx.z of KS; KS > 1 writes fp32 partial sums that the top-k
+// kernel adds in a fixed order, so few-token calls still spread over many
+// CUs). Both operands stream through a 4-slot LDS ring of 64-wide K chunks
+// filled by buffer loads that write LDS (three chunks in flight, 12 loads per
+// chunk); 16-byte chunks of each row sit XOR-swizzled so that the MFMA
+// fragment reads are bank-conflict free.
+constexpr int kRouterRing = 4;
+constexpr int kRouterSlotX = 4096;                       // 32 rows x 128 B
+constexpr int kRouterSlot = kRouterSlotX + 8192;         // + 64 expert rows x 128 B
+constexpr uint32_t kRouterRsrcWord3 = 0x00020000u;       // raw buffer descriptor flags (gfx9 family)
+
+__device__ __forceinline__ int rswz(int m) { return (m & 7) ^ ((m >> 3) & 1); }
+__device__ __forceinline__ int rchunk_off(int m, int c) { return (m * 8 + (c ^ rswz(m))) * 16; }
+
+__global__ __launch_bounds__(kWave) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ wr,
+                                                             const float* __restrict__ bias, int T, int H, int E,
+                                                             float* __restrict__ out) {
+  extern __shared__ __align__(16) uint8_t rsm[];
+  typedef __attribute__((address_space(3))) void* lptr;
+  const int lane = threadIdx.x;
   const int l32 = lane & 31, half = lane >> 5;
   const int t0 = blockIdx.x * kRouterRows;
   const int e0 = blockIdx.y * 64;
-  const int nt = min(kRouterRows, T - t0);
-  const bool row_ok = l32 < nt;
-  const int n0 = e0 + l32, n1 = e0 + 32 + l32;
-  const bool ok0 = n0 < E, ok1 = n1 < E;
-  const uint16_t* xr = x + size_t(t0 + (row_ok ? l32 : 0)) * H + 32 * half;
-  const uint16_t* w0 = wr + size_t(ok0 ? n0 : 0) * H + 32 * half;
-  const uint16_t* w1 = wr + size_t(ok1 ? n1 : 0) * H + 32 * half;
-  const int nchunks = H / 64;
-  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
-  u32x4 ca[4], cb0[4], cb1[4];
-  auto load = [&](int c, u32x4 (&A)[4], u32x4 (&B0)[4], u32x4 (&B1)[4]) {
+  const int KS = gridDim.z;
+  const int KC = H / KS;
+  const int k0 = blockIdx.z * KC;
+  const int nch = KC / 64;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 0x7FFFFFFF,
+                                                                     kRouterRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wr), 0, 0x7FFFFFFF,
+                                                                     kRouterRsrcWord3);
+  // load i fills chunk positions i*64 + lane: row i*8 + lane/8, slot lane%8,
+  // which holds logical chunk (lane%8) ^ swz(row); rows past T or E re-read
+  // the last valid row
+  uint32_t vx[4], vw[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      A[j] = row_ok ? *reinterpret_cast<const u32x4*>(xr + c * 64 + 8 * j) : u32x4{0, 0, 0, 0};
-      B0[j] = ok0 ? *reinterpret_cast<const u32x4*>(w0 + c * 64 + 8 * j) : u32x4{0, 0, 0, 0};
-      B1[j] = ok1 ? *reinterpret_cast<const u32x4*>(w1 + c * 64 + 8 * j) : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int m = i * 8 + (lane >> 3);
+    const int t = min(t0 + m, T - 1);
+    vx[i] = uint32_t(t) * uint32_t(H * 2) + uint32_t(((lane & 7) ^ rswz(m)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = i * 8 + (lane >> 3);
+    const int e = min(e0 + n, E - 1);
+    vw[i] = uint32_t(e) * uint32_t(H * 2) + uint32_t(((lane & 7) ^ rswz(n)) * 16);
+  }
+  auto issue = [&](int c) {
+    uint8_t* slot = rsm + (c % kRouterRing) * kRouterSlot;
+    const int soff = (k0 + 64 * c) * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lptr)(slot + i * 1024), 16, vx[i], soff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lptr)(slot + kRouterSlotX + i * 1024), 16, vw[i], soff, 0, 0);
   };
-  int c = wave;
-  if (c < nchunks) load(c, ca, cb0, cb1);
-  while (c < nchunks) {
-    u32x4 na[4], nb0[4], nb1[4];
-    const int cn = c + 4;
-    if (cn < nchunks) load(cn, na, nb0, nb1);
+  issue(0);
+  if (nch > 1) issue(1);
+  if (nch > 2) issue(2);
+  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  for (int c = 0; c < nch; ++c) {
+    // chunk c has landed once at most the (12-load) chunks c+1, c+2 are outstanding
+    // (s_waitcnt: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+    if (c + 2 < nch)
+      __builtin_amdgcn_s_waitcnt(0x4F78);   // vmcnt(24)
+    else if (c + 1 < nch)
+      __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (c + 3 < nch) issue(c + 3);   // refills the slot of chunk c-1, read in the previous iteration
+    const uint8_t* slot = rsm + (c % kRouterRing) * kRouterSlot;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, ca[j]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, cb0[j]), acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, cb1[j]), acc1, 0, 0, 0);
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = 2 * kk + half;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + rchunk_off(l32, ch)));
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8,
+                                           *reinterpret_cast<const u32x4*>(slot + kRouterSlotX + rchunk_off(l32, ch)));
+      const bf16x8 b1 = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(slot + kRouterSlotX + rchunk_off(32 + l32, ch)));
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc1, 0, 0, 0);
     }
-    if (cn < nchunks) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ca[j] = na[j];
-        cb0[j] = nb0[j];
-        cb1[j] = nb1[j];
-      }
-    }
-    c = cn;
   }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    red[wave][0][r][lane] = acc0[r];
-    red[wave][1][r][lane] = acc1[r];
-  }
-  __syncthreads();
   // output element (eb, r, lane): token 8(r/4) + 4*half + r%4, expert e0 + 32 eb + lane%32
-  for (int i = tid; i < 2 * 16 * 64; i += kRouteThreads) {
-    const int ln = i & 63, r = (i >> 6) & 15, eb = i >> 10;
-    const float v = red[0][eb][r][ln] + red[1][eb][r][ln] + red[2][eb][r][ln] + red[3][eb][r][ln];
-    const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-    const int n = e0 + 32 * eb + (ln & 31);
-    if (m < nt && n < E) logits[size_t(t0 + m) * E + n] = (v + (bias ? bias[n] : 0.0f)) + 0.0f;
+  float* dst = out + size_t(blockIdx.z) * size_t(T) * E;
+#pragma unroll
+  for (int eb = 0; eb < 2; ++eb) {
+    const int n = e0 + 32 * eb + l32;
+    if (n >= E) continue;
+    const float bv = (KS == 1 && bias) ? bias[n] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+      if (t0 + m < T) dst[size_t(t0 + m) * E + n] = ((eb ? acc1[r] : acc0[r]) + bv) + 0.0f;
+    }
   }
 }
 
@@ -139,9 +171,22 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
       const int e = lane + 64 * i;
       uint32_t key = 0u;
       if (e < E) {
-        float v = a.logits_in[size_t(t0 + m) * E + e];
+        // the logit, or the sum of the router's K-range partials in order
+        const size_t f = size_t(t0 + m) * E + e;
+        float v = a.logits_in[f];
+        if (a.n_parts > 1) {
+          float pv[kRouterSplits - 1];
+#pragma unroll
+          for (int p = 1; p < kRouterSplits; ++p)
+            pv[p - 1] = p < a.n_parts ? a.logits_in[size_t(p) * a.T * E + f] : 0.0f;
+#pragma unroll
+          for (int p = 1; p < kRouterSplits; ++p)
+            if (p < a.n_parts) v += pv[p - 1];
+        }
         if (a.bias) v = v + a.bias[e];
-        key = float_order_key(v + 0.0f);                         // + 0.0f turns -0 into +0
+        v = v + 0.0f;                                            // turns -0 into +0
+        if (a.logits_out) a.logits_out[f] = v;
+        key = float_order_key(v);
       }
       u[i] = key;
     }
@@ -345,23 +390,40 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArg
   }
 }
 
+int router_splits(int T, int H) {
+  // few tokens: split K so that the weight stream spreads over more CUs
+  return (T <= kRouterSplitMaxT && H % (64 * kRouterSplits) == 0) ? kRouterSplits : 1;
+}
+
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,
                         hipStream_t stream) {
   const int nblk = ceil_div(ra.T, kRouteTokens);
   const int nrb = ceil_div(ra.T, kRouterRows);
   if (from_x) {
-    // logits (biased) into logits_out, then top-k from them without the bias
-    hipLaunchKernelGGL(router_logits_kernel, dim3(nrb, ceil_div(ra.E, 64)), dim3(kRouteThreads), 0, stream, ra.x,
-                       ra.wr, ra.bias, ra.T, ra.H, ra.E, ra.logits_out);
+    // logits (biased) into logits_out, or K-range partials into logit_parts
+    // that the top-k kernel sums (adding the bias, writing logits_out)
+    const int ks = router_splits(ra.T, ra.H);
+    float* dst = ks > 1 ? ra.logit_parts : ra.logits_out;
+    hipLaunchKernelGGL(router_logits_kernel, dim3(nrb, ceil_div(ra.E, 64), ks), dim3(kWave),
+                       kRouterRing * kRouterSlot, stream, ra.x, ra.wr, ra.bias, ra.T, ra.H, ra.E, dst);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     RouteArgs rb = ra;
-    rb.logits_in = ra.logits_out;
-    rb.bias = nullptr;
-    rb.logits_out = nullptr;
+    if (ks > 1) {
+      rb.logits_in = ra.logit_parts;
+      rb.n_parts = ks;
+    } else {
+      rb.logits_in = ra.logits_out;
+      rb.n_parts = 1;
+      rb.bias = nullptr;
+      rb.logits_out = nullptr;
+    }
     hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, rb);
   } else {
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, ra);
+    RouteArgs rb = ra;
+    rb.n_parts = 1;
+    rb.logits_out = nullptr;
+    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, rb);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
