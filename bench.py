@@ -123,6 +123,78 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
                       f"{reps} replays timed with events"}
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_q4_swiglu_prefill4096_traffic.txt")
+KERNEL_SOURCES = ("int4_expert_routing_amd/csrc/gemm_q4.hip", "int4_expert_routing_amd/csrc/gemm_tiles.h",
+                  "int4_expert_routing_amd/csrc/moe_common.h", "int4_expert_routing_amd/csrc/moe_internal.h")
+GEMM_KERNEL_NAME = "gemm_q4_kernel<2>"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, if it
+    was taken on the current kernel source (else None)."""
+    try:
+        kv = dict(line.split("=", 1) for line in open(TRAFFIC_SUMMARY).read().splitlines()
+                  if "=" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    if kv.get("source_hash", "").strip() != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def counter_values(run_dir, counter):
+    """{dispatch kernel name: [value per dispatch]} from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def write_traffic_summary(fetch_dir, write_dir, copy_mib, cmd_fetch, cmd_write):
+    """Gate/up HBM traffic per launch from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the counter reads for the calibration copy
+    kernel of copy_mib MiB (read and written once)."""
+    fv, wv = counter_values(fetch_dir, "FETCH_SIZE"), counter_values(write_dir, "WRITE_SIZE")
+    pick = lambda d, key: [v for k, vs in d.items() if key in k for v in vs]
+    g_f, g_w = pick(fv, GEMM_KERNEL_NAME), pick(wv, GEMM_KERNEL_NAME)
+    c_f, c_w = pick(fv, "copy"), pick(wv, "copy")
+    if not (g_f and g_w and c_f and c_w):
+        raise SystemExit(f"counters missing: gemm {len(g_f)}/{len(g_w)}, copy {len(c_f)}/{len(c_w)}")
+    true_bytes = copy_mib * 2**20
+    f_scale = true_bytes / (max(c_f) * 1024.0)
+    w_scale = true_bytes / (max(c_w) * 1024.0)
+    fetch = float(np.median(g_f)) * 1024.0 * f_scale
+    write = float(np.median(g_w)) * 1024.0 * w_scale
+    lines = [
+        "gate/up grouped GEMM (gemm_q4_kernel<SwiGLU>), T=4096 layer: HBM traffic per launch",
+        f"  FETCH_SIZE pass: {cmd_fetch}",
+        f"  WRITE_SIZE pass: {cmd_write}",
+        f"  calibration copy kernel: {copy_mib} MiB read + written once; counter reads "
+        f"FETCH {max(c_f):.0f} KiB, WRITE {max(c_w):.0f} KiB -> scale fetch {f_scale:.4f}, write {w_scale:.4f}",
+        f"  gate/up dispatches: {len(g_f)}; median FETCH {np.median(g_f):.0f} KiB, WRITE {np.median(g_w):.0f} KiB",
+        f"fetch_bytes_per_launch={fetch:.0f}",
+        f"write_bytes_per_launch={write:.0f}",
+        f"traffic_bytes_per_launch={fetch + write:.0f}",
+        f"source_hash={kernel_source_hash()}",
+    ]
+    with open(os.environ.get("TRAFFIC_SUMMARY_OUT", TRAFFIC_SUMMARY), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -132,6 +204,10 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="after the timed steps, launch one device copy of this many MiB (counter calibration)")
+    p.add_argument("--write-traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CMD_FETCH", "CMD_WRITE"),
+                   help="build the gate/up traffic summary from two rocprofv3 --pmc runs and exit")
     return p.parse_args()
 
 
@@ -153,6 +229,10 @@ def cpu_baseline(inp):
 
 def main():
     args = parse()
+    if args.write_traffic_summary:
+        fd, wd, cf, cw = args.write_traffic_summary
+        write_traffic_summary(fd, wd, 512, cf, cw)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library runs on a "
               "single GPU; see DESIGN.md for how the layer would shard)", file=sys.stderr)
@@ -244,10 +324,16 @@ def main():
         "stage_ms": {n: float(v) for n, v in zip(names, stage_ms)},
         "roofline": {"kernel": "gemm_q4_kernel<SwiGLU> (gate/up grouped GEMM)", "bound": "mfma",
                      "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic(),
+                     "traffic_unit": "bytes per launch (HBM, FETCH_SIZE + WRITE_SIZE scaled by a copy kernel)",
                      "algorithmic_flops_per_launch": gu_flops},
         "weight_bytes": weight_bytes,
     }
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib * 2**20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_decode:
         out["decode"] = {}
         for dname in ("decode1", "decode8"):
