@@ -170,7 +170,10 @@ size_t moe_gemm_workspace_bytes(int32_t a_rows, int32_t K);
  *   the shared expert on every token with weight 1, and
  *   y[t] = bf16(sum_j w[t][j] Y[row of (t, j)] + S[t]).
  * (Page "Perplexity Open Sources Lily ..." Technical Details, Model and prefill
- * bullets.)
+ * bullets.) Calls with T <= 8 run decode-shaped kernels with the same result
+ * (decode bullet: the chosen experts' weights are streamed once per step).
+ * The call records no allocation or memset, so it may be captured in a HIP
+ * graph on the caller's stream.
  *
  *   x            device bf16 [T][H]
  *   router_w     device bf16 [E][H]
