@@ -23,6 +23,16 @@ struct RouteArgs {
   int32_t* block_counts;    // [nblk][E]
   int32_t* rank_in_block;   // [T*k]
   int T, H, E, k;
+  // a single routing block (T <= kRouteTokens) also finishes the tables
+  // itself: counts, offsets, block map and scatter (no scan/scatter launches)
+  int finish;
+  int block_rows;
+  int32_t* counts;          // [E]
+  int32_t* offsets;         // [E+1]
+  int32_t* tile_map;        // [max_tiles][2]
+  int32_t* num_tiles;       // [1]
+  int32_t* sorted_rows;     // [T*k]
+  int32_t* row_of_pair;     // [T*k]
 };
 
 struct ScanArgs {

@@ -146,10 +146,24 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&u)[kMaxKeysPerL
   return tau;
 }
 
+// Inclusive scan of v over n <= 1024 entries held in LDS (one per thread).
+__device__ void block_inclusive_scan(int32_t* v, int32_t* tmp, int n) {
+  const int tid = threadIdx.x;
+  for (int d = 1; d < n; d <<= 1) {
+    int32_t x = 0;
+    if (tid < n) x = v[tid] + (tid >= d ? v[tid - d] : 0);
+    __syncthreads();
+    if (tid < n) v[tid] = x;
+    __syncthreads();
+  }
+  (void)tmp;
+}
+
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   __shared__ uint32_t sel_key[kRouteTokens][kMaxTopk];
   __shared__ int32_t sel_e[kRouteTokens][kMaxTopk];
   __shared__ int32_t ids_s[kRouteTokens * kMaxTopk];
+  __shared__ int32_t rank_s[kRouteTokens * kMaxTopk];
   __shared__ int32_t hist[kMaxExperts];
 
   const int tid = threadIdx.x;
@@ -260,8 +274,9 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   // of the same expert (pair order f = t*k + j), which makes the scatter
   // stable. Wave 0 walks the pairs 64 at a time; lanes with the same expert
   // find each other through one ballot per expert-index bit.
+  const int npairs_all = nt * k;
   if (wave == 0) {
-    const int npairs = nt * k;
+    const int npairs = npairs_all;
     for (int c0 = 0; c0 < npairs; c0 += kWave) {
       const int p = c0 + lane;
       const int e = p < npairs ? ids_s[p] : kMaxExperts;   // past the end: a value no expert has
@@ -275,6 +290,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
         const int base = hist[e];
         const int before = __popcll(same & below);
         a.rank_in_block[size_t(t0) * k + p] = base + before;
+        rank_s[p] = base + before;
         if (before == 0) hist[e] = base + __popcll(same);   // every lane of the group has read hist[e]
       }
       __builtin_amdgcn_wave_barrier();
@@ -282,19 +298,42 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   }
   __syncthreads();
   for (int e = tid; e < E; e += kTopkThreads) a.block_counts[size_t(blk) * E + e] = hist[e];
-}
+  if (!a.finish) return;   // uniform: the scan and scatter kernels follow
 
-// Inclusive scan of v over n <= 1024 entries held in LDS (one per thread).
-__device__ void block_inclusive_scan(int32_t* v, int32_t* tmp, int n) {
-  const int tid = threadIdx.x;
-  for (int d = 1; d < n; d <<= 1) {
-    int32_t x = 0;
-    if (tid < n) x = v[tid] + (tid >= d ? v[tid - d] : 0);
-    __syncthreads();
-    if (tid < n) v[tid] = x;
-    __syncthreads();
+  // One block holds every pair: offsets are the exclusive scan of the
+  // histogram, the block map lists ceil(count / block_rows) tiles per expert
+  // in expert order, and each pair's row is its expert's offset plus its rank.
+  __shared__ int32_t off_s[kMaxExperts];
+  __shared__ int32_t til_s[kMaxExperts];
+  const int c = tid < E ? hist[tid] : 0;
+  const int ntl = ceil_div(c, a.block_rows);
+  if (tid < E) {
+    off_s[tid] = c;
+    til_s[tid] = ntl;
   }
-  (void)tmp;
+  __syncthreads();
+  block_inclusive_scan(off_s, nullptr, E);
+  block_inclusive_scan(til_s, nullptr, E);
+  if (tid < E) {
+    const int o = off_s[tid] - c;
+    a.counts[tid] = c;
+    a.offsets[tid] = o;
+    const int first = til_s[tid] - ntl;
+    for (int i = 0; i < ntl; ++i) {
+      a.tile_map[2 * (first + i)] = tid;
+      a.tile_map[2 * (first + i) + 1] = o + i * a.block_rows;
+    }
+    if (tid == E - 1) {
+      a.offsets[E] = off_s[tid];
+      *a.num_tiles = til_s[tid];
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < npairs_all; p += kTopkThreads) {
+    const int pos = off_s[ids_s[p]] - hist[ids_s[p]] + rank_s[p];
+    a.sorted_rows[pos] = p;
+    a.row_of_pair[p] = pos;
+  }
 }
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(ScanArgs a) {
@@ -399,6 +438,16 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
                         hipStream_t stream) {
   const int nblk = ceil_div(ra.T, kRouteTokens);
   const int nrb = ceil_div(ra.T, kRouterRows);
+  RouteArgs rb = ra;
+  // one routing block: the top-k kernel also builds the tables
+  rb.finish = nblk == 1 ? 1 : 0;
+  rb.block_rows = sa.block_rows;
+  rb.counts = sa.counts;
+  rb.offsets = sa.offsets;
+  rb.tile_map = sa.tile_map;
+  rb.num_tiles = sa.num_tiles;
+  rb.sorted_rows = ca.sorted_rows;
+  rb.row_of_pair = ca.row_of_pair;
   if (from_x) {
     // logits (biased) into logits_out, or K-range partials into logit_parts
     // that the top-k kernel sums (adding the bias, writing logits_out)
@@ -408,7 +457,6 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
                        kRouterRing * kRouterSlot, stream, ra.x, ra.wr, ra.bias, ra.T, ra.H, ra.E, dst);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    RouteArgs rb = ra;
     if (ks > 1) {
       rb.logits_in = ra.logit_parts;
       rb.n_parts = ks;
@@ -418,15 +466,13 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
       rb.bias = nullptr;
       rb.logits_out = nullptr;
     }
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, rb);
   } else {
-    RouteArgs rb = ra;
     rb.n_parts = 1;
     rb.logits_out = nullptr;
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, rb);
   }
+  hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, rb);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || rb.finish) return err;
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, sa);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
