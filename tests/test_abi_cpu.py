@@ -65,6 +65,14 @@ def test_check_dims_and_workspace(lib):
     assert lib.moe_check_dims(None) == _lib.MOE_ERR_NULL
 
 
+def test_workspace_holds_router_partials_for_few_tokens(lib):
+    # up to 256 tokens the router GEMM splits K eight ways into fp32 partial sums
+    few = lib.moe_workspace_bytes(ctypes.byref(MoeDims(8, 2048, 512, 256, 8, 0)))
+    assert few >= 8 * 8 * 256 * 4 + (8 * 9) * 2048 * 4
+    many = lib.moe_workspace_bytes(ctypes.byref(MoeDims(257, 2048, 512, 256, 8, 0)))
+    assert many >= (257 * 9) * 2048 * 4
+
+
 def test_max_tiles_bound(lib):
     assert lib.moe_max_tiles(ctypes.byref(MoeDims(4096, 0, 0, 256, 8, 128))) == 4096 * 8 // 128 + 256
     assert lib.moe_max_tiles(ctypes.byref(MoeDims(1, 0, 0, 256, 8, 64))) == 0 + 8
@@ -97,6 +105,15 @@ def test_calls_reject_bad_arguments_before_launching(lib):
                           (1, 256, 128))]
     st = lib.moe_layer_forward(ctypes.c_void_p(0x1002), fake, null, *[ctypes.byref(x) for x in ws],
                                ctypes.byref(d2), fake, null, null, null, null, 0, null)
+    assert st == _lib.MOE_ERR_ALIGN
+    # scales or biases not 16-byte aligned
+    ws_s = [MoeQ4Weights(w_.q, 0x2004, w_.b, w_.n_experts, w_.N, w_.K) for w_ in ws]
+    st = lib.moe_layer_forward(fake, fake, null, *[ctypes.byref(x) for x in ws_s], ctypes.byref(d2), fake, null,
+                               null, null, fake, 1 << 30, null)
+    assert st == _lib.MOE_ERR_ALIGN
+    ws_b = [MoeQ4Weights(w_.q, w_.s, 0x3008, w_.n_experts, w_.N, w_.K) for w_ in ws]
+    st = lib.moe_layer_forward(fake, fake, null, *[ctypes.byref(x) for x in ws_b], ctypes.byref(d2), fake, null,
+                               null, null, fake, 1 << 30, null)
     assert st == _lib.MOE_ERR_ALIGN
     # workspace too small
     st = lib.moe_layer_forward(fake, fake, null, *[ctypes.byref(x) for x in ws], ctypes.byref(d2), fake, null,

@@ -272,6 +272,13 @@ def test_layer_few_tokens(dev, T, H, I, E, k, bias_mode, seed):
     check_layer(inp, g)
 
 
+def test_layer_largest_reduction_sizes(dev):
+    # H = I = 2048: both grouped GEMMs at their largest reduction length
+    print("layer H=2048 I=2048 E=8 k=2 T=100", flush=True)
+    inp = resample_close_calls(make_layer(T=100, H=2048, I=2048, E=8, k=2, seed=11, bias_mode="random"))
+    check_layer(inp, run_layer(dev, inp))
+
+
 def test_layer_decode8_zipf_seeds(dev):
     print("layer decode8 zipf seeds 1, 2", flush=True)
     for seed in (1, 2):
