@@ -12,10 +12,11 @@
 //      top-k by the key (logit desc, expert asc) through a ballot radix
 //      select, softmax over the chosen k, the block's expert histogram and
 //      each pair's rank among the block's pairs of the same expert.
-//   2. route_scan_kernel  - one workgroup: per-expert scan over blocks, exclusive
-//      scan over experts (offsets), and the tile list of the block map.
-//   3. route_scatter_kernel - one workgroup per 16 tokens: final row of each
-//      pair = block base of its expert + its in-block rank.
+//   2. route_scan_kernel  - 16 experts per workgroup: per-expert scan over the
+//      routing blocks (block bases) and expert totals.
+//   3. route_scatter_kernel - one workgroup per 16 tokens: exclusive scan of the
+//      totals (offsets; workgroup 0 also writes them and the block map), and
+//      the final row of each pair = offset + block base + in-block rank.
 // Ranks count only earlier pairs, so the sort is stable and the result does not
 // depend on thread timing: repeated runs give identical tables.
 #include "moe_internal.h"
@@ -336,94 +337,93 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   }
 }
 
-__global__ __launch_bounds__(1024) void route_scan_kernel(ScanArgs a) {
-  __shared__ int32_t psum[1024];
-  __shared__ int32_t cnt[kMaxExperts];
-  __shared__ int32_t off[kMaxExperts];
-  __shared__ int32_t ntl[kMaxExperts];
-  const int tid = threadIdx.x;
-  const int E = a.E;
-  const int parts = 1024 / E;
-  const int chunk = ceil_div(a.nblk, parts);
-  const int e = tid % E;
-  const int part = tid / E;
-  const bool active = part < parts;
-  const int b0 = part * chunk;
-  const int b1 = min(a.nblk, b0 + chunk);
+// Per-expert scan over the routing blocks, 16 experts per workgroup:
+// block_base[b][e] = sum of block_counts[b'][e] over b' < b, and
+// counts[e] = the sum over all blocks. Thread (e, p) sums a contiguous range
+// of blocks, the 16 ranges of an expert are scanned in LDS, and each thread
+// writes the bases of its range.
+constexpr int kScanExperts = 16;
+constexpr int kScanParts = kRouteThreads / kScanExperts;
 
-  if (active) {
-    int32_t s = 0;
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(ScanArgs a) {
+  __shared__ int32_t part[kScanParts][kScanExperts];
+  const int tid = threadIdx.x;
+  const int el = tid % kScanExperts, p = tid / kScanExperts;
+  const int e = blockIdx.x * kScanExperts + el;
+  const bool ok = e < a.E;
+  const int chunk = ceil_div(a.nblk, kScanParts);
+  const int b0 = min(a.nblk, p * chunk), b1 = min(a.nblk, b0 + chunk);
+  int32_t s = 0;
+  if (ok) {
     int b = b0;
     for (; b + 8 <= b1; b += 8) {
       int32_t v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = a.block_counts[size_t(b + i) * E + e];
+      for (int i = 0; i < 8; ++i) v[i] = a.block_counts[size_t(b + i) * a.E + e];
 #pragma unroll
       for (int i = 0; i < 8; ++i) s += v[i];
     }
-    for (; b < b1; ++b) s += a.block_counts[size_t(b) * E + e];
-    psum[part * E + e] = s;
+    for (; b < b1; ++b) s += a.block_counts[size_t(b) * a.E + e];
   }
+  part[p][el] = s;
   __syncthreads();
-  if (tid < E) {
+  if (tid < kScanExperts) {
     int32_t run = 0;
-    for (int p = 0; p < parts; ++p) {
-      const int32_t v = psum[p * E + tid];
-      psum[p * E + tid] = run;
+    for (int q = 0; q < kScanParts; ++q) {
+      const int32_t v = part[q][tid];
+      part[q][tid] = run;
       run += v;
     }
-    cnt[tid] = run;
-    off[tid] = run;
-    ntl[tid] = ceil_div(run, a.block_rows);
+    if (blockIdx.x * kScanExperts + tid < a.E) a.counts[blockIdx.x * kScanExperts + tid] = run;
   }
   __syncthreads();
-  block_inclusive_scan(off, nullptr, E);   // inclusive scan of counts
-  block_inclusive_scan(ntl, nullptr, E);   // inclusive scan of tiles per expert
-  if (active) {
-    int32_t run = off[e] - cnt[e] + psum[part * E + e];
-    int b = b0;
-    for (; b + 8 <= b1; b += 8) {
-      int32_t v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = a.block_counts[size_t(b + i) * E + e];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        a.block_base[size_t(b + i) * E + e] = run;
-        run += v[i];
-      }
-    }
-    for (; b < b1; ++b) {
-      a.block_base[size_t(b) * E + e] = run;
-      run += a.block_counts[size_t(b) * E + e];
-    }
-  }
-  if (tid < E) {
-    const int32_t c = cnt[tid];
-    const int32_t o = off[tid] - c;
-    a.counts[tid] = c;
-    a.offsets[tid] = o;
-    const int nt_e = ceil_div(c, a.block_rows);
-    const int t_first = ntl[tid] - nt_e;
-    for (int i = 0; i < nt_e; ++i) {
-      a.tile_map[2 * (t_first + i)] = tid;
-      a.tile_map[2 * (t_first + i) + 1] = o + i * a.block_rows;
-    }
-    if (tid == E - 1) {
-      a.offsets[E] = off[tid];
-      *a.num_tiles = ntl[tid];
+  if (ok) {
+    int32_t run = part[p][el];
+    for (int b = b0; b < b1; ++b) {
+      a.block_base[size_t(b) * a.E + e] = run;
+      run += a.block_counts[size_t(b) * a.E + e];
     }
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArgs a) {
+// Final row of each pair: its expert's offset (exclusive scan of counts,
+// recomputed by every workgroup) + its block's base + its rank in the block.
+// Workgroup 0 also writes offsets and the block map.
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArgs a, ScanArgs sa) {
+  __shared__ int32_t off_s[kMaxExperts];
+  __shared__ int32_t til_s[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  const int c = tid < E ? sa.counts[tid] : 0;
+  const int ntl = ceil_div(c, sa.block_rows);
+  if (tid < E) {
+    off_s[tid] = c;
+    til_s[tid] = ntl;
+  }
+  __syncthreads();
+  block_inclusive_scan(off_s, nullptr, E);
+  if (blockIdx.x == 0) block_inclusive_scan(til_s, nullptr, E);   // uniform per workgroup
+  if (blockIdx.x == 0 && tid < E) {
+    const int o = off_s[tid] - c;
+    sa.offsets[tid] = o;
+    const int first = til_s[tid] - ntl;
+    for (int i = 0; i < ntl; ++i) {
+      sa.tile_map[2 * (first + i)] = tid;
+      sa.tile_map[2 * (first + i) + 1] = o + i * sa.block_rows;
+    }
+    if (tid == E - 1) {
+      sa.offsets[E] = off_s[tid];
+      *sa.num_tiles = til_s[tid];
+    }
+  }
   const int blk = blockIdx.x;
   const int t0 = blk * kRouteTokens;
   const int nt = min(kRouteTokens, a.T - t0);
   const int npairs = nt * a.k;
-  for (int p = threadIdx.x; p < npairs; p += kRouteThreads) {
+  for (int p = tid; p < npairs; p += kRouteThreads) {
     const size_t f = size_t(t0) * a.k + p;
     const int e = a.topk_ids[f];
-    const int pos = a.block_base[size_t(blk) * a.E + e] + a.rank_in_block[f];
+    const int pos = off_s[e] - sa.counts[e] + a.block_base[size_t(blk) * E + e] + a.rank_in_block[f];
     a.sorted_rows[pos] = int32_t(f);
     a.row_of_pair[f] = pos;
   }
@@ -473,10 +473,10 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
   hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, rb);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || rb.finish) return err;
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, sa);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(ceil_div(ra.E, kScanExperts)), dim3(kRouteThreads), 0, stream, sa);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kRouteThreads), 0, stream, ca);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kRouteThreads), 0, stream, ca, sa);
   return hipGetLastError();
 }
 
