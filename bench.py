@@ -125,7 +125,7 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_q4_swiglu_prefill4096_traffic.txt")
 KERNEL_SOURCES = ("int4_expert_routing_amd/csrc/gemm_q4.hip", "int4_expert_routing_amd/csrc/gemm_tiles.h",
-                  "int4_expert_routing_amd/csrc/moe_common.h", "int4_expert_routing_amd/csrc/moe_internal.h")
+                  "int4_expert_routing_amd/csrc/gemm_args.h", "int4_expert_routing_amd/csrc/moe_common.h")
 GEMM_KERNEL_NAME = "gemm_q4_kernel<2>"
 
 

@@ -1,19 +1,9 @@
-// Decode-shaped expert GEMV for gfx950: the same per-expert products as the
+// Decode-shaped expert GEMVs for gfx950: the same per-expert products as the
 // grouped GEMM (gemm_q4.hip), laid out for the few-token case where each expert
 // sees at most 8 rows and the layer is bound by streaming the chosen experts'
 // 4-bit weights from HBM (page "Perplexity Open Sources Lily ..." Technical
 // Details, decode bullet: decode reads the active experts' weights once per
 // token; itinai.com post: expansion of the 4-bit weights on chip only).
-//
-// Work split: one workgroup = 2 wave64s per (row tile, column block). A wave
-// owns 16 output columns; its 64 lanes are 16 columns x 4 quarters of the
-// reduction dimension K, so every lane streams K/8 contiguous bytes of one
-// column's codes and the quarters are summed with two lane exchanges at the
-// end. All code loads are issued at once, straight into LDS (buffer loads that
-// write LDS), so the weight stream is in flight while the activation rows are
-// staged; the K loop then runs as a short rolled loop over 64-wide groups.
-//   SwiGLU: wave 0 gate, wave 1 up, for the same 16 columns of h;
-//   STORE_F32: waves 0, 1 for 32 columns.
 //
 // Arithmetic (exact operand, fp32 accumulation, as in the grouped GEMM): each
 // code becomes the bf16 value 1 + q/16, a v_dot2 with the row's activations
@@ -21,37 +11,22 @@
 // group folds as acc += 16 s_g P_g + (b_g - 16 s_g) X_g, where X_g is the
 // row's group sum, computed in fp32 from the staged row.
 #include "gemm_tiles.h"
+#include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kDecWaves = 2;
-constexpr int kDecThreads = kDecWaves * 64;
 constexpr uint32_t kDecRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 
 typedef __attribute__((address_space(3))) void* dec_lds_t;
 
-// LDS row layout: quarter kq of a row starts 16 bytes later than an unpadded
-// layout would put it, so the four quarter groups of a wave read four distinct
-// bank ranges.
-__host__ __device__ constexpr int dec_row_bytes(int K) { return 2 * K + 64; }
-__device__ __forceinline__ int dec_off(int K, int r, int k) { return r * dec_row_bytes(K) + 2 * k + (k / (K / 4)) * 16; }
-
-// LDS of one workgroup: codes [2 waves][K/128 loads][64 lanes][16 B], scale and
-// bias pairs [2][K/256][64] u32, activation rows [8][row bytes], group sums
-// [8][K/64] f32, source rows [8].
-struct DecLds {
-  int codes, sb, xs, xt, src, total;
-};
-__host__ __device__ constexpr DecLds dec_lds(int K) {
-  const int codes = 0;
-  const int sb = codes + kDecWaves * (K / 128) * 1024;
-  const int xs = sb + kDecWaves * (K / 256) * 64 * 4;
-  const int xt = xs + kDecodeMaxRows * dec_row_bytes(K);
-  const int src = xt + kDecodeMaxRows * (K / kGroup) * 4;
-  return DecLds{codes, sb, xs, xt, src, src + kDecodeMaxRows * 4};
+// LDS row layout for lanes that read `parts` equal consecutive slices of K (4
+// per wave: one per lane quarter): slice i starts 16*i bytes later than an
+// unpadded layout would put it, so the four quarters of a wave read four
+// distinct bank ranges.
+__host__ __device__ constexpr int dec_row_bytes(int K, int parts = 4) { return 2 * K + 16 * parts; }
+__device__ __forceinline__ int dec_off(int K, int r, int k, int parts = 4) {
+  return r * dec_row_bytes(K, parts) + 2 * k + (k / (K / parts)) * 16;
 }
-
-size_t decode_lds_bytes(int K) { return size_t(dec_lds(K).total); }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -85,75 +60,104 @@ __device__ __forceinline__ void load_groups(const uint16_t* p, uint16_t (&v)[GQ]
   }
 }
 
-// STEPS = K/128: 16-byte code loads per lane (32 codes each, two per group).
-// PERMUTE: the activation rows arrive in natural order and are put into the
-// operand order [0,4,1,5,2,6,3,7] per 8-element chunk while staged.
-template <int NR, int STEPS, int EPI, bool PERMUTE>
-__device__ __forceinline__ void decode_tile(const GemmArgs& a, const TileInfo& ti, int cb, uint8_t* smem) {
-  constexpr int K = STEPS * 128;
-  constexpr int G = K / kGroup;
-  constexpr int GQ = STEPS / 2;          // groups per lane quarter
-  constexpr DecLds L = dec_lds(K);
+// ---------------------------------------------------------------------------
+// Gate/up projection with SwiGLU (few-token calls).
+//
+// Workgroup = (row tile, 16 columns of h), 2*KS waves: wave w computes the gate
+// (w even) or up (w odd) matrix's 16 columns over slice w/2 of KS equal slices
+// of K. Its 64 lanes are 16 columns x 4 quarters of the slice, so a lane
+// streams STEPS*16 contiguous code bytes of one column; all code loads are
+// issued at once, straight into LDS (buffer loads that write LDS), so the
+// weight stream is in flight while the activation rows are staged. The rows
+// arrive in natural element order and are put into the operand order
+// [0,4,1,5,2,6,3,7] per 8-element chunk while staged. The K loop is a short
+// rolled loop over the lane's 64-wide groups; quarters are summed with two
+// lane exchanges, slices in LDS in a fixed order, and h = silu(gate) * up is
+// written in bf16 in the operand order the down projection reads.
+template <int STEPS, int KS>
+struct DecShape {
+  static constexpr int K = STEPS * 128 * KS;
+  static constexpr int G = K / kGroup;
+  static constexpr int GQ = STEPS / 2;     // groups per lane
+  static constexpr int W = 2 * KS;         // waves
+  static constexpr int PARTS = 4 * KS;     // lane slices of K
+};
+
+// LDS of one workgroup whose tiles have at most nr rows: codes [W][STEPS][64
+// lanes][16 B], scale and bias pairs [W][GQ][64] u32, activation rows
+// [nr][row bytes], group sums [nr][K/64] f32, source rows [8]. The epilogue
+// reuses the code area.
+struct DecLds {
+  int codes, sb, xs, xt, src, total;
+};
+__host__ __device__ constexpr DecLds dec_lds(int steps, int ks, int nr) {
+  const int K = steps * 128 * ks;
+  const int codes = 0;
+  const int sb = codes + 2 * ks * steps * 1024;
+  const int xs = sb + 2 * ks * (steps / 2) * 64 * 4;
+  const int xt = xs + nr * dec_row_bytes(K, 4 * ks);
+  const int src = xt + nr * (K / kGroup) * 4;
+  return DecLds{codes, sb, xs, xt, src, src + kDecodeMaxRows * 4};
+}
+
+template <int NR, int STEPS, int KS>
+__device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const TileInfo& ti, int cb, uint8_t* smem, int nrmax) {
+  using S = DecShape<STEPS, KS>;
+  constexpr int K = S::K, G = S::G, GQ = S::GQ, PARTS = S::PARTS;
+  const DecLds L = dec_lds(STEPS, KS, nrmax);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, kq = lane >> 4;
+  const int up = wave & 1, ks = wave >> 1;
+  const int slice = ks * 4 + kq;            // the lane's slice of K
   uint8_t* codes = smem + L.codes + wave * STEPS * 1024;
   uint32_t* sb = reinterpret_cast<uint32_t*>(smem + L.sb) + wave * GQ * 64;
   uint8_t* xs = smem + L.xs;
   float* Xt = reinterpret_cast<float*>(smem + L.xt);
   int* srcs = reinterpret_cast<int*>(smem + L.src);
 
-  // ---- this wave's 16 columns: code stream into LDS, scales and biases -----
+  // ---- this wave's 16 columns and K slice: code stream into LDS -------------
   const int stack = ti.e == a.E ? 1 : 0;
   const int el = stack ? 0 : ti.e;
-  int col0;
-  const QStack* mat;
-  if constexpr (EPI == kEpiF32) {
-    col0 = cb * 32 + wave * 16;
-    mat = &a.w0[stack];
-  } else {
-    col0 = cb * 16;
-    mat = wave ? &a.w1[stack] : &a.w0[stack];
-  }
-  const size_t wrow0 = size_t(el) * a.N + col0;
+  const QStack& mat = up ? a.w1[stack] : a.w0[stack];
+  const size_t wrow0 = size_t(el) * a.N + cb * 16;
   {
     const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(mat->q + wrow0 * (K / 8)), 0, 0x7FFFFFFF, kDecRsrcWord3);
-    const uint32_t voff = uint32_t((c * (K / 8) + kq * (K / 32)) * 4);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(mat.q + wrow0 * (K / 8)), 0, 0x7FFFFFFF, kDecRsrcWord3);
+    const uint32_t voff = uint32_t((c * (K / 8) + slice * (K / 8 / PARTS)) * 4);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (dec_lds_t)(codes + s * 1024), 16, voff, s * 16, 0, 0);
   }
   {
     uint16_t sv[GQ], bv[GQ];
-    load_groups<GQ>(mat->s + (wrow0 + c) * G + kq * GQ, sv);
-    load_groups<GQ>(mat->b + (wrow0 + c) * G + kq * GQ, bv);
+    load_groups<GQ>(mat.s + (wrow0 + c) * G + slice * GQ, sv);
+    load_groups<GQ>(mat.b + (wrow0 + c) * G + slice * GQ, bv);
 #pragma unroll
     for (int i = 0; i < GQ; ++i) sb[i * 64 + lane] = uint32_t(sv[i]) | (uint32_t(bv[i]) << 16);
   }
 
-  // ---- activation rows and their group sums into LDS ------------------------
+  // ---- activation rows (operand order) and their group sums into LDS -------
   if (tid < NR) srcs[tid] = src_row(a, ti.r0 + tid);
   __syncthreads();
-  for (int i = tid; i < NR * (K / 8); i += kDecThreads) {
+  for (int i = tid; i < NR * (K / 8); i += S::W * 64) {
     const int r = i / (K / 8), ch = i % (K / 8);
-    u32x4 v = *reinterpret_cast<const u32x4*>(a.A + size_t(srcs[r]) * K + ch * 8);
-    if (PERMUTE) v = permute_chunk(v);
-    *reinterpret_cast<u32x4*>(xs + dec_off(K, r, ch * 8)) = v;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.A + size_t(srcs[r]) * K + ch * 8);
+    *reinterpret_cast<u32x4*>(xs + dec_off(K, r, ch * 8, PARTS)) = permute_chunk(v);
   }
   __syncthreads();
-  for (int i = tid; i < NR * G; i += kDecThreads) {
+  for (int i = tid; i < NR * G; i += S::W * 64) {
     const int r = i / G, g = i % G;
     float sum = 0.0f;
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch)
-      sum += chunk_sum(*reinterpret_cast<const u32x4*>(xs + dec_off(K, r, g * kGroup + ch * 8)));
+      sum += chunk_sum(*reinterpret_cast<const u32x4*>(xs + dec_off(K, r, g * kGroup + ch * 8, PARTS)));
     Xt[r * G + g] = sum;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's code loads have landed
   __syncthreads();
 
-  // ---- dot products over the lane's quarter of K, one group per iteration ---
+  // ---- dot products over the lane's slice, one group per iteration ---------
   float acc[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
@@ -171,10 +175,10 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, const TileInfo& t
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 p = __builtin_bit_cast(u32x4, unpack_word(wd[j], nib, magic));
-        const int k0 = kq * (K / 4) + 32 * s + 8 * j;
+        const int k0 = slice * (K / PARTS) + 32 * s + 8 * j;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + dec_off(K, r, k0));
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + dec_off(K, r, k0, PARTS));
           P[r] = dot2(p.x, xv.x, P[r]);
           P[r] = dot2(p.y, xv.y, P[r]);
           P[r] = dot2(p.z, xv.z, P[r]);
@@ -185,7 +189,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, const TileInfo& t
     const uint32_t sbv = sb[gl * 64 + lane];
     const float s16 = 16.0f * __uint_as_float(sbv << 16);
     const float off = __uint_as_float(sbv & 0xFFFF0000u) - s16;
-    const int g = kq * GQ + gl;
+    const int g = slice * GQ + gl;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       acc[r] = __builtin_fmaf(s16, P[r], acc[r]);
@@ -198,43 +202,38 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, const TileInfo& t
     acc[r] += __shfl_xor(acc[r], 32, kWave);
   }
 
-  // ---- epilogues -------------------------------------------------------------
-  if constexpr (EPI == kEpiF32) {
-    float* out = reinterpret_cast<float*>(a.out);
-    if (kq == 0) {
+  // ---- slices summed in order, SwiGLU, bf16 h in operand order -------------
+  __syncthreads();   // every wave is done with its codes (the epilogue reuses them)
+  float* part = reinterpret_cast<float*>(smem + L.codes);                    // [W][NR][16]
+  uint16_t* hs = reinterpret_cast<uint16_t*>(part + S::W * NR * 16);          // [NR][16]
+  if (lane < 16) {
 #pragma unroll
-      for (int r = 0; r < NR; ++r) out[size_t(ti.r0 + r) * a.N + col0 + c] = acc[r];
-    }
-  } else {
-    __syncthreads();   // every wave is done reading xs (the tiles below reuse it)
-    float* gs = reinterpret_cast<float*>(xs);                           // [NR][16]
-    uint16_t* hs = reinterpret_cast<uint16_t*>(xs + kDecodeMaxRows * 16 * 4);  // [NR][16]
-    if (wave == 0 && kq == 0) {
+    for (int r = 0; r < NR; ++r) part[(wave * NR + r) * 16 + c] = acc[r];
+  }
+  __syncthreads();
+  if (tid < NR * 16) {
+    const int r = tid >> 4, cc = tid & 15;
+    float gv = 0.0f, uv = 0.0f;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) gs[r * 16 + c] = acc[r];
+    for (int k2 = 0; k2 < KS; ++k2) {
+      gv += part[((2 * k2) * NR + r) * 16 + cc];
+      uv += part[((2 * k2 + 1) * NR + r) * 16 + cc];
     }
-    __syncthreads();
-    if (wave == 1 && kq == 0) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const float gv = gs[r * 16 + c];
-        const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[r];
-        hs[r * 16 + c] = uint16_t(f32_to_bf16_rne(hv));
-      }
-    }
-    __syncthreads();
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-    if (tid < NR * 2) {
-      // row tid/2, chunk tid%2 of this column block, stored in the operand order
-      const int r = tid >> 1, ch = tid & 1;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(hs + r * 16 + ch * 8);
-      *reinterpret_cast<u32x4*>(out + size_t(ti.r0 + r) * a.N + cb * 16 + ch * 8) = permute_chunk(v);
-    }
+    const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+    hs[r * 16 + cc] = uint16_t(f32_to_bf16_rne(hv));
+  }
+  __syncthreads();
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  if (tid < NR * 2) {
+    // row tid/2, chunk tid%2 of this column block, stored in the operand order
+    const int r = tid >> 1, ch = tid & 1;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(hs + r * 16 + ch * 8);
+    *reinterpret_cast<u32x4*>(out + size_t(ti.r0 + r) * a.N + cb * 16 + ch * 8) = permute_chunk(v);
   }
 }
 
-template <int STEPS, int EPI, bool PERMUTE>
-__global__ __launch_bounds__(kDecThreads) void decode_q4_kernel(GemmArgs a) {
+template <int STEPS, int KS>
+__global__ __launch_bounds__(2 * KS * 64) void decode_swiglu_kernel(GemmArgs a, int nrmax) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tile = blockIdx.x / a.NT;
   const int cb = blockIdx.x % a.NT;
@@ -242,45 +241,170 @@ __global__ __launch_bounds__(kDecThreads) void decode_q4_kernel(GemmArgs a) {
   TileInfo ti;
   if (!tile_info(a, tile, ti)) return;
   switch (ti.r1 - ti.r0) {
-    case 1: decode_tile<1, STEPS, EPI, PERMUTE>(a, ti, cb, smem); break;
-    case 2: decode_tile<2, STEPS, EPI, PERMUTE>(a, ti, cb, smem); break;
-    case 3: decode_tile<3, STEPS, EPI, PERMUTE>(a, ti, cb, smem); break;
-    case 4: decode_tile<4, STEPS, EPI, PERMUTE>(a, ti, cb, smem); break;
-    case 5: decode_tile<5, STEPS, EPI, PERMUTE>(a, ti, cb, smem); break;
-    case 6: decode_tile<6, STEPS, EPI, PERMUTE>(a, ti, cb, smem); break;
-    case 7: decode_tile<7, STEPS, EPI, PERMUTE>(a, ti, cb, smem); break;
-    case 8: decode_tile<8, STEPS, EPI, PERMUTE>(a, ti, cb, smem); break;
-    default: break;   // callers guarantee at most kDecodeMaxRows rows per tile
+    case 1: swiglu_tile<1, STEPS, KS>(a, ti, cb, smem, nrmax); break;
+    case 2: swiglu_tile<2, STEPS, KS>(a, ti, cb, smem, nrmax); break;
+    case 3: swiglu_tile<3, STEPS, KS>(a, ti, cb, smem, nrmax); break;
+    case 4: swiglu_tile<4, STEPS, KS>(a, ti, cb, smem, nrmax); break;
+    case 5: swiglu_tile<5, STEPS, KS>(a, ti, cb, smem, nrmax); break;
+    case 6: swiglu_tile<6, STEPS, KS>(a, ti, cb, smem, nrmax); break;
+    case 7: swiglu_tile<7, STEPS, KS>(a, ti, cb, smem, nrmax); break;
+    case 8: swiglu_tile<8, STEPS, KS>(a, ti, cb, smem, nrmax); break;
+    default: break;   // callers guarantee 1..nrmax rows per tile, nrmax <= kDecodeMaxRows
   }
 }
 
-bool decode_supported(int N, int K, int epilogue) {
-  const int steps = K / 128;
-  if (K % 128 != 0 || (steps != 2 && steps != 4 && steps != 8 && steps != 16)) return false;
-  return epilogue == kEpiF32 ? N % 32 == 0 : (epilogue == kEpiSwigluInternal && N % 16 == 0);
+// ---------------------------------------------------------------------------
+// Down projection fused with the weighted combine (few-token calls).
+//
+// Workgroup = (token t, 16 output columns), W = min(k + 1, 16) waves. The
+// token's pairs are j = 0..k-1 (routed expert topk_ids[t][j], h row
+// row_of_pair[t*k+j], weight topk_w[t][j]) and j = k (the shared expert, h row
+// shared_row0 + t, weight 1). Wave w takes pairs w, w + W, ...: it stages the
+// pair's h row and its group sums in its own LDS area, streams the 16 columns'
+// codes of that expert straight into registers (lane = column c x quarter kq
+// of K, as in the kernel above) and accumulates w_j * (h . Wd column) in pair
+// order. The waves' sums are then added in wave order, so the result does not
+// depend on timing, and y[t] is rounded to bf16 once.
+__host__ __device__ constexpr int dc_wave_bytes(int K) { return dec_row_bytes(K) + (K / kGroup) * 4; }
+constexpr int kDcMaxWaves = 16;
+
+template <int STEPS>
+__global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(DownCombineArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int K = STEPS * 128;
+  constexpr int G = K / kGroup;
+  constexpr int GQ = STEPS / 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = blockDim.x >> 6;
+  const int c = lane & 15, kq = lane >> 4;
+  const int ncb = a.N / 16;
+  const int t = blockIdx.x / ncb;
+  const int col0 = (blockIdx.x % ncb) * 16;
+  uint8_t* wl = smem + wave * dc_wave_bytes(K);
+  uint8_t* xs = wl;                                                     // the pair's h row
+  float* Xt = reinterpret_cast<float*>(wl + dec_row_bytes(K));          // its group sums
+  float* red = reinterpret_cast<float*>(smem + W * dc_wave_bytes(K));   // [W][16]
+  const uint32_t nib = kNib, magic = kMagic;
+
+  float tot = 0.0f;
+  for (int j = wave; j <= a.k; j += W) {
+    const bool routed = j < a.k;
+    const size_t f = size_t(t) * a.k + (routed ? j : 0);
+    const int el = routed ? a.topk_ids[f] : 0;
+    const int row = routed ? a.row_of_pair[f] : a.shared_row0 + t;
+    const float wj = routed ? a.topk_w[f] : 1.0f;
+    const uint32_t* mq = routed ? a.down.q : a.down_shared.q;
+    const uint16_t* ms = routed ? a.down.s : a.down_shared.s;
+    const uint16_t* mb = routed ? a.down.b : a.down_shared.b;
+    const size_t wrow = size_t(el) * a.N + col0 + c;
+    // the lane's K/8 contiguous code bytes (quarter kq of its column)
+    const u32x4* qp = reinterpret_cast<const u32x4*>(mq + wrow * (K / 8) + kq * (K / 32));
+    u32x4 w[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) w[s] = qp[s];
+    uint16_t sv[GQ], bv[GQ];
+    load_groups<GQ>(ms + wrow * G + kq * GQ, sv);
+    load_groups<GQ>(mb + wrow * G + kq * GQ, bv);
+    // stage the h row (already in operand order) and its fp32 group sums
+    __builtin_amdgcn_wave_barrier();   // the previous pair's reads of xs and Xt are done
+    const uint16_t* hr = a.h + size_t(row) * K;
+    for (int ch = lane; ch < K / 8; ch += 64)
+      *reinterpret_cast<u32x4*>(xs + dec_off(K, 0, ch * 8)) = *reinterpret_cast<const u32x4*>(hr + ch * 8);
+    __builtin_amdgcn_wave_barrier();
+    if (lane < G) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) sum += chunk_sum(*reinterpret_cast<const u32x4*>(xs + dec_off(K, 0, lane * kGroup + ch * 8)));
+      Xt[lane] = sum;
+    }
+    __builtin_amdgcn_wave_barrier();
+    float acc = 0.0f;
+#pragma unroll
+    for (int gl = 0; gl < GQ; ++gl) {
+      float P = 0.0f;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int s = 2 * gl + hh;
+        const uint32_t wd[4] = {w[s].x, w[s].y, w[s].z, w[s].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 pv = __builtin_bit_cast(u32x4, unpack_word(wd[q], nib, magic));
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + dec_off(K, 0, kq * (K / 4) + 32 * s + 8 * q));
+          P = dot2(pv.x, xv.x, P);
+          P = dot2(pv.y, xv.y, P);
+          P = dot2(pv.z, xv.z, P);
+          P = dot2(pv.w, xv.w, P);
+        }
+      }
+      const float s16 = 16.0f * __uint_as_float(uint32_t(sv[gl]) << 16);
+      const float off = __uint_as_float(uint32_t(bv[gl]) << 16) - s16;
+      acc = __builtin_fmaf(s16, P, acc);
+      acc = __builtin_fmaf(off, Xt[kq * GQ + gl], acc);
+    }
+    acc += __shfl_xor(acc, 16, kWave);
+    acc += __shfl_xor(acc, 32, kWave);
+    tot = __builtin_fmaf(wj, acc, tot);
+  }
+  if (lane < 16) red[wave * 16 + lane] = tot;
+  __syncthreads();
+  if (tid < 16) {
+    float sum = 0.0f;
+    for (int i = 0; i < W; ++i) sum += red[i * 16 + tid];
+    a.y[size_t(t) * a.N + col0 + tid] = uint16_t(f32_to_bf16_rne(sum));
+  }
 }
 
-template <int EPI, bool PERMUTE>
-static hipError_t launch_decode_epi(const GemmArgs& ga, dim3 grid, size_t lds, hipStream_t stream) {
-  switch (ga.K / 128) {
-    case 2: hipLaunchKernelGGL((decode_q4_kernel<2, EPI, PERMUTE>), grid, dim3(kDecThreads), lds, stream, ga); break;
-    case 4: hipLaunchKernelGGL((decode_q4_kernel<4, EPI, PERMUTE>), grid, dim3(kDecThreads), lds, stream, ga); break;
-    case 8: hipLaunchKernelGGL((decode_q4_kernel<8, EPI, PERMUTE>), grid, dim3(kDecThreads), lds, stream, ga); break;
-    default: hipLaunchKernelGGL((decode_q4_kernel<16, EPI, PERMUTE>), grid, dim3(kDecThreads), lds, stream, ga); break;
+bool decode_down_combine_supported(int N, int K) {
+  const int steps = K / 128;
+  return K % 128 == 0 && (steps == 2 || steps == 4 || steps == 8 || steps == 16) && N % 16 == 0;
+}
+
+hipError_t launch_decode_down_combine(const DownCombineArgs& da, hipStream_t stream) {
+  if (!decode_down_combine_supported(da.N, da.K)) return hipErrorInvalidValue;
+  if (da.T == 0) return hipSuccess;
+  const int W = da.k + 1 < kDcMaxWaves ? da.k + 1 : kDcMaxWaves;
+  const dim3 grid(unsigned(da.T) * unsigned(da.N / 16)), block(unsigned(W) * 64u);
+  const size_t lds = size_t(W) * dc_wave_bytes(da.K) + size_t(W) * 16 * 4;
+  switch (da.K / 128) {
+    case 2: hipLaunchKernelGGL(decode_down_combine_kernel<2>, grid, block, lds, stream, da); break;
+    case 4: hipLaunchKernelGGL(decode_down_combine_kernel<4>, grid, block, lds, stream, da); break;
+    case 8: hipLaunchKernelGGL(decode_down_combine_kernel<8>, grid, block, lds, stream, da); break;
+    default: hipLaunchKernelGGL(decode_down_combine_kernel<16>, grid, block, lds, stream, da); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const GemmArgs& ga, int epilogue, bool natural_rows, int max_row_tiles, hipStream_t stream) {
-  if (!decode_supported(ga.N, ga.K, epilogue)) return hipErrorInvalidValue;
+bool decode_supported(int N, int K) {
+  return (K == 256 || K == 512 || K == 1024 || K == 2048) && N % 16 == 0;
+}
+
+hipError_t launch_decode(const GemmArgs& ga, int max_row_tiles, int max_rows, hipStream_t stream) {
+  if (!decode_supported(ga.N, ga.K) || ga.NT != ga.N / 16 || max_rows < 1 || max_rows > kDecodeMaxRows)
+    return hipErrorInvalidValue;
   const dim3 grid(unsigned(max_row_tiles) * unsigned(ga.NT));
   if (grid.x == 0) return hipSuccess;
-  const size_t lds = decode_lds_bytes(ga.K);
-  if (epilogue == kEpiF32)
-    return natural_rows ? launch_decode_epi<kEpiF32, true>(ga, grid, lds, stream)
-                        : launch_decode_epi<kEpiF32, false>(ga, grid, lds, stream);
-  return natural_rows ? launch_decode_epi<kEpiSwigluInternal, true>(ga, grid, lds, stream)
-                      : launch_decode_epi<kEpiSwigluInternal, false>(ga, grid, lds, stream);
+  // K slices per column set: K/512 (at least 1, at most 4), so a lane streams
+  // 64 or 128 codes and a workgroup has 2, 4 or 8 waves
+  switch (ga.K) {
+    case 256:
+      hipLaunchKernelGGL((decode_swiglu_kernel<2, 1>), grid, dim3(128), dec_lds(2, 1, max_rows).total, stream, ga,
+                         max_rows);
+      break;
+    case 512:
+      hipLaunchKernelGGL((decode_swiglu_kernel<4, 1>), grid, dim3(128), dec_lds(4, 1, max_rows).total, stream, ga,
+                         max_rows);
+      break;
+    case 1024:
+      hipLaunchKernelGGL((decode_swiglu_kernel<4, 2>), grid, dim3(256), dec_lds(4, 2, max_rows).total, stream, ga,
+                         max_rows);
+      break;
+    default:
+      hipLaunchKernelGGL((decode_swiglu_kernel<4, 4>), grid, dim3(512), dec_lds(4, 4, max_rows).total, stream, ga,
+                         max_rows);
+      break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -1,0 +1,41 @@
+// Arguments of the grouped 4-bit GEMM kernel (internal, not part of the C ABI).
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int kMaxK = 2048;  // largest reduction size of the grouped GEMM (LDS budget)
+
+// One stack of 4-bit matrices [n][N][K/8] with bf16 scale/bias [n][N][K/64].
+struct QStack {
+  const uint32_t* q;
+  const uint16_t* s;
+  const uint16_t* b;
+};
+
+enum GemmEpilogue { kEpiF32 = 0, kEpiSwigluNatural = 1, kEpiSwigluInternal = 2 };
+
+struct GemmArgs {
+  const uint16_t* A;        // activations in the permuted chunk order [a_rows][K]
+  const uint16_t* Apart;    // group sums split in three bf16 parts [a_rows][xpart_cols(K)]
+  const int32_t* sorted_rows;  // gather for routed rows: src = sorted_rows[r] / row_div; null = identity
+  int row_div;
+  int routed_rows;          // rows [0, routed_rows) belong to routed tiles
+  int shared_src_base;      // a shared-expert row r reads activation row r - shared_src_base
+  QStack w0[2];             // [0] routed experts, [1] shared expert (gate, or the only matrix)
+  QStack w1[2];             // up projection (SwiGLU epilogues only)
+  int E;                    // a tile whose expert is E uses the shared stack
+  const int32_t* offsets;
+  const int32_t* tile_map;
+  const int32_t* num_tiles;
+  int n_shared_tiles;       // the first n_shared_tiles tiles cover the shared rows
+  int shared_rows;
+  int N, K, NT;             // NT = column tiles per row tile
+  void* out;                // f32 [rows][N], or bf16 [rows][N]
+  uint16_t* out_part;       // group-sum table of the bf16 output (internal SwiGLU only)
+};
+
+hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream);
+
+}  // namespace moe

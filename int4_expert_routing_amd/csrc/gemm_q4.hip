@@ -440,80 +440,4 @@ hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipS
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Activation preparation: permuted chunk order plus the group-sum table.
-// 8 lanes per group, one 16-byte chunk each; group sums in fp64, rounded once.
-__global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* A, int rows, int K, uint16_t* a_perm,
-                                                        uint16_t* a_part) {
-  const int G = K / kGroup;
-  const int KPx = xpart_cols(K);
-  const long gid = long(blockIdx.x) * blockDim.x + threadIdx.x;
-  const long team = gid >> 3;
-  const int sub = int(gid & 7);
-  const long total = long(rows) * G;
-  const bool ok = team < total;
-  const int row = ok ? int(team / G) : 0;
-  const int g = ok ? int(team % G) : 0;
-  u32x4 v = u32x4{0, 0, 0, 0};
-  if (ok) v = *reinterpret_cast<const u32x4*>(A + size_t(row) * K + g * kGroup + 8 * sub);
-  double s = chunk_sum_f64(v);
-  s += __shfl_xor(s, 1, kWave);
-  s += __shfl_xor(s, 2, kWave);
-  s += __shfl_xor(s, 4, kWave);
-  if (!ok) return;
-  *reinterpret_cast<u32x4*>(a_perm + size_t(row) * K + g * kGroup + 8 * sub) = permute_chunk(v);
-  uint16_t* xp = a_part + size_t(row) * KPx;
-  if (sub == 0) {
-    uint16_t h, m, l;
-    split3_bf16(float(s), h, m, l);
-    const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
-                     uint32_t(m) | (uint32_t(l) << 16), 0u};
-    *reinterpret_cast<u32x4*>(xp + 8 * g) = e;
-  }
-}
-
-hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
-                            hipStream_t stream) {
-  const long threads = long(rows) * (K / kGroup) * 8;
-  if (threads == 0) return hipSuccess;
-  const unsigned blocks = unsigned((threads + 255) / 256);
-  hipLaunchKernelGGL(prep_rows_kernel, dim3(blocks), dim3(256), 0, stream, A, rows, K, a_perm, a_part);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Weighted combine: y[t] = bf16(S[t] + sum_j w[t][j] * Y[row_of_pair[t*k+j]]).
-__global__ __launch_bounds__(256) void combine_kernel(const float* Y, const float* w, const int32_t* row_of_pair,
-                                                      int T, int k, int H, int shared_row0, uint16_t* y) {
-  const int t = blockIdx.x;
-  __shared__ int32_t rows[kMaxTopk];
-  __shared__ float ws[kMaxTopk];
-  if (threadIdx.x < k) {
-    rows[threadIdx.x] = row_of_pair[size_t(t) * k + threadIdx.x];
-    ws[threadIdx.x] = w[size_t(t) * k + threadIdx.x];
-  }
-  __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
-    f32x4 acc = *reinterpret_cast<const f32x4*>(Y + size_t(shared_row0 + t) * H + c);
-    for (int j = 0; j < k; ++j) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(Y + size_t(rows[j]) * H + c);
-      const float wj = ws[j];
-      acc[0] = __builtin_fmaf(wj, v[0], acc[0]);
-      acc[1] = __builtin_fmaf(wj, v[1], acc[1]);
-      acc[2] = __builtin_fmaf(wj, v[2], acc[2]);
-      acc[3] = __builtin_fmaf(wj, v[3], acc[3]);
-    }
-    uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-    *reinterpret_cast<uint2*>(y + size_t(t) * H + c) = make_uint2(lo, hi);
-  }
-}
-
-hipError_t launch_combine(const float* Y, const float* w, const int32_t* row_of_pair, int T, int k, int H,
-                          int shared_row0, uint16_t* y, hipStream_t stream) {
-  if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y);
-  return hipGetLastError();
-}
-
 }  // namespace moe

@@ -3,7 +3,7 @@
 // activation-row gather, and the exact 4-bit operand unpack.
 #pragma once
 
-#include "moe_internal.h"
+#include "gemm_args.h"
 
 namespace moe {
 

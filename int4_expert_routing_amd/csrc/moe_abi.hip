@@ -278,8 +278,8 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   // few tokens: every tile has at most kDecodeMaxRows rows, and the weight
   // stream, not the MFMA, bounds the layer (decode-shaped kernels, which read x
   // in natural order and need no group-sum tables)
-  const bool decode = T <= kDecodeMaxRows && decode_supported(I, H, kEpiSwigluInternal) &&
-                      decode_supported(H, I, kEpiF32);
+  const bool decode = T <= kDecodeMaxRows && decode_supported(I, H) &&
+                      decode_down_combine_supported(H, I);
 
   // 1. activations: permuted chunk order + group sums
   uint16_t* x_perm = at<uint16_t>(ws, L.x_perm);
@@ -342,9 +342,17 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.NT = decode ? I / 16 : I / 128;
   g1.out = h;
   g1.out_part = h_part;
-  const hipError_t e1 = decode ? launch_decode(g1, kEpiSwigluInternal, true, n_sh + max_routed, s)
+  const hipError_t e1 = decode ? launch_decode(g1, n_sh + max_routed, T, s)
                                : launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s);
   if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
+
+  // 6-7 (few tokens). down projection fused with the weighted combine
+  if (decode) {
+    const DownCombineArgs da{h, stack_of(down), stack_of(sh_down), ids, wts, row_of_pair, T, k, H, I,
+                             routed_rows, y};
+    if (launch_decode_down_combine(da, s) != hipSuccess || !mark(4) || !mark(5)) return MOE_ERR_HIP;
+    return MOE_OK;
+  }
 
   // 6. down grouped GEMM (fp32 rows)
   float* Y = at<float>(ws, L.Y);
@@ -360,11 +368,10 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g2.w1[1] = g2.w0[1];
   g2.N = H;
   g2.K = I;
-  g2.NT = decode ? H / 32 : ceil_div(H, 256);
+  g2.NT = ceil_div(H, 256);
   g2.out = Y;
   g2.out_part = nullptr;
-  const hipError_t e2 = decode ? launch_decode(g2, kEpiF32, false, n_sh + max_routed, s)
-                               : launch_gemm(g2, kEpiF32, n_sh + max_routed, s);
+  const hipError_t e2 = launch_gemm(g2, kEpiF32, n_sh + max_routed, s);
   if (e2 != hipSuccess || !mark(4)) return MOE_ERR_HIP;
 
   // 7. weighted combine + shared expert, bf16 output

@@ -1,14 +1,13 @@
 // Internal kernel argument structs and launchers (not part of the C ABI).
 #pragma once
 
-#include "moe_common.h"
+#include "gemm_args.h"
 #include "../../include/moe_q4.h"
 
 namespace moe {
 
 constexpr int kMaxExperts = MOE_MAX_EXPERTS;
 constexpr int kMaxTopk = MOE_MAX_TOPK;
-constexpr int kMaxK = 2048;  // largest reduction size of the grouped GEMM (LDS budget)
 
 struct RouteArgs {
   const uint16_t* x;        // bf16 [T][H] (router GEMM input) or null
@@ -62,46 +61,31 @@ int router_splits(int T, int H);
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,
                         hipStream_t stream);
 
-// One stack of 4-bit matrices [n][N][K/8] with bf16 scale/bias [n][N][K/64].
-struct QStack {
-  const uint32_t* q;
-  const uint16_t* s;
-  const uint16_t* b;
-};
-
-enum GemmEpilogue { kEpiF32 = 0, kEpiSwigluNatural = 1, kEpiSwigluInternal = 2 };
-
-struct GemmArgs {
-  const uint16_t* A;        // activations in the permuted chunk order [a_rows][K]
-  const uint16_t* Apart;    // group sums split in three bf16 parts [a_rows][xpart_cols(K)]
-  const int32_t* sorted_rows;  // gather for routed rows: src = sorted_rows[r] / row_div; null = identity
-  int row_div;
-  int routed_rows;          // rows [0, routed_rows) belong to routed tiles
-  int shared_src_base;      // a shared-expert row r reads activation row r - shared_src_base
-  QStack w0[2];             // [0] routed experts, [1] shared expert (gate, or the only matrix)
-  QStack w1[2];             // up projection (SwiGLU epilogues only)
-  int E;                    // a tile whose expert is E uses the shared stack
-  const int32_t* offsets;
-  const int32_t* tile_map;
-  const int32_t* num_tiles;
-  int n_shared_tiles;       // the first n_shared_tiles tiles cover the shared rows
-  int shared_rows;
-  int N, K, NT;             // NT = column tiles per row tile
-  void* out;                // f32 [rows][N], or bf16 [rows][N]
-  uint16_t* out_part;       // group-sum table of the bf16 output (internal SwiGLU only)
-};
-
-hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream);
-
 // Decode-shaped kernels: row tiles of at most kDecodeMaxRows rows (every tile
 // of a layer call with T <= kDecodeMaxRows tokens).
 constexpr int kDecodeMaxRows = 8;
-bool decode_supported(int N, int K, int epilogue);
-// ga.NT = N/16 column blocks (SwiGLU, internal epilogue: h in the operand chunk
-// order, no group-sum table) or N/32 (STORE_F32). natural_rows: ga.A holds rows
-// in natural element order (the kernel reorders them while staging).
-hipError_t launch_decode(const GemmArgs& ga, int epilogue, bool natural_rows, int max_row_tiles,
-                         hipStream_t stream);
+// Gate/up projection with SwiGLU: K in {256, 512, 1024, 2048}, N % 16 == 0,
+// ga.NT = N/16 column blocks, ga.A rows in natural element order; h is written
+// in the operand chunk order with no group-sum table. max_rows bounds every
+// tile's row count (1..kDecodeMaxRows).
+bool decode_supported(int N, int K);
+hipError_t launch_decode(const GemmArgs& ga, int max_row_tiles, int max_rows, hipStream_t stream);
+
+// Down projection fused with the weighted combine, for the same few-token
+// calls: y[t] = bf16(sum_j w[t][j] * (h[row_of_pair[t*k+j]] . Wd[e_tj]) +
+// h[shared_row0 + t] . Wd_shared), one workgroup per (token, 16 columns).
+struct DownCombineArgs {
+  const uint16_t* h;          // bf16 [routed rows + T][K], operand chunk order
+  QStack down;                // routed experts [E][N][K/8]
+  QStack down_shared;         // shared expert [1][N][K/8]
+  const int32_t* topk_ids;    // [T][k]
+  const float* topk_w;        // [T][k]
+  const int32_t* row_of_pair; // [T][k]
+  int T, k, N, K, shared_row0;
+  uint16_t* y;                // bf16 [T][N]
+};
+bool decode_down_combine_supported(int N, int K);
+hipError_t launch_decode_down_combine(const DownCombineArgs& da, hipStream_t stream);
 
 hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
                             hipStream_t stream);

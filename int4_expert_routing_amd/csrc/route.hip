@@ -147,17 +147,33 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&u)[kMaxKeysPerL
   return tau;
 }
 
-// Inclusive scan of v over n <= 1024 entries held in LDS (one per thread).
-__device__ void block_inclusive_scan(int32_t* v, int32_t* tmp, int n) {
-  const int tid = threadIdx.x;
-  for (int d = 1; d < n; d <<= 1) {
-    int32_t x = 0;
-    if (tid < n) x = v[tid] + (tid >= d ? v[tid - d] : 0);
-    __syncthreads();
-    if (tid < n) v[tid] = x;
-    __syncthreads();
+// Inclusive scans of two per-thread values over the whole workgroup (thread
+// order), one value pair per thread: a shuffle scan inside each wave, then each
+// wave adds the totals of the waves before it. tot holds 2 x (waves) ints of
+// LDS; every thread of the workgroup must call this.
+__device__ __forceinline__ void block_scan2(int32_t& a, int32_t& b, int32_t* tot) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nw = blockDim.x >> 6;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t ua = __shfl_up(a, d, kWave), ub = __shfl_up(b, d, kWave);
+    if (lane >= d) {
+      a += ua;
+      b += ub;
+    }
   }
-  (void)tmp;
+  if (lane == kWave - 1) {
+    tot[w] = a;
+    tot[nw + w] = b;
+  }
+  __syncthreads();
+  int32_t pa = 0, pb = 0;
+  for (int i = 0; i < w; ++i) {
+    pa += tot[i];
+    pb += tot[nw + i];
+  }
+  a += pa;
+  b += pb;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
@@ -305,33 +321,29 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   // histogram, the block map lists ceil(count / block_rows) tiles per expert
   // in expert order, and each pair's row is its expert's offset plus its rank.
   __shared__ int32_t off_s[kMaxExperts];
-  __shared__ int32_t til_s[kMaxExperts];
+  __shared__ int32_t scan_tot[2 * kRouteTokens];
   const int c = tid < E ? hist[tid] : 0;
   const int ntl = ceil_div(c, a.block_rows);
+  int32_t oc = c, tc = ntl;   // inclusive scans of counts and tile counts
+  block_scan2(oc, tc, scan_tot);
   if (tid < E) {
-    off_s[tid] = c;
-    til_s[tid] = ntl;
-  }
-  __syncthreads();
-  block_inclusive_scan(off_s, nullptr, E);
-  block_inclusive_scan(til_s, nullptr, E);
-  if (tid < E) {
-    const int o = off_s[tid] - c;
+    const int o = oc - c;
+    off_s[tid] = o;
     a.counts[tid] = c;
     a.offsets[tid] = o;
-    const int first = til_s[tid] - ntl;
+    const int first = tc - ntl;
     for (int i = 0; i < ntl; ++i) {
       a.tile_map[2 * (first + i)] = tid;
       a.tile_map[2 * (first + i) + 1] = o + i * a.block_rows;
     }
     if (tid == E - 1) {
-      a.offsets[E] = off_s[tid];
-      *a.num_tiles = til_s[tid];
+      a.offsets[E] = oc;
+      *a.num_tiles = tc;
     }
   }
   __syncthreads();
   for (int p = tid; p < npairs_all; p += kTopkThreads) {
-    const int pos = off_s[ids_s[p]] - hist[ids_s[p]] + rank_s[p];
+    const int pos = off_s[ids_s[p]] + rank_s[p];
     a.sorted_rows[pos] = p;
     a.row_of_pair[p] = pos;
   }
@@ -391,31 +403,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(ScanArgs a) {
 // Workgroup 0 also writes offsets and the block map.
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArgs a, ScanArgs sa) {
   __shared__ int32_t off_s[kMaxExperts];
-  __shared__ int32_t til_s[kMaxExperts];
+  __shared__ int32_t scan_tot[2 * (kRouteThreads / kWave)];
   const int tid = threadIdx.x;
   const int E = a.E;
   const int c = tid < E ? sa.counts[tid] : 0;
   const int ntl = ceil_div(c, sa.block_rows);
-  if (tid < E) {
-    off_s[tid] = c;
-    til_s[tid] = ntl;
-  }
-  __syncthreads();
-  block_inclusive_scan(off_s, nullptr, E);
-  if (blockIdx.x == 0) block_inclusive_scan(til_s, nullptr, E);   // uniform per workgroup
+  int32_t oc = c, tc = ntl;   // inclusive scans of counts and tile counts
+  block_scan2(oc, tc, scan_tot);
+  if (tid < E) off_s[tid] = oc - c;   // exclusive: the expert's first row
   if (blockIdx.x == 0 && tid < E) {
-    const int o = off_s[tid] - c;
+    const int o = oc - c;
     sa.offsets[tid] = o;
-    const int first = til_s[tid] - ntl;
+    const int first = tc - ntl;
     for (int i = 0; i < ntl; ++i) {
       sa.tile_map[2 * (first + i)] = tid;
       sa.tile_map[2 * (first + i) + 1] = o + i * sa.block_rows;
     }
     if (tid == E - 1) {
-      sa.offsets[E] = off_s[tid];
-      *sa.num_tiles = til_s[tid];
+      sa.offsets[E] = oc;
+      *sa.num_tiles = tc;
     }
   }
+  __syncthreads();
   const int blk = blockIdx.x;
   const int t0 = blk * kRouteTokens;
   const int nt = min(kRouteTokens, a.T - t0);
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArg
   for (int p = tid; p < npairs; p += kRouteThreads) {
     const size_t f = size_t(t0) * a.k + p;
     const int e = a.topk_ids[f];
-    const int pos = off_s[e] - sa.counts[e] + a.block_base[size_t(blk) * E + e] + a.rank_in_block[f];
+    const int pos = off_s[e] + a.block_base[size_t(blk) * E + e] + a.rank_in_block[f];
     a.sorted_rows[pos] = int32_t(f);
     a.row_of_pair[f] = pos;
   }
