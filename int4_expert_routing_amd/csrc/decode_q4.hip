@@ -66,14 +66,15 @@ __device__ __forceinline__ void load_groups(const uint16_t* p, uint16_t (&v)[GQ]
 // Workgroup = (row tile, 16 columns of h), 2*KS waves: wave w computes the gate
 // (w even) or up (w odd) matrix's 16 columns over slice w/2 of KS equal slices
 // of K. Its 64 lanes are 16 columns x 4 quarters of the slice, so a lane
-// streams STEPS*16 contiguous code bytes of one column; all code loads are
-// issued at once, straight into LDS (buffer loads that write LDS), so the
-// weight stream is in flight while the activation rows are staged. The rows
-// arrive in natural element order and are put into the operand order
-// [0,4,1,5,2,6,3,7] per 8-element chunk while staged. The K loop is a short
-// rolled loop over the lane's 64-wide groups; quarters are summed with two
-// lane exchanges, slices in LDS in a fixed order, and h = silu(gate) * up is
-// written in bf16 in the operand order the down projection reads.
+// streams STEPS*16 contiguous code bytes of one column into registers; every
+// code, scale and bias load is issued at once, so the weight stream is in
+// flight while the activation rows are staged in LDS (put into the operand
+// order [0,4,1,5,2,6,3,7] per 8-element chunk on the way). A tile's expert,
+// rows and their tokens come from one 16-byte descriptor written by the
+// routing, so a workgroup waits on one dependent load before its weight
+// stream starts. Quarters are summed with two lane exchanges, slices in LDS in
+// a fixed order, and h = silu(gate) * up is written in bf16 in the operand
+// order the down projection reads.
 template <int STEPS, int KS>
 struct DecShape {
   static constexpr int K = STEPS * 128 * KS;
@@ -83,66 +84,51 @@ struct DecShape {
   static constexpr int PARTS = 4 * KS;     // lane slices of K
 };
 
-// LDS of one workgroup whose tiles have at most nr rows: codes [W][STEPS][64
-// lanes][16 B], scale and bias pairs [W][GQ][64] u32, activation rows
-// [nr][row bytes], group sums [nr][K/64] f32, source rows [8]. The epilogue
-// reuses the code area.
-struct DecLds {
-  int codes, sb, xs, xt, src, total;
-};
-__host__ __device__ constexpr DecLds dec_lds(int steps, int ks, int nr) {
-  const int K = steps * 128 * ks;
-  const int codes = 0;
-  const int sb = codes + 2 * ks * steps * 1024;
-  const int xs = sb + 2 * ks * (steps / 2) * 64 * 4;
-  const int xt = xs + nr * dec_row_bytes(K, 4 * ks);
-  const int src = xt + nr * (K / kGroup) * 4;
-  return DecLds{codes, sb, xs, xt, src, src + kDecodeMaxRows * 4};
+// LDS of one workgroup whose tiles have at most nr rows: activation rows
+// [nr][row bytes] and their group sums [nr][K/64] f32; the epilogue reuses the
+// row area (at least as large as its [W][nr][16] f32 + [nr][16] bf16).
+__host__ __device__ constexpr int dec_xt_off(int steps, int ks, int nr) {
+  return nr * dec_row_bytes(steps * 128 * ks, 4 * ks);
+}
+__host__ __device__ constexpr int dec_lds_bytes(int steps, int ks, int nr) {
+  return dec_xt_off(steps, ks, nr) + nr * (steps * 128 * ks / kGroup) * 4;
 }
 
+struct DecTile {
+  int e, r0, n;
+  uint32_t tok;   // token of row j at bits 4j..4j+3
+};
+
 template <int NR, int STEPS, int KS>
-__device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const TileInfo& ti, int cb, uint8_t* smem, int nrmax) {
+__device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti, int cb, uint8_t* smem, int nrmax) {
   using S = DecShape<STEPS, KS>;
   constexpr int K = S::K, G = S::G, GQ = S::GQ, PARTS = S::PARTS;
-  const DecLds L = dec_lds(STEPS, KS, nrmax);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, kq = lane >> 4;
   const int up = wave & 1, ks = wave >> 1;
   const int slice = ks * 4 + kq;            // the lane's slice of K
-  uint8_t* codes = smem + L.codes + wave * STEPS * 1024;
-  uint32_t* sb = reinterpret_cast<uint32_t*>(smem + L.sb) + wave * GQ * 64;
-  uint8_t* xs = smem + L.xs;
-  float* Xt = reinterpret_cast<float*>(smem + L.xt);
-  int* srcs = reinterpret_cast<int*>(smem + L.src);
+  uint8_t* xs = smem;
+  float* Xt = reinterpret_cast<float*>(smem + dec_xt_off(STEPS, KS, nrmax));
 
-  // ---- this wave's 16 columns and K slice: code stream into LDS -------------
+  // ---- this lane's codes, scales and biases into registers -----------------
   const int stack = ti.e == a.E ? 1 : 0;
   const int el = stack ? 0 : ti.e;
   const QStack& mat = up ? a.w1[stack] : a.w0[stack];
-  const size_t wrow0 = size_t(el) * a.N + cb * 16;
-  {
-    const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(mat.q + wrow0 * (K / 8)), 0, 0x7FFFFFFF, kDecRsrcWord3);
-    const uint32_t voff = uint32_t((c * (K / 8) + slice * (K / 8 / PARTS)) * 4);
+  const size_t wrow = size_t(el) * a.N + cb * 16 + c;
+  const u32x4* qp = reinterpret_cast<const u32x4*>(mat.q + wrow * (K / 8) + slice * (K / 8 / PARTS));
+  u32x4 w[STEPS];
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (dec_lds_t)(codes + s * 1024), 16, voff, s * 16, 0, 0);
-  }
-  {
-    uint16_t sv[GQ], bv[GQ];
-    load_groups<GQ>(mat.s + (wrow0 + c) * G + slice * GQ, sv);
-    load_groups<GQ>(mat.b + (wrow0 + c) * G + slice * GQ, bv);
-#pragma unroll
-    for (int i = 0; i < GQ; ++i) sb[i * 64 + lane] = uint32_t(sv[i]) | (uint32_t(bv[i]) << 16);
-  }
+  for (int st = 0; st < STEPS; ++st) w[st] = qp[st];
+  uint16_t sv[GQ], bv[GQ];
+  load_groups<GQ>(mat.s + wrow * G + slice * GQ, sv);
+  load_groups<GQ>(mat.b + wrow * G + slice * GQ, bv);
 
   // ---- activation rows (operand order) and their group sums into LDS -------
-  if (tid < NR) srcs[tid] = src_row(a, ti.r0 + tid);
-  __syncthreads();
   for (int i = tid; i < NR * (K / 8); i += S::W * 64) {
     const int r = i / (K / 8), ch = i % (K / 8);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(a.A + size_t(srcs[r]) * K + ch * 8);
+    const int src = int((ti.tok >> (4 * r)) & 15u);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.A + size_t(src) * K + ch * 8);
     *reinterpret_cast<u32x4*>(xs + dec_off(K, r, ch * 8, PARTS)) = permute_chunk(v);
   }
   __syncthreads();
@@ -154,28 +140,26 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const TileInfo& t
       sum += chunk_sum(*reinterpret_cast<const u32x4*>(xs + dec_off(K, r, g * kGroup + ch * 8, PARTS)));
     Xt[r * G + g] = sum;
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's code loads have landed
   __syncthreads();
 
-  // ---- dot products over the lane's slice, one group per iteration ---------
+  // ---- dot products over the lane's slice -----------------------------------
   float acc[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
   const uint32_t nib = kNib, magic = kMagic;
-#pragma unroll 1
+#pragma unroll
   for (int gl = 0; gl < GQ; ++gl) {
     float P[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) P[r] = 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int s = 2 * gl + h;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(codes + s * 1024 + lane * 16);
-      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      const int st = 2 * gl + h;
+      const uint32_t wd[4] = {w[st].x, w[st].y, w[st].z, w[st].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 p = __builtin_bit_cast(u32x4, unpack_word(wd[j], nib, magic));
-        const int k0 = slice * (K / PARTS) + 32 * s + 8 * j;
+        const int k0 = slice * (K / PARTS) + 32 * st + 8 * j;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + dec_off(K, r, k0, PARTS));
@@ -186,9 +170,8 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const TileInfo& t
         }
       }
     }
-    const uint32_t sbv = sb[gl * 64 + lane];
-    const float s16 = 16.0f * __uint_as_float(sbv << 16);
-    const float off = __uint_as_float(sbv & 0xFFFF0000u) - s16;
+    const float s16 = 16.0f * __uint_as_float(uint32_t(sv[gl]) << 16);
+    const float off = __uint_as_float(uint32_t(bv[gl]) << 16) - s16;
     const int g = slice * GQ + gl;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -203,8 +186,8 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const TileInfo& t
   }
 
   // ---- slices summed in order, SwiGLU, bf16 h in operand order -------------
-  __syncthreads();   // every wave is done with its codes (the epilogue reuses them)
-  float* part = reinterpret_cast<float*>(smem + L.codes);                    // [W][NR][16]
+  __syncthreads();   // every wave is done with the rows (the epilogue reuses them)
+  float* part = reinterpret_cast<float*>(smem);                               // [W][NR][16]
   uint16_t* hs = reinterpret_cast<uint16_t*>(part + S::W * NR * 16);          // [NR][16]
   if (lane < 16) {
 #pragma unroll
@@ -232,15 +215,30 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const TileInfo& t
   }
 }
 
+// Tiles: the shared expert's (one, all T rows, tokens 0..T-1), then the routed
+// tiles' descriptors.
 template <int STEPS, int KS>
-__global__ __launch_bounds__(2 * KS * 64) void decode_swiglu_kernel(GemmArgs a, int nrmax) {
+__global__ __launch_bounds__(2 * KS * 64) void decode_swiglu_kernel(GemmArgs a, const u32x4* tile_desc, int nrmax) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tile = blockIdx.x / a.NT;
   const int cb = blockIdx.x % a.NT;
-  if (tile >= a.n_shared_tiles + *a.num_tiles) return;
-  TileInfo ti;
-  if (!tile_info(a, tile, ti)) return;
-  switch (ti.r1 - ti.r0) {
+  DecTile ti;
+  if (tile < a.n_shared_tiles) {
+    ti.e = a.E;
+    ti.r0 = a.routed_rows;
+    ti.n = a.shared_rows;
+    ti.tok = 0x76543210u;
+  } else {
+    const int i = tile - a.n_shared_tiles;
+    const int nt = *a.num_tiles;
+    const u32x4 d = tile_desc[i];   // in bounds for every launched tile; used only if i < nt
+    if (i >= nt) return;
+    ti.e = int(d.x);
+    ti.r0 = int(d.y);
+    ti.n = int(d.z);
+    ti.tok = d.w;
+  }
+  switch (ti.n) {
     case 1: swiglu_tile<1, STEPS, KS>(a, ti, cb, smem, nrmax); break;
     case 2: swiglu_tile<2, STEPS, KS>(a, ti, cb, smem, nrmax); break;
     case 3: swiglu_tile<3, STEPS, KS>(a, ti, cb, smem, nrmax); break;
@@ -379,8 +377,10 @@ bool decode_supported(int N, int K) {
   return (K == 256 || K == 512 || K == 1024 || K == 2048) && N % 16 == 0;
 }
 
-hipError_t launch_decode(const GemmArgs& ga, int max_row_tiles, int max_rows, hipStream_t stream) {
-  if (!decode_supported(ga.N, ga.K) || ga.NT != ga.N / 16 || max_rows < 1 || max_rows > kDecodeMaxRows)
+hipError_t launch_decode(const GemmArgs& ga, const u32x4* tile_desc, int max_row_tiles, int max_rows,
+                         hipStream_t stream) {
+  if (!decode_supported(ga.N, ga.K) || ga.NT != ga.N / 16 || max_rows < 1 || max_rows > kDecodeMaxRows ||
+      ga.n_shared_tiles > 1 || ga.shared_rows > max_rows || !tile_desc)
     return hipErrorInvalidValue;
   const dim3 grid(unsigned(max_row_tiles) * unsigned(ga.NT));
   if (grid.x == 0) return hipSuccess;
@@ -388,20 +388,20 @@ hipError_t launch_decode(const GemmArgs& ga, int max_row_tiles, int max_rows, hi
   // 64 or 128 codes and a workgroup has 2, 4 or 8 waves
   switch (ga.K) {
     case 256:
-      hipLaunchKernelGGL((decode_swiglu_kernel<2, 1>), grid, dim3(128), dec_lds(2, 1, max_rows).total, stream, ga,
-                         max_rows);
+      hipLaunchKernelGGL((decode_swiglu_kernel<2, 1>), grid, dim3(128), dec_lds_bytes(2, 1, max_rows), stream, ga,
+                         tile_desc, max_rows);
       break;
     case 512:
-      hipLaunchKernelGGL((decode_swiglu_kernel<4, 1>), grid, dim3(128), dec_lds(4, 1, max_rows).total, stream, ga,
-                         max_rows);
+      hipLaunchKernelGGL((decode_swiglu_kernel<4, 1>), grid, dim3(128), dec_lds_bytes(4, 1, max_rows), stream, ga,
+                         tile_desc, max_rows);
       break;
     case 1024:
-      hipLaunchKernelGGL((decode_swiglu_kernel<4, 2>), grid, dim3(256), dec_lds(4, 2, max_rows).total, stream, ga,
-                         max_rows);
+      hipLaunchKernelGGL((decode_swiglu_kernel<4, 2>), grid, dim3(256), dec_lds_bytes(4, 2, max_rows), stream, ga,
+                         tile_desc, max_rows);
       break;
     default:
-      hipLaunchKernelGGL((decode_swiglu_kernel<4, 4>), grid, dim3(512), dec_lds(4, 4, max_rows).total, stream, ga,
-                         max_rows);
+      hipLaunchKernelGGL((decode_swiglu_kernel<4, 4>), grid, dim3(512), dec_lds_bytes(4, 4, max_rows), stream, ga,
+                         tile_desc, max_rows);
       break;
   }
   return hipGetLastError();

@@ -25,7 +25,7 @@ struct Carve {
 // Workspace of one layer call. Offsets in bytes from the workspace base.
 struct LayerLayout {
   size_t logits, logit_parts, ids, w, block_counts, block_base, rank, counts, offsets, sorted_rows, row_of_pair,
-      tile_map, num_tiles, x_perm, x_part, h, h_part, Y, total;
+      tile_map, tile_desc, num_tiles, x_perm, x_part, h, h_part, Y, total;
 };
 
 int64_t max_tiles_of(int64_t T, int64_t E, int64_t k, int64_t bm) {
@@ -52,6 +52,7 @@ LayerLayout layer_layout(const moe_dims& d) {
   L.sorted_rows = c.take(T * k * 4);
   L.row_of_pair = c.take(T * k * 4);
   L.tile_map = c.take(size_t(max_tiles_of(d.T, d.E, d.k, bm)) * 8);
+  L.tile_desc = c.take(d.T <= kDecodeMaxRows ? size_t(max_tiles_of(d.T, d.E, d.k, bm)) * 16 : 0);
   L.num_tiles = c.take(4);
   L.x_perm = c.take(T * H * 2);
   L.x_part = c.take(T * size_t(xpart_cols(d.H)) * 2);
@@ -311,6 +312,8 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   ScanArgs sa{ra.block_counts, at<int32_t>(ws, L.block_base), at<int32_t>(ws, L.counts), offsets, tile_map,
               num_tiles, nblk, E, bm};
   ScatterArgs ca{ids, sa.block_base, ra.rank_in_block, sorted_rows, row_of_pair, T, E, k};
+  u32x4* tile_desc = at<u32x4>(ws, L.tile_desc);
+  ra.tile_desc = decode ? tile_desc : nullptr;
   if (launch_route(ra, sa, ca, true, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
 
   // 5. gate/up grouped GEMM with SwiGLU, routed tiles + shared-expert tiles
@@ -342,7 +345,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.NT = decode ? I / 16 : I / 128;
   g1.out = h;
   g1.out_part = h_part;
-  const hipError_t e1 = decode ? launch_decode(g1, n_sh + max_routed, T, s)
+  const hipError_t e1 = decode ? launch_decode(g1, tile_desc, n_sh + max_routed, T, s)
                                : launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s);
   if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 

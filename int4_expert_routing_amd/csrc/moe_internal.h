@@ -32,6 +32,9 @@ struct RouteArgs {
   int32_t* num_tiles;       // [1]
   int32_t* sorted_rows;     // [T*k]
   int32_t* row_of_pair;     // [T*k]
+  // optional (finish only): per tile {expert, first row, rows, token ids of
+  // its rows at 4 bits each}, for tiles of at most 8 rows
+  u32x4* tile_desc;
 };
 
 struct ScanArgs {
@@ -65,11 +68,14 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
 // of a layer call with T <= kDecodeMaxRows tokens).
 constexpr int kDecodeMaxRows = 8;
 // Gate/up projection with SwiGLU: K in {256, 512, 1024, 2048}, N % 16 == 0,
-// ga.NT = N/16 column blocks, ga.A rows in natural element order; h is written
-// in the operand chunk order with no group-sum table. max_rows bounds every
-// tile's row count (1..kDecodeMaxRows).
+// ga.NT = N/16 column blocks, ga.A = the call's T rows in natural element
+// order; h is written in the operand chunk order with no group-sum table. The
+// shared expert is one tile of all T rows; routed tiles are described by the
+// routing's tile_desc. max_rows (>= T) bounds every tile's row count
+// (1..kDecodeMaxRows).
 bool decode_supported(int N, int K);
-hipError_t launch_decode(const GemmArgs& ga, int max_row_tiles, int max_rows, hipStream_t stream);
+hipError_t launch_decode(const GemmArgs& ga, const u32x4* tile_desc, int max_row_tiles, int max_rows,
+                         hipStream_t stream);
 
 // Down projection fused with the weighted combine, for the same few-token
 // calls: y[t] = bf16(sum_j w[t][j] * (h[row_of_pair[t*k+j]] . Wd[e_tj]) +

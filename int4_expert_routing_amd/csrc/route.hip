@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
       if (p < npairs) {
         const int base = hist[e];
         const int before = __popcll(same & below);
-        a.rank_in_block[size_t(t0) * k + p] = base + before;
+        if (!a.finish) a.rank_in_block[size_t(t0) * k + p] = base + before;
         rank_s[p] = base + before;
         if (before == 0) hist[e] = base + __popcll(same);   // every lane of the group has read hist[e]
       }
@@ -314,14 +314,17 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kTopkThreads) a.block_counts[size_t(blk) * E + e] = hist[e];
-  if (!a.finish) return;   // uniform: the scan and scatter kernels follow
+  if (!a.finish) {   // uniform: the scan and scatter kernels follow
+    for (int e = tid; e < E; e += kTopkThreads) a.block_counts[size_t(blk) * E + e] = hist[e];
+    return;
+  }
 
   // One block holds every pair: offsets are the exclusive scan of the
   // histogram, the block map lists ceil(count / block_rows) tiles per expert
   // in expert order, and each pair's row is its expert's offset plus its rank.
   __shared__ int32_t off_s[kMaxExperts];
   __shared__ int32_t scan_tot[2 * kRouteTokens];
+  __shared__ int32_t sorted_s[kRouteTokens * kMaxTopk];
   const int c = tid < E ? hist[tid] : 0;
   const int ntl = ceil_div(c, a.block_rows);
   int32_t oc = c, tc = ntl;   // inclusive scans of counts and tile counts
@@ -346,6 +349,20 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
     const int pos = off_s[ids_s[p]] + rank_s[p];
     a.sorted_rows[pos] = p;
     a.row_of_pair[p] = pos;
+    sorted_s[pos] = p;
+  }
+  if (!a.tile_desc) return;   // uniform
+  __syncthreads();
+  if (tid < E && c > 0) {
+    const int o = off_s[tid];
+    const int first = tc - ntl;
+    for (int i = 0; i < ntl; ++i) {
+      const int r0 = o + i * a.block_rows;
+      const int n = min(a.block_rows, c - i * a.block_rows);
+      uint32_t tok = 0;
+      for (int j = 0; j < n && j < 8; ++j) tok |= uint32_t(sorted_s[r0 + j] / k) << (4 * j);
+      a.tile_desc[first + i] = u32x4{uint32_t(tid), uint32_t(r0), uint32_t(n), tok};
+    }
   }
 }
 
