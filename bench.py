@@ -77,7 +77,7 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
     ys = [torch.empty(T, H, dtype=torch.bfloat16, device=dev) for _ in range(calls)]
     ids = [torch.empty(T, k, dtype=torch.int32, device=dev) for _ in range(calls)]
     dims = _lib.MoeDims(T, H, I, E, k, 0)
-    ws = torch.empty(int(lib.moe_workspace_bytes(ctypes.byref(dims))), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(int(lib.moe_workspace_bytes(ctypes.byref(dims))), dtype=torch.uint8, device=dev)
 
     def call(i):
         w = sets[i % n_sets]

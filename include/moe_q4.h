@@ -187,7 +187,13 @@ size_t moe_gemm_workspace_bytes(int32_t a_rows, int32_t K);
  *   logits_out   device float [T][E] or NULL: the logits routing used (biased)
  *   topk_ids_out device int32 [T][k] or NULL
  *   topk_w_out   device float [T][k] or NULL
- *   workspace    device, at least moe_workspace_bytes(dims) bytes
+ *   workspace    device, at least moe_workspace_bytes(dims) bytes. Its first
+ *                256 bytes hold a completion counter that calls with
+ *                T <= 4 use to run routing as one launch: they must be zero
+ *                before the first layer call (allocate the workspace zeroed)
+ *                and every layer call leaves them zero. moe_route never
+ *                touches them; any other use of the buffer must zero them
+ *                again before it serves a layer call.
  */
 int moe_layer_forward(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
                       const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,

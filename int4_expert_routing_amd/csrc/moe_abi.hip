@@ -24,7 +24,7 @@ struct Carve {
 
 // Workspace of one layer call. Offsets in bytes from the workspace base.
 struct LayerLayout {
-  size_t logits, logit_parts, ids, w, block_counts, block_base, rank, counts, offsets, sorted_rows, row_of_pair,
+  size_t done, logits, logit_parts, ids, w, block_counts, block_base, rank, counts, offsets, sorted_rows, row_of_pair,
       tile_map, tile_desc, num_tiles, x_perm, x_part, h, h_part, Y, total;
 };
 
@@ -40,6 +40,9 @@ LayerLayout layer_layout(const moe_dims& d) {
   const int bm = d.block_rows > 0 ? d.block_rows : kBlockRows;
   Carve c;
   LayerLayout L;
+  // completion counter of the one-launch routing (few tokens): kept at
+  // offset 0 for every T, zero before a call and after it
+  L.done = c.take(T > 0 ? 256 : 0);
   L.logits = c.take(T * E * 4);
   L.logit_parts = c.take(size_t(router_splits(d.T, d.H) > 1 ? kRouterSplits : 0) * T * E * 4);
   L.ids = c.take(T * k * 4);
@@ -314,6 +317,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   ScatterArgs ca{ids, sa.block_base, ra.rank_in_block, sorted_rows, row_of_pair, T, E, k};
   u32x4* tile_desc = at<u32x4>(ws, L.tile_desc);
   ra.tile_desc = decode ? tile_desc : nullptr;
+  ra.done = at<int32_t>(ws, L.done);
   if (launch_route(ra, sa, ca, true, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
 
   // 5. gate/up grouped GEMM with SwiGLU, routed tiles + shared-expert tiles

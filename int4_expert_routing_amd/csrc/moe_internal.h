@@ -14,6 +14,7 @@ struct RouteArgs {
   const uint16_t* wr;       // bf16 [E][H]
   const float* logits_in;   // float [T][E] when logits are given, or [n_parts][T][E] partial sums
   int n_parts;              // number of partial-sum planes in logits_in (1 = plain logits)
+  int coherent;             // read logits_in with device-coherent loads (written by other workgroups)
   float* logit_parts;       // workspace for the router's K-range partials [kRouterSplits][T][E]
   const float* bias;        // float [E] or null
   float* logits_out;        // float [T][E]: router GEMM output (layer path)
@@ -35,6 +36,9 @@ struct RouteArgs {
   // optional (finish only): per tile {expert, first row, rows, token ids of
   // its rows at 4 bits each}, for tiles of at most 8 rows
   u32x4* tile_desc;
+  // optional: a zeroed device counter; with it, routing from x for at most
+  // kRouteTokens tokens runs as one launch (and leaves the counter zero)
+  int32_t* done;
 };
 
 struct ScanArgs {

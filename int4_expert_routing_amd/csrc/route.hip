@@ -176,7 +176,9 @@ __device__ __forceinline__ void block_scan2(int32_t& a, int32_t& b, int32_t* tot
   b += pb;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
+// Top-k, softmax, histogram and ranks of routing block blk (and, for a single
+// block, the tables), run by one 1024-thread workgroup.
+__device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
   __shared__ uint32_t sel_key[kRouteTokens][kMaxTopk];
   __shared__ int32_t sel_e[kRouteTokens][kMaxTopk];
   __shared__ int32_t ids_s[kRouteTokens * kMaxTopk];
@@ -186,7 +188,6 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int blk = blockIdx.x;
   const int t0 = blk * kRouteTokens;
   const int nt = min(kRouteTokens, a.T - t0);
   const int E = a.E, k = a.k;
@@ -204,7 +205,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
       if (e < E) {
         // the logit, or the sum of the router's K-range partials in order
         const size_t f = size_t(t0 + m) * E + e;
-        float v = a.logits_in[f];
+        float v = a.coherent ? __hip_atomic_load(a.logits_in + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : a.logits_in[f];
         if (a.n_parts > 1) {
           float pv[kRouterSplits - 1];
 #pragma unroll
@@ -366,6 +368,95 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) { topk_block(a, blockIdx.x); }
+
+// Few-token routing in one launch (T <= kSmallRouteMaxT, from x). Workgroup j
+// computes the complete logits of experts [8j, 8j+8) for every token: 128
+// threads per expert each take 8-element chunks c, c+128, ... of H, add
+// x_t . W_r[e] over their chunks with v_dot2 (fp32), and the 128 partial sums
+// are reduced in a fixed tree (lane exchanges, then the two waves in order).
+// The logits (+ bias) go to logits_out with device-coherent stores. Each
+// workgroup waits for its stores to complete and counts itself on a
+// device-scope counter; the one that counts last reads every workgroup's
+// logits with device-coherent loads, returns the counter to zero for the next
+// call and runs the top-k, softmax and tables as a single routing block. No
+// cache-wide write-back or invalidate is needed: only the logits cross
+// workgroups, and they bypass the non-coherent cache levels.
+constexpr int kSmallExperts = kTopkThreads / 128;
+constexpr int kSmallRouteMaxT = 4;
+
+// c + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (fp32). The pairs are
+// taken as plain 32-bit values: bit-casting a vector element expression in
+// place reads element 0 with this compiler.
+__device__ __forceinline__ float bf16_dot2(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int TB>   // token bucket: TB >= T tokens are computed, rows past T repeat row T-1 and are not stored
+__global__ __launch_bounds__(kTopkThreads) void route_small_kernel(RouteArgs a, int32_t* done) {
+  __shared__ float red[kTopkThreads / kWave][kRouteTokens];
+  __shared__ int last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ej = tid >> 7, q = tid & 127;
+  const int e = blockIdx.x * kSmallExperts + ej;
+  const int T = a.T, H = a.H;
+  float acc[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+  if (e < a.E) {
+    const uint16_t* wr = a.wr + size_t(e) * H;
+    for (int ch = q; ch < H / 8; ch += 128) {
+      // every load of the chunk is issued before the first product
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(wr + ch * 8);
+      u32x4 xv[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) xv[t] = *reinterpret_cast<const u32x4*>(a.x + size_t(min(t, T - 1)) * H + ch * 8);
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        acc[t] = bf16_dot2(wv.x, xv[t].x, acc[t]);
+        acc[t] = bf16_dot2(wv.y, xv[t].y, acc[t]);
+        acc[t] = bf16_dot2(wv.z, xv[t].z, acc[t]);
+        acc[t] = bf16_dot2(wv.w, xv[t].w, acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    float v = acc[t];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    if (lane == 0) red[wave][t] = v;
+  }
+  __syncthreads();
+  if (tid < kSmallExperts * kRouteTokens) {
+    const int j = tid / kRouteTokens, t = tid % kRouteTokens;
+    const int ee = blockIdx.x * kSmallExperts + j;
+    if (t < T && ee < a.E) {
+      float v = red[2 * j][t] + red[2 * j + 1][t];
+      if (a.bias) v = v + a.bias[ee];
+      // device-coherent store (+ 0 turns -0 into +0)
+      __hip_atomic_store(a.logits_out + size_t(t) * a.E + ee, v + 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // this workgroup's logit stores have completed before it counts itself
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == int(gridDim.x) - 1;
+  __syncthreads();
+  if (!last) return;   // uniform
+  if (tid == 0) __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  RouteArgs b = a;
+  b.logits_in = a.logits_out;
+  b.coherent = 1;   // read the other workgroups' logits with device-coherent loads
+  b.n_parts = 1;
+  b.bias = nullptr;
+  b.logits_out = nullptr;
+  b.finish = 1;
+  topk_block(b, 0);
+}
+
 // Per-expert scan over the routing blocks, 16 experts per workgroup:
 // block_base[b][e] = sum of block_counts[b'][e] over b' < b, and
 // counts[e] = the sum over all blocks. Thread (e, p) sums a contiguous range
@@ -474,6 +565,19 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
   rb.num_tiles = sa.num_tiles;
   rb.sorted_rows = ca.sorted_rows;
   rb.row_of_pair = ca.row_of_pair;
+  if (from_x && ra.T <= kSmallRouteMaxT && ra.done && ra.logits_out && ra.H % 8 == 0) {
+    // one launch: complete logits per expert slice, top-k by the last workgroup
+    // (measured faster than the MFMA router + top-k launches up to 4 tokens;
+    // its per-token cost is higher, so larger calls keep the two launches)
+    const dim3 grid(ceil_div(ra.E, kSmallExperts)), block(kTopkThreads);
+    if (ra.T <= 1)
+      hipLaunchKernelGGL(route_small_kernel<1>, grid, block, 0, stream, rb, ra.done);
+    else if (ra.T <= 2)
+      hipLaunchKernelGGL(route_small_kernel<2>, grid, block, 0, stream, rb, ra.done);
+    else
+      hipLaunchKernelGGL(route_small_kernel<4>, grid, block, 0, stream, rb, ra.done);
+    return hipGetLastError();
+  }
   if (from_x) {
     // logits (biased) into logits_out, or K-range partials into logit_parts
     // that the top-k kernel sums (adding the bias, writing logits_out)

@@ -214,7 +214,7 @@ def moe_layer_forward(x: torch.Tensor, w: MoEWeights, k: int, y: Optional[torch.
     _need(y, torch.bfloat16, "y", dev)
     wsb = int(lib.moe_workspace_bytes(ctypes.byref(d)))
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
     structs = [s.c_struct() for s in (w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)]
     st = lib.moe_layer_forward(_ptr(x), _ptr(w.router_w), _ptr(w.logit_bias),
                                *[ctypes.byref(s) for s in structs], ctypes.byref(d), _ptr(y), _ptr(logits_out),
@@ -232,7 +232,7 @@ class MoELayer:
         self.k = k
         dev = weights.router_w.device
         wsb = workspace_bytes(max_tokens, weights.H, weights.I, weights.E, k)
-        self.workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        self.workspace = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
         self.max_tokens = max_tokens
 
     def __call__(self, x: torch.Tensor, **outs) -> torch.Tensor:

@@ -244,6 +244,32 @@ def test_layer_is_deterministic(dev):
         assert np.array_equal(a[key], b[key]), key
 
 
+def test_layer_workspace_reused_across_token_counts(dev):
+    # Calls with T <= 4 route in one launch that counts finished workgroups in
+    # the workspace's first 256 bytes and leaves them zero; reusing one
+    # workspace across token counts (one-launch, decode and general paths)
+    # must give the same bits as a fresh zeroed workspace, and end zeroed.
+    # E = 12 leaves the last expert slice of the router half empty.
+    print("layer workspace reuse, E=12 k=3, T = 1, 16, 40, 9, 3, 12", flush=True)
+    H, I, E, k = 256, 256, 12, 3
+    ws = torch.zeros(ops.workspace_bytes(40, H, I, E, k), dtype=torch.uint8, device=dev)
+    for i, T in enumerate((1, 16, 40, 9, 3, 12)):
+        inp = make_layer(T, H, I, E, k, seed=100 + i, bias_mode="random")
+        w = ops.MoEWeights.from_host(inp, dev)
+        x = ops.bf16_from_bits(inp.x, dev)
+        logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+        ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+        wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+        y = ops.moe_layer_forward(x, w, k, logits_out=logits, topk_ids_out=ids, topk_w_out=wts, workspace=ws)
+        torch.cuda.synchronize()
+        g = dict(y=om.bf16_bits_to_f64(ops.bits_from_bf16(y)), logits=_np(logits), ids=_np(ids), w=_np(wts))
+        fresh = run_layer(dev, inp)
+        for key in g:
+            assert np.array_equal(g[key], fresh[key]), (T, key)
+        check_layer(inp, g)
+        assert int(ws[:256].count_nonzero()) == 0, T
+
+
 @pytest.mark.parametrize("name", ["decode1", "decode8"])
 def test_layer_full_shape_decode(dev, name):
     print(f"layer {name}", flush=True)
