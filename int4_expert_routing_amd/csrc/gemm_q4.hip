@@ -12,14 +12,16 @@
 // Instead the MFMA operand is the exact value 1 + q/16, whose bf16 bit pattern
 // is 0x3F80 | (q << 3), so a shift and one AND/OR turn two packed codes into
 // two operands. With W = 16s * (1 + q/16) + (b - 16s), for each 64-wide group g
-// of K the MFMA chain of the group accumulates
+// of K the MFMA chain of the group adds
 //     P_g = sum_{k in g} x_k (1 + q_k/16)             (fp32)
-// which the kernel folds as acc += 16 s_g * P_g (one FMA per output per group;
-// 16 s_g is exact). The remaining sum_g (b_g - 16 s_g) X_g, X_g = sum_{k in g}
-// x_k, runs on the MFMA as 8 extra K columns per group: an exact three-part
-// bf16 split of X_g (from a side table) against b_g, again against -16 s_g,
-// and two zero columns, so that each 8-wide operand slice is one group; every
-// second group one such MFMA per row block covers the last two groups.
+// to an accumulator kept in units of U = 16 s_g: before the chain the
+// accumulator is multiplied by U_{g-1} / U_g (one multiply per output per
+// group, and no second accumulator set), and after the K loop by the last U.
+// The remaining sum_g (b_g - 16 s_g) X_g, X_g = sum_{k in g} x_k, runs on the
+// MFMA as 8 extra K columns per group: the group's coefficient in the current
+// unit, split into bf16 parts, against an exact three-part bf16 split of X_g
+// (a side table); every second group one such MFMA per block covers the last
+// two groups.
 //
 // Operand order. One 32-bit word holds codes k..k+7 (nibble i = code k+i); the
 // AND/OR unpack yields the bf16 pairs (k, k+4), (k+1, k+5), (k+2, k+6),
@@ -27,25 +29,26 @@
 // the order [0,4,1,5,2,6,3,7] (prep kernel / SwiGLU epilogue), so both MFMA
 // operands list the same K indices in the same slots.
 //
-// Tiling (one workgroup = 8 wave64s = 512 threads, tile = up to 128 rows):
-//   each wave owns 32 output columns of one weight matrix and all rows of the
-//   tile, as up to four 32-row MFMA blocks; only blocks that hold real rows are
-//   computed (the kernel is instantiated per live-block count), so MFMA work
-//   follows the real row count at 32-row granularity.
-//   SwiGLU: waves 0-3 = gate columns 0-127, waves 4-7 = up columns 0-127 of
-//           the workgroup's 128 (gate and up meet in LDS at the end);
-//   STORE_F32: waves 0-7 = columns 0-255.
+// Tiling (one workgroup = 4 wave64s = 256 threads, tile = up to 128 rows,
+// two workgroups per CU):
+//   each wave owns 64 output columns as two 32-column blocks and all rows of
+//   the tile, as up to four 32-row MFMA blocks, so each activation fragment
+//   read from LDS feeds two MFMAs; only row blocks that hold real rows are
+//   computed (the kernel is instantiated per live-block count).
+//   SwiGLU: wave w = gate columns 32w..32w+31 (block 0) and the same up
+//           columns (block 1) of the workgroup's 128, so gate and up meet in
+//           registers;
+//   STORE_F32: wave w = columns 64w..64w+63 of the workgroup's 256.
 //   MFMA v_mfma_f32_32x32x16_bf16: per 64-wide group a wave issues one chain
-//   of 4 MFMAs per row block; one group's weight codes are unpacked once and
-//   reused by every row block.
+//   of 4 MFMAs per (row block, column block); one group's weight codes are
+//   unpacked once and reused by every row block.
 // Streaming: per group, the activation tile (128 rows x 64 bf16, 16-byte chunks
-//   XOR-swizzled by row), the 256 columns' weight codes and the rows'
-//   side-table entries land in a 3-slot LDS ring through buffer loads that
-//   write LDS directly (no registers, one scalar offset per group), issued two
-//   groups ahead; one s_waitcnt + s_barrier per group. Scales and biases of the
-//   256 columns are staged once per tile. Every vector-memory instruction moves
-//   16 bytes per lane: the per-CU load path, not the MFMA, limits this kernel
-//   when instructions move less.
+//   XOR-swizzled by row) and the 256 columns' weight codes land in a 3-slot
+//   LDS ring through buffer loads that write LDS directly (no registers, one
+//   scalar offset per group), issued two groups ahead; the rows' side-table
+//   entries of each group pair land in a 2-slot ring the same way; scales and
+//   biases of a group pair go to registers with plain loads issued with the
+//   even group's. One s_waitcnt + s_barrier per group.
 // Work mapping: each XCD takes a contiguous chunk of the tile list and runs
 // all column slices of its tiles (see the kernel), so activation rows and
 // expert weights are fetched into one XCD's L2 rather than into all eight.
@@ -53,16 +56,24 @@
 
 namespace moe {
 
-constexpr int kGemmWaves = 8;
+constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = kGemmWaves * 64;
-constexpr int kRing = 4;                 // LDS ring slots: group g lives in slot g % 4
+constexpr int kRing = 3;                 // LDS ring slots: group g lives in slot g % 3
 constexpr int kSlotA = 0;                // 128 rows x 128 B of activations
-constexpr int kSlotB = 16384;            // 8 waves x 64 lanes x 16 B of weight codes
-constexpr int kSlotXP = 24576;           // odd groups: 128 rows x 32 B, side-table entries of groups g-1, g
-constexpr int kSlotBytes = 28672;
+constexpr int kSlotB = 16384;            // 4 waves x 2 column blocks x 64 lanes x 16 B of weight codes
+constexpr int kSlotBytes = 24576;
+constexpr int kXpBase = kRing * kSlotBytes;   // side-table ring: pair p lives in slot p % 2
+constexpr int kXpSlotBytes = 4096;            // 128 rows x 32 B (groups 2p, 2p+1)
+constexpr int kLdsLoop = kXpBase + 2 * kXpSlotBytes;
+// vector-memory instructions a wave issues for one group (the waits count them)
+constexpr int kLoadsEven = 4 + 2 + 4;    // activations, codes, scale and bias pairs of both column blocks
+constexpr int kLoadsOdd = 4 + 2 + 1;     // activations, codes, side-table entries of the pair
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 // s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
+// Scales below this magnitude count as zero (their products are below 2^-96
+// of the activations): the running unit must stay a normal fp32 number.
+constexpr float kMinUnit = 0x1p-96f;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -76,106 +87,122 @@ __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ 
 
 __device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
 
-// Scales and biases of a wave's 32 columns, staged at tile start as
-// [pair j][column][2 groups] (4 bytes per column and group pair), so that the
-// 32 lanes of one column read hit 32 consecutive LDS words.
-__host__ __device__ constexpr int staged_words(int G) { return 32 * (G / 2); }
-
-// LDS of one workgroup: the ring plus the staged scales and biases of the 256
-// columns during the K loop; afterwards, for SwiGLU, the gate tile (128 x 128
-// fp32) and the h tile (128 x 128 bf16).
-size_t gemm_lds_bytes(int K) {
-  const int G = K / kGroup;
-  const size_t loop = size_t(kRing) * kSlotBytes + size_t(2) * kGemmWaves * staged_words(G) * 4;
-  const size_t swiglu = size_t(kBlockRows) * 128 * 4 + size_t(kBlockRows) * 128 * 2;
-  return loop > swiglu ? loop : swiglu;
+// LDS of one workgroup: the two rings during the K loop; afterwards, for
+// SwiGLU, the h tile (128 x 128 bf16).
+size_t gemm_lds_bytes(int /*K*/) {
+  const size_t swiglu = size_t(kBlockRows) * 128 * 2;
+  return size_t(kLdsLoop) > swiglu ? size_t(kLdsLoop) : swiglu;
 }
 
-// Per-wave streaming state: buffer descriptors, per-lane byte offsets.
+// Per-wave streaming state: buffer descriptors, per-lane byte offsets, and the
+// scale/bias pair addresses of the lane's two columns.
 struct Stream {
-  __amdgpu_buffer_rsrc_t ra, rb, rxp;
-  uint32_t va[2];    // activation chunk offsets (2 instructions)
-  uint32_t vb;       // weight-code offset
-  uint32_t vxp;      // side-table offset of (row, half) (waves 0..3, odd groups)
+  __amdgpu_buffer_rsrc_t ra, rb0, rb1, rxp;
+  uint32_t va[4];    // activation chunk offsets (4 instructions)
+  uint32_t vb;       // code offset of the lane (same in both column blocks)
+  uint32_t vxp;      // side-table offset of (row, half)
+  const uint32_t* sp[2];   // scale pairs of the lane's column in blocks 0, 1
+  const uint32_t* bp[2];   // bias pairs
 };
 
-// Loads of group g into its slot: 2 activation + 1 weight-code instruction per
-// wave; for odd g, waves 0..3 also load the side-table entries of groups g-1
-// and g (32 contiguous bytes per row).
+// Scale and bias pairs (groups 2p, 2p+1) of the lane's two columns.
+struct SBPair {
+  uint32_t s[2], b[2];
+};
+
+// Loads of group g: activations and codes into ring slot g % 3; for even g the
+// scale/bias pairs of groups g, g+1 into registers; for odd g the side-table
+// entries of groups g-1, g into side-table slot (g/2) % 2.
 template <int ODD>
-__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* slot, int g, int wave) {
+__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave, SBPair& next) {
+  uint8_t* slot = ring + (g % kRing) * kSlotBytes;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + wave * 2048 + i * 1024), 16, st.va[i],
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + (wave * 4 + i) * 1024), 16, st.va[i],
                                              g * (kGroup * 2), 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb, lds(slot + kSlotB + wave * 1024), 16, st.vb, g * 32, 0, 0);
-  if (ODD && wave < 4)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rxp, lds(slot + kSlotXP + wave * 1024), 16, st.vxp, (g - 1) * 16, 0,
-                                             0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb0, lds(slot + kSlotB + (wave * 2) * 1024), 16, st.vb, g * 32, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb1, lds(slot + kSlotB + (wave * 2 + 1) * 1024), 16, st.vb, g * 32, 0,
+                                           0);
+  if (ODD) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rxp, lds(ring + kXpBase + ((g >> 1) & 1) * kXpSlotBytes + wave * 1024),
+                                             16, st.vxp, (g - 1) * 16, 0, 0);
+  } else {
+    const int p = g >> 1;
+    next.s[0] = st.sp[0][p];
+    next.s[1] = st.sp[1][p];
+    next.b[0] = st.bp[0][p];
+    next.b[1] = st.bp[1][p];
+  }
 }
 
-// Wait until at most N of this wave's buffer loads are outstanding.
+// Wait until at most N of this wave's vector-memory loads are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 16, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(kWaitVm0 | N);
 }
 
-__device__ __forceinline__ void fold(const f32x16& p, float sc, f32x16& acc) {
+__device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(sc, p[r], acc[r]);
+  for (int i = 0; i < 16; ++i) acc[i] *= r;
 }
 
-// Step g of the K loop (S = g % 4, a compile-time slot). Group g is in slot S;
-// groups g+1, g+2 may still be landing; group g+3 is issued into slot
-// (S+3)%4, which held group g-1.
+// Step g of the K loop (P4 = g % 4, a compile-time constant: group parity and
+// pair parity). Group g is in ring slot g % 3; group g+1 may still be landing;
+// group g+2 is issued into the slot that held group g-1.
 //
-// Per live row block rb: a chain of 4 MFMAs over the group's 64 K values
-// gives P_g. The NRB chains are issued level by level (level l = the l-th
-// 16-wide slice of the group), so consecutive MFMAs never depend on each
-// other. Chain rb's P_g is folded as acc += 16 s_g P_g just before the
-// chain's first MFMA of the next step, when the matrix pipe has long
-// finished it. For odd g one more MFMA per block adds the bias term of groups
-// g-1 and g (lanes 0..31: group g-1, 32..63: group g) from the rows' 8
-// side-table entries per group against (b, b, b, -16 s, -16 s, -16 s, 0, 0)
-// of the lane's column.
-template <int NRB, int S>
-__device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, const uint32_t* s_pairs,
-                                          const uint32_t* b_pairs, int g, int G, int wave, int lane, uint32_t& s_pair,
-                                          uint32_t& b_pair, float& sc_prev, f32x16 (&q)[4], f32x16 (&acc)[4]) {
-  constexpr int ODD = S & 1;
+// One accumulator per (row block, column block), kept in units of U = 16 s of
+// the lane's column for the latest group with a nonzero scale: acc holds
+// (result so far) / U. At group g the unit becomes U' = 16 s_g, acc is
+// multiplied by U / U', and the group's chains add P_g straight into it. A
+// group whose scale is 0 keeps the unit and zeroes its column's operand. The
+// chains are issued level by level (level l = the l-th 16-wide slice of the
+// group), so consecutive MFMAs never depend on each other. For odd g one more
+// MFMA per block adds the bias terms of groups g-1 and g (lanes 0..31: group
+// g-1, 32..63: group g) in the current unit: c = (b - 16 s) / U, split into
+// bf16 parts (h, m, l), against the rows' side-table entries
+// (Xh, Xm, Xl, Xh, Xm, Xh, 0, 0) as (h, h, h, m, m, l, 0, 0), i.e. X c up to
+// terms of 2^-24 relative.
+template <int NRB, int P4>
+__device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g, int G, int wave, int lane,
+                                          SBPair (&sb)[2], float (&U)[2], f32x16 (&acc)[4][2]) {
+  constexpr int ODD = P4 & 1;
+  constexpr int PS = P4 >> 1;   // pair (g/2) parity: side-table slot and scale/bias register set
   const int l32 = lane & 31, half = lane >> 5;
-  // this wave's loads of group g have landed once at most those of g+1 and
-  // g+2 are outstanding; the barrier makes it so for every wave, and orders
-  // every wave's reads of slot (S+3)%4 (previous step) before its refill
-  // (a wave issues 3 loads per group, waves 0..3 one more for odd groups)
-  if (g + 2 < G) {
-    if (wave < 4)
-      wait_vm<7>();
+  // this wave's loads of group g have landed once at most those of group g+1
+  // are outstanding; the barrier makes it so for every wave, and orders every
+  // wave's reads of the slot of group g-1 (previous step) before its refill
+  if (g + 1 < G) {
+    if (ODD)
+      wait_vm<kLoadsEven>();
     else
-      wait_vm<6>();
-  } else if (g + 1 < G) {
-    if (!ODD && wave < 4)
-      wait_vm<4>();
-    else
-      wait_vm<3>();
+      wait_vm<kLoadsOdd>();
   } else {
     wait_vm<0>();
   }
   __builtin_amdgcn_s_barrier();
-  if (g + 3 < G) issue_group<!ODD>(st, ring + ((S + 3) % kRing) * kSlotBytes, g + 3, wave);
-  const uint8_t* slot = ring + S * kSlotBytes;
+  if (g + 2 < G) issue_group<ODD>(st, ring, g + 2, wave, sb[PS ^ 1]);
+  const uint8_t* slot = ring + (g % kRing) * kSlotBytes;
 
-  const u32x4 w = *reinterpret_cast<const u32x4*>(slot + kSlotB + wave * 1024 + lane * 16);
-  if (!ODD) {
-    s_pair = s_pairs[(g >> 1) * 32];
-    b_pair = b_pairs[(g >> 1) * 32];
-  }
+  const u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + kSlotB + (wave * 2) * 1024 + lane * 16);
+  const u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + kSlotB + (wave * 2 + 1) * 1024 + lane * 16);
   bf16x8 fa[2][4];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
     fa[0][rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(rb * 32 + l32, 4 * half)));
-  const uint32_t nib = kNib, magic = kMagic;
+  // each column block's unit and the factor that moves acc into it
+  float r[2];
+  uint32_t nib[2], magic[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float sf = 16.0f * __uint_as_float(ODD ? (sb[PS].s[cb] & 0xFFFF0000u) : (sb[PS].s[cb] << 16));
+    const bool nz = __builtin_fabsf(sf) >= kMinUnit;
+    const float Un = nz ? sf : U[cb];
+    r[cb] = U[cb] * __builtin_amdgcn_rcpf(Un);
+    U[cb] = Un;
+    nib[cb] = nz ? kNib : 0u;
+    magic[cb] = nz ? kMagic : 0u;
+  }
 #pragma unroll
   for (int l = 0; l < 4; ++l) {
     if (l + 1 < 4) {
@@ -184,67 +211,71 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, const
         fa[(l + 1) & 1][rb] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(rb * 32 + l32, 4 * half + l + 1)));
     }
-    const bf16x8 bq = unpack_word(w[l], nib, magic);
+    const bf16x8 bq0 = unpack_word(w0[l], nib[0], magic[0]);
+    const bf16x8 bq1 = unpack_word(w1[l], nib[1], magic[1]);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       if (l == 0) {
-        fold(q[rb], sc_prev, acc[rb]);
-        q[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][rb], bq, f32x16{}, 0, 0, 0);
-      } else {
-        q[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[l & 1][rb], bq, q[rb], 0, 0, 0);
+        scale_acc(acc[rb][0], r[0]);
+        scale_acc(acc[rb][1], r[1]);
       }
+      acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[l & 1][rb], bq0, acc[rb][0], 0, 0, 0);
+      acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[l & 1][rb], bq1, acc[rb][1], 0, 0, 0);
     }
   }
-  sc_prev = 16.0f * __uint_as_float(ODD ? (s_pair & 0xFFFF0000u) : (s_pair << 16));
   if (ODD) {
     const int sh = half << 4;
-    const uint32_t sb = (s_pair >> sh) & 0xFFFFu, bb = (b_pair >> sh) & 0xFFFFu;
-    // -16 s is exact in bf16 (a power-of-two multiple), so truncating the
-    // fp32 product is the rounding
-    const uint32_t ns = __float_as_uint(-16.0f * __uint_as_float(sb << 16)) >> 16;
-    const u32x4 pk = {bb | (bb << 16), bb | (ns << 16), ns | (ns << 16), 0u};
-    const bf16x8 bv = __builtin_bit_cast(bf16x8, pk);
+    bf16x8 bv[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float sg = __uint_as_float(((sb[PS].s[cb] >> sh) & 0xFFFFu) << 16);
+      const float bg = __uint_as_float(((sb[PS].b[cb] >> sh) & 0xFFFFu) << 16);
+      const float c = (bg - 16.0f * sg) * __builtin_amdgcn_rcpf(U[cb]);
+      uint16_t ch, cm, cl;
+      split3_bf16(c, ch, cm, cl);
+      const u32x4 pk = {uint32_t(ch) | (uint32_t(ch) << 16), uint32_t(ch) | (uint32_t(cm) << 16),
+                        uint32_t(cm) | (uint32_t(cl) << 16), 0u};
+      bv[cb] = __builtin_bit_cast(bf16x8, pk);
+    }
+    const uint8_t* xps = ring + kXpBase + PS * kXpSlotBytes;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const bf16x8 xa =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + kSlotXP + (rb * 32 + l32) * 32 + half * 16));
-      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv, acc[rb], 0, 0, 0);
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xps + (rb * 32 + l32) * 32 + half * 16));
+      acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv[0], acc[rb][0], 0, 0, 0);
+      acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv[1], acc[rb][1], 0, 0, 0);
     }
   }
 }
 
-// G is even (K is a multiple of 128).
+// G is even (K is a multiple of 128). Groups 0 and 1 were issued by the caller.
 template <int NRB>
-__device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, const uint32_t* s_pairs,
-                                          const uint32_t* b_pairs, int G, int wave, int lane, f32x16 (&acc)[4]) {
-  uint32_t s_pair = 0, b_pair = 0;
-  float sc_prev = 0.0f;
-  f32x16 q[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) q[rb] = f32x16{};
-  // unrolled by the ring size so every slot offset and group parity is a constant
-  for (int g = 0; g < G; g += kRing) {
-    loop_step<NRB, 0>(st, ring, s_pairs, b_pairs, g, G, wave, lane, s_pair, b_pair, sc_prev, q, acc);
-    loop_step<NRB, 1>(st, ring, s_pairs, b_pairs, g + 1, G, wave, lane, s_pair, b_pair, sc_prev, q, acc);
+__device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, int G, int wave, int lane,
+                                          SBPair (&sb)[2], f32x16 (&acc)[4][2]) {
+  float U[2] = {1.0f, 1.0f};   // any normal value: acc is zero until the first nonzero scale
+  // unrolled by 4 so the group parity and the pair parity are constants
+  for (int g = 0; g < G; g += 4) {
+    loop_step<NRB, 0>(st, ring, g, G, wave, lane, sb, U, acc);
+    loop_step<NRB, 1>(st, ring, g + 1, G, wave, lane, sb, U, acc);
     if (g + 2 < G) {
-      loop_step<NRB, 2>(st, ring, s_pairs, b_pairs, g + 2, G, wave, lane, s_pair, b_pair, sc_prev, q, acc);
-      loop_step<NRB, 3>(st, ring, s_pairs, b_pairs, g + 3, G, wave, lane, s_pair, b_pair, sc_prev, q, acc);
+      loop_step<NRB, 2>(st, ring, g + 2, G, wave, lane, sb, U, acc);
+      loop_step<NRB, 3>(st, ring, g + 3, G, wave, lane, sb, U, acc);
     }
   }
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) fold(q[rb], sc_prev, acc[rb]);
+  for (int rb = 0; rb < NRB; ++rb) {
+    scale_acc(acc[rb][0], U[0]);
+    scale_acc(acc[rb][1], U[1]);
+  }
 }
 
 template <int EPI>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_q4_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K;
   const int G = K / kGroup;
   const int KPx = xpart_cols(K);
   uint8_t* ring = smem;
-  const int SW = staged_words(G);
-  uint32_t* s_st = reinterpret_cast<uint32_t*>(smem + kRing * kSlotBytes);   // [8 waves][SW]
-  uint32_t* b_st = s_st + kGemmWaves * SW;                                    // [8 waves][SW]
 
   // XCD-aware work mapping: workgroups are dispatched round-robin over the 8
   // XCDs (blockIdx % 8). The tile list (shared tiles, then routed tiles in
@@ -272,150 +303,138 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_q4_kernel(GemmArgs a) {
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // ---- this wave's weight matrix and its 32 columns ------------------------
-  // A wave past the last column (N not a multiple of the workgroup's width)
+  // ---- this wave's two 32-column blocks -------------------------------------
+  // A block past the last column (N not a multiple of the workgroup's width)
   // streams the last 32 columns again and stores nothing.
-  int col0;
-  const QStack* mat;
+  int cbase[2];
+  const QStack* mat[2];
   if constexpr (EPI == kEpiF32) {
-    col0 = nt * 256 + wave * 32;
-    mat = &a.w0[stack];
+    cbase[0] = nt * 256 + wave * 64;
+    cbase[1] = cbase[0] + 32;
+    mat[0] = mat[1] = &a.w0[stack];
   } else {
-    col0 = nt * 128 + (wave & 3) * 32;
-    mat = (wave >> 2) ? &a.w1[stack] : &a.w0[stack];
+    cbase[0] = cbase[1] = nt * 128 + wave * 32;
+    mat[0] = &a.w0[stack];
+    mat[1] = &a.w1[stack];
   }
-  const bool live = col0 < a.N;
-  col0 = live ? col0 : a.N - 32;
-  const size_t wrow0 = size_t(el) * a.N + col0;
-  const uint32_t* q_wave = mat->q + wrow0 * size_t(K / 8);
-  const uint16_t* s_glob = mat->s + wrow0 * size_t(G);     // 32 contiguous rows of G scales
-  const uint16_t* b_glob = mat->b + wrow0 * size_t(G);
-  const int ncol = col0 + l32;
+  bool live[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    live[cb] = cbase[cb] < a.N;
+    cbase[cb] = live[cb] ? cbase[cb] : a.N - 32;
+  }
 
   // ---- streaming descriptors and per-lane offsets -------------------------
   Stream st;
   st.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.A), 0, 0x7FFFFFFF, kRsrcWord3);
-  st.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q_wave), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rxp = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Apart), 0, 0x7FFFFFFF, kRsrcWord3);
   {
-    // activation load i of wave w fills chunk positions w*128 + i*64 + lane:
-    // row m = w*16 + i*8 + lane/8 and chunk slot lane%8, which holds logical
+    const uint32_t* q0 = mat[0]->q + (size_t(el) * a.N + cbase[0]) * size_t(K / 8);
+    const uint32_t* q1 = mat[1]->q + (size_t(el) * a.N + cbase[1]) * size_t(K / 8);
+    st.rb0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q0), 0, 0x7FFFFFFF, kRsrcWord3);
+    st.rb1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q1), 0, 0x7FFFFFFF, kRsrcWord3);
+    // lane (column l32, half): words 4*half..4*half+3 of the group's 8
+    st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
+  }
+  {
+    // activation load i of wave w fills chunk positions (4w + i)*64 + lane:
+    // row m = (4w + i)*8 + lane/8 and chunk slot lane%8, which holds logical
     // chunk (lane%8) ^ swz(m)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = wave * 16 + i * 8 + (lane >> 3);
+    for (int i = 0; i < 4; ++i) {
+      const int m = (wave * 4 + i) * 8 + (lane >> 3);
       const int cidx = (lane & 7) ^ swz(m);
       const int r = ti.r0 + min(m, nrows - 1);     // padding rows re-read the last real row
       st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
     }
-    st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
-    // side-table load of wave w (0..3): row w*32 + lane/2, 16-byte half lane%2
-    const int mx = (wave & 3) * 32 + (lane >> 1);
+    // side-table load of wave w: row w*32 + lane/2, 16-byte half lane%2
+    const int mx = wave * 32 + (lane >> 1);
     st.vxp = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KPx * 2) + uint32_t((lane & 1) * 16);
   }
-
-  // ---- prologue: scales and biases of the wave's 32 columns, groups 0..2 ----
-  {
-    // word p = j*32 + c of the wave's staging area holds column c's values of
-    // groups 2j, 2j+1, i.e. 4 bytes at (c*G + 2j)*2 of the column block
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s_glob), 0, 0x7FFFFFFF, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rbias =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b_glob), 0, 0x7FFFFFFF, kRsrcWord3);
-    for (int p0 = 0; p0 < SW; p0 += 64) {
-      const int p = p0 + lane;
-      if (p < SW) {
-        const uint32_t off = uint32_t(((p & 31) * G + 2 * (p >> 5)) * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(s_st + wave * SW + p0), 4, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, lds(b_st + wave * SW + p0), 4, off, 0, 0, 0);
-      }
-    }
-  }
-  issue_group<0>(st, ring, 0, wave);
-  issue_group<1>(st, ring + kSlotBytes, 1, wave);
-  if (G > 2) issue_group<0>(st, ring + 2 * kSlotBytes, 2, wave);
-
-  f32x16 acc[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x16{};
-  const uint32_t* s_pairs = s_st + wave * SW + l32;
-  const uint32_t* b_pairs = b_st + wave * SW + l32;
-  switch (nrb) {
-    case 1: main_loop<1>(st, ring, s_pairs, b_pairs, G, wave, lane, acc); break;
-    case 2: main_loop<2>(st, ring, s_pairs, b_pairs, G, wave, lane, acc); break;
-    case 3: main_loop<3>(st, ring, s_pairs, b_pairs, G, wave, lane, acc); break;
-    default: main_loop<4>(st, ring, s_pairs, b_pairs, G, wave, lane, acc); break;
+  for (int cb = 0; cb < 2; ++cb) {
+    // the lane's column's G scales (biases) as G/2 pairs of groups
+    const size_t wrow = size_t(el) * a.N + cbase[cb] + l32;
+    st.sp[cb] = reinterpret_cast<const uint32_t*>(mat[cb]->s + wrow * size_t(G));
+    st.bp[cb] = reinterpret_cast<const uint32_t*>(mat[cb]->b + wrow * size_t(G));
   }
-  __syncthreads();   // every wave is done with the ring
+
+  SBPair sb[2];
+  issue_group<0>(st, ring, 0, wave, sb[0]);
+  issue_group<1>(st, ring, 1, wave, sb[1]);   // G >= 2
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
+  switch (nrb) {
+    case 1: main_loop<1>(st, ring, G, wave, lane, sb, acc); break;
+    case 2: main_loop<2>(st, ring, G, wave, lane, sb, acc); break;
+    case 3: main_loop<3>(st, ring, G, wave, lane, sb, acc); break;
+    default: main_loop<4>(st, ring, G, wave, lane, sb, acc); break;
+  }
+  __syncthreads();   // every wave is done with the rings
 
   // ---- epilogues ------------------------------------------------------------
   if constexpr (EPI == kEpiF32) {
     float* out = reinterpret_cast<float*>(a.out);
 #pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (live[cb] && m < nrows) out[size_t(ti.r0 + m) * a.N + cbase[cb] + l32] = acc[rb][cb][r];
+        }
+  } else {
+    uint16_t* hs = reinterpret_cast<uint16_t*>(ring);   // [128][128] bf16
+    const int col = wave * 32 + l32;
+#pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (live && m < nrows) out[size_t(ti.r0 + m) * a.N + ncol] = acc[rb][r];
+        const float gv = acc[rb][0][r];
+        const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[rb][1][r];
+        hs[m * 128 + col] = uint16_t(f32_to_bf16_rne(hv));
       }
-  } else {
-    float* gate_s = reinterpret_cast<float*>(ring);                           // [128][128] fp32
-    uint16_t* hs = reinterpret_cast<uint16_t*>(ring + kBlockRows * 128 * 4);  // [128][128] bf16
-    const int col = (wave & 3) * 32 + l32;
-    if (wave < 4) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          gate_s[m * 128 + col] = acc[rb][r];
-        }
-    }
     __syncthreads();
-    if (wave >= 4) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float gv = gate_s[m * 128 + col];
-          const float uv = acc[rb][r];
-          const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-          hs[m * 128 + col] = uint16_t(f32_to_bf16_rne(hv));
-        }
-    }
-    __syncthreads();
-    // thread t: row t/4, quarter t%4 = 32 columns; quarters (0,1) and (2,3)
-    // are the two 64-wide groups of h this workgroup produced
+    // unit u: row u/4, quarter u%4 = 32 columns; quarters (0,1) and (2,3) are
+    // the two 64-wide groups of h this workgroup produced (units u and u^1 are
+    // in adjacent lanes)
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-    const int srow = tid >> 2, sq = tid & 3;
-    const int row = ti.r0 + srow;
-    u32x4 ch[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ch[i] = *reinterpret_cast<const u32x4*>(hs + srow * 128 + sq * 32 + 8 * i);
-    if constexpr (EPI == kEpiSwigluInternal) {
-      double part = 0.0;
+    for (int it = 0; it < 2; ++it) {
+      const int u = tid + it * kGemmThreads;
+      const int srow = u >> 2, sq = u & 3;
+      const int row = ti.r0 + srow;
+      u32x4 ch[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part += chunk_sum_f64(ch[i]);
-      const float X = float(part + __shfl_xor(part, 1, kWave));
-      if (srow < nrows) {
-        uint16_t* dst = out + size_t(row) * a.N + nt * 128 + sq * 32;
+      for (int i = 0; i < 4; ++i) ch[i] = *reinterpret_cast<const u32x4*>(hs + srow * 128 + sq * 32 + 8 * i);
+      if constexpr (EPI == kEpiSwigluInternal) {
+        double part = 0.0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = permute_chunk(ch[i]);
-        if ((sq & 1) == 0) {
-          const int go = 2 * nt + (sq >> 1);   // group of h this pair of quarters covers
-          uint16_t h, m, l;
-          split3_bf16(X, h, m, l);
-          const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
-                           uint32_t(m) | (uint32_t(l) << 16), 0u};
-          *reinterpret_cast<u32x4*>(a.out_part + size_t(row) * xpart_cols(a.N) + 8 * go) = e;
+        for (int i = 0; i < 4; ++i) part += chunk_sum_f64(ch[i]);
+        const float X = float(part + __shfl_xor(part, 1, kWave));
+        if (srow < nrows) {
+          uint16_t* dst = out + size_t(row) * a.N + nt * 128 + sq * 32;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = permute_chunk(ch[i]);
+          if ((sq & 1) == 0) {
+            const int go = 2 * nt + (sq >> 1);   // group of h this pair of quarters covers
+            uint16_t h, m, l;
+            split3_bf16(X, h, m, l);
+            const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
+                             uint32_t(m) | (uint32_t(h) << 16), 0u};
+            *reinterpret_cast<u32x4*>(a.out_part + size_t(row) * xpart_cols(a.N) + 8 * go) = e;
+          }
         }
-      }
-    } else {
-      if (srow < nrows && nt * 128 + sq * 32 < a.N) {
-        uint16_t* dst = out + size_t(row) * a.N + nt * 128 + sq * 32;
+      } else {
+        if (srow < nrows && nt * 128 + sq * 32 < a.N) {
+          uint16_t* dst = out + size_t(row) * a.N + nt * 128 + sq * 32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = ch[i];
+          for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = ch[i];
+        }
       }
     }
   }

@@ -115,9 +115,11 @@ __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / 
 
 // Per activation row the GEMM needs each 64-wide group's sum X_g, split
 // exactly into three bf16 parts (hi, mid, lo). The side table stores 8 bf16 per
-// group, [hi, mid, lo, hi, mid, lo, 0, 0], so that one 8-element MFMA operand
-// slice covers exactly one group: the bias correction pairs the first three
-// with b_g and the next three with -16 s_g. xpart_cols(K) = 8 * K/64.
+// group, [hi, mid, lo, hi, mid, hi, 0, 0], so that one 8-element MFMA operand
+// slice covers exactly one group: the bias correction pairs it with the parts
+// (h, m, l) of the group's coefficient as (h, h, h, m, m, l, 0, 0), which
+// gives X_g times the coefficient up to terms of 2^-24 relative.
+// xpart_cols(K) = 8 * K/64.
 __host__ __device__ constexpr int xpart_cols(int K) { return 8 * (K / kGroup); }
 
 }  // namespace moe

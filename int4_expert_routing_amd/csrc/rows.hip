@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* A, int r
     uint16_t h, m, l;
     split3_bf16(float(s), h, m, l);
     const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
-                     uint32_t(m) | (uint32_t(l) << 16), 0u};
+                     uint32_t(m) | (uint32_t(h) << 16), 0u};
     *reinterpret_cast<u32x4*>(xp + 8 * g) = e;
   }
 }
