@@ -87,11 +87,16 @@ __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ 
 
 __device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
 
-// LDS of one workgroup: the two rings during the K loop; afterwards, for
-// SwiGLU, the h tile (128 x 128 bf16).
+// LDS of one workgroup: the two rings during the K loop; afterwards the h
+// tile (SwiGLU: 128 x 128 bf16) or each wave's 128 x 32 fp32 staging block
+// (STORE_F32, row stride 36 floats).
+constexpr int kF32StageStride = 36;
 size_t gemm_lds_bytes(int /*K*/) {
   const size_t swiglu = size_t(kBlockRows) * 128 * 2;
-  return size_t(kLdsLoop) > swiglu ? size_t(kLdsLoop) : swiglu;
+  const size_t f32 = size_t(kGemmWaves) * kBlockRows * kF32StageStride * 4;
+  size_t m = size_t(kLdsLoop);
+  m = m > swiglu ? m : swiglu;
+  return m > f32 ? m : f32;
 }
 
 // Per-wave streaming state: buffer descriptors, per-lane byte offsets, and the
@@ -376,16 +381,30 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
 
   // ---- epilogues ------------------------------------------------------------
   if constexpr (EPI == kEpiF32) {
+    // each wave stages one 128 x 32 column block at a time in its own LDS area
+    // (row stride 36 floats) and writes whole 128-byte row segments
     float* out = reinterpret_cast<float*>(a.out);
+    float* stg = reinterpret_cast<float*>(ring) + wave * (kBlockRows * kF32StageStride);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (live[cb] && m < nrows) out[size_t(ti.r0 + m) * a.N + cbase[cb] + l32] = acc[rb][cb][r];
+          stg[m * kF32StageStride + l32] = acc[rb][cb][r];
         }
+      __builtin_amdgcn_wave_barrier();
+      if (live[cb]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = i * 8 + (lane >> 3), c4 = (lane & 7) * 4;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(stg + m * kF32StageStride + c4);
+          if (m < nrows) *reinterpret_cast<f32x4*>(out + size_t(ti.r0 + m) * a.N + cbase[cb] + c4) = v;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
   } else {
     uint16_t* hs = reinterpret_cast<uint16_t*>(ring);   // [128][128] bf16
     const int col = wave * 32 + l32;
