@@ -140,6 +140,40 @@ def test_gemm_f32_matches_oracle(dev, bias_mode):
     assert max_abs_frac(got, want) < 1e-4
 
 
+def test_gemm_f32_zero_and_spread_scales(dev):
+    # Scales that are exactly 0 (a group, a column's first group, every group of
+    # a column) and scales spread over 2^-12..2^12 inside one column: the
+    # accumulator's unit must skip the zeros and follow the spread exactly
+    # enough; the bias terms of zero-scale groups still count.
+    T, E, k, N, K = 300, 8, 2, 256, 512
+    inp = make_layer(T, K, N, E, k, seed=17, bias_mode="random")
+    s = om.bf16_bits_to_f64(inp.gate.s).copy()
+    G = K // 64
+    rng = np.random.default_rng(3)
+    s[:, 0:8, 0] = 0.0                      # first group of columns 0..7
+    s[:, 8:16, :] = 0.0                     # every group of columns 8..15
+    s[:, 16:64, 3] = 0.0                    # one middle group
+    spread = 2.0 ** rng.integers(-12, 13, size=(E, 64, G))
+    s[:, 64:128, :] *= spread               # power-of-two spread (exact in bf16)
+    gate = Q4Weights(inp.gate.q, om.f64_to_bf16_bits(s), inp.gate.b)
+    A = ops.bf16_from_bits(inp.x, dev)
+    W = ops.Q4Stack.from_host(gate, dev)
+    r = _route_for(dev, T, E, k, 19)
+    out = ops.moe_grouped_gemm_q4(A, W, r["offsets"], r["tile_map"], r["num_tiles"], ops.MOE_EPI_STORE_F32,
+                                  T * k, sorted_rows=r["sorted_rows"], row_div=k)
+    torch.cuda.synchronize()
+    got = _np(out).astype(np.float64)
+    srt = _np(r["sorted_rows"])
+    offs = _np(r["offsets"])
+    x = om.bf16_bits_to_f64(inp.x)
+    want = np.zeros((T * k, N))
+    for e in range(E):
+        rows = np.arange(offs[e], offs[e + 1])
+        want[rows] = x[srt[rows] // k] @ om.expert_weights(gate, e).T
+    for lo, hi in ((0, 16), (16, 64), (64, 128), (128, N)):
+        assert rel_l2(got[:, lo:hi], want[:, lo:hi]) < 1e-5, (lo, hi, rel_l2(got[:, lo:hi], want[:, lo:hi]))
+
+
 def test_gemm_swiglu_matches_oracle(dev):
     T, E, k, I, H = 200, 8, 2, 128, 512
     inp = make_layer(T, H, I, E, k, seed=11, bias_mode="random")
