@@ -197,29 +197,48 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
 
   const int m = wave;                                            // this wave's token
   if (m < nt) {
+    // every load of the token's logits (or of their K-range partials) is
+    // issued before the first use, so the wave waits for one round trip;
+    // experts past E read the last expert's entry and get key 0
+    float v[kMaxKeysPerLane];
+    size_t f[kMaxKeysPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) f[i] = size_t(t0 + m) * E + min(lane + 64 * i, E - 1);
+    if (a.n_parts == kRouterSplits) {
+      float pv[kMaxKeysPerLane][kRouterSplits];
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i)
+#pragma unroll
+        for (int p = 0; p < kRouterSplits; ++p) pv[i][p] = a.logits_in[size_t(p) * a.T * E + f[i]];
+      // the partials are added in plane order
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i) {
+        v[i] = pv[i][0];
+#pragma unroll
+        for (int p = 1; p < kRouterSplits; ++p) v[i] += pv[i][p];
+      }
+    } else if (a.coherent) {
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i)
+        v[i] = __hip_atomic_load(a.logits_in + f[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i) {
+        v[i] = a.logits_in[f[i]];
+        for (int p = 1; p < a.n_parts; ++p) v[i] += a.logits_in[size_t(p) * a.T * E + f[i]];
+      }
+    }
     uint32_t u[kMaxKeysPerLane];
 #pragma unroll
     for (int i = 0; i < kMaxKeysPerLane; ++i) {
       const int e = lane + 64 * i;
       uint32_t key = 0u;
       if (e < E) {
-        // the logit, or the sum of the router's K-range partials in order
-        const size_t f = size_t(t0 + m) * E + e;
-        float v = a.coherent ? __hip_atomic_load(a.logits_in + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                             : a.logits_in[f];
-        if (a.n_parts > 1) {
-          float pv[kRouterSplits - 1];
-#pragma unroll
-          for (int p = 1; p < kRouterSplits; ++p)
-            pv[p - 1] = p < a.n_parts ? a.logits_in[size_t(p) * a.T * E + f] : 0.0f;
-#pragma unroll
-          for (int p = 1; p < kRouterSplits; ++p)
-            if (p < a.n_parts) v += pv[p - 1];
-        }
-        if (a.bias) v = v + a.bias[e];
-        v = v + 0.0f;                                            // turns -0 into +0
-        if (a.logits_out) a.logits_out[f] = v;
-        key = float_order_key(v);
+        float x = v[i];
+        if (a.bias) x = x + a.bias[e];
+        x = x + 0.0f;                                            // turns -0 into +0
+        if (a.logits_out) a.logits_out[f[i]] = x;
+        key = float_order_key(x);
       }
       u[i] = key;
     }
@@ -258,6 +277,7 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
     if (lane < k) {
       my_key = sel_key[m][lane];
       my_e = sel_e[m][lane];
+#pragma unroll 8
       for (int q = 0; q < k; ++q) {
         const uint32_t kq = sel_key[m][q];
         const int eq = sel_e[m][q];
@@ -277,9 +297,9 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
     }
     const float l0 = float_from_order_key(sel_key[m][0]);
     const float ex = lane < k ? expf(my_l - l0) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) sum += __shfl_xor(sum, msk, kWave);
+    // the k terms added in rank order (lane reads, no cross-lane shuffles)
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
     if (lane < k) {
       const size_t f = size_t(t0 + m) * k + lane;
       a.topk_ids[f] = my_e;
