@@ -125,11 +125,23 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti
   load_groups<GQ>(mat.b + wrow * G + slice * GQ, bv);
 
   // ---- activation rows (operand order) and their group sums into LDS -------
-  for (int i = tid; i < NR * (K / 8); i += S::W * 64) {
+  // every chunk load of the rows is issued before the first store
+  constexpr int kChunks = NR * (K / 8), kPer = (kChunks + S::W * 64 - 1) / (S::W * 64);
+  u32x4 xv[kPer];
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int i = min(tid + it * S::W * 64, kChunks - 1);
     const int r = i / (K / 8), ch = i % (K / 8);
     const int src = int((ti.tok >> (4 * r)) & 15u);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(a.A + size_t(src) * K + ch * 8);
-    *reinterpret_cast<u32x4*>(xs + dec_off(K, r, ch * 8, PARTS)) = permute_chunk(v);
+    xv[it] = *reinterpret_cast<const u32x4*>(a.A + size_t(src) * K + ch * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int i = tid + it * S::W * 64;
+    if (i < kChunks) {
+      const int r = i / (K / 8), ch = i % (K / 8);
+      *reinterpret_cast<u32x4*>(xs + dec_off(K, r, ch * 8, PARTS)) = permute_chunk(xv[it]);
+    }
   }
   __syncthreads();
   for (int i = tid; i < NR * G; i += S::W * 64) {
@@ -215,8 +227,8 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti
   }
 }
 
-// Tiles: the shared expert's (one, all T rows, tokens 0..T-1), then the routed
-// tiles' descriptors.
+// Tiles: the shared expert's (one per token: tile t is row routed_rows + t,
+// token t), then the routed tiles' descriptors.
 template <int STEPS, int KS>
 __global__ __launch_bounds__(2 * KS * 64) void decode_swiglu_kernel(GemmArgs a, const u32x4* tile_desc, int nrmax) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -225,9 +237,9 @@ __global__ __launch_bounds__(2 * KS * 64) void decode_swiglu_kernel(GemmArgs a, 
   DecTile ti;
   if (tile < a.n_shared_tiles) {
     ti.e = a.E;
-    ti.r0 = a.routed_rows;
-    ti.n = a.shared_rows;
-    ti.tok = 0x76543210u;
+    ti.r0 = a.routed_rows + tile;
+    ti.n = 1;
+    ti.tok = uint32_t(tile);
   } else {
     const int i = tile - a.n_shared_tiles;
     const int nt = *a.num_tiles;
@@ -380,7 +392,7 @@ bool decode_supported(int N, int K) {
 hipError_t launch_decode(const GemmArgs& ga, const u32x4* tile_desc, int max_row_tiles, int max_rows,
                          hipStream_t stream) {
   if (!decode_supported(ga.N, ga.K) || ga.NT != ga.N / 16 || max_rows < 1 || max_rows > kDecodeMaxRows ||
-      ga.n_shared_tiles > 1 || ga.shared_rows > max_rows || !tile_desc)
+      ga.n_shared_tiles != ga.shared_rows || ga.shared_rows > max_rows || !tile_desc)
     return hipErrorInvalidValue;
   const dim3 grid(unsigned(max_row_tiles) * unsigned(ga.NT));
   if (grid.x == 0) return hipSuccess;

@@ -341,7 +341,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.offsets = offsets;
   g1.tile_map = tile_map;
   g1.num_tiles = num_tiles;
-  g1.n_shared_tiles = n_sh;
+  g1.n_shared_tiles = decode ? T : n_sh;   // decode: one shared-expert tile per token
   g1.shared_rows = T;
   g1.N = I;
   g1.K = H;
@@ -349,7 +349,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.NT = decode ? I / 16 : I / 128;
   g1.out = h;
   g1.out_part = h_part;
-  const hipError_t e1 = decode ? launch_decode(g1, tile_desc, n_sh + max_routed, T, s)
+  const hipError_t e1 = decode ? launch_decode(g1, tile_desc, T + max_routed, T, s)
                                : launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s);
   if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
