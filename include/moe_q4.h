@@ -224,6 +224,32 @@ int moe_layer_forward_timed(const uint16_t* x, const uint16_t* router_w, const f
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const* events, int32_t n_events);
 
+/*
+ * moe_quantize_q4 - quantise bf16 weights into the layout the other entry
+ * points read: for each row and each 64 consecutive elements along K, a bf16
+ * scale s and bias b and 16-level codes q with W = s*q + b. The pages give the
+ * format ("Perplexity Open Sources Lily ..." Technical Details, prefill bullet:
+ * groupwise affine 4-bit, 64 weights per group; 技术解析: a bf16 scale per 64
+ * weights) but not the quantiser; this one is min-max affine, each step in
+ * fp32 (IEEE division, round half to even):
+ *   lo = min, hi = max of the group (-0 taken as +0);
+ *   s = bf16(fp32(hi - lo) / 15);  b = lo;
+ *   q = 0 if s == 0, else min(15, max(0, rint((w - b) / s))).
+ * Every weight is then reproduced within s/2, plus at most 15 * 2^-9 * s at
+ * the top of a group from the bf16 rounding of s.
+ *
+ *   w      device bf16 [rows][K], 16-byte aligned, finite values
+ *   rows   number of rows (for an expert stack: n_experts * N); 0 is a no-op
+ *   K      multiple of 64
+ *   q      device uint32 [rows][K/8], 16-byte aligned; element 8j+i of a row in
+ *          bits 4i..4i+3 of word j
+ *   s, b   device bf16 bit patterns [rows][K/64], 2-byte aligned
+ * Returns MOE_OK, MOE_ERR_SHAPE (rows < 0, K not a positive multiple of 64,
+ * rows*K above 2^40), MOE_ERR_NULL, MOE_ERR_ALIGN or MOE_ERR_HIP.
+ */
+int moe_quantize_q4(const uint16_t* w, int64_t rows, int32_t K, uint32_t* q, uint16_t* s, uint16_t* b,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,7 @@ SIGNATURES = {
     "moe_layer_forward": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_forward_timed": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ,
                                                _P, ctypes.POINTER(ctypes.c_void_p), _I32]),
+    "moe_quantize_q4": (ctypes.c_int, [_P, ctypes.c_int64, _I32, _P, _P, _P, _P]),
 }
 
 MOE_LAYER_STAGE_EVENTS = 6

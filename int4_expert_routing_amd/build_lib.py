@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libmoe_q4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["route.hip", "gemm_q4.hip", "rows.hip", "decode_q4.hip", "moe_abi.hip"]
+SOURCES = ["route.hip", "gemm_q4.hip", "rows.hip", "decode_q4.hip", "quant_q4.hip", "moe_abi.hip"]
 ARCH = "gfx950"
 
 

@@ -405,4 +405,17 @@ int moe_layer_forward_timed(const uint16_t* x, const uint16_t* router_w, const f
                             topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, events, n_events);
 }
 
+int moe_quantize_q4(const uint16_t* w, int64_t rows, int32_t K, uint32_t* q, uint16_t* s, uint16_t* b,
+                    void* stream) {
+  if (rows < 0 || K <= 0 || K % kGroup != 0) return MOE_ERR_SHAPE;
+  // thread indexes (rows * K/64 groups x 8 lanes) stay within a 32-bit grid of 256-thread blocks
+  if (rows > (int64_t(1) << 40) / K) return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!w || !q || !s || !b) return MOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || (reinterpret_cast<uintptr_t>(s) & 1u) || (reinterpret_cast<uintptr_t>(b) & 1u))
+    return MOE_ERR_ALIGN;
+  return launch_quantize(w, long(rows), K, q, s, b, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK
+                                                                                                   : MOE_ERR_HIP;
+}
+
 }  // extern "C"

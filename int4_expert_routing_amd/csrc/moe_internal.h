@@ -97,6 +97,11 @@ struct DownCombineArgs {
 bool decode_down_combine_supported(int N, int K);
 hipError_t launch_decode_down_combine(const DownCombineArgs& da, hipStream_t stream);
 
+// Min-max affine 4-bit quantiser: bf16 [rows][K] -> codes [rows][K/8],
+// bf16 scale and bias [rows][K/64].
+hipError_t launch_quantize(const uint16_t* w, long rows, int K, uint32_t* q, uint16_t* s, uint16_t* b,
+                           hipStream_t stream);
+
 hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
                             hipStream_t stream);
 

@@ -154,6 +154,23 @@ def moe_grouped_gemm_q4(A: torch.Tensor, W0: Q4Stack, offsets: torch.Tensor, til
     return out
 
 
+def quantize_q4(w: torch.Tensor, out: Optional["Q4Stack"] = None) -> "Q4Stack":
+    """bf16 weights [n][N][K] (a stack of n matrices, K a multiple of 64) -> the
+    4-bit groupwise-affine stack the GEMMs read (min-max affine per 64 elements)."""
+    _need(w, torch.bfloat16, "w")
+    if w.dim() != 3 or w.shape[2] % 64:
+        raise ValueError("w must be [n][N][K] with K a multiple of 64")
+    n, N, K = w.shape
+    dev = w.device
+    if out is None:
+        out = Q4Stack(torch.empty(n, N, K // 8, dtype=torch.int32, device=dev),
+                      torch.empty(n, N, K // 64, dtype=torch.bfloat16, device=dev),
+                      torch.empty(n, N, K // 64, dtype=torch.bfloat16, device=dev))
+    st = _lib.load().moe_quantize_q4(_ptr(w), n * N, K, _ptr(out.q), _ptr(out.s), _ptr(out.b), _stream(dev))
+    check(st, "moe_quantize_q4")
+    return out
+
+
 @dataclasses.dataclass
 class MoEWeights:
     """Device weights of one layer."""

@@ -132,3 +132,17 @@ def test_calls_reject_bad_arguments_before_launching(lib):
     st = lib.moe_grouped_gemm_q4(fake, 8, null, 1, ctypes.byref(w0), null, fake, fake, fake, 4, 7, fake, null, 0,
                                  null)
     assert st == _lib.MOE_ERR_SHAPE
+
+
+def test_quantize_validation_launches_nothing(lib):
+    # shape and pointer errors are reported before any launch (no GPU needed)
+    P = ctypes.c_void_p
+    fake = P(0x100000)   # never dereferenced: every call below fails validation or is a no-op
+    assert lib.moe_quantize_q4(fake, 4, 100, fake, fake, fake, None) == -2      # K % 64
+    assert lib.moe_quantize_q4(fake, -1, 64, fake, fake, fake, None) == -2      # rows < 0
+    assert lib.moe_quantize_q4(fake, 4, 0, fake, fake, fake, None) == -2        # K == 0
+    assert lib.moe_quantize_q4(fake, 1 << 40, 2048, fake, fake, fake, None) == -2
+    assert lib.moe_quantize_q4(None, 0, 64, None, None, None, None) == 0        # rows == 0: no-op
+    assert lib.moe_quantize_q4(None, 4, 64, fake, fake, fake, None) == -1
+    assert lib.moe_quantize_q4(P(0x100008), 4, 64, fake, fake, fake, None) == -3  # w not 16-byte aligned
+    assert lib.moe_quantize_q4(fake, 4, 64, fake, P(0x100001), fake, None) == -3  # s not 2-byte aligned
