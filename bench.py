@@ -8,7 +8,9 @@ Prints one JSON line: value = tokens/s of the T=4096 layer, roofline = the
 gate/up grouped GEMM (the dominant kernel) against the bf16 dense MFMA peak,
 cpu_baseline = the fp64 oracle on the host cores, decode = the T=1 and T=8
 layer as HBM bytes per second (weights rotated over 8 device-resident layer
-sets so that the 256 MB last-level cache cannot hold the working set).
+sets so that the 256 MB last-level cache cannot hold the working set),
+quantize = the 4-bit quantiser over one 256 x 512 x 2048 bf16 expert stack as
+HBM bytes per second.
 """
 from __future__ import annotations
 
@@ -123,6 +125,31 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
                       f"{reps} replays timed with events"}
 
 
+def quantize_measure(ops, torch, dev, n=256, N=512, K=2048, reps=10):
+    """The quantiser over one whole expert weight stack (n experts of N x K bf16,
+    the gate stack of the layer) timed with events on the launch stream; bytes =
+    the bf16 weights read plus codes, scales and offsets written."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    w = (torch.randn(n, N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    out = ops.quantize_q4(w)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ops.quantize_q4(w, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = n * N * K * 2 + q4_bytes(n * N, K)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del w, out
+    return {"kernel": "quantize_q4_kernel", "shape": [n, N, K], "us": us, "bytes": nbytes,
+            "GB_per_s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "bound": "hbm",
+            "method": f"{reps} back-to-back calls timed with events"}
+
+
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_q4_swiglu_prefill4096_traffic.txt")
 KERNEL_SOURCES = ("int4_expert_routing_amd/csrc/gemm_q4.hip", "int4_expert_routing_amd/csrc/gemm_tiles.h",
                   "int4_expert_routing_amd/csrc/gemm_args.h", "int4_expert_routing_amd/csrc/moe_common.h")
@@ -170,7 +197,7 @@ def write_traffic_summary(fetch_dir, write_dir, copy_mib, cmd_fetch, cmd_write):
     fv, wv = counter_values(fetch_dir, "FETCH_SIZE"), counter_values(write_dir, "WRITE_SIZE")
     pick = lambda d, key: [v for k, vs in d.items() if key in k for v in vs]
     g_f, g_w = pick(fv, GEMM_KERNEL_NAME), pick(wv, GEMM_KERNEL_NAME)
-    c_f, c_w = pick(fv, "copy"), pick(wv, "copy")
+    c_f, c_w = pick(fv, "copyBuffer"), pick(wv, "copyBuffer")
     if not (g_f and g_w and c_f and c_w):
         raise SystemExit(f"counters missing: gemm {len(g_f)}/{len(g_w)}, copy {len(c_f)}/{len(c_w)}")
     true_bytes = copy_mib * 2**20
@@ -204,6 +231,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-quantize", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after the timed steps, launch one device copy of this many MiB (counter calibration)")
     p.add_argument("--write-traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CMD_FETCH", "CMD_WRITE"),
@@ -341,6 +369,8 @@ def main():
             dw = ops.MoEWeights.from_host(dinp, dev)
             out["decode"][dname] = decode_measure(lib, _lib, ops, torch, dev, dw, dinp.T, dinp.k)
             del dw
+    if not args.no_quantize:
+        out["quantize"] = quantize_measure(ops, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
