@@ -45,10 +45,14 @@
 // Streaming: per group, the activation tile (128 rows x 64 bf16, 16-byte chunks
 //   XOR-swizzled by row) and the 256 columns' weight codes land in a 3-slot
 //   LDS ring through buffer loads that write LDS directly (no registers, one
-//   scalar offset per group), issued two groups ahead; the rows' side-table
-//   entries of each group pair land in a 2-slot ring the same way; scales and
-//   biases of a group pair go to registers with plain loads issued with the
-//   even group's. One s_waitcnt + s_barrier per group.
+//   scalar offset per group), issued two groups ahead; the scale and bias
+//   words of a group pair land in a 2-slot ring with the even group's loads
+//   (global loads that write LDS), and the rows' side-table entries of the
+//   current pair in a single slot, issued at its even step. No load returns
+//   to registers: a register-returning load would make the compiler wait for
+//   it with a count that ignores the LDS-writing loads issued after it, i.e.
+//   stall on the loads just issued. One s_waitcnt + s_barrier per group, one
+//   more per pair before the side table is read.
 // Work mapping: each XCD takes a contiguous chunk of the tile list and runs
 // all column slices of its tiles (see the kernel), so activation rows and
 // expert weights are fetched into one XCD's L2 rather than into all eight.
@@ -62,12 +66,15 @@ constexpr int kRing = 3;                 // LDS ring slots: group g lives in slo
 constexpr int kSlotA = 0;                // 128 rows x 128 B of activations
 constexpr int kSlotB = 16384;            // 4 waves x 2 column blocks x 64 lanes x 16 B of weight codes
 constexpr int kSlotBytes = 24576;
-constexpr int kXpBase = kRing * kSlotBytes;   // side-table ring: pair p lives in slot p % 2
+constexpr int kXpBase = kRing * kSlotBytes;   // side table of the current group pair (one slot)
 constexpr int kXpSlotBytes = 4096;            // 128 rows x 32 B (groups 2p, 2p+1)
-constexpr int kLdsLoop = kXpBase + 2 * kXpSlotBytes;
-// vector-memory instructions a wave issues for one group (the waits count them)
-constexpr int kLoadsEven = 4 + 2 + 4;    // activations, codes, scale and bias pairs of both column blocks
-constexpr int kLoadsOdd = 4 + 2 + 1;     // activations, codes, side-table entries of the pair
+constexpr int kSbBase = kXpBase + kXpSlotBytes;   // scale/bias ring: pair p lives in slot p % 2
+constexpr int kSbSlotBytes = 2048;            // 4 waves x 2 column blocks x 64 words
+constexpr int kLdsLoop = kSbBase + 2 * kSbSlotBytes;
+// vector-memory instructions a wave issues for one group (the waits count them);
+// an even step also issues the pair's side-table load ahead of its group's
+constexpr int kLoadsEven = 4 + 2 + 2;    // activations, codes, scale|bias words of both column blocks
+constexpr int kLoadsOdd = 4 + 2;         // activations, codes
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 // s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
@@ -76,6 +83,7 @@ constexpr int kWaitVm0 = 0x0F70;
 constexpr float kMinUnit = 0x1p-96f;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 // Row m of an activation tile holds its 8 16-byte chunks permuted by
 // c -> c ^ swz(m). Within any 16 consecutive rows, (m & 1, chunk slot) never
@@ -86,6 +94,7 @@ __device__ __forceinline__ int swz(int m) { return (m & 7) ^ ((m >> 3) & 1); }
 __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ swz(m))) * 16; }
 
 __device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
+__device__ __forceinline__ gbl_ptr_t gbl(const void* p) { return (gbl_ptr_t)const_cast<void*>(p); }
 
 // LDS of one workgroup: the two rings during the K loop; afterwards the h
 // tile (SwiGLU: 128 x 128 bf16) or each wave's 128 x 32 fp32 staging block
@@ -106,8 +115,7 @@ struct Stream {
   uint32_t va[4];    // activation chunk offsets (4 instructions)
   uint32_t vb;       // code offset of the lane (same in both column blocks)
   uint32_t vxp;      // side-table offset of (row, half)
-  const uint32_t* sp[2];   // scale pairs of the lane's column in blocks 0, 1
-  const uint32_t* bp[2];   // bias pairs
+  const uint32_t* sbp[2];  // lanes 0-31: scale pairs, lanes 32-63: bias pairs of the lane's column (blocks 0, 1)
 };
 
 // Scale and bias pairs (groups 2p, 2p+1) of the lane's two columns.
@@ -115,11 +123,13 @@ struct SBPair {
   uint32_t s[2], b[2];
 };
 
-// Loads of group g: activations and codes into ring slot g % 3; for even g the
-// scale/bias pairs of groups g, g+1 into registers; for odd g the side-table
-// entries of groups g-1, g into side-table slot (g/2) % 2.
+// Loads of group g: activations and codes into ring slot g % 3; for even g also
+// the scale and bias pairs of groups g, g+1 into scale/bias slot (g/2) % 2
+// (per wave and column block: 32 scale words, then 32 bias words). Every load
+// writes LDS directly, so the compiler tracks no register results of them and
+// only the explicit waits order them.
 template <int ODD>
-__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave, SBPair& next) {
+__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave) {
   uint8_t* slot = ring + (g % kRing) * kSlotBytes;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -128,16 +138,19 @@ __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int
   __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb0, lds(slot + kSlotB + (wave * 2) * 1024), 16, st.vb, g * 32, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb1, lds(slot + kSlotB + (wave * 2 + 1) * 1024), 16, st.vb, g * 32, 0,
                                            0);
-  if (ODD) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rxp, lds(ring + kXpBase + ((g >> 1) & 1) * kXpSlotBytes + wave * 1024),
-                                             16, st.vxp, (g - 1) * 16, 0, 0);
-  } else {
+  if (!ODD) {
     const int p = g >> 1;
-    next.s[0] = st.sp[0][p];
-    next.s[1] = st.sp[1][p];
-    next.b[0] = st.bp[0][p];
-    next.b[1] = st.bp[1][p];
+    uint8_t* sbs = ring + kSbBase + (p & 1) * kSbSlotBytes + wave * 512;
+    __builtin_amdgcn_global_load_lds(gbl(st.sbp[0] + p), lds(sbs), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(gbl(st.sbp[1] + p), lds(sbs + 256), 4, 0, 0);
   }
+}
+
+// Side-table entries of group pair p (groups 2p, 2p+1; every wave loads 32
+// rows) into the side-table slot, issued at step 2p once every wave is past
+// step 2p-1, the last reader of pair p-1.
+__device__ __forceinline__ void issue_xp(const Stream& st, uint8_t* ring, int p, int wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rxp, lds(ring + kXpBase + wave * 1024), 16, st.vxp, p * 32, 0, 0);
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding.
@@ -170,24 +183,34 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 // terms of 2^-24 relative.
 template <int NRB, int P4>
 __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g, int G, int wave, int lane,
-                                          SBPair (&sb)[2], float (&U)[2], f32x16 (&acc)[4][2]) {
+                                          SBPair& sb, float (&U)[2], f32x16 (&acc)[4][2]) {
   constexpr int ODD = P4 & 1;
-  constexpr int PS = P4 >> 1;   // pair (g/2) parity: side-table slot and scale/bias register set
   const int l32 = lane & 31, half = lane >> 5;
-  // this wave's loads of group g have landed once at most those of group g+1
-  // are outstanding; the barrier makes it so for every wave, and orders every
-  // wave's reads of the slot of group g-1 (previous step) before its refill
+  // this wave's loads of group g have landed once at most those issued after
+  // them are outstanding (odd g: the side table and group g+1; even g: group
+  // g+1); the barrier makes it so for every wave, and orders every wave's
+  // reads of the slot of group g-1 (previous step) before its refill
   if (g + 1 < G) {
     if (ODD)
-      wait_vm<kLoadsEven>();
+      wait_vm<kLoadsEven + 1>();
     else
       wait_vm<kLoadsOdd>();
   } else {
     wait_vm<0>();
   }
   __builtin_amdgcn_s_barrier();
-  if (g + 2 < G) issue_group<ODD>(st, ring, g + 2, wave, sb[PS ^ 1]);
+  if (!ODD) issue_xp(st, ring, g >> 1, wave);
+  if (g + 2 < G) issue_group<ODD>(st, ring, g + 2, wave);
   const uint8_t* slot = ring + (g % kRing) * kSlotBytes;
+  if (!ODD) {
+    // this pair's scale and bias words of the lane's column
+    const uint8_t* sbs = ring + kSbBase + ((g >> 1) & 1) * kSbSlotBytes + wave * 512;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      sb.s[cb] = *reinterpret_cast<const uint32_t*>(sbs + cb * 256 + l32 * 4);
+      sb.b[cb] = *reinterpret_cast<const uint32_t*>(sbs + cb * 256 + 128 + l32 * 4);
+    }
+  }
 
   const u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + kSlotB + (wave * 2) * 1024 + lane * 16);
   const u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + kSlotB + (wave * 2 + 1) * 1024 + lane * 16);
@@ -200,7 +223,7 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
   uint32_t nib[2], magic[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const float sf = 16.0f * __uint_as_float(ODD ? (sb[PS].s[cb] & 0xFFFF0000u) : (sb[PS].s[cb] << 16));
+    const float sf = 16.0f * __uint_as_float(ODD ? (sb.s[cb] & 0xFFFF0000u) : (sb.s[cb] << 16));
     const bool nz = __builtin_fabsf(sf) >= kMinUnit;
     const float Un = nz ? sf : U[cb];
     r[cb] = U[cb] * __builtin_amdgcn_rcpf(Un);
@@ -229,12 +252,18 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
     }
   }
   if (ODD) {
+    // the side table of this pair was issued at step g-1 ahead of group g+1's
+    // loads, and group g+2's followed it: every wave waits for its part
+    if (g + 1 < G) {
+      wait_vm<kLoadsEven + kLoadsOdd>();
+      __builtin_amdgcn_s_barrier();
+    }
     const int sh = half << 4;
     bf16x8 bv[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const float sg = __uint_as_float(((sb[PS].s[cb] >> sh) & 0xFFFFu) << 16);
-      const float bg = __uint_as_float(((sb[PS].b[cb] >> sh) & 0xFFFFu) << 16);
+      const float sg = __uint_as_float(((sb.s[cb] >> sh) & 0xFFFFu) << 16);
+      const float bg = __uint_as_float(((sb.b[cb] >> sh) & 0xFFFFu) << 16);
       const float c = (bg - 16.0f * sg) * __builtin_amdgcn_rcpf(U[cb]);
       uint16_t ch, cm, cl;
       split3_bf16(c, ch, cm, cl);
@@ -242,7 +271,7 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
                         uint32_t(cm) | (uint32_t(cl) << 16), 0u};
       bv[cb] = __builtin_bit_cast(bf16x8, pk);
     }
-    const uint8_t* xps = ring + kXpBase + PS * kXpSlotBytes;
+    const uint8_t* xps = ring + kXpBase;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const bf16x8 xa =
@@ -256,7 +285,7 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
 // G is even (K is a multiple of 128). Groups 0 and 1 were issued by the caller.
 template <int NRB>
 __device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, int G, int wave, int lane,
-                                          SBPair (&sb)[2], f32x16 (&acc)[4][2]) {
+                                          SBPair& sb, f32x16 (&acc)[4][2]) {
   float U[2] = {1.0f, 1.0f};   // any normal value: acc is zero until the first nonzero scale
   // unrolled by 4 so the group parity and the pair parity are constants
   for (int g = 0; g < G; g += 4) {
@@ -358,15 +387,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   }
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    // the lane's column's G scales (biases) as G/2 pairs of groups
+    // the lane's column's G scales (lanes 32-63: biases) as G/2 pairs of groups
     const size_t wrow = size_t(el) * a.N + cbase[cb] + l32;
-    st.sp[cb] = reinterpret_cast<const uint32_t*>(mat[cb]->s + wrow * size_t(G));
-    st.bp[cb] = reinterpret_cast<const uint32_t*>(mat[cb]->b + wrow * size_t(G));
+    st.sbp[cb] = reinterpret_cast<const uint32_t*>((half ? mat[cb]->b : mat[cb]->s) + wrow * size_t(G));
   }
 
-  SBPair sb[2];
-  issue_group<0>(st, ring, 0, wave, sb[0]);
-  issue_group<1>(st, ring, 1, wave, sb[1]);   // G >= 2
+  SBPair sb;
+  issue_group<0>(st, ring, 0, wave);
+  issue_group<1>(st, ring, 1, wave);   // G >= 2
 
   f32x16 acc[4][2];
 #pragma unroll
