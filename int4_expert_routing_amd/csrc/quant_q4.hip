@@ -12,7 +12,8 @@
 //   b = lo;  q = 0 if s == 0, else min(15, max(0, rint((w - b) / s))).
 //
 // Work split: 8 lanes per group, each lane loads 8 consecutive bf16 (16 bytes),
-// so a wave covers 8 groups = 1 KB of contiguous weights; min and max meet
+// so one wave load covers 8 groups = 1 KB of contiguous weights (four such
+// loads per lane, see the kernel); min and max meet
 // through three lane exchanges inside the 8-lane team; each lane writes its 8
 // codes as one word (8 lanes = 32 contiguous bytes) and the team's first lane
 // writes the scale and bias.
@@ -20,15 +21,11 @@
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __restrict__ w, long groups,
-                                                          uint32_t* __restrict__ q, uint16_t* __restrict__ s,
-                                                          uint16_t* __restrict__ b) {
-  const long gid = long(blockIdx.x) * blockDim.x + threadIdx.x;
-  const long team = gid >> 3;
-  const int sub = int(gid & 7);
-  const bool ok = team < groups;
-  u32x4 v = u32x4{0u, 0u, 0u, 0u};
-  if (ok) v = *reinterpret_cast<const u32x4*>(w + team * kGroup + sub * 8);
+// One group's codes, scale and bias from its 8 lanes' weights v (lane sub
+// holds elements 8*sub .. 8*sub+7). Every lane of the wave calls this (the
+// min/max exchange is wave-wide); lanes with ok == false store nothing.
+__device__ __forceinline__ void quantize_team(u32x4 v, bool ok, long team, int sub, uint32_t* __restrict__ q,
+                                              uint16_t* __restrict__ s, uint16_t* __restrict__ b) {
   const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
   float x[8];
 #pragma unroll
@@ -52,9 +49,21 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __rest
   const float sv = __uint_as_float(s_bits << 16);
   uint32_t word = 0;
   if (sv != 0.0f) {
+    // q = rint(fl((w - lo) / s)) without a full division per weight: t = (w - lo)
+    // * rcp(s) is within 2^-18 of the correctly rounded quotient (rcp 1 ulp, one
+    // rounding each; quotients are below 16), so rint(t) is the same integer
+    // unless t lies within 2^-16 of a half-integer. Those rare lanes, and
+    // scales outside [2^-100, 2^100] (reciprocal kept normal), take the IEEE
+    // division.
+    const bool fast = sv >= 0x1p-100f && sv <= 0x1p100f;
+    const float rs = __builtin_amdgcn_rcpf(sv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float r = fminf(fmaxf(__builtin_rintf((x[i] - lo) / sv), 0.0f), 15.0f);
+      const float d = x[i] - lo;
+      const float t = d * rs;
+      float r = __builtin_rintf(t);
+      if (!fast || __builtin_fabsf(t - __builtin_floorf(t) - 0.5f) < 0x1p-16f) r = __builtin_rintf(d / sv);
+      r = fminf(fmaxf(r, 0.0f), 15.0f);
       word |= uint32_t(r) << (4 * i);
     }
   }
@@ -66,13 +75,35 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __rest
   }
 }
 
+// A workgroup takes kQuantPer x 32 consecutive groups: load j of a wave reads
+// 8 consecutive groups (1 KB), and all kQuantPer loads of a lane are issued
+// before the first is used, so four times the bytes are in flight per lane.
+constexpr int kQuantPer = 4;
+
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __restrict__ w, long groups,
+                                                          uint32_t* __restrict__ q, uint16_t* __restrict__ s,
+                                                          uint16_t* __restrict__ b) {
+  const long team0 = long(blockIdx.x) * (kQuantPer * 32) + (threadIdx.x >> 3);
+  const int sub = int(threadIdx.x & 7);
+  u32x4 v[kQuantPer];
+#pragma unroll
+  for (int j = 0; j < kQuantPer; ++j) {
+    const long team = team0 + j * 32;
+    v[j] = team < groups ? *reinterpret_cast<const u32x4*>(w + team * kGroup + sub * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int j = 0; j < kQuantPer; ++j) {
+    const long team = team0 + j * 32;
+    quantize_team(v[j], team < groups, team, sub, q, s, b);
+  }
+}
+
 hipError_t launch_quantize(const uint16_t* w, long rows, int K, uint32_t* q, uint16_t* s, uint16_t* b,
                            hipStream_t stream) {
   const long groups = rows * long(K / kGroup);
   if (groups == 0) return hipSuccess;
-  const long threads = groups * 8;
-  hipLaunchKernelGGL(quantize_q4_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, w, groups, q,
-                     s, b);
+  const long blocks = (groups + kQuantPer * 32 - 1) / (kQuantPer * 32);
+  hipLaunchKernelGGL(quantize_q4_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, w, groups, q, s, b);
   return hipGetLastError();
 }
 

@@ -47,6 +47,14 @@ def test_quantize_matches_oracle_bit_exact(dev, std):
     _check(dev, om.f64_to_bf16_bits(rng.normal(0.0, std, size=(3, 64, 512))))
 
 
+@pytest.mark.parametrize("rows,K", [(37, 192), (1, 64), (129, 128), (5, 2048)])
+def test_quantize_ragged_group_counts(dev, rows, K):
+    # group counts that leave the last workgroup's 128 groups partly empty
+    print(f"quantize ragged rows={rows} K={K}", flush=True)
+    rng = np.random.default_rng(rows * 31 + K)
+    _check(dev, om.f64_to_bf16_bits(rng.normal(0.0, 0.05, size=(1, rows, K))))
+
+
 def test_quantize_edge_groups(dev):
     # constant groups, signed zeros, exact grid values with half-way points
     # (ties to even), a single outlier, and groups of two values
