@@ -10,7 +10,8 @@ cpu_baseline = the fp64 oracle on the host cores, decode = the T=1 and T=8
 layer as HBM bytes per second (weights rotated over 8 device-resident layer
 sets so that the 256 MB last-level cache cannot hold the working set),
 quantize = the 4-bit quantiser over one 256 x 512 x 2048 bf16 expert stack as
-HBM bytes per second.
+HBM bytes per second, prefill = the same layer at T=512, at T=4096 with a
+Zipf(1.2) logit skew, and at T=32768, as tokens/s and % of the MFMA peak.
 """
 from __future__ import annotations
 
@@ -125,6 +126,55 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
                       f"{reps} replays timed with events"}
 
 
+def prefill_measure(lib, _lib, ops, torch, dev, w, T, k, zipf=None, steps=10, warmup=3):
+    """Layer calls at T tokens on the same layer weights (x drawn on the device,
+    N(0,1) in bf16; optional Zipf logit bias -zipf*ln(e+1)), timed with events
+    around `steps` back-to-back calls on the launch stream."""
+    import ctypes
+    E, H, I = w.E, w.H, w.I
+    g = torch.Generator(device=dev)
+    g.manual_seed(11 + T)
+    x = torch.randn(T, H, device=dev, generator=g).to(torch.bfloat16)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    bias = None
+    if zipf is not None:
+        bias = (-float(zipf) * torch.log(torch.arange(1, E + 1, dtype=torch.float64))).to(torch.float32).to(dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    structs = [s.c_struct() for s in (w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)]
+    dims = _lib.MoeDims(T, H, I, E, k, 0)
+    ws = torch.zeros(int(lib.moe_workspace_bytes(ctypes.byref(dims))), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        st = lib.moe_layer_forward(
+            ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.router_w.data_ptr()),
+            ctypes.c_void_p(bias.data_ptr()) if bias is not None else None,
+            *[ctypes.byref(s) for s in structs], ctypes.byref(dims), ctypes.c_void_p(y.data_ptr()),
+            None, ctypes.c_void_p(ids.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+            ctypes.c_void_p(stream.cuda_stream))
+        _lib.check(st, "moe_layer_forward")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    counts = torch.bincount(ids.flatten().long(), minlength=E).cpu().numpy()
+    flops = layer_flops(T, H, I, E, k)
+    out = {"T": T, "ms_per_layer": ms, "tokens_per_s": T / (ms * 1e-3),
+           "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+           "logit_bias": f"zipf{zipf}" if zipf is not None else None,
+           "experts_hit": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max()),
+           "method": f"{steps} back-to-back layer calls timed with events"}
+    del x, y, ws, ids
+    return out
+
+
 def quantize_measure(ops, torch, dev, n=256, N=512, K=2048, reps=10):
     """The quantiser over one whole expert weight stack (n experts of N x K bf16,
     the gate stack of the layer) timed with events on the launch stream; bytes =
@@ -232,6 +282,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-quantize", action="store_true")
+    p.add_argument("--no-prefill-sweep", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after the timed steps, launch one device copy of this many MiB (counter calibration)")
     p.add_argument("--write-traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CMD_FETCH", "CMD_WRITE"),
@@ -369,6 +420,12 @@ def main():
             dw = ops.MoEWeights.from_host(dinp, dev)
             out["decode"][dname] = decode_measure(lib, _lib, ops, torch, dev, dw, dinp.T, dinp.k)
             del dw
+    if not args.no_prefill_sweep:
+        out["prefill"] = {
+            "prefill512": prefill_measure(lib, _lib, ops, torch, dev, w, 512, k),
+            "prefill4096_zipf": prefill_measure(lib, _lib, ops, torch, dev, w, 4096, k, zipf=1.2),
+            "prefill32768": prefill_measure(lib, _lib, ops, torch, dev, w, 32768, k, steps=5, warmup=2),
+        }
     if not args.no_quantize:
         out["quantize"] = quantize_measure(ops, torch, dev)
     if not args.no_cpu_baseline:

@@ -47,37 +47,84 @@ hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm
 }
 
 // ---------------------------------------------------------------------------
-// Weighted combine: y[t] = bf16(S[t] + sum_j w[t][j] * Y[row_of_pair[t*k+j]]).
+// Weighted combine: y[t] = bf16(S[t] + sum_j w[t][j] * Y[row_of_pair[t*k+j]]),
+// summed in that order (shared row first, then j ascending) with fp32 FMAs.
+// One workgroup per token; a thread owns 4 consecutive columns in each of the
+// H/1024 column chunks. KK > 0 fixes k at compile time, so that every row
+// load of the token (both column chunks at H = 2048) is issued before the
+// first FMA; KK = 0 is the generic loop.
+template <int KK>
 __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const float* w, const int32_t* row_of_pair,
-                                                      int T, int k, int H, int shared_row0, uint16_t* y) {
+                                                      int T, int k_rt, int H, int shared_row0, uint16_t* y) {
+  constexpr int kChunks = 2;   // column chunks of 1024 handled together
   const int t = blockIdx.x;
-  __shared__ int32_t rows[kMaxTopk];
-  __shared__ float ws[kMaxTopk];
-  if (threadIdx.x < k) {
-    rows[threadIdx.x] = row_of_pair[size_t(t) * k + threadIdx.x];
-    ws[threadIdx.x] = w[size_t(t) * k + threadIdx.x];
+  const int k = KK > 0 ? KK : k_rt;
+  int rows[KK > 0 ? KK : 1];
+  float ws[KK > 0 ? KK : 1];
+#pragma unroll
+  for (int j = 0; j < KK; ++j) {
+    rows[j] = row_of_pair[size_t(t) * k + j];
+    ws[j] = w[size_t(t) * k + j];
   }
-  __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
-    f32x4 acc = *reinterpret_cast<const f32x4*>(Y + size_t(shared_row0 + t) * H + c);
-    for (int j = 0; j < k; ++j) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(Y + size_t(rows[j]) * H + c);
-      const float wj = ws[j];
-      acc[0] = __builtin_fmaf(wj, v[0], acc[0]);
-      acc[1] = __builtin_fmaf(wj, v[1], acc[1]);
-      acc[2] = __builtin_fmaf(wj, v[2], acc[2]);
-      acc[3] = __builtin_fmaf(wj, v[3], acc[3]);
+  for (int c0 = threadIdx.x * 4; c0 < H; c0 += kChunks * 1024) {
+    f32x4 acc[kChunks];
+    bool in[kChunks];
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      const int c = c0 + u * 1024;
+      in[u] = c < H;
+      acc[u] = in[u] ? *reinterpret_cast<const f32x4*>(Y + size_t(shared_row0 + t) * H + c) : f32x4{};
     }
-    uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-    *reinterpret_cast<uint2*>(y + size_t(t) * H + c) = make_uint2(lo, hi);
+    if constexpr (KK > 0) {
+      f32x4 v[KK][kChunks];
+#pragma unroll
+      for (int j = 0; j < KK; ++j)
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u)
+          v[j][u] = in[u] ? *reinterpret_cast<const f32x4*>(Y + size_t(rows[j]) * H + c0 + u * 1024) : f32x4{};
+#pragma unroll
+      for (int j = 0; j < KK; ++j)
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[u][e] = __builtin_fmaf(ws[j], v[j][u][e], acc[u][e]);
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int row = row_of_pair[size_t(t) * k + j];
+        const float wj = w[size_t(t) * k + j];
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u) {
+          if (!in[u]) continue;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(Y + size_t(row) * H + c0 + u * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[u][e] = __builtin_fmaf(wj, v[e], acc[u][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      if (!in[u]) continue;
+      const uint32_t lo = f32_to_bf16_rne(acc[u][0]) | (f32_to_bf16_rne(acc[u][1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[u][2]) | (f32_to_bf16_rne(acc[u][3]) << 16);
+      *reinterpret_cast<uint2*>(y + size_t(t) * H + c0 + u * 1024) = make_uint2(lo, hi);
+    }
   }
 }
 
 hipError_t launch_combine(const float* Y, const float* w, const int32_t* row_of_pair, int T, int k, int H,
                           int shared_row0, uint16_t* y, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y);
+  switch (k) {
+    case 8:
+      hipLaunchKernelGGL(combine_kernel<8>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y);
+      break;
+    case 2:
+      hipLaunchKernelGGL(combine_kernel<2>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y);
+      break;
+    default:
+      hipLaunchKernelGGL(combine_kernel<0>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y);
+      break;
+  }
   return hipGetLastError();
 }
 
