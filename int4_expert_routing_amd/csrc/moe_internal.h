@@ -15,7 +15,7 @@ struct RouteArgs {
   const float* logits_in;   // float [T][E] when logits are given, or [n_parts][T][E] partial sums
   int n_parts;              // number of partial-sum planes in logits_in (1 = plain logits)
   int coherent;             // read logits_in with device-coherent loads (written by other workgroups)
-  float* logit_parts;       // workspace for the router's K-range partials [kRouterSplits][T][E]
+  float* logit_parts;       // workspace for the router's K-range partials [router_splits][T][E]
   const float* bias;        // float [E] or null
   float* logits_out;        // float [T][E]: router GEMM output (layer path)
   int32_t* topk_ids;        // [T][k]
@@ -60,9 +60,7 @@ struct ScatterArgs {
   int T, E, k;
 };
 
-// Few-token layer calls split the router GEMM's K range in kRouterSplits.
-constexpr int kRouterSplits = 8;
-constexpr int kRouterSplitMaxT = 256;
+// Number of K ranges the router GEMM splits into at T tokens (8, 4, 2 or 1).
 int router_splits(int T, int H);
 
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,

@@ -129,6 +129,25 @@ __global__ __launch_bounds__(kWave) void router_logits_kernel(const uint16_t* __
   }
 }
 
+// A token's logits from NP K-range partial planes (plane stride `plane`):
+// every load is issued before the first add, and the planes are added in
+// order, so the result does not depend on when the loads return.
+template <int NP>
+__device__ __forceinline__ void sum_parts(const float* parts, size_t plane, const size_t (&f)[kMaxKeysPerLane],
+                                          float (&v)[kMaxKeysPerLane]) {
+  float pv[kMaxKeysPerLane][NP];
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) pv[i][p] = parts[size_t(p) * plane + f[i]];
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) {
+    v[i] = pv[i][0];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) v[i] += pv[i][p];
+  }
+}
+
 // Top-k of one token held by one wave: lane l holds the order keys of experts
 // l, l+64, l+128, l+192 (0 for experts >= E, below every finite logit's key).
 // The k-th largest key tau is found by a most-significant-bit-first radix
@@ -204,19 +223,12 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
     size_t f[kMaxKeysPerLane];
 #pragma unroll
     for (int i = 0; i < kMaxKeysPerLane; ++i) f[i] = size_t(t0 + m) * E + min(lane + 64 * i, E - 1);
-    if (a.n_parts == kRouterSplits) {
-      float pv[kMaxKeysPerLane][kRouterSplits];
-#pragma unroll
-      for (int i = 0; i < kMaxKeysPerLane; ++i)
-#pragma unroll
-        for (int p = 0; p < kRouterSplits; ++p) pv[i][p] = a.logits_in[size_t(p) * a.T * E + f[i]];
-      // the partials are added in plane order
-#pragma unroll
-      for (int i = 0; i < kMaxKeysPerLane; ++i) {
-        v[i] = pv[i][0];
-#pragma unroll
-        for (int p = 1; p < kRouterSplits; ++p) v[i] += pv[i][p];
-      }
+    if (a.n_parts == 8) {
+      sum_parts<8>(a.logits_in, size_t(a.T) * E, f, v);
+    } else if (a.n_parts == 4) {
+      sum_parts<4>(a.logits_in, size_t(a.T) * E, f, v);
+    } else if (a.n_parts == 2) {
+      sum_parts<2>(a.logits_in, size_t(a.T) * E, f, v);
     } else if (a.coherent) {
 #pragma unroll
       for (int i = 0; i < kMaxKeysPerLane; ++i)
@@ -567,8 +579,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArg
 }
 
 int router_splits(int T, int H) {
-  // few tokens: split K so that the weight stream spreads over more CUs
-  return (T <= kRouterSplitMaxT && H % (64 * kRouterSplits) == 0) ? kRouterSplits : 1;
+  // One wave per 32-token x 64-expert tile leaves few waves per CU up to about
+  // a thousand tokens (16 x 4 = 64 single-wave workgroups at T = 512): there K
+  // is split into ks ranges of whole 64-wide chunks, and the top-k kernel adds
+  // the ks partials in plane order. Larger calls keep one range: at T = 4096 a
+  // two-way split measured slower (the tiles' operand re-reads from L2, not
+  // the wave count, bound the router there, and the partials add traffic).
+  int ks = T <= 1024 ? 8 : 1;
+  while (ks > 1 && H % (64 * ks) != 0) ks >>= 1;
+  return ks;
 }
 
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,

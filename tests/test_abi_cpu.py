@@ -65,12 +65,19 @@ def test_check_dims_and_workspace(lib):
     assert lib.moe_check_dims(None) == _lib.MOE_ERR_NULL
 
 
-def test_workspace_holds_router_partials_for_few_tokens(lib):
-    # up to 256 tokens the router GEMM splits K eight ways into fp32 partial sums
-    few = lib.moe_workspace_bytes(ctypes.byref(MoeDims(8, 2048, 512, 256, 8, 0)))
-    assert few >= 8 * 8 * 256 * 4 + (8 * 9) * 2048 * 4
-    many = lib.moe_workspace_bytes(ctypes.byref(MoeDims(257, 2048, 512, 256, 8, 0)))
-    assert many >= (257 * 9) * 2048 * 4
+def test_workspace_holds_router_partials(lib):
+    # the router GEMM splits K into 8 fp32 partial-sum planes up to 1024
+    # tokens (fewer when H is not a multiple of 64 * 8), none above; each
+    # plane is [T, E]
+    def ws(T, H=2048):
+        return lib.moe_workspace_bytes(ctypes.byref(MoeDims(T, H, 512, 256, 8, 0)))
+
+    for T, planes in ((8, 8), (512, 8), (1024, 8)):
+        without = ws(T) - planes * T * 256 * 4
+        assert without >= (T * 9) * 2048 * 4 + T * 256 * 4, T     # Y and the logits still fit
+    # splits fall back when H is not a multiple of 64 * planes
+    assert ws(1024, 256) < ws(1024, 512)
+    assert ws(1025) >= (1025 * 9) * 2048 * 4 + 1025 * 256 * 4
 
 
 def test_max_tiles_bound(lib):

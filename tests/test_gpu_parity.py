@@ -256,6 +256,14 @@ def test_layer_ragged_token_counts(dev, T):
     check_layer(inp, run_layer(dev, inp))
 
 
+@pytest.mark.parametrize("T,H", [(600, 512), (1000, 256), (1100, 512)])
+def test_layer_router_split_ranges(dev, T, H):
+    # the router GEMM splits K into 8, 4 and 1 partial-sum planes here
+    print(f"layer router split T={T} H={H}", flush=True)
+    inp = make_layer(T, H, 128, 16, 2, seed=T, bias_mode="random")
+    check_layer(inp, run_layer(dev, inp))
+
+
 def test_layer_k_equals_E(dev):
     inp = make_layer(40, 256, 128, 4, 4, seed=4, bias_mode="random")
     check_layer(inp, run_layer(dev, inp))
