@@ -45,8 +45,10 @@
 // Streaming: per group, the activation tile (128 rows x 64 bf16, 16-byte chunks
 //   XOR-swizzled by row) and the 256 columns' weight codes land in a 3-slot
 //   LDS ring through buffer loads that write LDS directly (no registers, one
-//   scalar offset per group), issued two groups ahead; the scale and bias
-//   words of a group pair land in a 2-slot ring with the even group's loads
+//   scalar offset per group), issued two groups ahead (tiles of at most 32
+//   rows: 32-row activation tiles in a 5-slot ring, four groups ahead); the
+//   scale and bias words of a group pair land in a 2-slot (3-slot) ring with
+//   the even group's loads
 //   (global loads that write LDS), and the rows' side-table entries of the
 //   current pair in a single slot, issued at its even step. No load returns
 //   to registers: a register-returning load would make the compiler wait for
@@ -62,19 +64,36 @@ namespace moe {
 
 constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = kGemmWaves * 64;
-constexpr int kRing = 3;                 // LDS ring slots: group g lives in slot g % 3
-constexpr int kSlotA = 0;                // 128 rows x 128 B of activations
-constexpr int kSlotB = 16384;            // 4 waves x 2 column blocks x 64 lanes x 16 B of weight codes
-constexpr int kSlotBytes = 24576;
-constexpr int kXpBase = kRing * kSlotBytes;   // side table of the current group pair (one slot)
-constexpr int kXpSlotBytes = 4096;            // 128 rows x 32 B (groups 2p, 2p+1)
-constexpr int kSbBase = kXpBase + kXpSlotBytes;   // scale/bias ring: pair p lives in slot p % 2
-constexpr int kSbSlotBytes = 2048;            // 4 waves x 2 column blocks x 64 words
-constexpr int kLdsLoop = kSbBase + 2 * kSbSlotBytes;
-// vector-memory instructions a wave issues for one group (the waits count them);
-// an even step also issues the pair's side-table load ahead of its group's
-constexpr int kLoadsEven = 4 + 2 + 2;    // activations, codes, scale|bias words of both column blocks
-constexpr int kLoadsOdd = 4 + 2;         // activations, codes
+constexpr int kXpSlotBytes = 4096;       // side table of one group pair: 128 rows x 32 B (groups 2p, 2p+1)
+constexpr int kSbSlotBytes = 2048;       // scale/bias words of one group pair: 4 waves x 2 column blocks x 64 words
+
+// LDS ring geometry. Group g lives in slot g % RING and is loaded DIST steps
+// ahead (issued at step g - DIST into the slot that group g - 1 used); the
+// scale/bias words of pair p live in slot p % SBS.
+//   full tiles (33..128 rows): 3 slots of 128 activation rows + codes, DIST 2;
+//   small tiles (at most 32 rows): 5 slots of 32 activation rows + codes,
+//     DIST 4. Such a tile does too little arithmetic per group to cover a
+//     memory round trip in two steps; its activation tile is a quarter of a
+//     full one, so the same LDS holds twice the groups in flight.
+template <bool SR>
+struct Ring {
+  static constexpr int RING = SR ? 5 : 3;
+  static constexpr int DIST = RING - 1;
+  static constexpr int AROWS = SR ? 32 : 128;          // activation rows per slot
+  static constexpr int ALOADS = AROWS / 32;               // activation loads per wave and group (8 rows each)
+  static constexpr int SLOT_B = AROWS * 128;              // codes: 4 waves x 2 column blocks x 64 lanes x 16 B
+  static constexpr int SLOT = SLOT_B + 8192;
+  static constexpr int XP = RING * SLOT;
+  static constexpr int SB = XP + kXpSlotBytes;
+  static constexpr int SBS = SR ? 3 : 2;               // pair p's words are read at step 2p, loaded at 2p - DIST
+  static constexpr int END = SB + SBS * kSbSlotBytes;
+  // vector-memory instructions a wave issues for one group (the waits count
+  // them); an even step also issues the pair's side-table load ahead of its
+  // group's
+  static constexpr int LOADS_EVEN = ALOADS + 2 + 2;      // activations, codes, scale|bias words of both blocks
+  static constexpr int LOADS_ODD = ALOADS + 2;           // activations, codes
+};
+constexpr int kLdsLoop = Ring<false>::END > Ring<true>::END ? Ring<false>::END : Ring<true>::END;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 // s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
@@ -96,6 +115,17 @@ __device__ __forceinline__ int a_chunk_off(int m, int c) { return (m * 8 + (c ^ 
 __device__ __forceinline__ lds_ptr_t lds(void* p) { return (lds_ptr_t)p; }
 __device__ __forceinline__ gbl_ptr_t gbl(const void* p) { return (gbl_ptr_t)const_cast<void*>(p); }
 
+// One 16-byte-per-lane buffer load that writes LDS at dst + 16 * lane, and one
+// 4-byte-per-lane global load that writes LDS at dst + 4 * lane. (Plain
+// functions, so that the templates below reach the builtins only through
+// them.)
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds(dst), 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void global_to_lds4(const uint32_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(gbl(src), lds(dst), 4, 0, 0);
+}
+
 // LDS of one workgroup: the two rings during the K loop; afterwards the h
 // tile (SwiGLU: 128 x 128 bf16) or each wave's 128 x 32 fp32 staging block
 // (STORE_F32, row stride 36 floats).
@@ -112,7 +142,7 @@ size_t gemm_lds_bytes(int /*K*/) {
 // scale/bias pair addresses of the lane's two columns.
 struct Stream {
   __amdgpu_buffer_rsrc_t ra, rb0, rb1, rxp;
-  uint32_t va[4];    // activation chunk offsets (4 instructions)
+  uint32_t va[4];    // activation chunk offsets (4 instructions; small tiles use va[0] only)
   uint32_t vb;       // code offset of the lane (same in both column blocks)
   uint32_t vxp;      // side-table offset of (row, half)
   const uint32_t* sbp[2];  // lanes 0-31: scale pairs, lanes 32-63: bias pairs of the lane's column (blocks 0, 1)
@@ -123,34 +153,34 @@ struct SBPair {
   uint32_t s[2], b[2];
 };
 
-// Loads of group g: activations and codes into ring slot g % 3; for even g also
-// the scale and bias pairs of groups g, g+1 into scale/bias slot (g/2) % 2
-// (per wave and column block: 32 scale words, then 32 bias words). Every load
-// writes LDS directly, so the compiler tracks no register results of them and
-// only the explicit waits order them.
-template <int ODD>
+// Loads of group g: activations and codes into ring slot g % RING; for even g
+// also the scale and bias pairs of groups g, g+1 into scale/bias slot
+// (g/2) % SBS (per wave and column block: 32 scale words, then 32 bias
+// words). Every load writes LDS directly, so the compiler tracks no register
+// results of them and only the explicit waits order them.
+template <int ODD, bool SR>
 __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave) {
-  uint8_t* slot = ring + (g % kRing) * kSlotBytes;
+  using R = Ring<SR>;
+  uint8_t* slot = ring + (g % R::RING) * R::SLOT;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, lds(slot + kSlotA + (wave * 4 + i) * 1024), 16, st.va[i],
-                                             g * (kGroup * 2), 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb0, lds(slot + kSlotB + (wave * 2) * 1024), 16, st.vb, g * 32, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb1, lds(slot + kSlotB + (wave * 2 + 1) * 1024), 16, st.vb, g * 32, 0,
-                                           0);
+  for (int i = 0; i < R::ALOADS; ++i)
+    buffer_to_lds16(st.ra, slot + (wave * R::ALOADS + i) * 1024, st.va[i], g * (kGroup * 2));
+  buffer_to_lds16(st.rb0, slot + R::SLOT_B + (wave * 2) * 1024, st.vb, g * 32);
+  buffer_to_lds16(st.rb1, slot + R::SLOT_B + (wave * 2 + 1) * 1024, st.vb, g * 32);
   if (!ODD) {
     const int p = g >> 1;
-    uint8_t* sbs = ring + kSbBase + (p & 1) * kSbSlotBytes + wave * 512;
-    __builtin_amdgcn_global_load_lds(gbl(st.sbp[0] + p), lds(sbs), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(gbl(st.sbp[1] + p), lds(sbs + 256), 4, 0, 0);
+    uint8_t* sbs = ring + R::SB + (p % R::SBS) * kSbSlotBytes + wave * 512;
+    global_to_lds4(st.sbp[0] + p, sbs);
+    global_to_lds4(st.sbp[1] + p, sbs + 256);
   }
 }
 
 // Side-table entries of group pair p (groups 2p, 2p+1; every wave loads 32
 // rows) into the side-table slot, issued at step 2p once every wave is past
 // step 2p-1, the last reader of pair p-1.
+template <bool SR>
 __device__ __forceinline__ void issue_xp(const Stream& st, uint8_t* ring, int p, int wave) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rxp, lds(ring + kXpBase + wave * 1024), 16, st.vxp, p * 32, 0, 0);
+  buffer_to_lds16(st.rxp, ring + Ring<SR>::XP + wave * 1024, st.vxp, p * 32);
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding.
@@ -181,30 +211,68 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 // bf16 parts (h, m, l), against the rows' side-table entries
 // (Xh, Xm, Xl, Xh, Xm, Xh, 0, 0) as (h, h, h, m, m, l, 0, 0), i.e. X c up to
 // terms of 2^-24 relative.
-template <int NRB, int P4>
+// Wait at the top of step g until this wave's loads of group g have landed.
+// Issue order: groups 0 .. DIST-1 before the loop, then at every step j the
+// side table of pair j/2 (even j) followed by group j + DIST. At most the
+// loads issued after group g's may still be outstanding:
+//   full ring (DIST 2): even g: group g+1; odd g: the side table of step g-1
+//     and group g+1; none at the last step;
+//   small ring (DIST 4, G >= 8): groups g+1 .. min(g+3, G-1) and the side
+//     tables of the even steps in [max(g-3, 0), g-1]; below G = 8 it waits
+//     for every load.
+template <int ODD, bool SR>
+__device__ __forceinline__ void wait_group(int g, int G) {
+  using R = Ring<SR>;
+  constexpr int E = R::LOADS_EVEN, O = R::LOADS_ODD;
+  if constexpr (!SR) {
+    if (g + 1 < G) {
+      if (ODD)
+        wait_vm<E + 1>();
+      else
+        wait_vm<O>();
+    } else {
+      wait_vm<0>();
+    }
+  } else {
+    if (G < 8) {
+      wait_vm<0>();
+    } else if (ODD) {
+      if (g == 1)
+        wait_vm<E + O + E + 1>();
+      else if (g == G - 3)
+        wait_vm<E + O + 2>();
+      else if (g == G - 1)
+        wait_vm<2>();
+      else
+        wait_vm<E + O + E + 2>();
+    } else {
+      if (g == 0)
+        wait_vm<O + E + O>();
+      else if (g == G - 2)
+        wait_vm<O + 1>();
+      else
+        wait_vm<O + E + O + 1>();
+    }
+  }
+}
+
+template <int NRB, int P4, bool SR>
 __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g, int G, int wave, int lane,
                                           SBPair& sb, float (&U)[2], f32x16 (&acc)[4][2]) {
+  using R = Ring<SR>;
   constexpr int ODD = P4 & 1;
   const int l32 = lane & 31, half = lane >> 5;
-  // this wave's loads of group g have landed once at most those issued after
-  // them are outstanding (odd g: the side table and group g+1; even g: group
-  // g+1); the barrier makes it so for every wave, and orders every wave's
-  // reads of the slot of group g-1 (previous step) before its refill
-  if (g + 1 < G) {
-    if (ODD)
-      wait_vm<kLoadsEven + 1>();
-    else
-      wait_vm<kLoadsOdd>();
-  } else {
-    wait_vm<0>();
-  }
+  // this wave's loads of group g have landed; the barrier makes it so for
+  // every wave, and orders every wave's reads of the slot of group g-1
+  // (previous step) before its refill
+  wait_group<ODD, SR>(g, G);
   __builtin_amdgcn_s_barrier();
-  if (!ODD) issue_xp(st, ring, g >> 1, wave);
-  if (g + 2 < G) issue_group<ODD>(st, ring, g + 2, wave);
-  const uint8_t* slot = ring + (g % kRing) * kSlotBytes;
+  if (!ODD) issue_xp<SR>(st, ring, g >> 1, wave);
+  if (g + R::DIST < G) issue_group<ODD, SR>(st, ring, g + R::DIST, wave);
+  const uint8_t* slot = ring + (g % R::RING) * R::SLOT;
   if (!ODD) {
     // this pair's scale and bias words of the lane's column
-    const uint8_t* sbs = ring + kSbBase + ((g >> 1) & 1) * kSbSlotBytes + wave * 512;
+    const uint8_t* sbs = ring + R::SB + ((g >> 1) % R::SBS) * kSbSlotBytes + wave * 512;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       sb.s[cb] = *reinterpret_cast<const uint32_t*>(sbs + cb * 256 + l32 * 4);
@@ -212,8 +280,8 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
     }
   }
 
-  const u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + kSlotB + (wave * 2) * 1024 + lane * 16);
-  const u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + kSlotB + (wave * 2 + 1) * 1024 + lane * 16);
+  const u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + R::SLOT_B + (wave * 2) * 1024 + lane * 16);
+  const u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + R::SLOT_B + (wave * 2 + 1) * 1024 + lane * 16);
   bf16x8 fa[2][4];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
@@ -252,10 +320,20 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
     }
   }
   if (ODD) {
-    // the side table of this pair was issued at step g-1 ahead of group g+1's
-    // loads, and group g+2's followed it: every wave waits for its part
-    if (g + 1 < G) {
-      wait_vm<kLoadsEven + kLoadsOdd>();
+    // the side table of this pair was issued at step g-1 ahead of group
+    // g-1+DIST's loads, and group g+DIST's followed it: every wave waits for
+    // its part. The full ring's last step already waited for every load at
+    // its top; the small ring's last steps leave side tables outstanding there.
+    if constexpr (!SR) {
+      if (g + 1 < G) {
+        wait_vm<R::LOADS_EVEN + R::LOADS_ODD>();
+        __builtin_amdgcn_s_barrier();
+      }
+    } else {
+      if (g + R::DIST < G)
+        wait_vm<R::LOADS_EVEN + R::LOADS_ODD>();
+      else
+        wait_vm<0>();
       __builtin_amdgcn_s_barrier();
     }
     const int sh = half << 4;
@@ -271,7 +349,7 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
                         uint32_t(cm) | (uint32_t(cl) << 16), 0u};
       bv[cb] = __builtin_bit_cast(bf16x8, pk);
     }
-    const uint8_t* xps = ring + kXpBase;
+    const uint8_t* xps = ring + R::XP;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const bf16x8 xa =
@@ -282,18 +360,25 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
   }
 }
 
-// G is even (K is a multiple of 128). Groups 0 and 1 were issued by the caller.
-template <int NRB>
+// G is even (K is a multiple of 128). SR: the small-tile ring (NRB == 1).
+template <int NRB, bool SR>
 __device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, int G, int wave, int lane,
                                           SBPair& sb, f32x16 (&acc)[4][2]) {
+  // groups 0 .. DIST-1 (those that exist) before the first step
+  issue_group<0, SR>(st, ring, 0, wave);
+  issue_group<1, SR>(st, ring, 1, wave);
+  if constexpr (SR) {
+    if (2 < G) issue_group<0, SR>(st, ring, 2, wave);
+    if (3 < G) issue_group<1, SR>(st, ring, 3, wave);
+  }
   float U[2] = {1.0f, 1.0f};   // any normal value: acc is zero until the first nonzero scale
   // unrolled by 4 so the group parity and the pair parity are constants
   for (int g = 0; g < G; g += 4) {
-    loop_step<NRB, 0>(st, ring, g, G, wave, lane, sb, U, acc);
-    loop_step<NRB, 1>(st, ring, g + 1, G, wave, lane, sb, U, acc);
+    loop_step<NRB, 0, SR>(st, ring, g, G, wave, lane, sb, U, acc);
+    loop_step<NRB, 1, SR>(st, ring, g + 1, G, wave, lane, sb, U, acc);
     if (g + 2 < G) {
-      loop_step<NRB, 2>(st, ring, g + 2, G, wave, lane, sb, U, acc);
-      loop_step<NRB, 3>(st, ring, g + 3, G, wave, lane, sb, U, acc);
+      loop_step<NRB, 2, SR>(st, ring, g + 2, G, wave, lane, sb, U, acc);
+      loop_step<NRB, 3, SR>(st, ring, g + 3, G, wave, lane, sb, U, acc);
     }
   }
 #pragma unroll
@@ -371,12 +456,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
     st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
   }
   {
-    // activation load i of wave w fills chunk positions (4w + i)*64 + lane:
-    // row m = (4w + i)*8 + lane/8 and chunk slot lane%8, which holds logical
+    // activation load i of wave w fills chunk positions (A w + i)*64 + lane,
+    // A = activation loads per wave (4, or 1 in the small-tile ring): row
+    // m = (A w + i)*8 + lane/8 and chunk slot lane%8, which holds logical
     // chunk (lane%8) ^ swz(m)
+    const int aloads = nrb == 1 ? Ring<true>::ALOADS : Ring<false>::ALOADS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = (wave * 4 + i) * 8 + (lane >> 3);
+      const int m = (wave * aloads + i) * 8 + (lane >> 3);
       const int cidx = (lane & 7) ^ swz(m);
       const int r = ti.r0 + min(m, nrows - 1);     // padding rows re-read the last real row
       st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
@@ -393,17 +480,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   }
 
   SBPair sb;
-  issue_group<0>(st, ring, 0, wave);
-  issue_group<1>(st, ring, 1, wave);   // G >= 2
 
   f32x16 acc[4][2];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
   switch (nrb) {
-    case 1: main_loop<1>(st, ring, G, wave, lane, sb, acc); break;
-    case 2: main_loop<2>(st, ring, G, wave, lane, sb, acc); break;
-    case 3: main_loop<3>(st, ring, G, wave, lane, sb, acc); break;
-    default: main_loop<4>(st, ring, G, wave, lane, sb, acc); break;
+    case 1: main_loop<1, true>(st, ring, G, wave, lane, sb, acc); break;
+    case 2: main_loop<2, false>(st, ring, G, wave, lane, sb, acc); break;
+    case 3: main_loop<3, false>(st, ring, G, wave, lane, sb, acc); break;
+    default: main_loop<4, false>(st, ring, G, wave, lane, sb, acc); break;
   }
   __syncthreads();   // every wave is done with the rings
 

@@ -140,6 +140,33 @@ def test_gemm_f32_matches_oracle(dev, bias_mode):
     assert max_abs_frac(got, want) < 1e-4
 
 
+@pytest.mark.parametrize("K", [128, 256, 512, 640, 768, 1280, 2048])
+def test_gemm_f32_small_tiles_every_group_count(dev, K):
+    # ~6 rows per expert: every tile has one 32-row block and streams through
+    # the deeper small-tile ring, whose waits differ for the first steps, the
+    # last steps and K below 512
+    print(f"gemm f32 small tiles K={K}", flush=True)
+    T, E, k, N = 96, 32, 2, 256
+    inp = make_layer(T, K, N, E, k, seed=K, bias_mode="random")
+    A = ops.bf16_from_bits(inp.x, dev)
+    W = ops.Q4Stack.from_host(inp.gate, dev)
+    r = _route_for(dev, T, E, k, 21)
+    out = ops.moe_grouped_gemm_q4(A, W, r["offsets"], r["tile_map"], r["num_tiles"], ops.MOE_EPI_STORE_F32,
+                                  T * k, sorted_rows=r["sorted_rows"], row_div=k)
+    torch.cuda.synchronize()
+    got = _np(out).astype(np.float64)
+    srt = _np(r["sorted_rows"])
+    offs = _np(r["offsets"])
+    assert np.diff(offs).max() <= 32
+    x = om.bf16_bits_to_f64(inp.x)
+    want = np.zeros((T * k, N))
+    for e in range(E):
+        rows = np.arange(offs[e], offs[e + 1])
+        want[rows] = x[srt[rows] // k] @ om.expert_weights(inp.gate, e).T
+    assert rel_l2(got, want) < 1e-5, rel_l2(got, want)
+    assert max_abs_frac(got, want) < 1e-4
+
+
 def test_gemm_f32_zero_and_spread_scales(dev):
     # Scales that are exactly 0 (a group, a column's first group, every group of
     # a column) and scales spread over 2^-12..2^12 inside one column: the
