@@ -228,9 +228,13 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti
 }
 
 // Tiles: the shared expert's (one per token: tile t is row routed_rows + t,
-// token t), then the routed tiles' descriptors.
+// token t), then the routed tiles' descriptors. Register budget: 64 VGPRs, so
+// that 8 waves fit per SIMD (four 8-wave workgroups per CU at K = 2048) and
+// more of the weight stream is in flight; the compiler keeps the few values
+// past that budget in scratch (T=8 layer 45.9 -> 44.2 us; 67 VGPRs before).
 template <int STEPS, int KS>
-__global__ __launch_bounds__(2 * KS * 64) void decode_swiglu_kernel(GemmArgs a, const u32x4* tile_desc, int nrmax) {
+__global__ __launch_bounds__(2 * KS * 64) __attribute__((amdgpu_waves_per_eu(8)))
+void decode_swiglu_kernel(GemmArgs a, const u32x4* tile_desc, int nrmax) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tile = blockIdx.x / a.NT;
   const int cb = blockIdx.x % a.NT;
