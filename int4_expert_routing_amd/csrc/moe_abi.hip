@@ -44,7 +44,7 @@ LayerLayout layer_layout(const moe_dims& d) {
   // offset 0 for every T, zero before a call and after it
   L.done = c.take(T > 0 ? 256 : 0);
   L.logits = c.take(T * E * 4);
-  const int ks = router_splits(d.T, d.H);
+  const int ks = router_splits(d.T, d.H, d.E);
   L.logit_parts = c.take(size_t(ks > 1 ? ks : 0) * T * E * 4);
   L.ids = c.take(T * k * 4);
   L.w = c.take(T * k * 4);

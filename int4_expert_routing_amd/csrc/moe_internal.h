@@ -60,8 +60,10 @@ struct ScatterArgs {
   int T, E, k;
 };
 
-// Number of K ranges the router GEMM splits into at T tokens (8, 4, 2 or 1).
-int router_splits(int T, int H);
+// Number of K ranges the router GEMM splits into at T tokens (8, 4, 2 or 1),
+// and the token count above which the 64 x 128 tile router kernel runs.
+constexpr int kRouterTileMinT = 1024;
+int router_splits(int T, int H, int E);
 
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,
                         hipStream_t stream);

@@ -129,6 +129,111 @@ __global__ __launch_bounds__(kWave) void router_logits_kernel(const uint16_t* __
   }
 }
 
+// Router GEMM for calls above a thousand tokens: a workgroup of 4 waves
+// computes a 64-token x 128-expert tile over one K range (blockIdx.z of KS).
+// Wave w takes tokens 32 (w & 1) .. +31 and experts 64 (w >> 1) .. +63 of the
+// tile (two 32 x 32 MFMA blocks, as in the single-wave kernel), so every
+// activation and router-weight row that lands in LDS serves two waves, and
+// each operand row is fetched from L2 by half as many workgroups as with
+// 32 x 64 tiles (the single-wave kernel's L2 re-reads bound it at T = 4096).
+// The operands stream through a 3-slot LDS ring of 64-wide K chunks, two
+// chunks ahead; each wave issues 6 of a chunk's 24 buffer loads that write LDS.
+constexpr int kRtTok = 64, kRtExp = 128;
+constexpr int kRtRing = 3;
+constexpr int kRtSlotX = kRtTok * 128;                   // 64 token rows x 128 B
+constexpr int kRtSlot = kRtSlotX + kRtExp * 128;         // + 128 expert rows x 128 B
+constexpr int kRtThreads = 4 * kWave;
+
+__global__ __launch_bounds__(kRtThreads, 2) void router_tile_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ wr,
+                                                                   const float* __restrict__ bias, int T, int H,
+                                                                   int E, float* __restrict__ out) {
+  extern __shared__ __align__(16) uint8_t rsm[];
+  typedef __attribute__((address_space(3))) void* lptr;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const int tb = wave & 1, ebk = wave >> 1;
+  const int t0 = blockIdx.x * kRtTok;
+  const int e0 = blockIdx.y * kRtExp;
+  const int KS = gridDim.z;
+  const int KC = H / KS;
+  const int k0 = blockIdx.z * KC;
+  const int nch = KC / 64;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 0x7FFFFFFF,
+                                                                     kRouterRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wr), 0, 0x7FFFFFFF,
+                                                                     kRouterRsrcWord3);
+  // load i of wave w fills 8 rows: token rows (2w + i)*8 + lane/8 (i < 2) and
+  // expert rows (4w + i)*8 + lane/8 (i < 4); slot lane%8 holds logical chunk
+  // (lane%8) ^ swz(row). Rows past T or E re-read the last valid row.
+  uint32_t vx[2], vw[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = (wave * 2 + i) * 8 + (lane >> 3);
+    const int t = min(t0 + m, T - 1);
+    vx[i] = uint32_t(t) * uint32_t(H * 2) + uint32_t(((lane & 7) ^ rswz(m)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = (wave * 4 + i) * 8 + (lane >> 3);
+    const int e = min(e0 + n, E - 1);
+    vw[i] = uint32_t(e) * uint32_t(H * 2) + uint32_t(((lane & 7) ^ rswz(n)) * 16);
+  }
+  auto issue = [&](int c) {
+    uint8_t* slot = rsm + (c % kRtRing) * kRtSlot;
+    const int soff = (k0 + 64 * c) * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lptr)(slot + (wave * 2 + i) * 1024), 16, vx[i], soff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lptr)(slot + kRtSlotX + (wave * 4 + i) * 1024), 16, vw[i], soff,
+                                               0, 0);
+  };
+  issue(0);
+  if (nch > 1) issue(1);
+  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  for (int c = 0; c < nch; ++c) {
+    // this wave's loads of chunk c have landed once at most chunk c+1's 6 are
+    // outstanding; the barrier makes it so for every wave and orders every
+    // wave's reads of chunk c-1's slot before it is refilled with chunk c+2
+    if (c + 1 < nch)
+      __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (c + 2 < nch) issue(c + 2);
+    const uint8_t* slot = rsm + (c % kRtRing) * kRtSlot;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = 2 * kk + half;
+      const bf16x8 av =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + rchunk_off(tb * 32 + l32, ch)));
+      const bf16x8 b0 = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(slot + kRtSlotX + rchunk_off(ebk * 64 + l32, ch)));
+      const bf16x8 b1 = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(slot + kRtSlotX + rchunk_off(ebk * 64 + 32 + l32, ch)));
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc1, 0, 0, 0);
+    }
+  }
+  // output element (eb, r, lane): token t0 + 32 tb + 8(r/4) + 4*half + r%4,
+  // expert e0 + 64 ebk + 32 eb + lane%32
+  float* dst = out + size_t(blockIdx.z) * size_t(T) * E;
+#pragma unroll
+  for (int eb = 0; eb < 2; ++eb) {
+    const int n = e0 + ebk * 64 + 32 * eb + l32;
+    if (n >= E) continue;
+    const float bv = (KS == 1 && bias) ? bias[n] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = tb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (t0 + m < T) dst[size_t(t0 + m) * E + n] = ((eb ? acc1[r] : acc0[r]) + bv) + 0.0f;
+    }
+  }
+}
+
 // A token's logits from NP K-range partial planes (plane stride `plane`):
 // every load is issued before the first add, and the planes are added in
 // order, so the result does not depend on when the loads return.
@@ -578,14 +683,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArg
   }
 }
 
-int router_splits(int T, int H) {
-  // One wave per 32-token x 64-expert tile leaves few waves per CU up to about
-  // a thousand tokens (16 x 4 = 64 single-wave workgroups at T = 512): there K
-  // is split into ks ranges of whole 64-wide chunks, and the top-k kernel adds
-  // the ks partials in plane order. Larger calls keep one range: at T = 4096 a
-  // two-way split measured slower (the tiles' operand re-reads from L2, not
-  // the wave count, bound the router there, and the partials add traffic).
-  int ks = T <= 1024 ? 8 : 1;
+int router_splits(int T, int H, int E) {
+  // Up to about a thousand tokens the single-wave 32 x 64 tiles are few (16 x 4
+  // = 64 workgroups at T = 512), so K is split 8 ways. Above that the 64 x 128
+  // tile kernel runs, with K split so that about 512 workgroups (two per CU)
+  // stream the operands. The top-k kernel adds the partials in plane order.
+  int ks;
+  if (T <= kRouterTileMinT) {
+    ks = 8;
+  } else {
+    const int tiles = ceil_div(T, kRtTok) * ceil_div(E, kRtExp);
+    ks = 1;
+    while (ks < 8 && tiles * ks * 2 <= 512) ks <<= 1;
+  }
   while (ks > 1 && H % (64 * ks) != 0) ks >>= 1;
   return ks;
 }
@@ -620,10 +730,14 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
   if (from_x) {
     // logits (biased) into logits_out, or K-range partials into logit_parts
     // that the top-k kernel sums (adding the bias, writing logits_out)
-    const int ks = router_splits(ra.T, ra.H);
+    const int ks = router_splits(ra.T, ra.H, ra.E);
     float* dst = ks > 1 ? ra.logit_parts : ra.logits_out;
-    hipLaunchKernelGGL(router_logits_kernel, dim3(nrb, ceil_div(ra.E, 64), ks), dim3(kWave),
-                       kRouterRing * kRouterSlot, stream, ra.x, ra.wr, ra.bias, ra.T, ra.H, ra.E, dst);
+    if (ra.T <= kRouterTileMinT)
+      hipLaunchKernelGGL(router_logits_kernel, dim3(nrb, ceil_div(ra.E, 64), ks), dim3(kWave),
+                         kRouterRing * kRouterSlot, stream, ra.x, ra.wr, ra.bias, ra.T, ra.H, ra.E, dst);
+    else
+      hipLaunchKernelGGL(router_tile_kernel, dim3(ceil_div(ra.T, kRtTok), ceil_div(ra.E, kRtExp), ks),
+                         dim3(kRtThreads), kRtRing * kRtSlot, stream, ra.x, ra.wr, ra.bias, ra.T, ra.H, ra.E, dst);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ks > 1) {

@@ -66,18 +66,18 @@ def test_check_dims_and_workspace(lib):
 
 
 def test_workspace_holds_router_partials(lib):
-    # the router GEMM splits K into 8 fp32 partial-sum planes up to 1024
-    # tokens (fewer when H is not a multiple of 64 * 8), none above; each
-    # plane is [T, E]
+    # the router GEMM splits K into fp32 partial-sum planes [T, E]: 8 up to
+    # 1024 tokens, then as many (up to 8) as keep its 64 x 128 tiles at about
+    # 512 workgroups, fewer when H is not a multiple of 64 * planes
     def ws(T, H=2048):
         return lib.moe_workspace_bytes(ctypes.byref(MoeDims(T, H, 512, 256, 8, 0)))
 
-    for T, planes in ((8, 8), (512, 8), (1024, 8)):
+    for T, planes in ((8, 8), (512, 8), (1024, 8), (2048, 8), (4096, 4), (8192, 2)):
         without = ws(T) - planes * T * 256 * 4
         assert without >= (T * 9) * 2048 * 4 + T * 256 * 4, T     # Y and the logits still fit
     # splits fall back when H is not a multiple of 64 * planes
     assert ws(1024, 256) < ws(1024, 512)
-    assert ws(1025) >= (1025 * 9) * 2048 * 4 + 1025 * 256 * 4
+    assert ws(16384) >= (16384 * 9) * 2048 * 4 + 16384 * 256 * 4
 
 
 def test_max_tiles_bound(lib):

@@ -283,11 +283,16 @@ def test_layer_ragged_token_counts(dev, T):
     check_layer(inp, run_layer(dev, inp))
 
 
-@pytest.mark.parametrize("T,H", [(600, 512), (1000, 256), (1100, 512)])
-def test_layer_router_split_ranges(dev, T, H):
-    # the router GEMM splits K into 8, 4 and 1 partial-sum planes here
-    print(f"layer router split T={T} H={H}", flush=True)
-    inp = make_layer(T, H, 128, 16, 2, seed=T, bias_mode="random")
+@pytest.mark.parametrize("T,H,E,zipf", [(600, 512, 16, None), (1000, 256, 16, None), (1100, 512, 16, None),
+                                         (3000, 256, 16, 1.2), (5000, 128, 16, None), (9000, 256, 16, 1.2),
+                                         (2500, 256, 200, None)])
+def test_layer_router_split_ranges(dev, T, H, E, zipf):
+    # single-wave router tiles with K split 8 / 4 ways (T <= 1024), then the
+    # 64 x 128 tile kernel with 8, 4, 2 and 1 K ranges; the logit bias is added
+    # by the top-k kernel after a split and by the router without one; E = 200
+    # leaves the last expert tile partly empty
+    print(f"layer router split T={T} H={H} E={E} zipf={zipf}", flush=True)
+    inp = make_layer(T, H, 128, E, 2, seed=T, bias_mode="random", zipf=zipf)
     check_layer(inp, run_layer(dev, inp))
 
 
