@@ -301,6 +301,15 @@ def test_layer_k_equals_E(dev):
     check_layer(inp, run_layer(dev, inp))
 
 
+@pytest.mark.parametrize("T", [3, 40])
+def test_layer_max_topk(dev, T):
+    # k at its maximum (32 of 64 experts): the one-launch routing, the decode
+    # kernels' 16-wave down+combine (T = 3) and the generic combine (T = 40)
+    print(f"layer k=32 T={T}", flush=True)
+    inp = make_layer(T, 256, 128, 64, 32, seed=50 + T, bias_mode="random")
+    check_layer(inp, run_layer(dev, inp))
+
+
 def test_layer_zero_tokens_is_a_noop(dev):
     inp = make_layer(3, 256, 128, 16, 2, seed=0)
     w = ops.MoEWeights.from_host(inp, dev)
