@@ -313,8 +313,9 @@ def main():
         write_traffic_summary(fd, wd, 512, cf, cw)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library runs on a "
-              "single GPU; see DESIGN.md for how the layer would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this library runs on a "
+              "single GPU (with the weights replicated, the layer shards over tokens with no exchange, "
+              "so N GPUs would each run this benchmark on their own tokens)", file=sys.stderr)
         sys.exit(2)
     import ctypes
 

@@ -76,8 +76,8 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                               "or python -m int4_expert_routing_amd.build_lib")
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "python -m int4_expert_routing_amd.build_lib")
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
