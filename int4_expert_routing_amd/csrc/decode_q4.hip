@@ -227,11 +227,11 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti
   }
 }
 
-// Tiles: the shared expert's (one per token: tile t is row routed_rows + t,
-// token t), then the routed tiles' descriptors. Register budget: 64 VGPRs, so
-// that 8 waves fit per SIMD (four 8-wave workgroups per CU at K = 2048) and
-// more of the weight stream is in flight; the compiler keeps the few values
-// past that budget in scratch (T=8 layer 45.9 -> 44.2 us; 67 VGPRs before).
+// Tiles: the shared expert's (one tile of all T rows), then the routed
+// tiles' descriptors. Register budget: 64 VGPRs, so that 8 waves fit per SIMD
+// (four 8-wave workgroups per CU at K = 2048) and more of the weight stream is
+// in flight; the compiler keeps the few values past that budget in scratch
+// (T=8 layer 45.9 -> 44.2 us; 67 VGPRs before).
 template <int STEPS, int KS>
 __global__ __launch_bounds__(2 * KS * 64) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_swiglu_kernel(GemmArgs a, const u32x4* tile_desc, int nrmax) {
@@ -240,10 +240,13 @@ void decode_swiglu_kernel(GemmArgs a, const u32x4* tile_desc, int nrmax) {
   const int cb = blockIdx.x % a.NT;
   DecTile ti;
   if (tile < a.n_shared_tiles) {
+    // the shared expert: one tile of every token's row (row routed_rows + t
+    // is token t), so its weights stream once per call
     ti.e = a.E;
-    ti.r0 = a.routed_rows + tile;
-    ti.n = 1;
-    ti.tok = uint32_t(tile);
+    ti.r0 = a.routed_rows;
+    ti.n = a.shared_rows;
+    ti.tok = 0u;
+    for (int j = 0; j < a.shared_rows; ++j) ti.tok |= uint32_t(j) << (4 * j);
   } else {
     const int i = tile - a.n_shared_tiles;
     const int nt = *a.num_tiles;
@@ -396,7 +399,7 @@ bool decode_supported(int N, int K) {
 hipError_t launch_decode(const GemmArgs& ga, const u32x4* tile_desc, int max_row_tiles, int max_rows,
                          hipStream_t stream) {
   if (!decode_supported(ga.N, ga.K) || ga.NT != ga.N / 16 || max_rows < 1 || max_rows > kDecodeMaxRows ||
-      ga.n_shared_tiles != ga.shared_rows || ga.shared_rows > max_rows || !tile_desc)
+      ga.n_shared_tiles != (ga.shared_rows > 0 ? 1 : 0) || ga.shared_rows > max_rows || !tile_desc)
     return hipErrorInvalidValue;
   const dim3 grid(unsigned(max_row_tiles) * unsigned(ga.NT));
   if (grid.x == 0) return hipSuccess;

@@ -342,7 +342,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.offsets = offsets;
   g1.tile_map = tile_map;
   g1.num_tiles = num_tiles;
-  g1.n_shared_tiles = decode ? T : n_sh;   // decode: one shared-expert tile per token
+  g1.n_shared_tiles = decode ? 1 : n_sh;   // decode: the shared expert's T rows form one tile
   g1.shared_rows = T;
   g1.N = I;
   g1.K = H;
@@ -350,7 +350,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.NT = decode ? I / 16 : I / 128;
   g1.out = h;
   g1.out_part = h_part;
-  const hipError_t e1 = decode ? launch_decode(g1, tile_desc, T + max_routed, T, s)
+  const hipError_t e1 = decode ? launch_decode(g1, tile_desc, 1 + max_routed, T, s)
                                : launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s);
   if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 

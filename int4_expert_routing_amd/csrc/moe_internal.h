@@ -74,9 +74,9 @@ constexpr int kDecodeMaxRows = 8;
 // Gate/up projection with SwiGLU: K in {256, 512, 1024, 2048}, N % 16 == 0,
 // ga.NT = N/16 column blocks, ga.A = the call's T rows in natural element
 // order; h is written in the operand chunk order with no group-sum table. The
-// shared expert has one tile per token (n_shared_tiles = shared_rows = T);
-// routed tiles are described by the routing's tile_desc. max_rows (>= T) bounds every tile's row count
-// (1..kDecodeMaxRows).
+// shared expert's T rows form one tile (n_shared_tiles = 1, shared_rows = T);
+// routed tiles are described by the routing's tile_desc. max_rows (>= T)
+// bounds every tile's row count (1..kDecodeMaxRows).
 bool decode_supported(int N, int K);
 hipError_t launch_decode(const GemmArgs& ga, const u32x4* tile_desc, int max_row_tiles, int max_rows,
                          hipStream_t stream);
