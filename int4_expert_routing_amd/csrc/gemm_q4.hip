@@ -67,23 +67,31 @@ constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kXpSlotBytes = 4096;       // side table of one group pair: 128 rows x 32 B (groups 2p, 2p+1)
 constexpr int kSbSlotBytes = 2048;       // scale/bias words of one group pair: 4 waves x 2 column blocks x 64 words
 
-// LDS ring geometry. Group g lives in slot g % RING and is loaded DIST steps
-// ahead (issued at step g - DIST into the slot that group g - 1 used); the
+// LDS ring geometry. Group g's activation tile lives in A slot g % A_RING and
+// its codes in code slot g % C_RING; groups are loaded DIST steps ahead. The
 // scale/bias words of pair p live in slot p % SBS.
-//   full tiles (33..128 rows): 3 slots of 128 activation rows + codes, DIST 2;
-//   small tiles (at most 32 rows): 5 slots of 32 activation rows + codes,
-//     DIST 4. Such a tile does too little arithmetic per group to cover a
-//     memory round trip in two steps; its activation tile is a quarter of a
-//     full one, so the same LDS holds twice the groups in flight.
+//   full tiles (33..128 rows): 3 slots, each 128 activation rows then the
+//     codes; group g issued at step g - 2 into the slot group g - 1 used;
+//   small tiles (at most 32 rows): 5 slots of 32 activation rows and 6 code
+//     slots; group g's activations issued at step g - 4, and both groups of a
+//     pair's codes at the pair's even step 2p - 4, back to back, so the second
+//     group's loads find the 128-byte lines the first group's brought into L1
+//     (a column's codes of two groups are 64 contiguous bytes). Such a tile
+//     does too little arithmetic per group to cover a memory round trip in two
+//     steps; its activation tile is a quarter of a full one, so the same LDS
+//     holds twice the groups in flight.
 template <bool SR>
 struct Ring {
-  static constexpr int RING = SR ? 5 : 3;
-  static constexpr int DIST = RING - 1;
-  static constexpr int AROWS = SR ? 32 : 128;          // activation rows per slot
+  static constexpr int DIST = SR ? 4 : 2;
+  static constexpr int AROWS = SR ? 32 : 128;             // activation rows per slot
   static constexpr int ALOADS = AROWS / 32;               // activation loads per wave and group (8 rows each)
-  static constexpr int SLOT_B = AROWS * 128;              // codes: 4 waves x 2 column blocks x 64 lanes x 16 B
-  static constexpr int SLOT = SLOT_B + 8192;
-  static constexpr int XP = RING * SLOT;
+  static constexpr int A_RING = DIST + 1;
+  static constexpr int C_RING = SR ? DIST + 2 : DIST + 1;
+  static constexpr int CODES = 8192;                      // 4 waves x 2 column blocks x 64 lanes x 16 B
+  static constexpr int A_SLOT = SR ? AROWS * 128 : AROWS * 128 + CODES;
+  static constexpr int C_BASE = SR ? A_RING * A_SLOT : AROWS * 128;
+  static constexpr int C_SLOT = SR ? CODES : A_SLOT;
+  static constexpr int XP = SR ? C_BASE + C_RING * C_SLOT : A_RING * A_SLOT;
   static constexpr int SB = XP + kXpSlotBytes;
   static constexpr int SBS = SR ? 3 : 2;               // pair p's words are read at step 2p, loaded at 2p - DIST
   static constexpr int END = SB + SBS * kSbSlotBytes;
@@ -95,7 +103,8 @@ struct Ring {
 };
 constexpr int kLdsLoop = Ring<false>::END > Ring<true>::END ? Ring<false>::END : Ring<true>::END;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
-// s_waitcnt immediates (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]); only vmcnt waits.
+// s_waitcnt immediates (gfx9: vmcnt[3:0] and [15:14], expcnt[6:4],
+// lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
 // Scales below this magnitude count as zero (their products are below 2^-96
 // of the activations): the running unit must stay a normal fp32 number.
@@ -158,20 +167,33 @@ struct SBPair {
 // (g/2) % SBS (per wave and column block: 32 scale words, then 32 bias
 // words). Every load writes LDS directly, so the compiler tracks no register
 // results of them and only the explicit waits order them.
+template <bool SR>
+__device__ __forceinline__ void issue_codes(const Stream& st, uint8_t* ring, int g, int wave) {
+  using R = Ring<SR>;
+  uint8_t* cs = ring + R::C_BASE + (g % R::C_RING) * R::C_SLOT;
+  buffer_to_lds16(st.rb0, cs + (wave * 2) * 1024, st.vb, g * 32);
+  buffer_to_lds16(st.rb1, cs + (wave * 2 + 1) * 1024, st.vb, g * 32);
+}
+
+// Loads of group g (in this order, which the waits count on):
+//   full ring: activations and codes of g; for even g the scale/bias words of
+//     pair g/2;
+//   small ring, even g: activations and codes of g, the scale/bias words of
+//     pair g/2, then the codes of g+1; odd g: activations of g.
 template <int ODD, bool SR>
 __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave) {
   using R = Ring<SR>;
-  uint8_t* slot = ring + (g % R::RING) * R::SLOT;
+  uint8_t* slot = ring + (g % R::A_RING) * R::A_SLOT;
 #pragma unroll
   for (int i = 0; i < R::ALOADS; ++i)
     buffer_to_lds16(st.ra, slot + (wave * R::ALOADS + i) * 1024, st.va[i], g * (kGroup * 2));
-  buffer_to_lds16(st.rb0, slot + R::SLOT_B + (wave * 2) * 1024, st.vb, g * 32);
-  buffer_to_lds16(st.rb1, slot + R::SLOT_B + (wave * 2 + 1) * 1024, st.vb, g * 32);
+  if (!SR || !ODD) issue_codes<SR>(st, ring, g, wave);
   if (!ODD) {
     const int p = g >> 1;
     uint8_t* sbs = ring + R::SB + (p % R::SBS) * kSbSlotBytes + wave * 512;
     global_to_lds4(st.sbp[0] + p, sbs);
     global_to_lds4(st.sbp[1] + p, sbs + 256);
+    if (SR) issue_codes<SR>(st, ring, g + 1, wave);   // g + 1 < G: G is even
   }
 }
 
@@ -186,8 +208,8 @@ __device__ __forceinline__ void issue_xp(const Stream& st, uint8_t* ring, int p,
 // Wait until at most N of this wave's vector-memory loads are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(kWaitVm0 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(kWaitVm0 | (N & 15) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
@@ -211,15 +233,21 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 // bf16 parts (h, m, l), against the rows' side-table entries
 // (Xh, Xm, Xl, Xh, Xm, Xh, 0, 0) as (h, h, h, m, m, l, 0, 0), i.e. X c up to
 // terms of 2^-24 relative.
-// Wait at the top of step g until this wave's loads of group g have landed.
-// Issue order: groups 0 .. DIST-1 before the loop, then at every step j the
-// side table of pair j/2 (even j) followed by group j + DIST. At most the
-// loads issued after group g's may still be outstanding:
-//   full ring (DIST 2): even g: group g+1; odd g: the side table of step g-1
-//     and group g+1; none at the last step;
-//   small ring (DIST 4, G >= 8): groups g+1 .. min(g+3, G-1) and the side
-//     tables of the even steps in [max(g-3, 0), g-1]; below G = 8 it waits
-//     for every load.
+// Wait at the top of step g until this wave's loads that step g reads have
+// landed (activations and codes of group g; at even g the scale/bias words of
+// pair g/2). Issue order: the first DIST groups before the loop, then at every
+// step j the side table of pair j/2 (even j) followed by group j + DIST (see
+// issue_group). At most the loads issued after the last needed one may still
+// be outstanding:
+//   full ring: even g: group g+1 (4+2); odd g: the side table of step g-1 and
+//     group g+1 (4+2+2, + 1); none at the last step;
+//   small ring (an even step issues 7 loads after its side table, an odd step
+//     1; G is even):
+//     even g: the codes of g+1 and the activations of g+1 (3), the side table
+//       of step g-2 (g >= 2), and groups g+2, g+3 (8) while g <= G-4;
+//     odd g: the side table of step g-3 (g >= 3), groups g+1, g+2 (7 + 1)
+//       while g <= G-3, the side table of step g-1, and groups g+3, g+4 (7,
+//       the activations of g+4 following at step g) while g <= G-5.
 template <int ODD, bool SR>
 __device__ __forceinline__ void wait_group(int g, int G) {
   using R = Ring<SR>;
@@ -233,25 +261,36 @@ __device__ __forceinline__ void wait_group(int g, int G) {
     } else {
       wait_vm<0>();
     }
-  } else {
-    if (G < 8) {
-      wait_vm<0>();
-    } else if (ODD) {
-      if (g == 1)
-        wait_vm<E + O + E + 1>();
-      else if (g == G - 3)
-        wait_vm<E + O + 2>();
-      else if (g == G - 1)
+  } else if constexpr (ODD) {
+    const bool xp3 = g >= 3;
+    if (g <= G - 5) {
+      if (xp3)
+        wait_vm<17>();
+      else
+        wait_vm<16>();
+    } else if (g == G - 3) {
+      if (xp3)
+        wait_vm<10>();
+      else
+        wait_vm<9>();
+    } else {   // g == G - 1
+      if (xp3)
         wait_vm<2>();
       else
-        wait_vm<E + O + E + 2>();
-    } else {
-      if (g == 0)
-        wait_vm<O + E + O>();
-      else if (g == G - 2)
-        wait_vm<O + 1>();
+        wait_vm<1>();
+    }
+  } else {
+    const bool xp2 = g >= 2;
+    if (g <= G - 4) {
+      if (xp2)
+        wait_vm<12>();
       else
-        wait_vm<O + E + O + 1>();
+        wait_vm<11>();
+    } else {   // g == G - 2
+      if (xp2)
+        wait_vm<4>();
+      else
+        wait_vm<3>();
     }
   }
 }
@@ -269,7 +308,8 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
   __builtin_amdgcn_s_barrier();
   if (!ODD) issue_xp<SR>(st, ring, g >> 1, wave);
   if (g + R::DIST < G) issue_group<ODD, SR>(st, ring, g + R::DIST, wave);
-  const uint8_t* slot = ring + (g % R::RING) * R::SLOT;
+  const uint8_t* slot = ring + (g % R::A_RING) * R::A_SLOT;
+  const uint8_t* cslot = ring + R::C_BASE + (g % R::C_RING) * R::C_SLOT;
   if (!ODD) {
     // this pair's scale and bias words of the lane's column
     const uint8_t* sbs = ring + R::SB + ((g >> 1) % R::SBS) * kSbSlotBytes + wave * 512;
@@ -280,8 +320,8 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
     }
   }
 
-  const u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + R::SLOT_B + (wave * 2) * 1024 + lane * 16);
-  const u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + R::SLOT_B + (wave * 2 + 1) * 1024 + lane * 16);
+  const u32x4 w0 = *reinterpret_cast<const u32x4*>(cslot + (wave * 2) * 1024 + lane * 16);
+  const u32x4 w1 = *reinterpret_cast<const u32x4*>(cslot + (wave * 2 + 1) * 1024 + lane * 16);
   bf16x8 fa[2][4];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
@@ -330,8 +370,10 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
         __builtin_amdgcn_s_barrier();
       }
     } else {
+      // issued after the side table: step g-1's group (7 loads) and step g's
+      // activations (1), while g + 4 < G
       if (g + R::DIST < G)
-        wait_vm<R::LOADS_EVEN + R::LOADS_ODD>();
+        wait_vm<8>();
       else
         wait_vm<0>();
       __builtin_amdgcn_s_barrier();
