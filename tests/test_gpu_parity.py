@@ -310,6 +310,43 @@ def test_layer_max_topk(dev, T):
     check_layer(inp, run_layer(dev, inp))
 
 
+@pytest.mark.parametrize("T", [1, 3, 8, 40, 600])
+def test_layer_graph_replays_match_eager(dev, T):
+    # One layer call captured in a HIP graph (it records no allocation or
+    # memset) and replayed three times, each after an eager call on other
+    # tokens that overwrites the workspace: every replay gives the eager call's
+    # bits, and the one-launch routing's counter (T <= 4) is back at zero.
+    # Covers the one-launch, decode and prefill paths.
+    print(f"layer graph T={T}", flush=True)
+    H, I, E, k = 256, 128, 16, 2
+    inp = make_layer(T, H, I, E, k, seed=70 + T, bias_mode="random")
+    w = ops.MoEWeights.from_host(inp, dev)
+    layer = ops.MoELayer(w, k, T)
+    x = ops.bf16_from_bits(inp.x, dev)
+    x2 = ops.bf16_from_bits(make_layer(T, H, I, E, k, seed=170 + T).x, dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    y2 = torch.empty_like(y)
+    ids2 = torch.empty_like(ids)
+    layer(x, y=y, topk_ids_out=ids)
+    torch.cuda.synchronize()
+    y_eager, ids_eager = y.clone(), ids.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer(x, y=y, topk_ids_out=ids)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.fill_(0)
+        ids.fill_(-1)
+        layer(x2, y=y2, topk_ids_out=ids2)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager) and torch.equal(ids, ids_eager)
+        assert int(layer.workspace[:256].count_nonzero()) == 0
+    ref = run_layer(dev, inp)
+    assert np.array_equal(om.bf16_bits_to_f64(ops.bits_from_bf16(y)), ref["y"])
+
+
 def test_layer_zero_tokens_is_a_noop(dev):
     inp = make_layer(3, 256, 128, 16, 2, seed=0)
     w = ops.MoEWeights.from_host(inp, dev)
