@@ -264,6 +264,32 @@ def check_brute(om, cfg=dict(T=64, H=256, I=128, E=16, k=2), seeds=(0,), modes=(
                 assert err < 1e-12, f"layer differs from per-token brute force: rel {err:.3g}"
 
 
+def check_layer_tokens(om, cases=(dict(T=64, H=256, I=128, E=16, k=2, seed=0, bias_mode="random"),
+                                  dict(T=24, H=128, I=64, E=4, k=4, seed=1, bias_mode="random"),
+                                  dict(T=12, H=128, I=64, E=64, k=32, seed=2, bias_mode="random"),
+                                  dict(T=48, H=256, I=128, E=16, k=2, seed=3, bias_mode="sym", zipf=1.2))):
+    """The per-token oracle (``moe_layer_tokens``, the reference for sampled and
+    decode-shaped layer checks) against the independent per-token brute force
+    and against the sort-based layer on the same logits: tiny, k = E, k = 32,
+    a Zipf logit bias, both bias modes, all tokens and a shuffled subset."""
+    for cfg in cases:
+        inp = make_layer(**cfg)
+        rng = np.random.default_rng(cfg["seed"] + 40)
+        l = om.router_logits(inp.x, inp.router_w, inp.logit_bias)
+        # exact ties inside the top-k and at its boundary on some tokens
+        l[::5] = np.round(l[::5] * 2) / 2
+        full = om.moe_layer(inp, logits=l)["y_unrounded"]
+        toks = list(range(inp.T))
+        sub = rng.permutation(inp.T)[: max(3, inp.T // 3)].tolist()
+        for tk in (toks, sub):
+            got = om.moe_layer_tokens(inp, tk, l)
+            yb, _, _ = brute_force.layer_brute_force(inp, l, tk)
+            err_b = np.linalg.norm(got - yb) / np.linalg.norm(yb)
+            assert err_b < 1e-12, f"per-token oracle differs from the brute force: rel {err_b:.3g}"
+            err_f = np.max(np.abs(got - full[tk])) / np.max(np.abs(full))
+            assert err_f < 1e-14, f"per-token oracle differs from the layer oracle: rel {err_f:.3g}"
+
+
 def brute_force_logits(inp):
     """Router logits computed token by token with Python floats -> fp64 dot -> fp32."""
     x = brute_force.bf16_decode(inp.x)
@@ -278,4 +304,4 @@ def brute_force_logits(inp):
 
 
 ALL_CHECKS = [check_bf16, check_unpack, check_dequant, check_logits, check_topk, check_golden_routing,
-              check_routing_invariants, check_dense_ffn, check_integer_ffn, check_brute]
+              check_routing_invariants, check_dense_ffn, check_integer_ffn, check_brute, check_layer_tokens]

@@ -104,6 +104,41 @@ def _round_bf16_truncate(v):
     return r.view(np.float32).astype(np.float64)
 
 
+_real_layer_tokens = om.moe_layer_tokens
+
+
+def _tokens_slot_weights_swapped(inp, tokens, logits, round_h=True):
+    # the weights of each token's chosen experts applied in reverse slot order
+    real = om.select_topk
+
+    def swapped(l, k):
+        ids, w = real(l, k)
+        return ids, w[:, ::-1]
+    om.select_topk = swapped
+    try:
+        return _real_layer_tokens(inp, tokens, logits, round_h)
+    finally:
+        om.select_topk = real
+
+
+def _tokens_expert_off_by_one(inp, tokens, logits, round_h=True):
+    # expert e's output computed with expert (e + 1) % E's weights
+    import copy
+    shifted = copy.copy(inp)
+    for name in ("gate", "up", "down"):
+        w = getattr(inp, name)
+        setattr(shifted, name, type(w)(np.roll(w.q, -1, 0), np.roll(w.s, -1, 0), np.roll(w.b, -1, 0)))
+    return _real_layer_tokens(shifted, tokens, logits, round_h)
+
+
+def _tokens_no_shared(inp, tokens, logits, round_h=True):
+    import copy
+    zeroed = copy.copy(inp)
+    w = inp.sh_down
+    zeroed.sh_down = type(w)(w.q, np.zeros_like(w.s), np.zeros_like(w.b))
+    return _real_layer_tokens(zeroed, tokens, logits, round_h)
+
+
 MUTANTS = {
     "nibble order": ("unpack_q4", _unpack_high_first),
     "bias dropped": ("dequant_q4", _dequant_no_bias),
@@ -117,6 +152,9 @@ MUTANTS = {
     "tile size off by one": ("routing_tables", _tables_tile_off_by_one),
     "router rows reversed": ("router_logits", _logits_reversed_experts),
     "bf16 truncation": ("round_bf16", _round_bf16_truncate),
+    "per-token oracle: slot weights swapped": ("moe_layer_tokens", _tokens_slot_weights_swapped),
+    "per-token oracle: expert index off by one": ("moe_layer_tokens", _tokens_expert_off_by_one),
+    "per-token oracle: shared expert dropped": ("moe_layer_tokens", _tokens_no_shared),
 }
 
 

@@ -84,7 +84,28 @@ def check_packing(quantize):
     assert om.bf16_bits_to_f64(s)[0, 0] == 1.0 and om.bf16_bits_to_f64(b)[0, 0] == 0.0
 
 
-CHECKS = [check_error_bound, check_grid_round_trip, check_constant_groups, check_order, check_packing]
+def check_ties_to_even(quantize):
+    # A hand-built group whose quotients (w - b)/s land exactly half-way between
+    # two codes: lo = 0 and hi = 15 give s = 1 and b = 0 exactly, and every
+    # value k + 1/2 (k = 0..14) is a bf16 number. Round half to even sends
+    # 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, 3.5 -> 4, ..., 13.5 -> 14, 14.5 -> 14.
+    # A second group is the same grid moved by -8 (lo = -8, hi = 7: b = -8, s = 1).
+    halves = [k + 0.5 for k in range(15)]
+    want = [0, 2, 2, 4, 4, 6, 6, 8, 8, 10, 10, 12, 12, 14, 14]
+    g0 = [0.0, 15.0] + halves + [0.0] * (64 - 17)
+    g1 = [v - 8.0 for v in g0]
+    q, s, b = quantize(om.f64_to_bf16_bits(np.array([g0 + g1])))
+    codes = om.unpack_q4(q)[0]
+    assert om.bf16_bits_to_f64(s)[0].tolist() == [1.0, 1.0]
+    assert om.bf16_bits_to_f64(b)[0].tolist() == [0.0, -8.0]
+    for grp in (0, 1):
+        c = codes[64 * grp: 64 * grp + 64]
+        assert c[0] == 0 and c[1] == 15
+        assert c[2:17].tolist() == want, c[2:17].tolist()
+
+
+CHECKS = [check_error_bound, check_grid_round_trip, check_constant_groups, check_order, check_packing,
+          check_ties_to_even]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -137,7 +158,18 @@ def _mut_max_as_bias(w_bits):
     return oq.pack_q4(nib.astype(np.uint8)), neg, (hi.view(np.uint32) >> 16).astype(np.uint16)
 
 
-MUTANTS = [_mut_divide_by_16, _mut_truncate, _mut_nibbles_reversed, _mut_max_as_bias]
+def _mut_round_half_up(w_bits):
+    q, s, b = oq.quantize_q4(w_bits)
+    wb = np.asarray(w_bits, np.uint16)
+    w = (wb.astype(np.uint32) << 16).view(np.float32).reshape(*wb.shape[:-1], -1, 64)
+    sf = (s.astype(np.uint32) << 16).view(np.float32)[..., None]
+    lo = (b.astype(np.uint32) << 16).view(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qq = np.where(sf == 0, 0, np.clip(np.floor((w - lo) / sf + np.float32(0.5)), 0, 15))
+    return oq.pack_q4(qq.reshape(wb.shape).astype(np.uint8)), s, b
+
+
+MUTANTS = [_mut_divide_by_16, _mut_truncate, _mut_nibbles_reversed, _mut_max_as_bias, _mut_round_half_up]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda m: m.__name__)
