@@ -17,7 +17,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
-from scipy.special import softmax
+from scipy.special import expit, softmax
 
 
 def _bf16_value(bits: int) -> float:
@@ -67,10 +67,12 @@ def dequant_bytes(q_words: np.ndarray, s_bits: np.ndarray, b_bits: np.ndarray) -
 
 
 def token_output(xt: np.ndarray, logits_row: np.ndarray, k: int, experts, shared,
-                 round_h: bool = True) -> np.ndarray:
+                 round_h: bool = True, gate_w=None) -> np.ndarray:
     """One token's layer output before the final rounding (fp64).
 
-    ``experts(e)`` and ``shared()`` return (Wg, Wu, Wd) as fp64 arrays."""
+    ``experts(e)`` and ``shared()`` return (Wg, Wu, Wd) as fp64 arrays;
+    ``gate_w`` (fp64 [H] or None) gates the shared expert by the logistic
+    function of x . gate_w (scipy's expit of a math.fsum dot product)."""
     E = logits_row.shape[0]
     lrow = [float(v) for v in logits_row]
     chosen = sorted(range(E), key=lambda e: (-lrow[e], e))[:k]
@@ -87,6 +89,8 @@ def token_output(xt: np.ndarray, logits_row: np.ndarray, k: int, experts, shared
         return wd @ h
 
     out = ffn(shared())
+    if gate_w is not None:
+        out = out * float(expit(math.fsum(xt * gate_w)))
     for wj, e in zip(w, chosen):
         out = out + wj * ffn(experts(e))
     return out, chosen, w
@@ -108,11 +112,14 @@ def layer_brute_force(inp, logits: np.ndarray, tokens=None, round_h: bool = True
                                 for w in (inp.sh_gate, inp.sh_up, inp.sh_down))
         return cache["sh"]
 
+    gate_w = None
+    if getattr(inp, "shared_gate", None) is not None:
+        gate_w = bf16_decode(inp.shared_gate)
     ys, ids, ws = [], [], []
     for t in tokens:
         xt = bf16_decode(inp.x[t])
         y, chosen, w = token_output(xt, np.asarray(logits[t], dtype=np.float32).astype(np.float64),
-                                    inp.k, experts, shared, round_h)
+                                    inp.k, experts, shared, round_h, gate_w)
         ys.append(y)
         ids.append(chosen)
         ws.append(w)

@@ -38,7 +38,14 @@ reorders this work). Page references are to the three pages on the subject:
  10. shared expert   the same FFN on every token with weight 1
                      (P1 Technical Details, Model bullet: one shared expert
                      besides the 8 routed ones; reading: added ungated)
- 11. combine         y[t] = bf16(sum_j w[t,j] Y[row_of_pair[t*k+j]] + S[t])
+ 10'. gated variant  optional: with a gate vector w_sg (bf16 [H]) the shared
+                     expert's output of token t is scaled by
+                     g[t] = sigmoid(x[t] . w_sg), exact in fp64 (reading: the
+                     pages do not say how the shared expert is weighted; a
+                     sigmoid gate from the token's activations is the common
+                     form of a gated shared expert)
+ 11. combine         y[t] = bf16(sum_j w[t,j] Y[row_of_pair[t*k+j]] + g[t] S[t]),
+                     g[t] = 1 for the ungated layer
 
 Only h and y are rounded (to bf16, round-to-nearest-even); everything else is
 exact fp64. Routing can be driven from caller-supplied fp32 logits so that the
@@ -190,6 +197,14 @@ def swiglu_ffn(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
     return h @ wd.T
 
 
+def shared_gate(inp, x: np.ndarray) -> np.ndarray:
+    """Per-token factor of the shared expert: 1, or sigmoid(x . w_sg) in fp64 (step 10')."""
+    if getattr(inp, "shared_gate", None) is None:
+        return np.ones(x.shape[0])
+    z = x @ bf16_bits_to_f64(inp.shared_gate)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
 def expert_weights(w, e: int):
     """fp64 dequantised matrix of expert e from a Q4Weights-like stack."""
     return dequant_q4(w.q[e], w.s[e], w.b[e])
@@ -219,7 +234,7 @@ def moe_layer(inp, logits: Optional[np.ndarray] = None, block_rows: int = 64,
     S = swiglu_ffn(x, expert_weights(inp.sh_gate, 0), expert_weights(inp.sh_up, 0),
                    expert_weights(inp.sh_down, 0), round_h)
     rop = tabs["row_of_pair"].reshape(T, k)
-    y = S.copy()
+    y = shared_gate(inp, x)[:, None] * S
     for j in range(k):
         y += w[:, j:j + 1] * Y[rop[:, j]]
     y_out = round_bf16(y) if round_y else y
@@ -240,7 +255,7 @@ def moe_layer_tokens(inp, tokens: Sequence[int], logits: np.ndarray,
     ids, w = select_topk(l, inp.k)
     x = bf16_bits_to_f64(inp.x[tokens])
     sh = (expert_weights(inp.sh_gate, 0), expert_weights(inp.sh_up, 0), expert_weights(inp.sh_down, 0))
-    y = swiglu_ffn(x, *sh, round_h=round_h)
+    y = shared_gate(inp, x)[:, None] * swiglu_ffn(x, *sh, round_h=round_h)
     for e in np.unique(ids):
         mats = (expert_weights(inp.gate, e), expert_weights(inp.up, e), expert_weights(inp.down, e))
         rows, slots = np.nonzero(ids == e)

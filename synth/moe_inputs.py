@@ -22,7 +22,9 @@ Recipe (numpy PCG64 ``default_rng(seed)``, draws in this order):
      b = -8 s (exact in bf16) or, for the "random" bias mode,
      b = bf16(-s * U(0, 15)).
   4. optional logit bias (a Zipf(1.2) skew over expert index):
-     beta[e] = -1.2 * ln(e + 1) as float32.
+     beta[e] = -1.2 * ln(e + 1) as float32 (no draw).
+  5. optional shared-expert gate vector (gated_shared=True), drawn last so that
+     every earlier draw is unchanged: shared_gate = bf16(N(0, 1) / sqrt(H)) [H].
 """
 from __future__ import annotations
 
@@ -74,6 +76,7 @@ class MoEInputs:
     sh_down: Q4Weights         # n=1, [H, I]
     seed: int = 0
     bias_mode: str = "sym"
+    shared_gate: Optional[np.ndarray] = None   # uint16 [H] or None (ungated shared expert)
 
 
 def _to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -103,7 +106,8 @@ def _draw_q4(rng: np.random.Generator, n: int, N: int, K: int, bias_mode: str) -
 
 
 def make_layer(T: int, H: int, I: int, E: int, k: int, seed: int = 0,
-               bias_mode: str = "sym", zipf: Optional[float] = None) -> MoEInputs:
+               bias_mode: str = "sym", zipf: Optional[float] = None,
+               gated_shared: bool = False) -> MoEInputs:
     """Draw one MoE layer's inputs in the documented order."""
     if not (1 <= k <= E):
         raise ValueError("need 1 <= k <= E")
@@ -119,9 +123,10 @@ def make_layer(T: int, H: int, I: int, E: int, k: int, seed: int = 0,
     logit_bias = None
     if zipf is not None:
         logit_bias = (-float(zipf) * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)
+    shared_gate = _to_bf16_bits(rng.standard_normal(H) / math.sqrt(H)) if gated_shared else None
     return MoEInputs(T=T, H=H, I=I, E=E, k=k, x=x, router_w=router_w, logit_bias=logit_bias,
                      gate=gate, up=up, down=down, sh_gate=sh_gate, sh_up=sh_up, sh_down=sh_down,
-                     seed=seed, bias_mode=bias_mode)
+                     seed=seed, bias_mode=bias_mode, shared_gate=shared_gate)
 
 
 def redraw_token_rows(inp: MoEInputs, rows: np.ndarray, seed: int) -> None:

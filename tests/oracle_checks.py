@@ -267,7 +267,9 @@ def check_brute(om, cfg=dict(T=64, H=256, I=128, E=16, k=2), seeds=(0,), modes=(
 def check_layer_tokens(om, cases=(dict(T=64, H=256, I=128, E=16, k=2, seed=0, bias_mode="random"),
                                   dict(T=24, H=128, I=64, E=4, k=4, seed=1, bias_mode="random"),
                                   dict(T=12, H=128, I=64, E=64, k=32, seed=2, bias_mode="random"),
-                                  dict(T=48, H=256, I=128, E=16, k=2, seed=3, bias_mode="sym", zipf=1.2))):
+                                  dict(T=48, H=256, I=128, E=16, k=2, seed=3, bias_mode="sym", zipf=1.2),
+                                  dict(T=32, H=256, I=128, E=16, k=4, seed=4, bias_mode="random",
+                                       gated_shared=True))):
     """The per-token oracle (``moe_layer_tokens``, the reference for sampled and
     decode-shaped layer checks) against the independent per-token brute force
     and against the sort-based layer on the same logits: tiny, k = E, k = 32,
@@ -290,6 +292,36 @@ def check_layer_tokens(om, cases=(dict(T=64, H=256, I=128, E=16, k=2, seed=0, bi
             assert err_f < 1e-14, f"per-token oracle differs from the layer oracle: rel {err_f:.3g}"
 
 
+def check_gated_shared(om):
+    """The gated shared expert: against the independent brute force (scipy's
+    expit of a math.fsum dot product), and against two closed forms on the
+    dense special case E = k = 1 with the shared expert equal to the routed
+    one: a zero gate vector gives the factor 1/2 exactly, so y = 1.5 * FFN(x);
+    a one-hot gate vector e_0 gives y = (1 + sigmoid(x_0)) * FFN(x), with the
+    FFN and the sigmoid from torch in fp64."""
+    for cfg in (dict(T=40, H=256, I=128, E=16, k=2, seed=5, bias_mode="random"),
+                dict(T=24, H=128, I=64, E=8, k=8, seed=6, bias_mode="sym", zipf=1.2)):
+        inp = make_layer(gated_shared=True, **cfg)
+        out = om.moe_layer(inp)
+        l_ref = brute_force_logits(inp)
+        yb, _, _ = brute_force.layer_brute_force(inp, l_ref)
+        err = np.linalg.norm(out["y_unrounded"] - yb) / np.linalg.norm(yb)
+        assert err < 1e-12, f"gated layer differs from the per-token brute force: rel {err:.3g}"
+    inp = _one_expert_layer(seed=31)
+    xb = torch.tensor(inp.x.astype(np.int16)).view(torch.bfloat16).double()
+
+    def deq(w):
+        return torch.tensor(brute_force.dequant_bytes(w.q[0], w.s[0], w.b[0]))
+    ffn = (torch.nn.functional.silu(xb @ deq(inp.gate).T) * (xb @ deq(inp.up).T)) @ deq(inp.down).T
+    inp.shared_gate = np.zeros(inp.H, np.uint16)
+    y = torch.tensor(om.moe_layer(inp, round_h=False, round_y=False)["y"])
+    assert float((y - 1.5 * ffn).abs().max() / ffn.abs().max()) < 1e-13, "zero gate vector: factor is not 1/2"
+    inp.shared_gate = _bits_of(np.eye(1, inp.H, 0, dtype=np.float32)[0])
+    y = torch.tensor(om.moe_layer(inp, round_h=False, round_y=False)["y"])
+    want = (1.0 + torch.sigmoid(xb[:, :1])) * ffn
+    assert float((y - want).abs().max() / want.abs().max()) < 1e-13, "one-hot gate vector"
+
+
 def brute_force_logits(inp):
     """Router logits computed token by token with Python floats -> fp64 dot -> fp32."""
     x = brute_force.bf16_decode(inp.x)
@@ -304,4 +336,5 @@ def brute_force_logits(inp):
 
 
 ALL_CHECKS = [check_bf16, check_unpack, check_dequant, check_logits, check_topk, check_golden_routing,
-              check_routing_invariants, check_dense_ffn, check_integer_ffn, check_brute, check_layer_tokens]
+              check_routing_invariants, check_dense_ffn, check_integer_ffn, check_brute, check_layer_tokens,
+               check_gated_shared]

@@ -139,6 +139,24 @@ def _tokens_no_shared(inp, tokens, logits, round_h=True):
     return _real_layer_tokens(zeroed, tokens, logits, round_h)
 
 
+_real_shared_gate = om.shared_gate
+
+
+def _gate_sign_flipped(inp, x):
+    g = _real_shared_gate(inp, x)
+    return g if getattr(inp, "shared_gate", None) is None else 1.0 - g
+
+
+def _gate_ignored(inp, x):
+    return np.ones(x.shape[0])
+
+
+def _gate_without_sigmoid(inp, x):
+    if getattr(inp, "shared_gate", None) is None:
+        return np.ones(x.shape[0])
+    return x @ om.bf16_bits_to_f64(inp.shared_gate)
+
+
 MUTANTS = {
     "nibble order": ("unpack_q4", _unpack_high_first),
     "bias dropped": ("dequant_q4", _dequant_no_bias),
@@ -155,6 +173,9 @@ MUTANTS = {
     "per-token oracle: slot weights swapped": ("moe_layer_tokens", _tokens_slot_weights_swapped),
     "per-token oracle: expert index off by one": ("moe_layer_tokens", _tokens_expert_off_by_one),
     "per-token oracle: shared expert dropped": ("moe_layer_tokens", _tokens_no_shared),
+    "shared gate: 1 - sigmoid": ("shared_gate", _gate_sign_flipped),
+    "shared gate ignored": ("shared_gate", _gate_ignored),
+    "shared gate without the sigmoid": ("shared_gate", _gate_without_sigmoid),
 }
 
 
