@@ -39,9 +39,12 @@ extern "C" {
 
 /* Weights per quantisation group along the reduction dimension. */
 #define MOE_Q4_GROUP 64
-/* Rows per GEMM tile; tile maps passed to moe_grouped_gemm_q4 and built for
- * moe_layer_forward use this block size. */
+/* Rows per GEMM tile of moe_grouped_gemm_q4's tile maps, and the default tile
+ * height of moe_layer_forward (dims.block_rows = 0). */
 #define MOE_GEMM_BLOCK_ROWS 128
+/* Bytes at the start of a moe_layer_forward workspace that must be zero
+ * before the first layer call; every layer call leaves them zero. */
+#define MOE_WORKSPACE_HEAD_BYTES 8448
 /* Largest supported expert count and top-k. */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
@@ -147,8 +150,12 @@ int32_t moe_max_tiles(const moe_dims* dims);
  *
  *   A           device bf16 [a_rows][K]
  *   W0, W1      host structs; W1 only for SWIGLU (same n_experts, N, K as W0),
- *               K % 128 == 0, K <= 2048; N % 64 == 0 (SWIGLU) or N % 128 == 0 (STORE_F32);
- *               q, s and b 16-byte aligned
+ *               K % 64 == 0 (else MOE_ERR_SHAPE) with an even number of 64-wide
+ *               groups, K % 128 == 0 (else MOE_ERR_UNSUPPORTED: scale/bias words
+ *               are read two groups at a time); N % 64 == 0 (SWIGLU) or
+ *               N % 128 == 0 (STORE_F32); q, s and b 16-byte aligned
+ *   a_rows      rows of A; a_rows * K * 2 must stay below 2^31 (A is addressed
+ *               with 32-bit byte offsets), else MOE_ERR_UNSUPPORTED
  *   offsets, tile_map, num_tiles  device, as produced by moe_route with
  *               block_rows = MOE_GEMM_BLOCK_ROWS; max_tiles bounds *num_tiles
  *   workspace   device, at least moe_gemm_workspace_bytes(a_rows, K) bytes
@@ -181,19 +188,27 @@ size_t moe_gemm_workspace_bytes(int32_t a_rows, int32_t K);
  *   gate, up     host structs, n_experts = E, N = I, K = H
  *   down         host struct,  n_experts = E, N = H, K = I
  *   sh_gate, sh_up, sh_down  the shared expert, n_experts = 1, same shapes
- *   dims         host; H % 128 == 0, I % 128 == 0, H and I <= 2048,
- *                block_rows = 0 or MOE_GEMM_BLOCK_ROWS
+ *   dims         host; H % 64 == 0 and I % 64 == 0 (else MOE_ERR_SHAPE);
+ *                an odd number of 64-wide groups in H or I returns
+ *                MOE_ERR_UNSUPPORTED (the grouped GEMM reads scale/bias words
+ *                two groups at a time); block_rows = 0 (MOE_GEMM_BLOCK_ROWS),
+ *                32, 64 or 128 rows per routed tile (others:
+ *                MOE_ERR_UNSUPPORTED); T*H*2, T*(k+1)*I*2 and E*H*2 bytes must
+ *                stay below 2^31 (operands addressed with 32-bit byte offsets),
+ *                else MOE_ERR_UNSUPPORTED
  *   y            device bf16 [T][H]
  *   logits_out   device float [T][E] or NULL: the logits routing used (biased)
  *   topk_ids_out device int32 [T][k] or NULL
  *   topk_w_out   device float [T][k] or NULL
  *   workspace    device, at least moe_workspace_bytes(dims) bytes. Its first
- *                256 bytes hold a completion counter that calls with
- *                T <= 4 use to run routing as one launch: they must be zero
- *                before the first layer call (allocate the workspace zeroed)
- *                and every layer call leaves them zero. moe_route never
- *                touches them; any other use of the buffer must zero them
- *                again before it serves a layer call.
+ *                MOE_WORKSPACE_HEAD_BYTES bytes hold a completion counter and
+ *                per-(token, expert) logit slots that calls with T <= 4 use to
+ *                run routing as one launch: they must be zero before the
+ *                first layer call (allocate the workspace zeroed) and every
+ *                layer call leaves them zero. moe_route never touches them;
+ *                any other use of the buffer must zero them again before it
+ *                serves a layer call. Calls that share a workspace must not
+ *                run concurrently.
  */
 int moe_layer_forward(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
                       const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,
@@ -201,6 +216,46 @@ int moe_layer_forward(const uint16_t* x, const uint16_t* router_w, const float* 
                       const moe_q4_weights* sh_down, const moe_dims* dims, uint16_t* y,
                       float* logits_out, int32_t* topk_ids_out, float* topk_w_out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Options of moe_layer_forward_ex (host struct; every field may be 0/NULL). */
+typedef struct {
+    /* device bf16 [H] or NULL. When given, the shared expert's output of token
+     * t is scaled by g[t] = sigmoid(x[t] . shared_gate) (fp32 dot product and
+     * logistic function), so y[t] = bf16(sum_j w[t][j] Y[t][j] + g[t] S[t]).
+     * The pages name one shared expert beside the routed ones (page
+     * "Perplexity Open Sources Lily ...", Technical Details, Model bullet) but
+     * not how it is weighted; this gated form is an option, off by default.
+     * 16-byte aligned. */
+    const uint16_t* shared_gate;
+    /* hipStream_t or NULL. When given, the shared expert's tiles (which need
+     * no routing) run on this stream while the main stream routes; the main
+     * stream waits for them before the combine. The page's single command
+     * buffer and concurrent decode pass ("Perplexity Open Sources Lily ...",
+     * Technical Details, prefill and decode bullets) in HIP stream form. The
+     * side stream must be a different stream of the same device, at the
+     * default priority. */
+    void* side_stream;
+    /* hipEvent_t handles created by the caller (no timing needed), required
+     * with side_stream: fork_event is recorded on the main stream and waited
+     * for on the side stream, join_event the other way round. */
+    void* fork_event;
+    void* join_event;
+} moe_layer_options;
+
+/*
+ * moe_layer_forward_ex - moe_layer_forward with options (opts may be NULL,
+ * which is moe_layer_forward). Same arguments, results and errors; in
+ * addition MOE_ERR_ALIGN for a misaligned shared_gate and MOE_ERR_NULL for a
+ * side stream without both events. The call may be captured in a HIP graph
+ * on the main stream (the side stream forks from and joins back into it).
+ */
+int moe_layer_forward_ex(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
+                         const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,
+                         const moe_q4_weights* sh_gate, const moe_q4_weights* sh_up,
+                         const moe_q4_weights* sh_down, const moe_dims* dims, uint16_t* y,
+                         float* logits_out, int32_t* topk_ids_out, float* topk_w_out,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         const moe_layer_options* opts);
 
 /* Number of stage boundaries moe_layer_forward_timed can mark. */
 #define MOE_LAYER_STAGE_EVENTS 6

@@ -27,6 +27,7 @@ MOE_Q4_GROUP = 64
 MOE_GEMM_BLOCK_ROWS = 128
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
+MOE_WORKSPACE_HEAD_BYTES = 8448
 
 
 class MoeDims(ctypes.Structure):
@@ -37,6 +38,11 @@ class MoeDims(ctypes.Structure):
 class MoeQ4Weights(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("b", ctypes.c_void_p),
                 ("n_experts", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
+
+
+class MoeLayerOptions(ctypes.Structure):
+    _fields_ = [("shared_gate", ctypes.c_void_p), ("side_stream", ctypes.c_void_p),
+                ("fork_event", ctypes.c_void_p), ("join_event", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -55,6 +61,8 @@ SIGNATURES = {
     "moe_grouped_gemm_q4": (ctypes.c_int, [_P, _I32, _P, _I32, _W, _W, _P, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
     "moe_gemm_workspace_bytes": (_SZ, [_I32, _I32]),
     "moe_layer_forward": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward_ex": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ, _P,
+                                            ctypes.POINTER(MoeLayerOptions)]),
     "moe_layer_forward_timed": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ,
                                                _P, ctypes.POINTER(ctypes.c_void_p), _I32]),
     "moe_quantize_q4": (ctypes.c_int, [_P, ctypes.c_int64, _I32, _P, _P, _P, _P]),

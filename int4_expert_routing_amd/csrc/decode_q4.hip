@@ -249,6 +249,7 @@ void decode_swiglu_kernel(GemmArgs a, const u32x4* tile_desc, int nrmax) {
     for (int j = 0; j < a.shared_rows; ++j) ti.tok |= uint32_t(j) << (4 * j);
   } else {
     const int i = tile - a.n_shared_tiles;
+    if (!a.routed_tiles) return;
     const int nt = *a.num_tiles;
     const u32x4 d = tile_desc[i];   // in bounds for every launched tile; used only if i < nt
     if (i >= nt) return;
@@ -302,9 +303,28 @@ __global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(D
   uint8_t* xs = wl;                                                     // the pair's h row
   float* Xt = reinterpret_cast<float*>(wl + dec_row_bytes(K));          // its group sums
   float* red = reinterpret_cast<float*>(smem + W * dc_wave_bytes(K));   // [W][16]
+  float* sred = red + W * 16;                                           // [W][16] gated shared pair
+  float* gpart = sred + W * 16;                                         // [W] gate partial sums
   const uint32_t nib = kNib, magic = kMagic;
+  const bool gated = a.shared_gate != nullptr;
 
-  float tot = 0.0f;
+  // gated shared expert: this thread's part of x_t . w_sg (added in a fixed
+  // order after the pairs); the shared pair then enters with weight g
+  if (gated) {
+    float d = 0.0f;
+    for (int c = tid * 8; c < a.N; c += W * 64 * 8) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + size_t(t) * a.N + c);
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(a.shared_gate + c);
+      d = dot2(xv.x, wv.x, d);
+      d = dot2(xv.y, wv.y, d);
+      d = dot2(xv.z, wv.z, d);
+      d = dot2(xv.w, wv.w, d);
+    }
+    d = wave_sum_f32(d);
+    if (lane == 0) gpart[wave] = d;
+  }
+
+  float tot = 0.0f, sacc = 0.0f;
   for (int j = wave; j <= a.k; j += W) {
     const bool routed = j < a.k;
     const size_t f = size_t(t) * a.k + (routed ? j : 0);
@@ -361,13 +381,27 @@ __global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(D
     }
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);
-    tot = __builtin_fmaf(wj, acc, tot);
+    if (routed || !gated)
+      tot = __builtin_fmaf(wj, acc, tot);
+    else
+      sacc = acc;
   }
-  if (lane < 16) red[wave * 16 + lane] = tot;
+  if (lane < 16) {
+    red[wave * 16 + lane] = tot;
+    sred[wave * 16 + lane] = sacc;
+  }
   __syncthreads();
   if (tid < 16) {
     float sum = 0.0f;
     for (int i = 0; i < W; ++i) sum += red[i * 16 + tid];
+    if (gated) {
+      float z = 0.0f, sv = 0.0f;
+      for (int i = 0; i < W; ++i) {
+        z += gpart[i];
+        sv += sred[i * 16 + tid];
+      }
+      sum = __builtin_fmaf(1.0f / (1.0f + expf(-z)), sv, sum);
+    }
     a.y[size_t(t) * a.N + col0 + tid] = uint16_t(f32_to_bf16_rne(sum));
   }
 }
@@ -382,7 +416,7 @@ hipError_t launch_decode_down_combine(const DownCombineArgs& da, hipStream_t str
   if (da.T == 0) return hipSuccess;
   const int W = da.k + 1 < kDcMaxWaves ? da.k + 1 : kDcMaxWaves;
   const dim3 grid(unsigned(da.T) * unsigned(da.N / 16)), block(unsigned(W) * 64u);
-  const size_t lds = size_t(W) * dc_wave_bytes(da.K) + size_t(W) * 16 * 4;
+  const size_t lds = size_t(W) * dc_wave_bytes(da.K) + size_t(W) * (2 * 16 + 1) * 4;
   switch (da.K / 128) {
     case 2: hipLaunchKernelGGL(decode_down_combine_kernel<2>, grid, block, lds, stream, da); break;
     case 4: hipLaunchKernelGGL(decode_down_combine_kernel<4>, grid, block, lds, stream, da); break;

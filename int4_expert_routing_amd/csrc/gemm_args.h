@@ -5,8 +5,6 @@
 
 namespace moe {
 
-constexpr int kMaxK = 2048;  // largest reduction size of the grouped GEMM (LDS budget)
-
 // One stack of 4-bit matrices [n][N][K/8] with bf16 scale/bias [n][N][K/64].
 struct QStack {
   const uint32_t* q;
@@ -27,9 +25,11 @@ struct GemmArgs {
   QStack w1[2];             // up projection (SwiGLU epilogues only)
   int E;                    // a tile whose expert is E uses the shared stack
   const int32_t* offsets;
-  const int32_t* tile_map;
+  const int32_t* tile_map;  // (expert, first row) of each routed tile of at most bm rows
   const int32_t* num_tiles;
-  int n_shared_tiles;       // the first n_shared_tiles tiles cover the shared rows
+  int bm;                   // rows per routed tile (32, 64 or kBlockRows)
+  int n_shared_tiles;       // the first n_shared_tiles tiles cover the shared rows, kBlockRows each
+  int routed_tiles;         // 1: the routed tiles of the block map follow them; 0: shared tiles only
   int shared_rows;
   int N, K, NT;             // NT = column tiles per row tile
   void* out;                // f32 [rows][N], or bf16 [rows][N]

@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   // within a chunk the column slices of a tile are consecutive. So every
   // column slice of a row tile reads the activation rows from the same L2, and
   // consecutive tiles of one expert share its weights in that L2.
-  const int ntot = a.n_shared_tiles + *a.num_tiles;
+  const int ntot = a.n_shared_tiles + (a.routed_tiles ? *a.num_tiles : 0);
   const int chunk = (ntot + 7) >> 3;
   const int xcd = blockIdx.x & 7;
   const int j = blockIdx.x >> 3;

@@ -25,10 +25,10 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int tile, TileInfo&
     return true;
   }
   const int i = tile - a.n_shared_tiles;
-  if (i >= *a.num_tiles) return false;
+  if (!a.routed_tiles || i >= *a.num_tiles) return false;
   ti.e = a.tile_map[2 * i];
   ti.r0 = a.tile_map[2 * i + 1];
-  ti.r1 = min(ti.r0 + kBlockRows, a.offsets[ti.e + 1]);
+  ti.r1 = min(ti.r0 + a.bm, a.offsets[ti.e + 1]);
   return true;
 }
 

@@ -7,6 +7,7 @@ namespace moe {
 namespace {
 
 constexpr size_t kAlign = 256;
+static_assert(kHandoffBytes == MOE_WORKSPACE_HEAD_BYTES, "workspace head size in the header");
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -42,7 +43,7 @@ LayerLayout layer_layout(const moe_dims& d) {
   LayerLayout L;
   // completion counter of the one-launch routing (few tokens): kept at
   // offset 0 for every T, zero before a call and after it
-  L.done = c.take(T > 0 ? 256 : 0);
+  L.done = c.take(T > 0 ? kHandoffBytes : 0);
   L.logits = c.take(T * E * 4);
   const int ks = router_splits(d.T, d.H, d.E);
   L.logit_parts = c.take(size_t(ks > 1 ? ks : 0) * T * E * 4);
@@ -77,13 +78,26 @@ int check_route_dims(const moe_dims* d) {
   return MOE_OK;
 }
 
+// The GEMM and router kernels address their activation operands through
+// buffer descriptors with 32-bit byte offsets: every such operand must stay
+// below 2 GiB.
+constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
+
 int check_layer_dims(const moe_dims* d) {
   const int st = check_route_dims(d);
   if (st != MOE_OK) return st;
-  if (d->H < 128 || d->I < 128 || d->H % 128 != 0 || d->I % 128 != 0) return MOE_ERR_SHAPE;
-  if (d->H > kMaxK || d->I > kMaxK) return MOE_ERR_UNSUPPORTED;
-  if (d->block_rows != 0 && d->block_rows != kBlockRows) return MOE_ERR_UNSUPPORTED;
+  if (d->H < 64 || d->I < 64 || d->H % 64 != 0 || d->I % 64 != 0) return MOE_ERR_SHAPE;
+  // the grouped GEMM loads scale/bias words and group-sum entries two groups
+  // at a time: the reduction sizes need an even number of 64-wide groups
+  if (d->H % 128 != 0 || d->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->block_rows != 0 && d->block_rows != 32 && d->block_rows != 64 && d->block_rows != kBlockRows)
+    return MOE_ERR_UNSUPPORTED;
   if (int64_t(d->T) * (d->k + 1) * d->H > (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  // x (router, activation prep), h (down GEMM) and W_r within 32-bit offsets
+  const int64_t rows = int64_t(d->T) * (d->k + 1);
+  if (int64_t(d->T) * d->H * 2 >= kMaxOperandBytes || rows * d->I * 2 >= kMaxOperandBytes ||
+      int64_t(d->E) * d->H * 2 >= kMaxOperandBytes)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -193,8 +207,9 @@ int moe_grouped_gemm_q4(const uint16_t* A, int32_t a_rows, const int32_t* sorted
   if (a_rows < 0 || max_tiles < 0) return MOE_ERR_SHAPE;
   if (sorted_rows && row_div < 1) return MOE_ERR_SHAPE;
   const int n = W0->n_experts, N = W0->N, K = W0->K;
-  if (n < 1 || N < 1 || K < 2 * kGroup || K % (2 * kGroup)) return MOE_ERR_SHAPE;
-  if (K > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (n < 1 || N < 1 || K < kGroup || K % kGroup) return MOE_ERR_SHAPE;
+  if (K % (2 * kGroup)) return MOE_ERR_UNSUPPORTED;   // an even number of 64-wide groups
+  if (int64_t(a_rows) * K * 2 >= kMaxOperandBytes) return MOE_ERR_UNSUPPORTED;
   int st = check_weights(W0, n, N, K);
   if (st != MOE_OK) return st;
   if (epilogue == MOE_EPI_SWIGLU_BF16) {
@@ -226,7 +241,9 @@ int moe_grouped_gemm_q4(const uint16_t* A, int32_t a_rows, const int32_t* sorted
   ga.offsets = offsets;
   ga.tile_map = tile_map;
   ga.num_tiles = num_tiles;
+  ga.bm = kBlockRows;
   ga.n_shared_tiles = 0;
+  ga.routed_tiles = 1;
   ga.shared_rows = 0;
   ga.N = N;
   ga.K = K;
@@ -247,7 +264,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
                               const moe_q4_weights* sh_gate, const moe_q4_weights* sh_up,
                               const moe_q4_weights* sh_down, const moe_dims* dims, uint16_t* y, float* logits_out,
                               int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
-                              void* stream, void* const* events, int n_events) {
+                              void* stream, void* const* events, int n_events, const moe_layer_options* opts) {
   int st = check_layer_dims(dims);
   if (st != MOE_OK) return st;
   const moe_dims d = *dims;
@@ -266,7 +283,10 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   if (n_events < 0 || (n_events > 0 && !events)) return MOE_ERR_NULL;
   for (int i = 0; i < n_events; ++i)
     if (!events[i]) return MOE_ERR_NULL;
-  if (d.T == 0) return MOE_OK;
+  const uint16_t* shared_gate = opts ? opts->shared_gate : nullptr;
+  hipStream_t s2 = opts ? static_cast<hipStream_t>(opts->side_stream) : nullptr;
+  if (shared_gate && !aligned16(shared_gate)) return MOE_ERR_ALIGN;
+  if (s2 && (!opts->fork_event || !opts->join_event)) return MOE_ERR_NULL;
   const LayerLayout L = layer_layout(d);
   if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -275,10 +295,20 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   auto mark = [&](int i) -> bool {
     return i >= n_events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
   };
+  // the side stream waits for everything enqueued on the main stream so far
+  auto fork = [&]() -> bool {
+    return hipEventRecord(static_cast<hipEvent_t>(opts->fork_event), s) == hipSuccess &&
+           hipStreamWaitEvent(s2, static_cast<hipEvent_t>(opts->fork_event), 0) == hipSuccess;
+  };
+  // the main stream waits for everything enqueued on the side stream
+  auto join = [&]() -> bool {
+    return hipEventRecord(static_cast<hipEvent_t>(opts->join_event), s2) == hipSuccess &&
+           hipStreamWaitEvent(s, static_cast<hipEvent_t>(opts->join_event), 0) == hipSuccess;
+  };
   if (!mark(0)) return MOE_ERR_HIP;
   const int T = d.T, E = d.E, k = d.k, H = d.H, I = d.I;
   const int nblk = ceil_div(T, kRouteTokens);
-  const int bm = kBlockRows;
+  const int bm = d.block_rows > 0 ? d.block_rows : kBlockRows;   // routed tile height
 
   // few tokens: every tile has at most kDecodeMaxRows rows, and the weight
   // stream, not the MFMA, bounds the layer (decode-shaped kernels, which read x
@@ -290,6 +320,82 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   uint16_t* x_perm = at<uint16_t>(ws, L.x_perm);
   uint16_t* x_part = at<uint16_t>(ws, L.x_part);
   if ((!decode && launch_prep_rows(x, T, H, x_perm, x_part, s) != hipSuccess) || !mark(1)) return MOE_ERR_HIP;
+
+  // gate/up arguments: routed tiles + shared-expert tiles
+  const int routed_rows = T * k;
+  const int n_sh = ceil_div(T, kBlockRows);   // the shared expert's rows in full-height tiles
+  const int max_routed = int(max_tiles_of(T, E, k, bm));
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* tile_map = at<int32_t>(ws, L.tile_map);
+  int32_t* num_tiles = at<int32_t>(ws, L.num_tiles);
+  int32_t* sorted_rows = at<int32_t>(ws, L.sorted_rows);
+  int32_t* row_of_pair = at<int32_t>(ws, L.row_of_pair);
+  u32x4* tile_desc = at<u32x4>(ws, L.tile_desc);
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  uint16_t* h_part = at<uint16_t>(ws, L.h_part);
+  GemmArgs g1{};
+  g1.A = decode ? x : x_perm;
+  g1.Apart = x_part;
+  g1.sorted_rows = sorted_rows;
+  g1.row_div = k;
+  g1.routed_rows = routed_rows;
+  g1.shared_src_base = routed_rows;
+  g1.w0[0] = stack_of(gate);
+  g1.w0[1] = stack_of(sh_gate);
+  g1.w1[0] = stack_of(up);
+  g1.w1[1] = stack_of(sh_up);
+  g1.E = E;
+  g1.offsets = offsets;
+  g1.tile_map = tile_map;
+  g1.num_tiles = num_tiles;
+  g1.bm = bm;
+  g1.n_shared_tiles = decode ? 1 : n_sh;   // decode: the shared expert's T rows form one tile
+  g1.routed_tiles = 1;
+  g1.shared_rows = T;
+  g1.N = I;
+  g1.K = H;
+  g1.NT = decode ? I / 16 : I / 128;
+  g1.out = h;
+  g1.out_part = h_part;
+  // down arguments (prefill): fp32 rows of every routed and shared row
+  float* Y = at<float>(ws, L.Y);
+  GemmArgs g2 = g1;
+  g2.A = h;
+  g2.Apart = h_part;
+  g2.sorted_rows = nullptr;
+  g2.row_div = 1;
+  g2.shared_src_base = 0;
+  g2.w0[0] = stack_of(down);
+  g2.w0[1] = stack_of(sh_down);
+  g2.w1[0] = g2.w0[0];
+  g2.w1[1] = g2.w0[1];
+  g2.N = H;
+  g2.K = I;
+  g2.NT = ceil_div(H, 256);
+  g2.out = Y;
+  g2.out_part = nullptr;
+
+  // Side stream: the shared expert needs no routing, so its tiles run there
+  // while the main stream routes (after the activation prep, which both read);
+  // the main stream then runs only the routed tiles and joins before the
+  // combine.
+  if (s2) {
+    if (!fork()) return MOE_ERR_HIP;
+    GemmArgs s1 = g1;
+    s1.routed_tiles = 0;
+    if (decode) {
+      if (launch_decode(s1, tile_desc, 1, T, s2) != hipSuccess) return MOE_ERR_HIP;
+    } else {
+      GemmArgs s2a = g2;
+      s2a.routed_tiles = 0;
+      if (launch_gemm(s1, kEpiSwigluInternal, n_sh, s2) != hipSuccess ||
+          launch_gemm(s2a, kEpiF32, n_sh, s2) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
+    g1.n_shared_tiles = 0;
+    g2.n_shared_tiles = 0;
+    g1.shared_rows = 0;
+  }
 
   // 2-4. router GEMM, top-k, histogram, scan, scatter, block map
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
@@ -308,82 +414,37 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   ra.H = H;
   ra.E = E;
   ra.k = k;
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* tile_map = at<int32_t>(ws, L.tile_map);
-  int32_t* num_tiles = at<int32_t>(ws, L.num_tiles);
-  int32_t* sorted_rows = at<int32_t>(ws, L.sorted_rows);
-  int32_t* row_of_pair = at<int32_t>(ws, L.row_of_pair);
   ScanArgs sa{ra.block_counts, at<int32_t>(ws, L.block_base), at<int32_t>(ws, L.counts), offsets, tile_map,
               num_tiles, nblk, E, bm};
   ScatterArgs ca{ids, sa.block_base, ra.rank_in_block, sorted_rows, row_of_pair, T, E, k};
-  u32x4* tile_desc = at<u32x4>(ws, L.tile_desc);
   ra.tile_desc = decode ? tile_desc : nullptr;
   ra.done = at<int32_t>(ws, L.done);
+  ra.slots = at<uint64_t>(ws, L.done + 256);
   if (launch_route(ra, sa, ca, true, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
 
-  // 5. gate/up grouped GEMM with SwiGLU, routed tiles + shared-expert tiles
-  const int routed_rows = T * k;
-  const int n_sh = ceil_div(T, bm);
-  const int max_routed = int(max_tiles_of(T, E, k, bm));
-  uint16_t* h = at<uint16_t>(ws, L.h);
-  uint16_t* h_part = at<uint16_t>(ws, L.h_part);
-  GemmArgs g1{};
-  g1.A = x_perm;
-  g1.Apart = x_part;
-  g1.sorted_rows = sorted_rows;
-  g1.row_div = k;
-  g1.routed_rows = routed_rows;
-  g1.shared_src_base = routed_rows;
-  g1.w0[0] = stack_of(gate);
-  g1.w0[1] = stack_of(sh_gate);
-  g1.w1[0] = stack_of(up);
-  g1.w1[1] = stack_of(sh_up);
-  g1.E = E;
-  g1.offsets = offsets;
-  g1.tile_map = tile_map;
-  g1.num_tiles = num_tiles;
-  g1.n_shared_tiles = decode ? 1 : n_sh;   // decode: the shared expert's T rows form one tile
-  g1.shared_rows = T;
-  g1.N = I;
-  g1.K = H;
-  if (decode) g1.A = x;
-  g1.NT = decode ? I / 16 : I / 128;
-  g1.out = h;
-  g1.out_part = h_part;
-  const hipError_t e1 = decode ? launch_decode(g1, tile_desc, 1 + max_routed, T, s)
-                               : launch_gemm(g1, kEpiSwigluInternal, n_sh + max_routed, s);
+  // 5. gate/up grouped GEMM with SwiGLU
+  const int n_tiles1 = (decode ? g1.n_shared_tiles : (s2 ? 0 : n_sh)) + max_routed;
+  const hipError_t e1 = decode ? launch_decode(g1, tile_desc, n_tiles1, T, s)
+                               : launch_gemm(g1, kEpiSwigluInternal, n_tiles1, s);
   if (e1 != hipSuccess || !mark(3)) return MOE_ERR_HIP;
 
   // 6-7 (few tokens). down projection fused with the weighted combine
   if (decode) {
+    if (s2 && !join()) return MOE_ERR_HIP;
     const DownCombineArgs da{h, stack_of(down), stack_of(sh_down), ids, wts, row_of_pair, T, k, H, I,
-                             routed_rows, y};
+                             routed_rows, y, x, shared_gate};
     if (launch_decode_down_combine(da, s) != hipSuccess || !mark(4) || !mark(5)) return MOE_ERR_HIP;
     return MOE_OK;
   }
 
   // 6. down grouped GEMM (fp32 rows)
-  float* Y = at<float>(ws, L.Y);
-  GemmArgs g2 = g1;
-  g2.A = h;
-  g2.Apart = h_part;
-  g2.sorted_rows = nullptr;
-  g2.row_div = 1;
-  g2.shared_src_base = 0;
-  g2.w0[0] = stack_of(down);
-  g2.w0[1] = stack_of(sh_down);
-  g2.w1[0] = g2.w0[0];
-  g2.w1[1] = g2.w0[1];
-  g2.N = H;
-  g2.K = I;
-  g2.NT = ceil_div(H, 256);
-  g2.out = Y;
-  g2.out_part = nullptr;
-  const hipError_t e2 = launch_gemm(g2, kEpiF32, n_sh + max_routed, s);
+  const hipError_t e2 = launch_gemm(g2, kEpiF32, (s2 ? 0 : n_sh) + max_routed, s);
   if (e2 != hipSuccess || !mark(4)) return MOE_ERR_HIP;
 
-  // 7. weighted combine + shared expert, bf16 output
-  if (launch_combine(Y, wts, row_of_pair, T, k, H, routed_rows, y, s) != hipSuccess || !mark(5)) return MOE_ERR_HIP;
+  // 7. weighted combine + (gated) shared expert, bf16 output
+  if (s2 && !join()) return MOE_ERR_HIP;
+  if (launch_combine(Y, wts, row_of_pair, T, k, H, routed_rows, y, x, shared_gate, s) != hipSuccess || !mark(5))
+    return MOE_ERR_HIP;
   return MOE_OK;
 }
 
@@ -393,7 +454,17 @@ int moe_layer_forward(const uint16_t* x, const uint16_t* router_w, const float* 
                       const moe_dims* dims, uint16_t* y, float* logits_out, int32_t* topk_ids_out,
                       float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
   return layer_forward_impl(x, router_w, logit_bias, gate, up, down, sh_gate, sh_up, sh_down, dims, y, logits_out,
-                            topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, nullptr, 0);
+                            topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+int moe_layer_forward_ex(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
+                         const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,
+                         const moe_q4_weights* sh_gate, const moe_q4_weights* sh_up, const moe_q4_weights* sh_down,
+                         const moe_dims* dims, uint16_t* y, float* logits_out, int32_t* topk_ids_out,
+                         float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream,
+                         const moe_layer_options* opts) {
+  return layer_forward_impl(x, router_w, logit_bias, gate, up, down, sh_gate, sh_up, sh_down, dims, y, logits_out,
+                            topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, nullptr, 0, opts);
 }
 
 int moe_layer_forward_timed(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
@@ -403,7 +474,7 @@ int moe_layer_forward_timed(const uint16_t* x, const uint16_t* router_w, const f
                             int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
                             void* stream, void* const* events, int32_t n_events) {
   return layer_forward_impl(x, router_w, logit_bias, gate, up, down, sh_gate, sh_up, sh_down, dims, y, logits_out,
-                            topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, events, n_events);
+                            topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, events, n_events, nullptr);
 }
 
 int moe_quantize_q4(const uint16_t* w, int64_t rows, int32_t K, uint32_t* q, uint16_t* s, uint16_t* b,

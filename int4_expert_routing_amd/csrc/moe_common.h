@@ -10,6 +10,11 @@ constexpr int kGroup = 64;        // weights per quantisation group along K
 constexpr int kBlockRows = 128;   // rows per GEMM tile
 constexpr int kRouteTokens = 16;  // tokens per routing block (top-k, histogram, scatter)
 constexpr int kWave = 64;
+// Head of a layer workspace that must be zero before a call and that every
+// call leaves zero: the one-launch routing's completion counter (256 bytes)
+// and its 64-bit logit slots for up to kHandoffTokens tokens x 256 experts.
+constexpr int kHandoffTokens = 4;
+constexpr int kHandoffBytes = 256 + kHandoffTokens * 256 * 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -109,6 +114,37 @@ __device__ __forceinline__ void split3_bf16(float v, uint16_t& hi, uint16_t& mid
   hi = uint16_t(h);
   mid = uint16_t(m);
   lo = uint16_t(f32_to_bf16_rne(r2));
+}
+
+// Shared-expert gate of one token, g = sigmoid(x . w) in fp32, computed by a
+// whole workgroup (blockDim.x a multiple of 64, at most 1024 threads): thread i
+// takes the 8-element chunks i, i + blockDim.x, ... of H; the partial sums are
+// added in a fixed tree (lane exchanges, then the waves in order). Every
+// thread of the workgroup must call it; every thread gets g.
+// c + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (fp32). The pairs
+// are passed as plain 32-bit values: bit-casting a vector element expression
+// in place reads element 0 with this compiler.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float token_gate(const uint16_t* xt, const uint16_t* w, int H, float* red) {
+  float d = 0.0f;
+  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(xt + c);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + c);
+    d = dot2_bf16(xv.x, wv.x, d);
+    d = dot2_bf16(xv.y, wv.y, d);
+    d = dot2_bf16(xv.z, wv.z, d);
+    d = dot2_bf16(xv.w, wv.w, d);
+  }
+  d = wave_sum_f32(d);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = d;
+  __syncthreads();
+  float z = 0.0f;
+  for (int i = 0; i < int(blockDim.x >> 6); ++i) z += red[i];
+  return 1.0f / (1.0f + expf(-z));
 }
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }

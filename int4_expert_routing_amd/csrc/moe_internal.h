@@ -36,9 +36,11 @@ struct RouteArgs {
   // optional (finish only): per tile {expert, first row, rows, token ids of
   // its rows at 4 bits each}, for tiles of at most 8 rows
   u32x4* tile_desc;
-  // optional: a zeroed device counter; with it, routing from x for at most
-  // kRouteTokens tokens runs as one launch (and leaves the counter zero)
+  // optional: a zeroed device counter and zeroed logit slots
+  // [kHandoffTokens][kMaxExperts]; with them, routing from x for at most
+  // kHandoffTokens tokens runs as one launch (and leaves both zero)
   int32_t* done;
+  uint64_t* slots;
 };
 
 struct ScanArgs {
@@ -93,6 +95,8 @@ struct DownCombineArgs {
   const int32_t* row_of_pair; // [T][k]
   int T, k, N, K, shared_row0;
   uint16_t* y;                // bf16 [T][N]
+  const uint16_t* x;          // bf16 [T][N] layer input (for the shared-expert gate)
+  const uint16_t* shared_gate;  // bf16 [N] gate vector, or null (ungated shared expert)
 };
 bool decode_down_combine_supported(int N, int K);
 hipError_t launch_decode_down_combine(const DownCombineArgs& da, hipStream_t stream);
@@ -105,7 +109,10 @@ hipError_t launch_quantize(const uint16_t* w, long rows, int K, uint32_t* q, uin
 hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
                             hipStream_t stream);
 
+// x: bf16 [T][H] activations and shared_gate: bf16 [H] gate vector, or null
+// (ungated shared expert)
 hipError_t launch_combine(const float* Y, const float* w, const int32_t* row_of_pair, int T, int k, int H,
-                          int shared_row0, uint16_t* y, hipStream_t stream);
+                          int shared_row0, uint16_t* y, const uint16_t* x, const uint16_t* shared_gate,
+                          hipStream_t stream);
 
 }  // namespace moe

@@ -47,17 +47,21 @@ hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm
 }
 
 // ---------------------------------------------------------------------------
-// Weighted combine: y[t] = bf16(S[t] + sum_j w[t][j] * Y[row_of_pair[t*k+j]]),
-// summed in that order (shared row first, then j ascending) with fp32 FMAs.
+// Weighted combine: y[t] = bf16(g[t] S[t] + sum_j w[t][j] * Y[row_of_pair[t*k+j]]),
+// summed in that order (shared row first, then j ascending) with fp32 FMAs;
+// g[t] = 1, or the shared-expert gate of the token when a gate vector is given.
 // One workgroup per token; a thread owns 4 consecutive columns in each of the
 // H/1024 column chunks. KK > 0 fixes k at compile time, so that every row
 // load of the token (both column chunks at H = 2048) is issued before the
 // first FMA; KK = 0 is the generic loop.
 template <int KK>
 __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const float* w, const int32_t* row_of_pair,
-                                                      int T, int k_rt, int H, int shared_row0, uint16_t* y) {
+                                                      int T, int k_rt, int H, int shared_row0, uint16_t* y,
+                                                      const uint16_t* x, const uint16_t* shared_gate) {
   constexpr int kChunks = 2;   // column chunks of 1024 handled together
   const int t = blockIdx.x;
+  __shared__ float gred[256 / kWave];
+  const float g = shared_gate ? token_gate(x + size_t(t) * H, shared_gate, H, gred) : 1.0f;   // uniform branch
   const int k = KK > 0 ? KK : k_rt;
   int rows[KK > 0 ? KK : 1];
   float ws[KK > 0 ? KK : 1];
@@ -74,6 +78,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const floa
       const int c = c0 + u * 1024;
       in[u] = c < H;
       acc[u] = in[u] ? *reinterpret_cast<const f32x4*>(Y + size_t(shared_row0 + t) * H + c) : f32x4{};
+      if (shared_gate) acc[u] *= g;
     }
     if constexpr (KK > 0) {
       f32x4 v[KK][kChunks];
@@ -112,17 +117,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const floa
 }
 
 hipError_t launch_combine(const float* Y, const float* w, const int32_t* row_of_pair, int T, int k, int H,
-                          int shared_row0, uint16_t* y, hipStream_t stream) {
+                          int shared_row0, uint16_t* y, const uint16_t* x, const uint16_t* shared_gate,
+                          hipStream_t stream) {
   if (T == 0) return hipSuccess;
   switch (k) {
     case 8:
-      hipLaunchKernelGGL(combine_kernel<8>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y);
+      hipLaunchKernelGGL(combine_kernel<8>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y,
+                         x, shared_gate);
       break;
     case 2:
-      hipLaunchKernelGGL(combine_kernel<2>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y);
+      hipLaunchKernelGGL(combine_kernel<2>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y,
+                         x, shared_gate);
       break;
     default:
-      hipLaunchKernelGGL(combine_kernel<0>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y);
+      hipLaunchKernelGGL(combine_kernel<0>, dim3(T), dim3(256), 0, stream, Y, w, row_of_pair, T, k, H, shared_row0, y,
+                         x, shared_gate);
       break;
   }
   return hipGetLastError();

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import MoeDims, MoeQ4Weights, check
+from ._lib import MoeDims, MoeLayerOptions, MoeQ4Weights, check
 
 MOE_EPI_STORE_F32 = _lib.MOE_EPI_STORE_F32
 MOE_EPI_SWIGLU_BF16 = _lib.MOE_EPI_SWIGLU_BF16
@@ -182,6 +182,7 @@ class MoEWeights:
     sh_up: Q4Stack
     sh_down: Q4Stack
     logit_bias: Optional[torch.Tensor] = None   # float [E]
+    shared_gate: Optional[torch.Tensor] = None  # bf16 [H]: gated shared expert
 
     @property
     def E(self) -> int:
@@ -201,7 +202,10 @@ class MoEWeights:
         lb = None
         if getattr(inp, "logit_bias", None) is not None:
             lb = torch.from_numpy(np.asarray(inp.logit_bias, np.float32)).to(device)
-        return MoEWeights(router_w=bf16_from_bits(inp.router_w, device),
+        sg = None
+        if getattr(inp, "shared_gate", None) is not None:
+            sg = bf16_from_bits(inp.shared_gate, device)
+        return MoEWeights(router_w=bf16_from_bits(inp.router_w, device), shared_gate=sg,
                           gate=Q4Stack.from_host(inp.gate, device), up=Q4Stack.from_host(inp.up, device),
                           down=Q4Stack.from_host(inp.down, device),
                           sh_gate=Q4Stack.from_host(inp.sh_gate, device),
@@ -212,8 +216,13 @@ class MoEWeights:
 def moe_layer_forward(x: torch.Tensor, w: MoEWeights, k: int, y: Optional[torch.Tensor] = None,
                       logits_out: Optional[torch.Tensor] = None, topk_ids_out: Optional[torch.Tensor] = None,
                       topk_w_out: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = MoE layer(x), bf16 [T][H]; optional outputs are filled when given."""
+                      workspace: Optional[torch.Tensor] = None, block_rows: int = 0,
+                      side_stream: Optional["torch.cuda.Stream"] = None, events=None) -> torch.Tensor:
+    """y = MoE layer(x), bf16 [T][H]; optional outputs are filled when given.
+    block_rows: routed tile height (0 = the library default, or 32, 64, 128).
+    side_stream: run the shared expert on this stream (events: a (fork, join)
+    pair of torch.cuda.Event already recorded once, so that they exist).
+    A gate vector in w.shared_gate gates the shared expert."""
     _need(x, torch.bfloat16, "x")
     dev = x.device
     T, H = x.shape
@@ -224,7 +233,7 @@ def moe_layer_forward(x: torch.Tensor, w: MoEWeights, k: int, y: Optional[torch.
                      (topk_w_out, "topk_w_out", torch.float32)):
         if t is not None:
             _need(t, dt, n, dev)
-    d = MoeDims(T, H, w.I, w.E, k, 0)
+    d = MoeDims(T, H, w.I, w.E, k, block_rows)
     lib = _lib.load()
     if y is None:
         y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
@@ -233,26 +242,50 @@ def moe_layer_forward(x: torch.Tensor, w: MoEWeights, k: int, y: Optional[torch.
     if workspace is None:
         workspace = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
     structs = [s.c_struct() for s in (w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)]
-    st = lib.moe_layer_forward(_ptr(x), _ptr(w.router_w), _ptr(w.logit_bias),
-                               *[ctypes.byref(s) for s in structs], ctypes.byref(d), _ptr(y), _ptr(logits_out),
-                               _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(workspace), workspace.numel(),
-                               _stream(dev))
-    check(st, "moe_layer_forward")
+    args = (_ptr(x), _ptr(w.router_w), _ptr(w.logit_bias), *[ctypes.byref(s) for s in structs], ctypes.byref(d),
+            _ptr(y), _ptr(logits_out), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(workspace), workspace.numel(),
+            _stream(dev))
+    if w.shared_gate is None and side_stream is None:
+        check(lib.moe_layer_forward(*args), "moe_layer_forward")
+        return y
+    opts = MoeLayerOptions()
+    if w.shared_gate is not None:
+        _need(w.shared_gate, torch.bfloat16, "shared_gate", dev)
+        opts.shared_gate = w.shared_gate.data_ptr()
+    if side_stream is not None:
+        if events is None or len(events) != 2:
+            raise ValueError("side_stream needs a (fork, join) pair of recorded torch.cuda.Event")
+        opts.side_stream = side_stream.cuda_stream
+        opts.fork_event = events[0].cuda_event
+        opts.join_event = events[1].cuda_event
+    check(lib.moe_layer_forward_ex(*args, ctypes.byref(opts)), "moe_layer_forward_ex")
     return y
 
 
 class MoELayer:
     """A layer with its weights and workspace resident on one GPU."""
 
-    def __init__(self, weights: MoEWeights, k: int, max_tokens: int):
+    def __init__(self, weights: MoEWeights, k: int, max_tokens: int, block_rows: int = 0,
+                 side_stream: bool = False):
         self.w = weights
         self.k = k
+        self.block_rows = block_rows
         dev = weights.router_w.device
-        wsb = workspace_bytes(max_tokens, weights.H, weights.I, weights.E, k)
+        self.side_stream = None
+        self.events = None
+        if side_stream:
+            # a second stream at the default priority and two events that exist
+            # (torch creates an event's HIP handle when it is first recorded)
+            self.side_stream = torch.cuda.Stream(device=dev)
+            self.events = (torch.cuda.Event(), torch.cuda.Event())
+            for e in self.events:
+                e.record(torch.cuda.current_stream(dev))
+        wsb = workspace_bytes(max_tokens, weights.H, weights.I, weights.E, k, block_rows)
         self.workspace = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
         self.max_tokens = max_tokens
 
     def __call__(self, x: torch.Tensor, **outs) -> torch.Tensor:
         if x.shape[0] > self.max_tokens:
             raise ValueError("more tokens than the workspace was sized for")
-        return moe_layer_forward(x, self.w, self.k, workspace=self.workspace, **outs)
+        return moe_layer_forward(x, self.w, self.k, workspace=self.workspace, block_rows=self.block_rows,
+                                 side_stream=self.side_stream, events=self.events, **outs)

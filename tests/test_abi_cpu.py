@@ -26,8 +26,8 @@ def lib():
 
 def test_header_declares_the_documented_entry_points():
     names = declared_functions()
-    for must in ("moe_route", "moe_grouped_gemm_q4", "moe_layer_forward", "moe_workspace_bytes",
-                 "moe_status_string"):
+    for must in ("moe_route", "moe_grouped_gemm_q4", "moe_layer_forward", "moe_layer_forward_ex",
+                 "moe_workspace_bytes", "moe_status_string"):
         assert must in names
 
 
@@ -54,11 +54,21 @@ def test_check_dims_and_workspace(lib):
         (4096, 2048, 512, 256, 0, 0): _lib.MOE_ERR_SHAPE,        # k = 0
         (4096, 2048, 512, 8, 9, 0): _lib.MOE_ERR_SHAPE,          # k > E
         (4096, 2048, 512, 257, 8, 0): _lib.MOE_ERR_SHAPE,        # E too large
-        (4096, 2000, 512, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # H not a multiple of 128
-        (4096, 2048, 576, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # I not a multiple of 128
+        (4096, 2000, 512, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # H not a multiple of 64
+        (4096, 2048, 544, 256, 8, 0): _lib.MOE_ERR_SHAPE,        # I not a multiple of 64
         (-1, 2048, 512, 256, 8, 0): _lib.MOE_ERR_SHAPE,          # negative T
-        (4096, 2048, 512, 256, 8, 64): _lib.MOE_ERR_UNSUPPORTED,  # other tile height
-        (16, 4096, 512, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,    # K beyond the GEMM limit
+        (4096, 2112, 512, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,  # H: an odd number of 64-groups
+        (4096, 2048, 576, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,  # I: an odd number of 64-groups
+        (4096, 2048, 512, 256, 8, 96): _lib.MOE_ERR_UNSUPPORTED,  # tile height other than 32, 64, 128
+        (4096, 2048, 512, 256, 8, 32): _lib.MOE_OK,              # routed tiles of 32 rows
+        (4096, 2048, 512, 256, 8, 64): _lib.MOE_OK,
+        (16, 4096, 512, 256, 8, 0): _lib.MOE_OK,                 # reductions above 2048
+        (16, 8192, 4096, 256, 8, 0): _lib.MOE_OK,
+        # operands addressed with 32-bit byte offsets must stay below 2 GiB:
+        (262144, 2048, 512, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,  # h: T*(k+1)*I*2 = 2.4 GB
+        (600000, 2048, 128, 256, 1, 0): _lib.MOE_ERR_UNSUPPORTED,  # x: T*H*2 = 2.5 GB
+        (200000, 2048, 512, 256, 8, 0): _lib.MOE_OK,               # h = 1.84 GB, x = 0.8 GB
+        (1, 4194304, 128, 256, 8, 0): _lib.MOE_ERR_UNSUPPORTED,    # W_r: E*H*2 = 2 GiB
     }
     for dims, want in cases.items():
         assert lib.moe_check_dims(ctypes.byref(MoeDims(*dims))) == want, dims
@@ -126,6 +136,15 @@ def test_calls_reject_bad_arguments_before_launching(lib):
     st = lib.moe_layer_forward(fake, fake, null, *[ctypes.byref(x) for x in ws], ctypes.byref(d2), fake, null,
                                null, null, fake, 16, null)
     assert st == _lib.MOE_ERR_WORKSPACE
+    # options: a side stream needs both events; the gate vector must be 16-byte aligned
+    opts = _lib.MoeLayerOptions(0, 0x5000, 0x6000, 0)
+    st = lib.moe_layer_forward_ex(fake, fake, null, *[ctypes.byref(x) for x in ws], ctypes.byref(d2), fake, null,
+                                  null, null, fake, 1 << 30, null, ctypes.byref(opts))
+    assert st == _lib.MOE_ERR_NULL
+    opts = _lib.MoeLayerOptions(0x5008, 0, 0, 0)
+    st = lib.moe_layer_forward_ex(fake, fake, null, *[ctypes.byref(x) for x in ws], ctypes.byref(d2), fake, null,
+                                  null, null, fake, 1 << 30, null, ctypes.byref(opts))
+    assert st == _lib.MOE_ERR_ALIGN
     # T = 0 is a no-op
     d0 = MoeDims(0, 256, 128, 16, 2, 0)
     st = lib.moe_layer_forward(fake, fake, null, *[ctypes.byref(x) for x in ws], ctypes.byref(d0), fake, null,
@@ -139,6 +158,15 @@ def test_calls_reject_bad_arguments_before_launching(lib):
     st = lib.moe_grouped_gemm_q4(fake, 8, null, 1, ctypes.byref(w0), null, fake, fake, fake, 4, 7, fake, null, 0,
                                  null)
     assert st == _lib.MOE_ERR_SHAPE
+    # grouped GEMM: an odd number of 64-groups, and A beyond 32-bit byte offsets
+    w3 = MoeQ4Weights(0x1000, 0x2000, 0x3000, 4, 128, 192)
+    st = lib.moe_grouped_gemm_q4(fake, 8, null, 1, ctypes.byref(w3), null, fake, fake, fake, 4, 0, fake, null, 0,
+                                 null)
+    assert st == _lib.MOE_ERR_UNSUPPORTED
+    w4 = MoeQ4Weights(0x1000, 0x2000, 0x3000, 4, 128, 4096)
+    st = lib.moe_grouped_gemm_q4(fake, 1 << 18, null, 1, ctypes.byref(w4), null, fake, fake, fake, 4, 0, fake,
+                                 null, 0, null)
+    assert st == _lib.MOE_ERR_UNSUPPORTED    # 2^18 rows x 4096 x 2 bytes = 2 GiB
 
 
 def test_quantize_validation_launches_nothing(lib):

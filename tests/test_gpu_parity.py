@@ -41,6 +41,13 @@ def _logits(kind, T, E, seed):
     l = rng.standard_normal((T, E)).astype(np.float32)
     if kind == "ties":
         l = (np.round(l * 2) / 2).astype(np.float32)
+    if kind == "neginf":
+        # -inf logits (weight 0): a random third of the entries, and on every
+        # fourth token all but three experts, so that -inf entries fill the
+        # end of the top-k (they tie and go in expert order)
+        l[rng.random((T, E)) < 1 / 3] = -np.inf
+        l[::4, 3:] = -np.inf
+        l[::4, :3] = rng.standard_normal((l[::4].shape[0], 3))
     return l
 
 
@@ -49,6 +56,7 @@ ROUTE_CASES = [
     (64, 16, 2, 3, "ties"), (1, 256, 8, 64, "gauss"), (200, 8, 8, 16, "gauss"),
     (100, 32, 4, 64, "zeros"), (513, 256, 8, 64, "ties"), (32768, 256, 8, 64, "gauss"),
     (33, 256, 32, 1, "ties"), (257, 5, 3, 7, "gauss"),
+    (3, 256, 8, 128, "neginf"), (16, 64, 8, 128, "neginf"), (1000, 256, 8, 128, "neginf"),
 ]
 
 
@@ -228,17 +236,46 @@ def test_gemm_swiglu_matches_oracle(dev):
     assert np.mean(gotf == want) > 0.98
 
 
+@pytest.mark.parametrize("I", [64, 192])
+def test_gemm_swiglu_half_column_tile(dev, I):
+    # N % 128 == 64: the last 128-column slice has two live waves; the other
+    # two stream the last 32 columns again and store nothing
+    print(f"gemm swiglu N={I}", flush=True)
+    T, E, k, H = 150, 8, 2, 256
+    inp = make_layer(T, H, I, E, k, seed=23 + I, bias_mode="random")
+    A = ops.bf16_from_bits(inp.x, dev)
+    Wg = ops.Q4Stack.from_host(inp.gate, dev)
+    Wu = ops.Q4Stack.from_host(inp.up, dev)
+    r = _route_for(dev, T, E, k, 29)
+    out = torch.full((T * k + 1, I), -7.0, dtype=torch.bfloat16, device=dev)   # one guard row
+    ops.moe_grouped_gemm_q4(A, Wg, r["offsets"], r["tile_map"], r["num_tiles"], ops.MOE_EPI_SWIGLU_BF16,
+                            T * k, W1=Wu, sorted_rows=r["sorted_rows"], row_div=k, out=out)
+    torch.cuda.synchronize()
+    gotf = om.bf16_bits_to_f64(ops.bits_from_bf16(out))
+    assert np.all(gotf[T * k] == -7.0), "a store ran past the last row"
+    srt = _np(r["sorted_rows"])
+    offs = _np(r["offsets"])
+    x = om.bf16_bits_to_f64(inp.x)
+    want = np.zeros((T * k, I))
+    for e in range(E):
+        rows = np.arange(offs[e], offs[e + 1])
+        xs = x[srt[rows] // k]
+        want[rows] = om.round_bf16(om.silu(xs @ om.expert_weights(inp.gate, e).T) * (xs @ om.expert_weights(inp.up, e).T))
+    assert_close_bf16(gotf[:T * k], want, "SwiGLU h, N % 128 == 64")
+
+
 # ----------------------------------------------------------------------------
 # whole layer
 # ----------------------------------------------------------------------------
 
-def run_layer(dev, inp):
+def run_layer(dev, inp, block_rows=0):
     w = ops.MoEWeights.from_host(inp, dev)
     x = ops.bf16_from_bits(inp.x, dev)
     logits = torch.empty(inp.T, inp.E, dtype=torch.float32, device=dev)
     ids = torch.empty(inp.T, inp.k, dtype=torch.int32, device=dev)
     wts = torch.empty(inp.T, inp.k, dtype=torch.float32, device=dev)
-    y = ops.moe_layer_forward(x, w, inp.k, logits_out=logits, topk_ids_out=ids, topk_w_out=wts)
+    y = ops.moe_layer_forward(x, w, inp.k, logits_out=logits, topk_ids_out=ids, topk_w_out=wts,
+                              block_rows=block_rows)
     torch.cuda.synchronize()
     return dict(y=om.bf16_bits_to_f64(ops.bits_from_bf16(y)), logits=_np(logits), ids=_np(ids), w=_np(wts))
 
@@ -342,9 +379,11 @@ def test_layer_graph_replays_match_eager(dev, T):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager) and torch.equal(ids, ids_eager)
-        assert int(layer.workspace[:256].count_nonzero()) == 0
+        assert int(layer.workspace[:_lib.MOE_WORKSPACE_HEAD_BYTES].count_nonzero()) == 0
     ref = run_layer(dev, inp)
     assert np.array_equal(om.bf16_bits_to_f64(ops.bits_from_bf16(y)), ref["y"])
+    # and the replayed output against the oracle, routed from the GPU's logits
+    check_layer(inp, dict(ref, y=om.bf16_bits_to_f64(ops.bits_from_bf16(y))))
 
 
 def test_layer_zero_tokens_is_a_noop(dev):
@@ -366,7 +405,7 @@ def test_layer_is_deterministic(dev):
 
 def test_layer_workspace_reused_across_token_counts(dev):
     # Calls with T <= 4 route in one launch that counts finished workgroups in
-    # the workspace's first 256 bytes and leaves them zero; reusing one
+    # and parks logits in the workspace's head and leaves it zero; reusing one
     # workspace across token counts (one-launch, decode and general paths)
     # must give the same bits as a fresh zeroed workspace, and end zeroed.
     # E = 12 leaves the last expert slice of the router half empty.
@@ -387,7 +426,7 @@ def test_layer_workspace_reused_across_token_counts(dev):
         for key in g:
             assert np.array_equal(g[key], fresh[key]), (T, key)
         check_layer(inp, g)
-        assert int(ws[:256].count_nonzero()) == 0, T
+        assert int(ws[:_lib.MOE_WORKSPACE_HEAD_BYTES].count_nonzero()) == 0, T
 
 
 @pytest.mark.parametrize("name", ["decode1", "decode8"])
@@ -425,6 +464,105 @@ def test_layer_largest_reduction_sizes(dev):
     check_layer(inp, run_layer(dev, inp))
 
 
+@pytest.mark.parametrize("T,H,I", [(100, 4096, 512), (60, 2048, 2560), (5, 2560, 384), (3, 4096, 256)])
+def test_layer_reduction_sizes_above_2048(dev, T, H, I):
+    # reductions past 2048 (64 and 40 groups) in both grouped GEMMs; at T <= 8
+    # these sizes run the grouped GEMM instead of the decode kernels
+    print(f"layer T={T} H={H} I={I}", flush=True)
+    inp = resample_close_calls(make_layer(T=T, H=H, I=I, E=8, k=2, seed=H + I, bias_mode="random"))
+    check_layer(inp, run_layer(dev, inp))
+
+
+@pytest.mark.parametrize("bm", [32, 64, 128])
+@pytest.mark.parametrize("T,E,k", [(300, 16, 2), (700, 64, 8), (6, 16, 2)])
+def test_layer_routed_tile_heights(dev, bm, T, E, k):
+    # routed tiles of 32, 64 or 128 rows (the shared expert keeps 128-row tiles)
+    print(f"layer block_rows={bm} T={T} E={E} k={k}", flush=True)
+    inp = make_layer(T, 256, 128, E, k, seed=bm + T, bias_mode="random")
+    g = run_layer(dev, inp, block_rows=bm)
+    check_layer(inp, g)
+    if bm != 128:
+        ref = run_layer(dev, inp, block_rows=128)
+        assert np.array_equal(g["ids"], ref["ids"])
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(64, 256, 128, 16, 2), (1, 256, 256, 16, 2), (3, 512, 256, 16, 4),
+                                       (8, 256, 256, 16, 2), (300, 512, 256, 32, 4)])
+def test_layer_gated_shared_expert(dev, T, H, I, E, k):
+    # the shared expert scaled by sigmoid(x . w_sg): combine kernel (T > 8)
+    # and fused down + combine (T <= 8)
+    print(f"layer gated shared T={T} H={H} I={I} E={E} k={k}", flush=True)
+    inp = resample_close_calls(make_layer(T, H, I, E, k, seed=90 + T, bias_mode="random", gated_shared=True))
+    g = run_layer(dev, inp)
+    check_layer(inp, g)
+    # the gate matters: the ungated layer differs
+    plain = dict(vars(inp))
+    plain["shared_gate"] = None
+    ref_plain = om.moe_layer(type(inp)(**plain), logits=g["logits"])["y"]
+    assert rel_l2(g["y"], ref_plain) > 1e-2
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode8", "prefill512", "prefill4096"])
+def test_layer_full_shape_gated_shared_expert(dev, name):
+    print(f"layer {name} gated shared expert", flush=True)
+    inp = make_config(name, seed=3, bias_mode="random", gated_shared=True)
+    check_layer(inp, run_layer(dev, inp))
+
+
+def _run_layer_streams(dev, inp, side, k_graph=False):
+    w = ops.MoEWeights.from_host(inp, dev)
+    layer = ops.MoELayer(w, inp.k, inp.T, side_stream=side)
+    x = ops.bf16_from_bits(inp.x, dev)
+    logits = torch.empty(inp.T, inp.E, dtype=torch.float32, device=dev)
+    ids = torch.empty(inp.T, inp.k, dtype=torch.int32, device=dev)
+    wts = torch.empty(inp.T, inp.k, dtype=torch.float32, device=dev)
+    y = torch.empty(inp.T, inp.H, dtype=torch.bfloat16, device=dev)
+    layer(x, y=y, logits_out=logits, topk_ids_out=ids, topk_w_out=wts)
+    torch.cuda.synchronize()
+    return dict(y=om.bf16_bits_to_f64(ops.bits_from_bf16(y)), logits=_np(logits), ids=_np(ids), w=_np(wts)), layer
+
+
+@pytest.mark.parametrize("name,T,gated", [("tiny", None, False), ("tiny", 1, False), ("tiny", 6, True),
+                                          ("tiny", 200, True), ("prefill4096", None, False),
+                                          ("decode1", None, True), ("decode8", None, False)])
+def test_layer_side_stream_matches_one_stream(dev, name, T, gated):
+    # the shared expert's tiles on a second stream (forked after the activation
+    # prep, joined before the combine) give the one-stream bits
+    print(f"layer side stream {name} T={T} gated={gated}", flush=True)
+    over = {} if T is None else {"T": T}
+    inp = make_config(name, seed=7, bias_mode="random", gated_shared=gated, **over)
+    one, _ = _run_layer_streams(dev, inp, False)
+    two, _ = _run_layer_streams(dev, inp, True)
+    for key in one:
+        assert np.array_equal(one[key], two[key]), key
+    check_layer(inp, two, tokens=None if inp.T <= 512 else list(range(0, inp.T, 97)))
+
+
+@pytest.mark.parametrize("T", [2, 8, 300])
+def test_layer_side_stream_graph_replays(dev, T):
+    # captured with the side stream forked and joined inside the capture;
+    # every replay (after eager calls on other tokens) matches the eager bits
+    print(f"layer side stream graph T={T}", flush=True)
+    H, I, E, k = 256, 128, 16, 2
+    inp = make_layer(T, H, I, E, k, seed=80 + T, bias_mode="random", gated_shared=True)
+    g, layer = _run_layer_streams(dev, inp, True)
+    x = ops.bf16_from_bits(inp.x, dev)
+    x2 = ops.bf16_from_bits(make_layer(T, H, I, E, k, seed=180 + T).x, dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty_like(y)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer(x, y=y)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.fill_(0)
+        layer(x2, y=y2)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(om.bf16_bits_to_f64(ops.bits_from_bf16(y)), g["y"])
+    check_layer(inp, g)
+
+
 def test_layer_decode8_zipf_seeds(dev):
     print("layer decode8 zipf seeds 1, 2", flush=True)
     for seed in (1, 2):
@@ -432,25 +570,52 @@ def test_layer_decode8_zipf_seeds(dev):
         check_layer(inp, run_layer(dev, inp), tokens=list(range(inp.T)))
 
 
-def test_layer_full_shape_prefill512_all_tokens(dev):
-    print("layer prefill512", flush=True)
-    inp = make_config("prefill512", seed=1)
+@pytest.mark.parametrize("bias_mode", ["sym", "random"])
+def test_layer_full_shape_prefill512_all_tokens(dev, bias_mode):
+    print(f"layer prefill512 {bias_mode}", flush=True)
+    inp = make_config("prefill512", seed=1, bias_mode=bias_mode)
     check_layer(inp, run_layer(dev, inp))
 
 
-@pytest.mark.parametrize("name", ["prefill4096", "prefill4096_zipf"])
-def test_layer_full_shape_prefill4096_sampled(dev, name):
-    print(f"layer {name}", flush=True)
-    inp = make_config(name, seed=0)
-    g = run_layer(dev, inp)
-    rng = np.random.default_rng(0)
-    toks = sorted(set(rng.choice(inp.T, 24, replace=False).tolist()) | {0, inp.T - 1})
-    check_layer(inp, g, tokens=toks)
+@pytest.mark.parametrize("name,bias_mode", [("prefill4096", "sym"), ("prefill4096", "random"),
+                                            ("prefill4096_zipf", "sym"), ("prefill4096_zipf", "random")])
+def test_layer_full_shape_prefill4096_all_tokens(dev, name, bias_mode):
+    # every token of the benchmark workload against the full fp64 layer oracle
+    print(f"layer {name} {bias_mode}", flush=True)
+    inp = make_config(name, seed=0, bias_mode=bias_mode)
+    check_layer(inp, run_layer(dev, inp))
+
+
+def _tile_covering_tokens(logits, k, bm, n_random, seed):
+    """Tokens whose rows sit at the first, a middle and the last row of routed
+    tiles of every live 32-row block count (1..4), at the edges of the shared
+    expert's 128-row tiles, plus random ones."""
+    ids, _ = om.select_topk(logits, k)
+    tab = om.routing_tables(ids, logits.shape[1], bm)
+    offs, srt = tab["offsets"], tab["sorted_rows"]
+    T = logits.shape[0]
+    picked = set()
+    by_blocks = {1: [], 2: [], 3: [], 4: []}
+    for e, r0 in tab["tile_map"].tolist():
+        r1 = min(r0 + bm, int(offs[e + 1]))
+        by_blocks[-(-(r1 - r0) // 32)].append((r0, r1))
+    for nb, tiles in by_blocks.items():
+        for r0, r1 in tiles[:: max(1, len(tiles) // 12)]:
+            for r in (r0, (r0 + r1) // 2, r1 - 1):
+                picked.add(int(srt[r]) // k)
+    for t0 in range(0, T, 128 * 37):
+        picked.update({t0, min(t0 + 127, T - 1)})
+    picked.update({0, T - 1})
+    rng = np.random.default_rng(seed)
+    picked.update(rng.choice(T, n_random, replace=False).tolist())
+    return sorted(picked), by_blocks
 
 
 def test_layer_full_shape_prefill32768_sampled(dev):
     print("layer prefill32768", flush=True)
-    inp = make_config("prefill32768", seed=0)
+    inp = make_config("prefill32768", seed=0, bias_mode="random")
     g = run_layer(dev, inp)
-    toks = [0, 1, 4095, 4096, 20000, 32767]
+    toks, by_blocks = _tile_covering_tokens(g["logits"], inp.k, ops.BLOCK_ROWS, 360, 0)
+    assert all(by_blocks[n] for n in (1, 2, 3, 4)), {n: len(v) for n, v in by_blocks.items()}
+    assert len(toks) >= 512, len(toks)
     check_layer(inp, g, tokens=toks)
