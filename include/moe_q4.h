@@ -279,6 +279,34 @@ int moe_layer_forward_timed(const uint16_t* x, const uint16_t* router_w, const f
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const* events, int32_t n_events);
 
+/* Size of the device array behind moe_layer_forward_noalloc (per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * moe_layer_forward_noalloc - moe_layer_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without a workspace.
+ * Its scratch memory is one MOE_NOALLOC_SCRATCH_BYTES device array per GPU,
+ * part of the library's code object and held until the process ends; the call
+ * makes no allocation of its own. The caller still passes every input and
+ * output buffer.
+ *   - Sizes whose workspace (moe_workspace_bytes) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE and launch nothing:
+ *     at H=2048, I=512, E=256, k=8 that is a few hundred tokens; decode-sized
+ *     calls need well under 1 MiB.
+ *   - The first call on a device resolves the array's address
+ *     (hipGetSymbolAddress) and enqueues a kernel that zeroes its head; make
+ *     that first call outside graph capture.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (other streams, other threads) race; serialise them.
+ * Results are identical to moe_layer_forward's.
+ */
+int moe_layer_forward_noalloc(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
+                              const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,
+                              const moe_q4_weights* sh_gate, const moe_q4_weights* sh_up,
+                              const moe_q4_weights* sh_down, const moe_dims* dims, uint16_t* y,
+                              float* logits_out, int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 /*
  * moe_quantize_q4 - quantise bf16 weights into the layout the other entry
  * points read: for each row and each 64 consecutive elements along K, a bf16

@@ -28,6 +28,7 @@ MOE_GEMM_BLOCK_ROWS = 128
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
 MOE_WORKSPACE_HEAD_BYTES = 8448
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class MoeDims(ctypes.Structure):
@@ -63,6 +64,7 @@ SIGNATURES = {
     "moe_layer_forward": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_forward_ex": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ, _P,
                                             ctypes.POINTER(MoeLayerOptions)]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P]),
     "moe_layer_forward_timed": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ,
                                                _P, ctypes.POINTER(ctypes.c_void_p), _I32]),
     "moe_quantize_q4": (ctypes.c_int, [_P, ctypes.c_int64, _I32, _P, _P, _P, _P]),

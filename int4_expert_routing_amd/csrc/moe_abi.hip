@@ -1,7 +1,15 @@
 // extern "C" entry points of the library: argument validation, workspace
 // layout, and the launch sequence of each call (all on the caller's stream,
 // no host synchronisation).
+#include <mutex>
+
 #include "moe_internal.h"
+
+// Workspace of moe_layer_forward_noalloc: one array per GPU, held until the
+// process ends. Host code never uses this name as an address (in host code it
+// is a stand-in for the device symbol): the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace moe {
 namespace {
@@ -475,6 +483,64 @@ int moe_layer_forward_timed(const uint16_t* x, const uint16_t* router_w, const f
                             void* stream, void* const* events, int32_t n_events) {
   return layer_forward_impl(x, router_w, logit_bias, gate, up, down, sh_gate, sh_up, sh_down, dims, y, logits_out,
                             topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, events, n_events, nullptr);
+}
+
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];   // device address of `scratch` on each device, once resolved
+
+// Zeroes the first n 32-bit words of p (a kernel, not a memset, so that the
+// call can be captured in a graph).
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_layer_forward_noalloc(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
+                              const moe_q4_weights* gate, const moe_q4_weights* up, const moe_q4_weights* down,
+                              const moe_q4_weights* sh_gate, const moe_q4_weights* sh_up,
+                              const moe_q4_weights* sh_down, const moe_dims* dims, uint16_t* y, float* logits_out,
+                              int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  int st = check_layer_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  if (layer_layout(*dims).total > size_t(MOE_NOALLOC_SCRATCH_BYTES)) return MOE_ERR_WORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_HIP;
+  void* ptr = nullptr;
+  bool first = false;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch_ptr[dev] = p;
+      first = true;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (first) {
+    // the workspace head must be zero before the first layer call; every call
+    // leaves it zero
+    const int words = kHandoffBytes / 4;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(ceil_div(words, 256)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ptr), words);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  }
+  return layer_forward_impl(x, router_w, logit_bias, gate, up, down, sh_gate, sh_up, sh_down, dims, y, logits_out,
+                            topk_ids_out, topk_w_out, ptr, size_t(MOE_NOALLOC_SCRATCH_BYTES), stream, nullptr, 0,
+                            nullptr);
 }
 
 int moe_quantize_q4(const uint16_t* w, int64_t rows, int32_t K, uint32_t* q, uint16_t* s, uint16_t* b,

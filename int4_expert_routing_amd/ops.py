@@ -262,6 +262,30 @@ def moe_layer_forward(x: torch.Tensor, w: MoEWeights, k: int, y: Optional[torch.
     return y
 
 
+def moe_layer_forward_noalloc(x: torch.Tensor, w: MoEWeights, k: int, y: torch.Tensor,
+                              logits_out: Optional[torch.Tensor] = None,
+                              topk_ids_out: Optional[torch.Tensor] = None,
+                              topk_w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer with the library's per-GPU scratch array instead of a
+    workspace: allocates nothing (y and the optional outputs are the caller's)."""
+    _need(x, torch.bfloat16, "x")
+    dev = x.device
+    T, H = x.shape
+    _need(y, torch.bfloat16, "y", dev)
+    for t, n, dt in ((logits_out, "logits_out", torch.float32), (topk_ids_out, "topk_ids_out", torch.int32),
+                     (topk_w_out, "topk_w_out", torch.float32)):
+        if t is not None:
+            _need(t, dt, n, dev)
+    d = MoeDims(T, H, w.I, w.E, k, 0)
+    structs = [s.c_struct() for s in (w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)]
+    st = _lib.load().moe_layer_forward_noalloc(_ptr(x), _ptr(w.router_w), _ptr(w.logit_bias),
+                                               *[ctypes.byref(s) for s in structs], ctypes.byref(d), _ptr(y),
+                                               _ptr(logits_out), _ptr(topk_ids_out), _ptr(topk_w_out),
+                                               _stream(dev))
+    check(st, "moe_layer_forward_noalloc")
+    return y
+
+
 class MoELayer:
     """A layer with its weights and workspace resident on one GPU."""
 

@@ -169,6 +169,26 @@ def test_calls_reject_bad_arguments_before_launching(lib):
     assert st == _lib.MOE_ERR_UNSUPPORTED    # 2^18 rows x 4096 x 2 bytes = 2 GiB
 
 
+def test_noalloc_rejects_sizes_beyond_its_array_before_any_hip_call(lib):
+    # validation and the size check come before the device is touched
+    fake = ctypes.c_void_p(0x100000)
+    ws = [MoeQ4Weights(0x1000, 0x2000, 0x3000, n, N, K)
+          for n, N, K in ((256, 512, 2048), (256, 512, 2048), (256, 2048, 512), (1, 512, 2048), (1, 512, 2048),
+                          (1, 2048, 512))]
+    big = MoeDims(4096, 2048, 512, 256, 8, 0)
+    assert lib.moe_workspace_bytes(ctypes.byref(big)) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    st = lib.moe_layer_forward_noalloc(fake, fake, None, *[ctypes.byref(x) for x in ws], ctypes.byref(big), fake,
+                                       None, None, None, None)
+    assert st == _lib.MOE_ERR_WORKSPACE
+    bad = MoeDims(4096, 2048, 512, 256, 0, 0)
+    st = lib.moe_layer_forward_noalloc(fake, fake, None, *[ctypes.byref(x) for x in ws], ctypes.byref(bad), fake,
+                                       None, None, None, None)
+    assert st == _lib.MOE_ERR_SHAPE
+    hdr = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)" in hdr and _lib.MOE_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert "#define MOE_WORKSPACE_HEAD_BYTES 8448" in hdr and _lib.MOE_WORKSPACE_HEAD_BYTES == 8448
+
+
 def test_quantize_validation_launches_nothing(lib):
     # shape and pointer errors are reported before any launch (no GPU needed)
     P = ctypes.c_void_p
