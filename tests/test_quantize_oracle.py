@@ -181,3 +181,61 @@ def test_planted_quantiser_mistake_is_caught(mutant):
         except AssertionError:
             failed += 1
     assert failed > 0, f"{mutant.__name__} passed every pin"
+
+
+# ----------------------------------------------------------------------------
+# prepacked layout (oracle/prepack.py)
+# ----------------------------------------------------------------------------
+
+def test_prepack_hand_worked_example():
+    import json
+    import os
+    import oracle.prepack as op
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prepack_small.json")))
+    codes, sp, bp = op.prepack_q4(np.array(g["q"], np.uint32), np.array(g["s"], np.uint16),
+                                  np.array(g["b"], np.uint16))
+    assert codes.tolist() == g["codes"]
+    assert sp.tolist() == g["s_pairs"]
+    assert bp.tolist() == g["b_pairs"]
+
+
+def test_prepack_is_a_permutation_that_keeps_the_weights():
+    # every word and every scale/bias moves and none changes: the dequantised
+    # matrices rebuilt from the prepacked arrays by index are the canonical ones
+    import oracle.prepack as op
+    rng = np.random.default_rng(3)
+    n, N, K = 3, 48, 256
+    G = K // 64
+    q = rng.integers(0, 2**32, size=(n, N, K // 8), dtype=np.uint32)
+    s = rng.integers(0, 2**16, size=(n, N, G), dtype=np.uint16)
+    b = rng.integers(0, 2**16, size=(n, N, G), dtype=np.uint16)
+    codes, sp, bp = op.prepack_q4(q, s, b)
+    assert codes.shape == (n, G, N, 8) and sp.shape == (n, G // 2, N) and bp.shape == (n, G // 2, N)
+    assert sorted(codes.ravel().tolist()) == sorted(q.ravel().tolist())
+    for e, r, w in ((0, 0, 0), (2, 47, 31), (1, 17, 13)):
+        assert codes[e, w // 8, r, w % 8] == q[e, r, w]
+    for e, r, gg in ((0, 0, 0), (2, 47, 3), (1, 5, 2)):
+        assert (sp[e, gg // 2, r] >> (16 * (gg % 2))) & 0xFFFF == s[e, r, gg]
+        assert (bp[e, gg // 2, r] >> (16 * (gg % 2))) & 0xFFFF == b[e, r, gg]
+    with pytest.raises(ValueError):
+        op.prepack_q4(q[:, :, :24], s[:, :, :3], b[:, :, :3])   # an odd number of groups
+
+
+def test_prepack_planted_mistakes_fail_the_hand_worked_example():
+    import json
+    import os
+    import oracle.prepack as op
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prepack_small.json")))
+    q, s, b = np.array(g["q"], np.uint32), np.array(g["s"], np.uint16), np.array(g["b"], np.uint16)
+
+    def halves_swapped(q, s, b):
+        c, sp, bp = op.prepack_q4(q, s, b)
+        return c, (sp >> 16) | (sp << 16), bp
+
+    def rows_then_groups(q, s, b):   # [n][N][G][8] left in row-major order
+        c, sp, bp = op.prepack_q4(q, s, b)
+        return q.reshape(q.shape[0], q.shape[1], -1, 8), sp, bp
+
+    for mut in (halves_swapped, rows_then_groups):
+        c, sp, bp = mut(q, s, b)
+        assert (c.tolist() != g["codes"]) or (sp.tolist() != g["s_pairs"]) or (bp.tolist() != g["b_pairs"])
