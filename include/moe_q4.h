@@ -73,18 +73,31 @@ typedef struct {
     int32_t T, H, I, E, k, block_rows;
 } moe_dims;
 
+/* Layouts of a moe_q4_weights stack. */
+#define MOE_Q4_CANONICAL 0
+#define MOE_Q4_PREPACKED 1
+
 /* Host struct describing a stack of n_experts 4-bit matrices of shape [N][K]
- * (device pointers):
+ * (device pointers). The weight is W[n][k] = s[n][k/64] * q[n][k] + b[n][k/64]
+ * with q the unsigned 4-bit code of element k of row n. G = K/64.
+ * layout MOE_Q4_CANONICAL (0, the format every caller starts from):
  *   q : uint32 [n_experts][N][K/8]; nibble i (bits 4i..4i+3) of word w holds
- *       the unsigned 4-bit code q of element 8w+i of that row;
- *   s, b : bf16 [n_experts][N][K/64]; scale and bias of each run of 64
+ *       the code of element 8w+i of that row;
+ *   s, b : bf16 [n_experts][N][G]; scale and bias of each run of 64
  *       consecutive elements along K.
- * The weight is W[n][k] = s[n][k/64] * q[n][k] + b[n][k/64]. */
+ * layout MOE_Q4_PREPACKED (1, written by moe_prepack_q4; G even): the same
+ * values reordered so that one group of consecutive rows is contiguous:
+ *   q : uint32 [n_experts][G][N][8]: words 8g..8g+7 of row n at [g][n];
+ *   s, b : uint32 [n_experts][G/2][N] (passed as uint16_t pointers): the bf16
+ *       values of groups 2p (low half) and 2p+1 (high half) of row n at [p][n].
+ * Every entry point accepts either layout; the two matrices of a gate/up pair
+ * (gate and up, sh_gate and sh_up, W0 and W1) must share one. */
 typedef struct {
     const uint32_t* q;
     const uint16_t* s;
     const uint16_t* b;
     int32_t n_experts, N, K;
+    int32_t layout;
 } moe_q4_weights;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -278,6 +291,26 @@ int moe_layer_forward_timed(const uint16_t* x, const uint16_t* router_w, const f
                             float* logits_out, int32_t* topk_ids_out, float* topk_w_out,
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const* events, int32_t n_events);
+
+/* Bytes moe_prepack_q4 writes for a stack of these sizes (0 when K is not a
+ * positive multiple of 128 or a size is not positive). */
+size_t moe_prepack_q4_bytes(int32_t n_experts, int32_t N, int32_t K);
+
+/*
+ * moe_prepack_q4 - reorder a canonical stack into MOE_Q4_PREPACKED, done once
+ * when the weights are loaded. The itinai.com post on the engine says the
+ * 4-bit weights are expanded only on chip; the grouped GEMM reads one 64-wide
+ * group of 32 consecutive rows per load, which in the canonical layout takes
+ * 32 B from each of 32 lines and in the packed one whole lines.
+ *   src     host struct, layout MOE_Q4_CANONICAL, K % 128 == 0 (an odd number
+ *           of groups: MOE_ERR_UNSUPPORTED)
+ *   dst     device, 16-byte aligned, at least moe_prepack_q4_bytes bytes;
+ *           holds the codes, then the scale pairs, then the bias pairs
+ *   packed  host struct filled on success: pointers into dst, same sizes,
+ *           layout MOE_Q4_PREPACKED
+ * Asynchronous on stream; src must stay valid until the work completes.
+ */
+int moe_prepack_q4(const moe_q4_weights* src, void* dst, size_t dst_bytes, moe_q4_weights* packed, void* stream);
 
 /* Size of the device array behind moe_layer_forward_noalloc (per GPU). */
 #define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)

@@ -36,9 +36,14 @@ class MoeDims(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("block_rows", ctypes.c_int32)]
 
 
+MOE_Q4_CANONICAL = 0
+MOE_Q4_PREPACKED = 1
+
+
 class MoeQ4Weights(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("b", ctypes.c_void_p),
-                ("n_experts", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
+                ("n_experts", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class MoeLayerOptions(ctypes.Structure):
@@ -64,6 +69,8 @@ SIGNATURES = {
     "moe_layer_forward": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_forward_ex": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ, _P,
                                             ctypes.POINTER(MoeLayerOptions)]),
+    "moe_prepack_q4_bytes": (_SZ, [_I32, _I32, _I32]),
+    "moe_prepack_q4": (ctypes.c_int, [_W, _P, _SZ, _W, _P]),
     "moe_layer_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P]),
     "moe_layer_forward_timed": (ctypes.c_int, [_P, _P, _P, _W, _W, _W, _W, _W, _W, _DIMS, _P, _P, _P, _P, _P, _SZ,
                                                _P, ctypes.POINTER(ctypes.c_void_p), _I32]),

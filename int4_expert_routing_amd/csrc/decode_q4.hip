@@ -60,6 +60,59 @@ __device__ __forceinline__ void load_groups(const uint16_t* p, uint16_t (&v)[GQ]
   }
 }
 
+// Scale or bias values of GQ consecutive groups g0.. of one column from a
+// packed stack's pair plane [n][G/2][N] u32 (GQ >= 2 implies g0 even).
+template <int GQ>
+__device__ __forceinline__ void load_group_pairs(const uint16_t* plane, int el, int G, int N, int col, int g0,
+                                                 uint16_t (&v)[GQ]) {
+  const uint32_t* pl = reinterpret_cast<const uint32_t*>(plane) + (size_t(el) * (G / 2) + g0 / 2) * N + col;
+  if constexpr (GQ == 1) {
+    const uint32_t w = pl[0];
+    v[0] = uint16_t((g0 & 1) ? (w >> 16) : w);
+  } else {
+    uint32_t w[GQ / 2];
+#pragma unroll
+    for (int i = 0; i < GQ / 2; ++i) w[i] = pl[size_t(i) * N];
+#pragma unroll
+    for (int i = 0; i < GQ / 2; ++i) {
+      v[2 * i] = uint16_t(w[i]);
+      v[2 * i + 1] = uint16_t(w[i] >> 16);
+    }
+  }
+}
+
+// The codes a lane streams: STEPS 16-byte steps covering GQ = STEPS/2 groups
+// g0.. of one column (step st = half st%2 of group g0 + st/2), from either
+// layout.
+template <int STEPS>
+__device__ __forceinline__ void load_code_steps(const QStack& m, int el, int N, int K, int col, int g0,
+                                                u32x4 (&w)[STEPS]) {
+  const int G = K / kGroup;
+  if (m.packed) {
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st)
+      w[st] = *reinterpret_cast<const u32x4*>(m.q + ((size_t(el) * G + g0 + st / 2) * N + col) * 8 + (st & 1) * 4);
+  } else {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(m.q + (size_t(el) * N + col) * (K / 8) + g0 * 8);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) w[st] = qp[st];
+  }
+}
+
+template <int GQ>
+__device__ __forceinline__ void load_scale_bias(const QStack& m, int el, int N, int K, int col, int g0,
+                                                uint16_t (&sv)[GQ], uint16_t (&bv)[GQ]) {
+  const int G = K / kGroup;
+  if (m.packed) {
+    load_group_pairs<GQ>(m.s, el, G, N, col, g0, sv);
+    load_group_pairs<GQ>(m.b, el, G, N, col, g0, bv);
+  } else {
+    const size_t wrow = size_t(el) * N + col;
+    load_groups<GQ>(m.s + wrow * G + g0, sv);
+    load_groups<GQ>(m.b + wrow * G + g0, bv);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Gate/up projection with SwiGLU (few-token calls).
 //
@@ -115,14 +168,10 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti
   const int stack = ti.e == a.E ? 1 : 0;
   const int el = stack ? 0 : ti.e;
   const QStack& mat = up ? a.w1[stack] : a.w0[stack];
-  const size_t wrow = size_t(el) * a.N + cb * 16 + c;
-  const u32x4* qp = reinterpret_cast<const u32x4*>(mat.q + wrow * (K / 8) + slice * (K / 8 / PARTS));
   u32x4 w[STEPS];
-#pragma unroll
-  for (int st = 0; st < STEPS; ++st) w[st] = qp[st];
+  load_code_steps<STEPS>(mat, el, a.N, K, cb * 16 + c, slice * GQ, w);
   uint16_t sv[GQ], bv[GQ];
-  load_groups<GQ>(mat.s + wrow * G + slice * GQ, sv);
-  load_groups<GQ>(mat.b + wrow * G + slice * GQ, bv);
+  load_scale_bias<GQ>(mat, el, a.N, K, cb * 16 + c, slice * GQ, sv, bv);
 
   // ---- activation rows (operand order) and their group sums into LDS -------
   // every chunk load of the rows is issued before the first store
@@ -331,18 +380,12 @@ __global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(D
     const int el = routed ? a.topk_ids[f] : 0;
     const int row = routed ? a.row_of_pair[f] : a.shared_row0 + t;
     const float wj = routed ? a.topk_w[f] : 1.0f;
-    const uint32_t* mq = routed ? a.down.q : a.down_shared.q;
-    const uint16_t* ms = routed ? a.down.s : a.down_shared.s;
-    const uint16_t* mb = routed ? a.down.b : a.down_shared.b;
-    const size_t wrow = size_t(el) * a.N + col0 + c;
-    // the lane's K/8 contiguous code bytes (quarter kq of its column)
-    const u32x4* qp = reinterpret_cast<const u32x4*>(mq + wrow * (K / 8) + kq * (K / 32));
+    const QStack& mat = routed ? a.down : a.down_shared;
+    // the lane's codes: quarter kq of its column's K (GQ groups)
     u32x4 w[STEPS];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) w[s] = qp[s];
+    load_code_steps<STEPS>(mat, el, a.N, K, col0 + c, kq * GQ, w);
     uint16_t sv[GQ], bv[GQ];
-    load_groups<GQ>(ms + wrow * G + kq * GQ, sv);
-    load_groups<GQ>(mb + wrow * G + kq * GQ, bv);
+    load_scale_bias<GQ>(mat, el, a.N, K, col0 + c, kq * GQ, sv, bv);
     // stage the h row (already in operand order) and its fp32 group sums
     __builtin_amdgcn_wave_barrier();   // the previous pair's reads of xs and Xt are done
     const uint16_t* hr = a.h + size_t(row) * K;

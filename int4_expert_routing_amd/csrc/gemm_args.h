@@ -5,11 +5,16 @@
 
 namespace moe {
 
-// One stack of 4-bit matrices [n][N][K/8] with bf16 scale/bias [n][N][K/64].
+// One stack of n 4-bit matrices of shape [N][K] (G = K/64 groups).
+//   packed == 0 (canonical): q [n][N][K/8] u32, s and b [n][N][G] bf16;
+//   packed == 1: q [n][G][N][8] u32 (one group of consecutive rows is
+//     contiguous), s and b [n][G/2][N] u32 holding the bf16 values of groups
+//     2p (low half) and 2p+1 (high half).
 struct QStack {
   const uint32_t* q;
   const uint16_t* s;
   const uint16_t* b;
+  int packed;
 };
 
 enum GemmEpilogue { kEpiF32 = 0, kEpiSwigluNatural = 1, kEpiSwigluInternal = 2 };

@@ -154,6 +154,8 @@ struct Stream {
   uint32_t va[4];    // activation chunk offsets (4 instructions; small tiles use va[0] only)
   uint32_t vb;       // code offset of the lane (same in both column blocks)
   uint32_t vxp;      // side-table offset of (row, half)
+  int gstride;       // bytes between a column's codes of consecutive groups (32, or N * 32 when packed)
+  int sbstride;      // u32 words between a column's scale/bias pairs of consecutive pairs (1, or N when packed)
   const uint32_t* sbp[2];  // lanes 0-31: scale pairs, lanes 32-63: bias pairs of the lane's column (blocks 0, 1)
 };
 
@@ -171,8 +173,8 @@ template <bool SR>
 __device__ __forceinline__ void issue_codes(const Stream& st, uint8_t* ring, int g, int wave) {
   using R = Ring<SR>;
   uint8_t* cs = ring + R::C_BASE + (g % R::C_RING) * R::C_SLOT;
-  buffer_to_lds16(st.rb0, cs + (wave * 2) * 1024, st.vb, g * 32);
-  buffer_to_lds16(st.rb1, cs + (wave * 2 + 1) * 1024, st.vb, g * 32);
+  buffer_to_lds16(st.rb0, cs + (wave * 2) * 1024, st.vb, g * st.gstride);
+  buffer_to_lds16(st.rb1, cs + (wave * 2 + 1) * 1024, st.vb, g * st.gstride);
 }
 
 // Loads of group g (in this order, which the waits count on):
@@ -191,8 +193,8 @@ __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int
   if (!ODD) {
     const int p = g >> 1;
     uint8_t* sbs = ring + R::SB + (p % R::SBS) * kSbSlotBytes + wave * 512;
-    global_to_lds4(st.sbp[0] + p, sbs);
-    global_to_lds4(st.sbp[1] + p, sbs + 256);
+    global_to_lds4(st.sbp[0] + p * st.sbstride, sbs);
+    global_to_lds4(st.sbp[1] + p * st.sbstride, sbs + 256);
     if (SR) issue_codes<SR>(st, ring, g + 1, wave);   // g + 1 < G: G is even
   }
 }
@@ -489,13 +491,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   Stream st;
   st.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.A), 0, 0x7FFFFFFF, kRsrcWord3);
   st.rxp = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Apart), 0, 0x7FFFFFFF, kRsrcWord3);
+  // both matrices of a stack slot share its layout (checked on the host)
+  const bool packed = mat[0]->packed != 0;
   {
-    const uint32_t* q0 = mat[0]->q + (size_t(el) * a.N + cbase[0]) * size_t(K / 8);
-    const uint32_t* q1 = mat[1]->q + (size_t(el) * a.N + cbase[1]) * size_t(K / 8);
+    // descriptors based at the wave's first column of each block; the lane
+    // (column l32, half) reads words 4*half..4*half+3 of the group's 8
+    const uint32_t* q0 = packed ? mat[0]->q + (size_t(el) * G * a.N + cbase[0]) * 8
+                                : mat[0]->q + (size_t(el) * a.N + cbase[0]) * size_t(K / 8);
+    const uint32_t* q1 = packed ? mat[1]->q + (size_t(el) * G * a.N + cbase[1]) * 8
+                                : mat[1]->q + (size_t(el) * a.N + cbase[1]) * size_t(K / 8);
     st.rb0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q0), 0, 0x7FFFFFFF, kRsrcWord3);
     st.rb1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(q1), 0, 0x7FFFFFFF, kRsrcWord3);
-    // lane (column l32, half): words 4*half..4*half+3 of the group's 8
-    st.vb = uint32_t((l32 * (K / 8) + 4 * half) * 4);
+    st.vb = packed ? uint32_t((l32 * 8 + 4 * half) * 4) : uint32_t((l32 * (K / 8) + 4 * half) * 4);
+    st.gstride = packed ? a.N * 32 : 32;
+    st.sbstride = packed ? a.N : 1;
   }
   {
     // activation load i of wave w fills chunk positions (A w + i)*64 + lane,
@@ -517,8 +526,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     // the lane's column's G scales (lanes 32-63: biases) as G/2 pairs of groups
-    const size_t wrow = size_t(el) * a.N + cbase[cb] + l32;
-    st.sbp[cb] = reinterpret_cast<const uint32_t*>((half ? mat[cb]->b : mat[cb]->s) + wrow * size_t(G));
+    const uint16_t* sb = half ? mat[cb]->b : mat[cb]->s;
+    const int col = cbase[cb] + l32;
+    st.sbp[cb] = packed ? reinterpret_cast<const uint32_t*>(sb) + size_t(el) * (G / 2) * a.N + col
+                        : reinterpret_cast<const uint32_t*>(sb + (size_t(el) * a.N + col) * size_t(G));
   }
 
   SBPair sb;

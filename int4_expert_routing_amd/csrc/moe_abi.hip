@@ -113,12 +113,29 @@ int check_weights(const moe_q4_weights* w, int n, int N, int K) {
   if (!w) return MOE_ERR_NULL;
   if (!w->q || !w->s || !w->b) return MOE_ERR_NULL;
   if (w->n_experts != n || w->N != N || w->K != K) return MOE_ERR_SHAPE;
+  if (w->layout != MOE_Q4_CANONICAL && w->layout != MOE_Q4_PREPACKED) return MOE_ERR_SHAPE;
+  if (w->layout == MOE_Q4_PREPACKED && K % (2 * kGroup) != 0) return MOE_ERR_SHAPE;
   if (!aligned16(w->q)) return MOE_ERR_ALIGN;
   if (!aligned16(w->s) || !aligned16(w->b)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
-QStack stack_of(const moe_q4_weights* w) { return QStack{w->q, w->s, w->b}; }
+QStack stack_of(const moe_q4_weights* w) { return QStack{w->q, w->s, w->b, w->layout == MOE_Q4_PREPACKED ? 1 : 0}; }
+
+// byte offsets of the scale and bias pair planes inside a prepacked buffer
+struct PackLayout {
+  size_t s, b, total;
+};
+PackLayout pack_layout(int64_t n, int64_t N, int64_t K) {
+  const int64_t G = K / kGroup;
+  Carve c;
+  c.take(size_t(n * N * K / 2));
+  PackLayout p;
+  p.s = c.take(size_t(n * (G / 2) * N * 4));
+  p.b = c.take(size_t(n * (G / 2) * N * 4));
+  p.total = c.off;
+  return p;
+}
 
 template <typename T>
 T* at(void* base, size_t off) {
@@ -223,6 +240,7 @@ int moe_grouped_gemm_q4(const uint16_t* A, int32_t a_rows, const int32_t* sorted
   if (epilogue == MOE_EPI_SWIGLU_BF16) {
     st = check_weights(W1, n, N, K);
     if (st != MOE_OK) return st;
+    if (W1->layout != W0->layout) return MOE_ERR_SHAPE;
     if (N % 64) return MOE_ERR_UNSUPPORTED;
   } else if (N % 128) {
     return MOE_ERR_UNSUPPORTED;
@@ -284,6 +302,8 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   if ((st = check_weights(sh_gate, 1, d.I, d.H)) != MOE_OK) return st;
   if ((st = check_weights(sh_up, 1, d.I, d.H)) != MOE_OK) return st;
   if ((st = check_weights(sh_down, 1, d.H, d.I)) != MOE_OK) return st;
+  // the gate/up kernels read a stack slot's two matrices with one layout
+  if (gate->layout != up->layout || sh_gate->layout != sh_up->layout) return MOE_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(router_w) || !aligned16(y)) return MOE_ERR_ALIGN;
   if ((logit_bias && !aligned4(logit_bias)) || (logits_out && !aligned4(logits_out)) ||
       (topk_ids_out && !aligned4(topk_ids_out)) || (topk_w_out && !aligned4(topk_w_out)))
@@ -541,6 +561,38 @@ int moe_layer_forward_noalloc(const uint16_t* x, const uint16_t* router_w, const
   return layer_forward_impl(x, router_w, logit_bias, gate, up, down, sh_gate, sh_up, sh_down, dims, y, logits_out,
                             topk_ids_out, topk_w_out, ptr, size_t(MOE_NOALLOC_SCRATCH_BYTES), stream, nullptr, 0,
                             nullptr);
+}
+
+size_t moe_prepack_q4_bytes(int32_t n_experts, int32_t N, int32_t K) {
+  if (n_experts < 1 || N < 1 || K < 2 * kGroup || K % (2 * kGroup)) return 0;
+  return pack_layout(n_experts, N, K).total;
+}
+
+int moe_prepack_q4(const moe_q4_weights* src, void* dst, size_t dst_bytes, moe_q4_weights* packed, void* stream) {
+  if (!src || !packed) return MOE_ERR_NULL;
+  const int n = src->n_experts, N = src->N, K = src->K;
+  if (n < 1 || N < 1 || K < kGroup || K % kGroup) return MOE_ERR_SHAPE;
+  if (src->layout != MOE_Q4_CANONICAL) return MOE_ERR_SHAPE;
+  if (K % (2 * kGroup)) return MOE_ERR_UNSUPPORTED;   // pairs of groups
+  if (int64_t(n) * N * K > (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  int st = check_weights(src, n, N, K);
+  if (st != MOE_OK) return st;
+  if (!dst) return MOE_ERR_NULL;
+  if (!aligned16(dst)) return MOE_ERR_ALIGN;
+  const PackLayout p = pack_layout(n, N, K);
+  if (dst_bytes < p.total) return MOE_ERR_WORKSPACE;
+  uint8_t* base = static_cast<uint8_t*>(dst);
+  uint32_t* q = reinterpret_cast<uint32_t*>(base);
+  uint32_t* sp = reinterpret_cast<uint32_t*>(base + p.s);
+  uint32_t* bp = reinterpret_cast<uint32_t*>(base + p.b);
+  if (launch_prepack(stack_of(src), n, N, K, q, sp, bp, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  *packed = *src;
+  packed->q = q;
+  packed->s = reinterpret_cast<const uint16_t*>(sp);
+  packed->b = reinterpret_cast<const uint16_t*>(bp);
+  packed->layout = MOE_Q4_PREPACKED;
+  return MOE_OK;
 }
 
 int moe_quantize_q4(const uint16_t* w, int64_t rows, int32_t K, uint32_t* q, uint16_t* s, uint16_t* b,

@@ -106,6 +106,10 @@ hipError_t launch_decode_down_combine(const DownCombineArgs& da, hipStream_t str
 hipError_t launch_quantize(const uint16_t* w, long rows, int K, uint32_t* q, uint16_t* s, uint16_t* b,
                            hipStream_t stream);
 
+// Canonical stack -> packed layout (codes, scale pairs, bias pairs); K % 128 == 0.
+hipError_t launch_prepack(const QStack& src, int n, int N, int K, uint32_t* q, uint32_t* sp, uint32_t* bp,
+                          hipStream_t stream);
+
 hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
                             hipStream_t stream);
 

@@ -107,4 +107,55 @@ hipError_t launch_quantize(const uint16_t* w, long rows, int K, uint32_t* q, uin
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Prepack: the canonical stack reordered into the packed layout (see QStack):
+// codes [n][N][G][8] -> [n][G][N][8], and the scale and bias arrays
+// [n][N][G] -> pairs of consecutive groups [n][G/2][N]. One thread per 16-byte
+// half of a (row, group) code block or per pair word, indexed in output order
+// so that the writes are contiguous.
+__global__ __launch_bounds__(256) void prepack_codes_kernel(const uint32_t* __restrict__ q, uint32_t* __restrict__ out,
+                                                            long total, int N, int G) {
+  const long i = long(blockIdx.x) * blockDim.x + threadIdx.x;   // (e, g, r, half)
+  if (i >= total) return;
+  const int half = int(i & 1);
+  const long rr = i >> 1;
+  const int r = int(rr % N);
+  const long t = rr / N;
+  const int g = int(t % G);
+  const long e = t / G;
+  *reinterpret_cast<u32x4*>(out + i * 4) =
+      *reinterpret_cast<const u32x4*>(q + ((e * N + r) * G + g) * 8 + half * 4);
+}
+
+__global__ __launch_bounds__(256) void prepack_pairs_kernel(const uint16_t* __restrict__ s,
+                                                            const uint16_t* __restrict__ b, uint32_t* __restrict__ sp,
+                                                            uint32_t* __restrict__ bp, long total, int N, int G) {
+  const long i = long(blockIdx.x) * blockDim.x + threadIdx.x;   // (e, p, r)
+  if (i >= total) return;
+  const int r = int(i % N);
+  const long t = i / N;
+  const int p = int(t % (G / 2));
+  const long e = t / (G / 2);
+  const long src = ((e * N + r) * G) / 2 + p;   // the pair's word in the canonical arrays (G even)
+  sp[i] = reinterpret_cast<const uint32_t*>(s)[src];
+  bp[i] = reinterpret_cast<const uint32_t*>(b)[src];
+}
+
+hipError_t launch_prepack(const QStack& src, int n, int N, int K, uint32_t* q, uint32_t* sp, uint32_t* bp,
+                          hipStream_t stream) {
+  const int G = K / kGroup;
+  const long codes = long(n) * G * N * 2;
+  const long pairs = long(n) * (G / 2) * N;
+  if (codes > 0) {
+    hipLaunchKernelGGL(prepack_codes_kernel, dim3(unsigned((codes + 255) / 256)), dim3(256), 0, stream, src.q, q,
+                       codes, N, G);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pairs > 0)
+    hipLaunchKernelGGL(prepack_pairs_kernel, dim3(unsigned((pairs + 255) / 256)), dim3(256), 0, stream, src.s, src.b,
+                       sp, bp, pairs, N, G);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -47,29 +47,40 @@ def _need(t: torch.Tensor, dtype, name: str, device=None):
 
 @dataclasses.dataclass
 class Q4Stack:
-    """A stack of 4-bit matrices on the GPU: q int32 (bit patterns of uint32 words)
-    [n][N][K/8], s and b bf16 [n][N][K/64]."""
+    """A stack of 4-bit matrices on the GPU.
+
+    Canonical layout (layout 0): q int32 (bit patterns of uint32 words)
+    [n][N][K/8], s and b bf16 [n][N][K/64]. Prepacked layout (layout 1, from
+    prepack_q4): q int32 [n][G][N][8], s and b int32 [n][G/2][N] (bf16 pairs),
+    all views of one buffer; dims holds (n, N, K)."""
     q: torch.Tensor
     s: torch.Tensor
     b: torch.Tensor
+    layout: int = _lib.MOE_Q4_CANONICAL
+    dims: Optional[tuple] = None
 
     @property
     def n(self) -> int:
-        return self.q.shape[0]
+        return self.dims[0] if self.dims else self.q.shape[0]
 
     @property
     def N(self) -> int:
-        return self.q.shape[1]
+        return self.dims[1] if self.dims else self.q.shape[1]
 
     @property
     def K(self) -> int:
-        return self.q.shape[2] * 8
+        return self.dims[2] if self.dims else self.q.shape[2] * 8
 
     def c_struct(self) -> MoeQ4Weights:
         _need(self.q, torch.int32, "q")
-        _need(self.s, torch.bfloat16, "s", self.q.device)
-        _need(self.b, torch.bfloat16, "b", self.q.device)
-        return MoeQ4Weights(self.q.data_ptr(), self.s.data_ptr(), self.b.data_ptr(), self.n, self.N, self.K)
+        if self.layout == _lib.MOE_Q4_CANONICAL:
+            _need(self.s, torch.bfloat16, "s", self.q.device)
+            _need(self.b, torch.bfloat16, "b", self.q.device)
+        else:
+            _need(self.s, torch.int32, "s", self.q.device)
+            _need(self.b, torch.int32, "b", self.q.device)
+        return MoeQ4Weights(self.q.data_ptr(), self.s.data_ptr(), self.b.data_ptr(), self.n, self.N, self.K,
+                            self.layout)
 
     @staticmethod
     def from_host(w, device) -> "Q4Stack":
@@ -78,6 +89,30 @@ class Q4Stack:
         s = torch.from_numpy(np.ascontiguousarray(w.s).view(np.int16)).view(torch.bfloat16).to(device)
         b = torch.from_numpy(np.ascontiguousarray(w.b).view(np.int16)).view(torch.bfloat16).to(device)
         return Q4Stack(q, s, b)
+
+
+def prepack_q4(w: Q4Stack) -> Q4Stack:
+    """The stack in the prepacked layout (a new buffer; w is unchanged)."""
+    if w.layout != _lib.MOE_Q4_CANONICAL:
+        raise ValueError("prepack_q4 takes a canonical stack")
+    lib = _lib.load()
+    n, N, K = w.n, w.N, w.K
+    nbytes = int(lib.moe_prepack_q4_bytes(n, N, K))
+    if nbytes == 0:
+        raise ValueError("prepack needs K a positive multiple of 128")
+    dev = w.q.device
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src = w.c_struct()
+    out = MoeQ4Weights()
+    check(lib.moe_prepack_q4(ctypes.byref(src), _ptr(buf), nbytes, ctypes.byref(out), _stream(dev)), "moe_prepack_q4")
+    G = K // 64
+    base = buf.data_ptr()
+
+    def view(ptr, count, shape):
+        off = ptr - base
+        return buf[off: off + 4 * count].view(torch.int32).view(*shape)
+    return Q4Stack(view(out.q, n * G * N * 8, (n, G, N, 8)), view(out.s, n * (G // 2) * N, (n, G // 2, N)),
+                   view(out.b, n * (G // 2) * N, (n, G // 2, N)), layout=_lib.MOE_Q4_PREPACKED, dims=(n, N, K))
 
 
 def bf16_from_bits(a: np.ndarray, device) -> torch.Tensor:
@@ -195,6 +230,10 @@ class MoEWeights:
     @property
     def I(self) -> int:
         return self.gate.N
+
+    def prepacked(self, stacks=("gate", "up", "down", "sh_gate", "sh_up", "sh_down")) -> "MoEWeights":
+        """The same layer with the named stacks in the prepacked layout."""
+        return dataclasses.replace(self, **{n: prepack_q4(getattr(self, n)) for n in stacks})
 
     @staticmethod
     def from_host(inp, device) -> "MoEWeights":
