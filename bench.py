@@ -4,6 +4,11 @@ A step is one moe_layer_forward over one batch of synthetic tokens: router GEMM,
 top-k, routing tables, gate/up grouped GEMM with SwiGLU, down grouped GEMM,
 shared expert and combine. Inputs are resident in HBM before the timed region.
 
+Every timed layer reads its weights in the prepacked layout (moe_prepack_q4,
+run once before timing, as a model load would); canonical_layout repeats the
+T=4096 layer on the canonical layout for comparison (--layout canonical times
+everything on it).
+
 Prints one JSON line: value = tokens/s of the T=4096 layer, roofline = the
 gate/up grouped GEMM (the dominant kernel) against the bf16 dense MFMA peak,
 cpu_baseline = the fp64 oracle on the host cores, decode = the T=1 and T=8
@@ -65,14 +70,17 @@ def random_weights(ops, torch, dev, E, H, I, seed):
                           sh_gate=stack(1, I, H), sh_up=stack(1, I, H), sh_down=stack(1, H, I))
 
 
-def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, reps=25):
+def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, reps=25, prepack=False):
     """Layer calls at T tokens, captured as one HIP graph of `calls` calls that
     cycle over n_sets weight sets and `calls` fresh inputs, replayed `reps`
     times; bytes per call = the distinct experts the call routes to, plus the
-    shared expert, the router matrix, x and y."""
+    shared expert, the router matrix, x and y. prepack: every set (w0
+    included) is prepacked before timing."""
     import ctypes
     E, H, I = w0.E, w0.H, w0.I
     sets = [w0] + [random_weights(ops, torch, dev, E, H, I, 1000 + i) for i in range(n_sets - 1)]
+    if prepack:
+        sets = [ws.prepacked() for ws in sets]
     structs = [[s.c_struct() for s in (w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)] for w in sets]
     gx = torch.Generator(device=dev)
     gx.manual_seed(77)
@@ -126,7 +134,7 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
                       f"{reps} replays timed with events"}
 
 
-def prefill_measure(lib, _lib, ops, torch, dev, w, T, k, zipf=None, steps=10, warmup=3):
+def prefill_measure(lib, _lib, ops, torch, dev, w, T, k, zipf=None, steps=10, warmup=3, weight_bytes=None):
     """Layer calls at T tokens on the same layer weights (x drawn on the device,
     N(0,1) in bf16; optional Zipf logit bias -zipf*ln(e+1)), timed with events
     around `steps` back-to-back calls on the launch stream."""
@@ -171,6 +179,13 @@ def prefill_measure(lib, _lib, ops, torch, dev, w, T, k, zipf=None, steps=10, wa
            "logit_bias": f"zipf{zipf}" if zipf is not None else None,
            "experts_hit": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max()),
            "method": f"{steps} back-to-back layer calls timed with events"}
+    if weight_bytes:
+        # weights of the experts this call routed to (+ shared, + router), as HBM bytes per second
+        hit = int((counts > 0).sum())
+        nbytes = (hit + 1) * PER_EXPERT_BYTES + E * H * 2 + 2 * T * H * 2
+        out["weight_and_io_bytes"] = nbytes
+        out["GB_per_s"] = nbytes / (ms * 1e-3) / 1e9
+        out["frac_hbm"] = out["GB_per_s"] / PEAK_HBM_GBS
     del x, y, ws, ids
     return out
 
@@ -228,16 +243,48 @@ def read_traffic():
     return float(kv["traffic_bytes_per_launch"])
 
 
-def counter_values(run_dir, counter):
-    """{dispatch kernel name: [value per dispatch]} from a rocprofv3 --pmc csv run."""
+def counter_values(run_dir, counter, by_grid=False):
+    """{dispatch kernel name (and grid size): [value per dispatch]} from a rocprofv3 --pmc csv run."""
     import csv
     import glob
     out = {}
     for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter:
-                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                key = (r["Kernel_Name"], int(r["Grid_Size"])) if by_grid else r["Kernel_Name"]
+                out.setdefault(key, []).append(float(r["Counter_Value"]))
     return out
+
+
+def write_counter_summary(out_path, title, fetch_dir, write_dir, copy_mib, cmd_fetch, cmd_write):
+    """HBM bytes per dispatch of every library kernel in two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), grouped by kernel and grid
+    size, each counter scaled by what it reads for the calibration copy kernel
+    of copy_mib MiB (read and written once) in the same run."""
+    fv, wv = counter_values(fetch_dir, "FETCH_SIZE", True), counter_values(write_dir, "WRITE_SIZE", True)
+    c_f = [v for (kname, _), vs in fv.items() if "copyBuffer" in kname for v in vs]
+    c_w = [v for (kname, _), vs in wv.items() if "copyBuffer" in kname for v in vs]
+    if not (c_f and c_w):
+        raise SystemExit("calibration copy kernel missing from the counter runs")
+    true_bytes = copy_mib * 2**20
+    f_scale = true_bytes / (max(c_f) * 1024.0)
+    w_scale = true_bytes / (max(c_w) * 1024.0)
+    lines = [title, f"  FETCH_SIZE pass: {cmd_fetch}", f"  WRITE_SIZE pass: {cmd_write}",
+             f"  calibration copy kernel: {copy_mib} MiB read + written once; counter reads FETCH {max(c_f):.0f} KiB, "
+             f"WRITE {max(c_w):.0f} KiB -> scale fetch {f_scale:.4f}, write {w_scale:.4f}",
+             f"  {'kernel':58s} {'grid':>9s} {'n':>4s} {'fetch MB':>10s} {'write MB':>10s}  (median per dispatch)"]
+    for key in sorted(fv, key=lambda kk: (kk[0], kk[1])):
+        kname, grid = key
+        if "moe::" not in kname or key not in wv:
+            continue
+        fb = float(np.median(fv[key])) * 1024.0 * f_scale
+        wb = float(np.median(wv[key])) * 1024.0 * w_scale
+        short = kname.replace("void ", "").split("(")[0]
+        lines.append(f"  {short[:58]:58s} {grid:9d} {len(fv[key]):4d} {fb / 1e6:10.3f} {wb / 1e6:10.3f}")
+    lines.append(f"source_hash={kernel_source_hash()}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def write_traffic_summary(fetch_dir, write_dir, copy_mib, cmd_fetch, cmd_write):
@@ -283,27 +330,42 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-quantize", action="store_true")
     p.add_argument("--no-prefill-sweep", action="store_true")
+    p.add_argument("--layout", choices=("prepacked", "canonical"), default="prepacked",
+                   help="weight layout of every timed layer (prepacked once, before timing)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after the timed steps, launch one device copy of this many MiB (counter calibration)")
     p.add_argument("--write-traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CMD_FETCH", "CMD_WRITE"),
                    help="build the gate/up traffic summary from two rocprofv3 --pmc runs and exit")
+    p.add_argument("--write-counter-summary", nargs=6,
+                   metavar=("OUT", "TITLE", "FETCH_DIR", "WRITE_DIR", "CMD_FETCH", "CMD_WRITE"),
+                   help="per-kernel HBM bytes per dispatch from two rocprofv3 --pmc runs, and exit")
     return p.parse_args()
 
 
-def cpu_baseline(inp):
-    """Time the fp64 oracle (as it stands) on the whole workload once."""
+def cpu_baseline(inp, small):
+    """Time the fp64 oracle as it stands: the median of 3 full layer passes over
+    the timed workload with every BLAS thread, and one single-thread pass over
+    the T=512 workload."""
     import oracle.moe_oracle as om
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    om.moe_layer(inp)
-    dt = time.perf_counter() - t0
-    return {"value": inp.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full layer pass, T={inp.T} tokens (all of the timed workload), {dt:.1f} s",
-            "seconds": dt}
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        om.moe_layer(inp)
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        om.moe_layer(small)
+        dt1 = time.perf_counter() - t0
+    return {"value": inp.T / dt, "unit": "tokens/s", "cores": blas, "host_cpu_count": os.cpu_count(),
+            "blas_threads": blas, "kind": "oracle",
+            "sample": f"full layer passes over the T={inp.T} workload (all of it), median of 3: "
+                      f"{', '.join(f'{r:.2f}' for r in runs)} s",
+            "seconds": dt,
+            "single_thread_T512": {"value": small.T / dt1, "unit": "tokens/s", "cores": 1, "seconds": dt1,
+                                   "sample": f"one full layer pass, T={small.T}, BLAS limited to 1 thread"}}
 
 
 def main():
@@ -311,6 +373,10 @@ def main():
     if args.write_traffic_summary:
         fd, wd, cf, cw = args.write_traffic_summary
         write_traffic_summary(fd, wd, 512, cf, cw)
+        return
+    if args.write_counter_summary:
+        op_, title, fd, wd, cf, cw = args.write_counter_summary
+        write_counter_summary(op_, title, fd, wd, 512, cf, cw)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this library runs on a "
@@ -331,7 +397,9 @@ def main():
     cfg = CONFIGS[args.config]
     inp = make_config(args.config, seed=args.seed)
     T, H, I, E, k = inp.T, inp.H, inp.I, inp.E, inp.k
-    w = ops.MoEWeights.from_host(inp, dev)
+    w_canon = ops.MoEWeights.from_host(inp, dev)
+    packed = args.layout == "prepacked"
+    w = w_canon.prepacked() if packed else w_canon
     x = ops.bf16_from_bits(inp.x, dev)
     layer = ops.MoELayer(w, k, T)
     y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
@@ -398,7 +466,9 @@ def main():
         "config": {"workload": f"{args.config}: MoE layer T={T} H={H} I={I} E={E} top-{k} + 1 shared expert, "
                                "int4 g64 affine weights (bf16 scale/bias), bf16 activations",
                    "T": T, "H": H, "I": I, "E": E, "k": k, "seed": args.seed,
-                   "logit_bias": "zipf1.2" if cfg.get("zipf") else None},
+                   "logit_bias": "zipf1.2" if cfg.get("zipf") else None,
+                   "weight_layout": ("prepacked (moe_prepack_q4, once before timing)" if packed
+                                     else "canonical")},
         "layer_pct_mfma_peak": 100.0 * flops / (ms_per_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "layer_gpu_ms_events": gpu_ms,
         "stage_ms": {n: float(v) for n, v in zip(names, stage_ms)},
@@ -414,23 +484,28 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+    if packed and not args.no_prefill_sweep:
+        # the same workload with the weights in the canonical layout
+        c = prefill_measure(lib, _lib, ops, torch, dev, w_canon, T, k, zipf=cfg.get("zipf"))
+        out["canonical_layout"] = {"ms_per_layer": c["ms_per_layer"], "tokens_per_s": c["tokens_per_s"],
+                                   "method": c["method"]}
     if not args.no_decode:
         out["decode"] = {}
         for dname in ("decode1", "decode8"):
             dinp = make_config(dname, seed=args.seed)
             dw = ops.MoEWeights.from_host(dinp, dev)
-            out["decode"][dname] = decode_measure(lib, _lib, ops, torch, dev, dw, dinp.T, dinp.k)
+            out["decode"][dname] = decode_measure(lib, _lib, ops, torch, dev, dw, dinp.T, dinp.k, prepack=packed)
             del dw
     if not args.no_prefill_sweep:
         out["prefill"] = {
-            "prefill512": prefill_measure(lib, _lib, ops, torch, dev, w, 512, k),
+            "prefill512": prefill_measure(lib, _lib, ops, torch, dev, w, 512, k, weight_bytes=True),
             "prefill4096_zipf": prefill_measure(lib, _lib, ops, torch, dev, w, 4096, k, zipf=1.2),
             "prefill32768": prefill_measure(lib, _lib, ops, torch, dev, w, 32768, k, steps=5, warmup=2),
         }
     if not args.no_quantize:
         out["quantize"] = quantize_measure(ops, torch, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp)
+        out["cpu_baseline"] = cpu_baseline(inp, make_config("prefill512", seed=args.seed))
     print(json.dumps(out), flush=True)
 
 
