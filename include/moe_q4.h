@@ -42,9 +42,17 @@ extern "C" {
 /* Rows per GEMM tile of moe_grouped_gemm_q4's tile maps, and the default tile
  * height of moe_layer_forward (dims.block_rows = 0). */
 #define MOE_GEMM_BLOCK_ROWS 128
-/* Bytes at the start of a moe_layer_forward workspace that must be zero
- * before the first layer call; every layer call leaves them zero. */
-#define MOE_WORKSPACE_HEAD_BYTES 8448
+/* Bytes at the start of a moe_layer_forward workspace that hold state the
+ * library keeps between layer calls (completion counters, the decode kernel's
+ * epoch and its tagged hand-off words): zero before the first layer call, and
+ * changed by nothing else afterwards (zeroing them again between calls is
+ * allowed). */
+#define MOE_WORKSPACE_HEAD_BYTES 175872
+/* Byte offset, inside that head, of a uint32 status word: nonzero after a
+ * decode-sized call whose persistent kernel gave up waiting (a bounded wait
+ * ran out, e.g. when other work kept its workgroups from being resident);
+ * that call's outputs are then invalid. It stays set until the head is zeroed. */
+#define MOE_WORKSPACE_STATUS_OFFSET 8576
 /* Largest supported expert count and top-k. */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
@@ -214,13 +222,11 @@ size_t moe_gemm_workspace_bytes(int32_t a_rows, int32_t K);
  *   topk_ids_out device int32 [T][k] or NULL
  *   topk_w_out   device float [T][k] or NULL
  *   workspace    device, at least moe_workspace_bytes(dims) bytes. Its first
- *                MOE_WORKSPACE_HEAD_BYTES bytes hold a completion counter and
- *                per-(token, expert) logit slots that calls with T <= 4 use to
- *                run routing as one launch: they must be zero before the
- *                first layer call (allocate the workspace zeroed) and every
- *                layer call leaves them zero. moe_route never touches them;
- *                any other use of the buffer must zero them again before it
- *                serves a layer call. Calls that share a workspace must not
+ *                MOE_WORKSPACE_HEAD_BYTES bytes hold state kept between calls
+ *                (see MOE_WORKSPACE_HEAD_BYTES): allocate the workspace zeroed,
+ *                and let nothing else write that head (moe_route never touches
+ *                it; any other use of the buffer must zero it again before it
+ *                serves a layer call). Calls that share a workspace must not
  *                run concurrently.
  */
 int moe_layer_forward(const uint16_t* x, const uint16_t* router_w, const float* logit_bias,
@@ -253,6 +259,13 @@ typedef struct {
      * for on the side stream, join_event the other way round. */
     void* fork_event;
     void* join_event;
+    /* Nonzero: calls with T <= 8, T * k <= 64, H == 2048 and I == 256 or 512
+     * run the whole layer as one persistent launch (routing, gate/up and down
+     * + combine as work items of one resident grid, handed over through
+     * tagged words in the workspace head; see MOE_WORKSPACE_STATUS_OFFSET).
+     * Zero (default): three launches. Same results up to the logits' summation
+     * order at 5 <= T <= 8. Ignored with a side stream. */
+    int32_t persistent_decode;
 } moe_layer_options;
 
 /*

@@ -27,7 +27,8 @@ MOE_Q4_GROUP = 64
 MOE_GEMM_BLOCK_ROWS = 128
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
-MOE_WORKSPACE_HEAD_BYTES = 8448
+MOE_WORKSPACE_HEAD_BYTES = 175872
+MOE_WORKSPACE_STATUS_OFFSET = 8576
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -48,7 +49,8 @@ class MoeQ4Weights(ctypes.Structure):
 
 class MoeLayerOptions(ctypes.Structure):
     _fields_ = [("shared_gate", ctypes.c_void_p), ("side_stream", ctypes.c_void_p),
-                ("fork_event", ctypes.c_void_p), ("join_event", ctypes.c_void_p)]
+                ("fork_event", ctypes.c_void_p), ("join_event", ctypes.c_void_p),
+                ("persistent_decode", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p

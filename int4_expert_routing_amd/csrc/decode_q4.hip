@@ -11,7 +11,7 @@
 // group folds as acc += 16 s_g P_g + (b_g - 16 s_g) X_g, where X_g is the
 // row's group sum, computed in fp32 from the staged row.
 #include "gemm_tiles.h"
-#include "moe_internal.h"
+#include "route_block.h"
 
 namespace moe {
 
@@ -152,8 +152,11 @@ struct DecTile {
   uint32_t tok;   // token of row j at bits 4j..4j+3
 };
 
+// h_tag: null (h stored as bf16 into a.out), or the persistent kernel's tagged
+// h rows [rows][N/2] (each u64: tag << 32 | two bf16 of h in operand order)
 template <int NR, int STEPS, int KS>
-__device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti, int cb, uint8_t* smem, int nrmax) {
+__device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti, int cb, uint8_t* smem, int nrmax,
+                                            uint64_t* h_tag = nullptr, uint32_t tag = 0) {
   using S = DecShape<STEPS, KS>;
   constexpr int K = S::K, G = S::G, GQ = S::GQ, PARTS = S::PARTS;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -271,8 +274,17 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const DecTile& ti
   if (tid < NR * 2) {
     // row tid/2, chunk tid%2 of this column block, stored in the operand order
     const int r = tid >> 1, ch = tid & 1;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(hs + r * 16 + ch * 8);
-    *reinterpret_cast<u32x4*>(out + size_t(ti.r0 + r) * a.N + cb * 16 + ch * 8) = permute_chunk(v);
+    const u32x4 v = permute_chunk(*reinterpret_cast<const u32x4*>(hs + r * 16 + ch * 8));
+    if (h_tag) {
+      uint64_t* dst = h_tag + size_t(ti.r0 + r) * (a.N / 2) + (cb * 16 + ch * 8) / 2;
+      const uint64_t hi = uint64_t(tag) << 32;
+      __hip_atomic_store(dst + 0, hi | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1, hi | v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 2, hi | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 3, hi | v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *reinterpret_cast<u32x4*>(out + size_t(ti.r0 + r) * a.N + cb * 16 + ch * 8) = v;
+    }
   }
 }
 
@@ -335,19 +347,25 @@ void decode_swiglu_kernel(GemmArgs a, const u32x4* tile_desc, int nrmax) {
 __host__ __device__ constexpr int dc_wave_bytes(int K) { return dec_row_bytes(K) + (K / kGroup) * 4; }
 constexpr int kDcMaxWaves = 16;
 
-template <int STEPS>
-__global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(DownCombineArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
+// One (token t, 16 output columns) unit of the down projection and combine,
+// run by the W waves of a workgroup (LDS: W * dc_wave_bytes(K) + W * 33 floats).
+// pair(j) gives (expert, h row, weight) of the token's routed pair j < k;
+// stage_row(row, xs) writes that h row (K bf16 in operand order) into the
+// wave's LDS row xs with the wave's 64 lanes.
+struct DcPair {
+  int el, row;
+  float w;
+};
+
+template <int STEPS, class PairFn, class RowFn>
+__device__ __forceinline__ void down_combine_unit(const DownCombineArgs& a, int t, int col0, int W, uint8_t* smem,
+                                                  PairFn pair, RowFn stage_row) {
   constexpr int K = STEPS * 128;
   constexpr int G = K / kGroup;
   constexpr int GQ = STEPS / 2;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int W = blockDim.x >> 6;
   const int c = lane & 15, kq = lane >> 4;
-  const int ncb = a.N / 16;
-  const int t = blockIdx.x / ncb;
-  const int col0 = (blockIdx.x % ncb) * 16;
   uint8_t* wl = smem + wave * dc_wave_bytes(K);
   uint8_t* xs = wl;                                                     // the pair's h row
   float* Xt = reinterpret_cast<float*>(wl + dec_row_bytes(K));          // its group sums
@@ -361,9 +379,9 @@ __global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(D
   // order after the pairs); the shared pair then enters with weight g
   if (gated) {
     float d = 0.0f;
-    for (int c = tid * 8; c < a.N; c += W * 64 * 8) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + size_t(t) * a.N + c);
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(a.shared_gate + c);
+    for (int cc = tid * 8; cc < a.N; cc += W * 64 * 8) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + size_t(t) * a.N + cc);
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(a.shared_gate + cc);
       d = dot2(xv.x, wv.x, d);
       d = dot2(xv.y, wv.y, d);
       d = dot2(xv.z, wv.z, d);
@@ -376,21 +394,17 @@ __global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(D
   float tot = 0.0f, sacc = 0.0f;
   for (int j = wave; j <= a.k; j += W) {
     const bool routed = j < a.k;
-    const size_t f = size_t(t) * a.k + (routed ? j : 0);
-    const int el = routed ? a.topk_ids[f] : 0;
-    const int row = routed ? a.row_of_pair[f] : a.shared_row0 + t;
-    const float wj = routed ? a.topk_w[f] : 1.0f;
+    DcPair pj{0, a.shared_row0 + t, 1.0f};
+    if (routed) pj = pair(j);
     const QStack& mat = routed ? a.down : a.down_shared;
     // the lane's codes: quarter kq of its column's K (GQ groups)
     u32x4 w[STEPS];
-    load_code_steps<STEPS>(mat, el, a.N, K, col0 + c, kq * GQ, w);
+    load_code_steps<STEPS>(mat, pj.el, a.N, K, col0 + c, kq * GQ, w);
     uint16_t sv[GQ], bv[GQ];
-    load_scale_bias<GQ>(mat, el, a.N, K, col0 + c, kq * GQ, sv, bv);
+    load_scale_bias<GQ>(mat, pj.el, a.N, K, col0 + c, kq * GQ, sv, bv);
     // stage the h row (already in operand order) and its fp32 group sums
     __builtin_amdgcn_wave_barrier();   // the previous pair's reads of xs and Xt are done
-    const uint16_t* hr = a.h + size_t(row) * K;
-    for (int ch = lane; ch < K / 8; ch += 64)
-      *reinterpret_cast<u32x4*>(xs + dec_off(K, 0, ch * 8)) = *reinterpret_cast<const u32x4*>(hr + ch * 8);
+    stage_row(pj.row, xs);
     __builtin_amdgcn_wave_barrier();
     if (lane < G) {
       float sum = 0.0f;
@@ -425,7 +439,7 @@ __global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(D
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);
     if (routed || !gated)
-      tot = __builtin_fmaf(wj, acc, tot);
+      tot = __builtin_fmaf(pj.w, acc, tot);
     else
       sacc = acc;
   }
@@ -447,6 +461,26 @@ __global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(D
     }
     a.y[size_t(t) * a.N + col0 + tid] = uint16_t(f32_to_bf16_rne(sum));
   }
+}
+
+template <int STEPS>
+__global__ __launch_bounds__(kDcMaxWaves * 64) void decode_down_combine_kernel(DownCombineArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int K = STEPS * 128;
+  const int ncb = a.N / 16;
+  const int t = blockIdx.x / ncb;
+  const int col0 = (blockIdx.x % ncb) * 16;
+  const int lane = threadIdx.x & 63;
+  auto pair = [&](int j) {
+    const size_t f = size_t(t) * a.k + j;
+    return DcPair{a.topk_ids[f], a.row_of_pair[f], a.topk_w[f]};
+  };
+  auto stage_row = [&](int row, uint8_t* xs) {
+    const uint16_t* hr = a.h + size_t(row) * K;
+    for (int ch = lane; ch < K / 8; ch += 64)
+      *reinterpret_cast<u32x4*>(xs + dec_off(K, 0, ch * 8)) = *reinterpret_cast<const u32x4*>(hr + ch * 8);
+  };
+  down_combine_unit<STEPS>(a, t, col0, int(blockDim.x >> 6), smem, pair, stage_row);
 }
 
 bool decode_down_combine_supported(int N, int K) {
@@ -500,6 +534,336 @@ hipError_t launch_decode(const GemmArgs& ga, const u32x4* tile_desc, int max_row
                          tile_desc, max_rows);
       break;
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Persistent decode kernel: the whole few-token layer in one launch.
+//
+// The three launches above leave a chain of dependent memory round trips with
+// a kernel boundary between each pair of stages; the weight stream itself is a
+// small part of a decode call. Here one grid of workgroups takes work items in
+// phase order (item index = phase order):
+//   routing items (one wave per expert: the logits of every token),
+//   one top-k item (top-k, softmax and the routing tables, as in the one-block
+//     routing kernel),
+//   gate/up items (one (row tile, 16 columns of h) each; tile 0 is the shared
+//     expert, which needs no routing),
+//   down items (one (token, 16 output columns) each, the down projection fused
+//     with the weighted combine).
+// Workgroup b takes items b, b + gridDim.x, ... in increasing order, and every
+// workgroup is resident at once (the host sizes the grid from the occupancy),
+// so an item only ever waits for items of earlier phases, which their
+// workgroups reach before any later item: no wait can block the grid.
+//
+// Hand-off without fences: every value one item passes to another (a logit, a
+// tile descriptor, a pair's expert, row and weight, a pair of bf16 of h) is
+// written as one 64-bit agent-scope atomic store tag << 32 | value, and read
+// with agent-scope atomic loads until the tag matches (AMDGPU memory model:
+// agent-scope atomics are coherent for every workgroup and become visible in
+// finite time). The tag is the call's epoch + 1: every workgroup reads the
+// epoch word when it starts, and the last workgroup to finish advances it
+// (and returns the exit counter to zero), so a later call can never take a
+// stale word for a fresh one. Every wait is bounded by the 100 MHz real-time
+// counter; a wait that gives up writes 1 to the status word (the call's
+// results are then invalid) instead of hanging the GPU.
+constexpr int kFzThreads = 512;
+constexpr int kFzWaves = kFzThreads / kWave;
+constexpr int kFzMaxT = kDecodeMaxRows;
+constexpr int kFzMaxPairs = 64;                              // T * k
+constexpr int kFzMaxRows = kFzMaxPairs + kFzMaxT;            // routed + shared h rows
+constexpr int kFzMaxTiles = kFzMaxPairs / 32 + kFzMaxPairs;  // routed tiles at block rows >= 32
+constexpr int kFzMaxHalfI = 256;                             // I <= 512
+constexpr uint64_t kFzPollTicks = 20000000;                  // 200 ms of the 100 MHz counter
+// byte offsets inside the region (the workspace head after the one-launch
+// routing's part)
+constexpr size_t kFzEpoch = 0, kFzExit = 64, kFzStatus = 128, kFzNtiles = 192;
+constexpr size_t kFzSlots = 256;                                                    // [kFzMaxT][kMaxExperts]
+constexpr size_t kFzDesc = kFzSlots + size_t(kFzMaxT) * kMaxExperts * 8;           // [kFzMaxTiles][4]
+constexpr size_t kFzPairs = kFzDesc + size_t((kFzMaxTiles * 32 + 255) / 256) * 256; // [kFzMaxPairs][2]
+constexpr size_t kFzH = kFzPairs + size_t(kFzMaxPairs) * 16;                       // [kFzMaxRows][kFzMaxHalfI]
+constexpr size_t kFzBytes = kFzH + size_t(kFzMaxRows) * kFzMaxHalfI * 8;
+static_assert(kHandoffBytes + kFzBytes == MOE_WORKSPACE_HEAD_BYTES, "workspace head size in the header");
+
+__device__ __forceinline__ uint64_t fz_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fz_store(uint64_t* p, uint32_t tag, uint32_t v) {
+  __hip_atomic_store(p, (uint64_t(tag) << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The value of *p once it carries the tag. Every lane of the wave calls this
+// (need == false: the lane waits for nothing); bounded as described above.
+__device__ __forceinline__ uint32_t fz_wait(const uint64_t* p, uint32_t tag, bool need, uint32_t* status) {
+  uint64_t v = need ? fz_load(p) : (uint64_t(tag) << 32);
+  if (__all((v >> 32) == tag)) return uint32_t(v);
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    if ((v >> 32) != tag) v = fz_load(p);
+    if (__all((v >> 32) == tag)) break;
+    if (wall_clock64() - t0 > kFzPollTicks) {
+      if ((v >> 32) != tag) __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
+  return uint32_t(v);
+}
+
+struct FusedArgs {
+  RouteArgs ra;        // router, top-k and tables (finish mode, with tile descriptors)
+  GemmArgs g;          // gate/up (A = x in natural order, NT = N / 16)
+  DownCombineArgs d;   // down + combine
+  uint8_t* fz;         // the region described above
+  int n_route, n_gu, n_dn;
+};
+
+// Routing item: wave w computes expert (item * kFzWaves + w)'s logit of every
+// token (lane l takes every 64th 8-element chunk of H; a fixed lane tree).
+__device__ __forceinline__ void fz_route_item(const FusedArgs& f, int item, uint32_t tag) {
+  const RouteArgs& a = f.ra;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = item * kFzWaves + wave;
+  const int T = a.T, H = a.H, E = a.E, nch = H / 8;
+  float acc[kFzMaxT];
+#pragma unroll
+  for (int t = 0; t < kFzMaxT; ++t) acc[t] = 0.0f;
+  if (e < E) {
+    const uint16_t* wr = a.wr + size_t(e) * H;
+    for (int c0 = lane; c0 < nch; c0 += 2 * kWave) {
+      u32x4 wv[2], xv[2][kFzMaxT];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ch = min(c0 + i * kWave, nch - 1);
+        wv[i] = *reinterpret_cast<const u32x4*>(wr + ch * 8);
+#pragma unroll
+        for (int t = 0; t < kFzMaxT; ++t)
+          if (t < T) xv[i][t] = *reinterpret_cast<const u32x4*>(a.x + size_t(t) * H + ch * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (c0 + i * kWave >= nch) break;
+#pragma unroll
+        for (int t = 0; t < kFzMaxT; ++t) {
+          if (t < T) {
+            acc[t] = dot2(wv[i].x, xv[i][t].x, acc[t]);
+            acc[t] = dot2(wv[i].y, xv[i][t].y, acc[t]);
+            acc[t] = dot2(wv[i].z, xv[i][t].z, acc[t]);
+            acc[t] = dot2(wv[i].w, xv[i][t].w, acc[t]);
+          }
+        }
+      }
+    }
+  }
+  float mine = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kFzMaxT; ++t) {
+    const float v = wave_sum_f32(acc[t]);
+    mine = lane == t ? v : mine;
+  }
+  if (e < E && lane < T) {
+    float v = mine;
+    if (a.bias) v = v + a.bias[e];
+    v = v + 0.0f;   // turns -0 into +0
+    fz_store(reinterpret_cast<uint64_t*>(f.fz + kFzSlots) + lane * E + e, tag, __float_as_uint(v));
+  }
+}
+
+// Top-k item: the logits into LDS (and logits_out), the routing block, then
+// the tile descriptors, the tile count and each pair's (expert, row, weight)
+// published as tagged words.
+__device__ __forceinline__ void fz_topk_item(const FusedArgs& f, uint32_t tag, float* lg) {
+  const RouteArgs& a = f.ra;
+  const int T = a.T, E = a.E, k = a.k, tid = threadIdx.x;
+  uint32_t* status = reinterpret_cast<uint32_t*>(f.fz + kFzStatus);
+  const uint64_t* slots = reinterpret_cast<const uint64_t*>(f.fz + kFzSlots);
+  for (int i0 = 0; i0 < T * E; i0 += kFzThreads) {
+    const int i = i0 + tid;
+    const float v = __uint_as_float(fz_wait(slots + min(i, T * E - 1), tag, i < T * E, status));
+    if (i < T * E) {
+      lg[i] = v;
+      a.logits_out[i] = v;
+    }
+  }
+  __syncthreads();
+  RouteArgs b = a;
+  b.logits_in = lg;
+  b.coherent = 0;
+  b.n_parts = 1;
+  b.bias = nullptr;
+  b.logits_out = nullptr;
+  b.finish = 1;
+  topk_block(b, 0);
+  __syncthreads();   // this workgroup's table stores are visible to its threads
+  const int nt = *b.num_tiles;
+  uint64_t* desc = reinterpret_cast<uint64_t*>(f.fz + kFzDesc);
+  if (tid < nt) {
+    const u32x4 d = b.tile_desc[tid];
+    fz_store(desc + 4 * tid + 0, tag, d.x);
+    fz_store(desc + 4 * tid + 1, tag, d.y);
+    fz_store(desc + 4 * tid + 2, tag, d.z);
+    fz_store(desc + 4 * tid + 3, tag, d.w);
+  }
+  uint64_t* pairs = reinterpret_cast<uint64_t*>(f.fz + kFzPairs);
+  if (tid < T * k) {
+    fz_store(pairs + 2 * tid, tag, uint32_t(b.topk_ids[tid]) | (uint32_t(b.row_of_pair[tid]) << 16));
+    fz_store(pairs + 2 * tid + 1, tag, __float_as_uint(b.topk_w[tid]));
+  }
+  if (tid == 0) fz_store(reinterpret_cast<uint64_t*>(f.fz + kFzNtiles), tag, uint32_t(nt));
+}
+
+// Gate/up item: one (row tile, 16 columns of h); h goes out as tagged words.
+__device__ __forceinline__ void fz_gu_item(const FusedArgs& f, int gi, uint32_t tag, uint8_t* smem) {
+  __shared__ uint32_t desc_s[5];
+  const GemmArgs& g = f.g;
+  const int tile = gi / g.NT, cb = gi % g.NT;
+  uint32_t* status = reinterpret_cast<uint32_t*>(f.fz + kFzStatus);
+  DecTile ti;
+  if (tile == 0) {
+    ti.e = g.E;
+    ti.r0 = g.routed_rows;
+    ti.n = g.shared_rows;
+    ti.tok = 0u;
+    for (int j = 0; j < g.shared_rows; ++j) ti.tok |= uint32_t(j) << (4 * j);
+  } else {
+    const int i = tile - 1;
+    if (threadIdx.x < kWave) {
+      const int l = threadIdx.x;
+      const uint32_t nt = fz_wait(reinterpret_cast<const uint64_t*>(f.fz + kFzNtiles), tag, true, status);
+      uint32_t dv = 0;
+      if (uint32_t(i) < nt)
+        dv = fz_wait(reinterpret_cast<const uint64_t*>(f.fz + kFzDesc) + 4 * i + min(l, 3), tag, l < 4, status);
+      if (l == 0) desc_s[4] = nt;
+      if (l < 4) desc_s[l] = dv;
+    }
+    __syncthreads();
+    if (uint32_t(i) >= min(desc_s[4], uint32_t(kFzMaxTiles))) return;   // uniform: no such tile in this call
+    // the values are checked to stay in bounds even if a wait gave up
+    ti.n = int(min(desc_s[2], uint32_t(g.shared_rows)));
+    ti.e = int(min(desc_s[0], uint32_t(g.E - 1)));
+    ti.r0 = int(min(desc_s[1], uint32_t(g.routed_rows - ti.n)));
+    ti.tok = 0u;
+    for (int j = 0; j < ti.n; ++j) ti.tok |= min((desc_s[3] >> (4 * j)) & 15u, uint32_t(g.shared_rows - 1)) << (4 * j);
+  }
+  uint64_t* h = reinterpret_cast<uint64_t*>(f.fz + kFzH);
+  switch (ti.n) {
+    case 1: swiglu_tile<1, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
+    case 2: swiglu_tile<2, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
+    case 3: swiglu_tile<3, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
+    case 4: swiglu_tile<4, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
+    case 5: swiglu_tile<5, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
+    case 6: swiglu_tile<6, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
+    case 7: swiglu_tile<7, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
+    case 8: swiglu_tile<8, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
+    default: break;   // 1..T rows per tile (a wait that gave up may leave garbage here)
+  }
+}
+
+// Down item: one (token, 16 output columns); the pairs and the h rows come
+// from tagged words.
+template <int DSTEPS>
+__device__ __forceinline__ void fz_dn_item(const FusedArgs& f, int di, uint32_t tag, uint8_t* smem) {
+  constexpr int K = DSTEPS * 128;
+  const DownCombineArgs& a = f.d;
+  const int ncb = a.N / 16;
+  const int t = di / ncb, col0 = (di % ncb) * 16;
+  const int lane = threadIdx.x & 63;
+  uint32_t* status = reinterpret_cast<uint32_t*>(f.fz + kFzStatus);
+  const uint64_t* pairs = reinterpret_cast<const uint64_t*>(f.fz + kFzPairs);
+  const uint64_t* h = reinterpret_cast<const uint64_t*>(f.fz + kFzH);
+  auto pair = [&](int j) {
+    const uint64_t* pw = pairs + 2 * (t * a.k + j);
+    const uint32_t ir = fz_wait(pw, tag, true, status);
+    const uint32_t wb = fz_wait(pw + 1, tag, true, status);
+    // in bounds even if a wait gave up
+    return DcPair{min(int(ir & 0xFFFFu), f.ra.E - 1), min(int(ir >> 16), f.g.routed_rows - 1), __uint_as_float(wb)};
+  };
+  auto stage_row = [&](int row, uint8_t* xs) {
+    const uint64_t* hr = h + size_t(row) * (K / 2);   // row < T * k + T <= kFzMaxRows
+    for (int i0 = 0; i0 < K / 2; i0 += kWave) {
+      const uint32_t v = fz_wait(hr + i0 + lane, tag, true, status);
+      *reinterpret_cast<uint32_t*>(xs + dec_off(K, 0, 2 * (i0 + lane))) = v;
+    }
+  };
+  down_combine_unit<DSTEPS>(a, t, col0, kFzWaves, smem, pair, stage_row);
+}
+
+template <int DSTEPS>
+__global__ __launch_bounds__(kFzThreads) void decode_fused_kernel(FusedArgs f) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float lg[kFzMaxT * kMaxExperts];
+  __shared__ uint32_t tag_s;
+  uint32_t* epoch = reinterpret_cast<uint32_t*>(f.fz + kFzEpoch);
+  if (threadIdx.x == 0) tag_s = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  __syncthreads();
+  const uint32_t tag = tag_s;
+  const int n0 = f.n_route, n1 = n0 + 1, n2 = n1 + f.n_gu, n3 = n2 + f.n_dn;
+  for (int item = blockIdx.x; item < n3; item += gridDim.x) {
+    if (item < n0)
+      fz_route_item(f, item, tag);
+    else if (item < n1)
+      fz_topk_item(f, tag, lg);
+    else if (item < n2)
+      fz_gu_item(f, item - n1, tag, smem);
+    else
+      fz_dn_item<DSTEPS>(f, item - n2, tag, smem);
+    __syncthreads();   // LDS is reused by the next item
+  }
+  if (threadIdx.x == 0) {
+    uint32_t* ex = reinterpret_cast<uint32_t*>(f.fz + kFzExit);
+    if (__hip_atomic_fetch_add(ex, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
+      // every workgroup has read the epoch and finished: the next call's tag
+      __hip_atomic_store(ex, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+bool decode_fused_supported(int T, int k, int H, int I) {
+  return T >= 1 && T <= kFzMaxT && T * k <= kFzMaxPairs && H == 2048 && (I == 256 || I == 512);
+}
+
+static_assert(kHandoffBytes + kFzStatus == MOE_WORKSPACE_STATUS_OFFSET, "status word offset in the header");
+
+namespace {
+constexpr int kFzMaxDevices = 64;
+int g_fz_grid[kFzMaxDevices][2];   // resident workgroups per device for I = 256, 512 (0: not queried)
+}  // namespace
+
+hipError_t launch_decode_fused(const RouteArgs& ra, const GemmArgs& g, const DownCombineArgs& d, uint8_t* fz,
+                               hipStream_t stream) {
+  const int T = ra.T, I = g.N;
+  if (!decode_fused_supported(T, ra.k, ra.H, I)) return hipErrorInvalidValue;
+  FusedArgs f{ra, g, d, fz, ceil_div(ra.E, kFzWaves), 0, 0};
+  const int max_routed = ra.T * ra.k / max(ra.block_rows, 1) + min(ra.E, ra.T * ra.k);
+  f.n_gu = (1 + max_routed) * g.NT;
+  f.n_dn = T * (d.N / 16);
+  const size_t lds_gu = size_t(dec_lds_bytes(4, 4, kFzMaxT));
+  const size_t lds_dn = size_t(kFzWaves) * dc_wave_bytes(I) + size_t(kFzWaves) * 33 * 4;
+  const size_t lds = lds_gu > lds_dn ? lds_gu : lds_dn;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kFzMaxDevices) return hipErrorInvalidDevice;
+  const int slot = I == 256 ? 0 : 1;
+  if (g_fz_grid[dev][slot] == 0) {
+    // every workgroup of the grid must be resident at once (the items wait on
+    // one another): the grid is at most the resident capacity of the device
+    int per_cu = 0, cus = 0;
+    hipError_t e = I == 256 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<2>,
+                                                                           kFzThreads, lds)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<4>,
+                                                                           kFzThreads, lds);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+    g_fz_grid[dev][slot] = per_cu * cus;
+  }
+  const int items = f.n_route + 1 + f.n_gu + f.n_dn;
+  const int grid = min(items, g_fz_grid[dev][slot]);
+  if (I == 256)
+    hipLaunchKernelGGL(decode_fused_kernel<2>, dim3(grid), dim3(kFzThreads), lds, stream, f);
+  else
+    hipLaunchKernelGGL(decode_fused_kernel<4>, dim3(grid), dim3(kFzThreads), lds, stream, f);
   return hipGetLastError();
 }
 

@@ -15,7 +15,6 @@ namespace moe {
 namespace {
 
 constexpr size_t kAlign = 256;
-static_assert(kHandoffBytes == MOE_WORKSPACE_HEAD_BYTES, "workspace head size in the header");
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -51,7 +50,7 @@ LayerLayout layer_layout(const moe_dims& d) {
   LayerLayout L;
   // completion counter of the one-launch routing (few tokens): kept at
   // offset 0 for every T, zero before a call and after it
-  L.done = c.take(T > 0 ? kHandoffBytes : 0);
+  L.done = c.take(T > 0 ? size_t(MOE_WORKSPACE_HEAD_BYTES) : 0);
   L.logits = c.take(T * E * 4);
   const int ks = router_splits(d.T, d.H, d.E);
   L.logit_parts = c.take(size_t(ks > 1 ? ks : 0) * T * E * 4);
@@ -428,6 +427,39 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   // 2-4. router GEMM, top-k, histogram, scan, scatter, block map
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
   float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+
+  // few tokens at the full hidden size: the whole layer as one persistent launch
+  if (decode && !s2 && opts && opts->persistent_decode && decode_fused_supported(T, k, H, I)) {
+    RouteArgs fa{};
+    fa.x = x;
+    fa.wr = router_w;
+    fa.bias = logit_bias;
+    fa.logits_out = logits_out ? logits_out : at<float>(ws, L.logits);
+    fa.topk_ids = ids;
+    fa.topk_w = wts;
+    fa.block_counts = at<int32_t>(ws, L.block_counts);
+    fa.rank_in_block = at<int32_t>(ws, L.rank);
+    fa.T = T;
+    fa.H = H;
+    fa.E = E;
+    fa.k = k;
+    fa.finish = 1;
+    fa.block_rows = bm;
+    fa.counts = at<int32_t>(ws, L.counts);
+    fa.offsets = offsets;
+    fa.tile_map = tile_map;
+    fa.num_tiles = num_tiles;
+    fa.sorted_rows = sorted_rows;
+    fa.row_of_pair = row_of_pair;
+    fa.tile_desc = tile_desc;
+    const DownCombineArgs da{h, stack_of(down), stack_of(sh_down), ids, wts, row_of_pair, T, k, H, I,
+                             routed_rows, y, x, shared_gate};
+    uint8_t* fz = at<uint8_t>(ws, L.done + kHandoffBytes);
+    const hipError_t ef = launch_decode_fused(fa, g1, da, fz, s);
+    if (ef == hipSuccess) return (mark(2) && mark(3) && mark(4) && mark(5)) ? MOE_OK : MOE_ERR_HIP;
+    if (ef != hipErrorInvalidConfiguration) return MOE_ERR_HIP;
+    // no resident grid possible on this device: the three-launch path below
+  }
   RouteArgs ra{};
   ra.x = x;
   ra.wr = router_w;
@@ -553,7 +585,7 @@ int moe_layer_forward_noalloc(const uint16_t* x, const uint16_t* router_w, const
   if (first) {
     // the workspace head must be zero before the first layer call; every call
     // leaves it zero
-    const int words = kHandoffBytes / 4;
+    const int words = MOE_WORKSPACE_HEAD_BYTES / 4;
     hipLaunchKernelGGL(zero_words_kernel, dim3(ceil_div(words, 256)), dim3(256), 0, s,
                        static_cast<uint32_t*>(ptr), words);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;

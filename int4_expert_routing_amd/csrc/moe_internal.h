@@ -101,6 +101,15 @@ struct DownCombineArgs {
 bool decode_down_combine_supported(int N, int K);
 hipError_t launch_decode_down_combine(const DownCombineArgs& da, hipStream_t stream);
 
+// The whole few-token layer as one persistent launch (H = 2048, I = 256 or
+// 512, T <= kDecodeMaxRows, T * k <= 64): routing, gate/up and down + combine
+// as work items handed over through tagged words in `fz`, the workspace head
+// after the one-launch routing's part. hipErrorInvalidConfiguration: the
+// device cannot hold a resident grid (use the three-launch path).
+bool decode_fused_supported(int T, int k, int H, int I);
+hipError_t launch_decode_fused(const RouteArgs& ra, const GemmArgs& g, const DownCombineArgs& d, uint8_t* fz,
+                               hipStream_t stream);
+
 // Min-max affine 4-bit quantiser: bf16 [rows][K] -> codes [rows][K/8],
 // bf16 scale and bias [rows][K/64].
 hipError_t launch_quantize(const uint16_t* w, long rows, int K, uint32_t* q, uint16_t* s, uint16_t* b,

@@ -19,14 +19,13 @@
 //      the final row of each pair = offset + block base + in-block rank.
 // Ranks count only earlier pairs, so the sort is stable and the result does not
 // depend on thread timing: repeated runs give identical tables.
-#include "moe_internal.h"
+#include "route_block.h"
 
 namespace moe {
 
 constexpr int kRouteThreads = 256;
 constexpr int kRouterRows = 32;                          // tokens per router-GEMM workgroup (one MFMA block)
 constexpr int kTopkThreads = kRouteTokens * kWave;       // top-k: one wave per token
-constexpr int kMaxKeysPerLane = kMaxExperts / kWave;
 
 // Router GEMM: logits[t][e] = fp32(sum_h x[t][h] W_r[e][h]) + bias[e].
 // One wave per workgroup computes a 32-token x 64-expert tile over one K
@@ -230,278 +229,6 @@ __global__ __launch_bounds__(kRtThreads, 2) void router_tile_kernel(const uint16
     for (int r = 0; r < 16; ++r) {
       const int m = tb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
       if (t0 + m < T) dst[size_t(t0 + m) * E + n] = ((eb ? acc1[r] : acc0[r]) + bv) + 0.0f;
-    }
-  }
-}
-
-// A token's logits from NP K-range partial planes (plane stride `plane`):
-// every load is issued before the first add, and the planes are added in
-// order, so the result does not depend on when the loads return.
-template <int NP>
-__device__ __forceinline__ void sum_parts(const float* parts, size_t plane, const size_t (&f)[kMaxKeysPerLane],
-                                          float (&v)[kMaxKeysPerLane]) {
-  float pv[kMaxKeysPerLane][NP];
-#pragma unroll
-  for (int i = 0; i < kMaxKeysPerLane; ++i)
-#pragma unroll
-    for (int p = 0; p < NP; ++p) pv[i][p] = parts[size_t(p) * plane + f[i]];
-#pragma unroll
-  for (int i = 0; i < kMaxKeysPerLane; ++i) {
-    v[i] = pv[i][0];
-#pragma unroll
-    for (int p = 1; p < NP; ++p) v[i] += pv[i][p];
-  }
-}
-
-// Top-k of one token held by one wave: lane l holds the order keys of experts
-// l, l+64, l+128, l+192 (0 for experts >= E, below every finite logit's key).
-// The k-th largest key tau is found by a most-significant-bit-first radix
-// select whose counts are wave ballots; the chosen set is every key > tau plus
-// the lowest-index experts with key == tau, which is the set the key
-// (logit desc, expert asc) orders first.
-__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&u)[kMaxKeysPerLane], int k) {
-  uint32_t tau = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = tau | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) cnt += __popcll(__ballot(u[i] >= cand));
-    tau = cnt >= k ? cand : tau;
-  }
-  return tau;
-}
-
-// Inclusive scans of two per-thread values over the whole workgroup (thread
-// order), one value pair per thread: a shuffle scan inside each wave, then each
-// wave adds the totals of the waves before it. tot holds 2 x (waves) ints of
-// LDS; every thread of the workgroup must call this.
-__device__ __forceinline__ void block_scan2(int32_t& a, int32_t& b, int32_t* tot) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nw = blockDim.x >> 6;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int32_t ua = __shfl_up(a, d, kWave), ub = __shfl_up(b, d, kWave);
-    if (lane >= d) {
-      a += ua;
-      b += ub;
-    }
-  }
-  if (lane == kWave - 1) {
-    tot[w] = a;
-    tot[nw + w] = b;
-  }
-  __syncthreads();
-  int32_t pa = 0, pb = 0;
-  for (int i = 0; i < w; ++i) {
-    pa += tot[i];
-    pb += tot[nw + i];
-  }
-  a += pa;
-  b += pb;
-}
-
-// Top-k, softmax, histogram and ranks of routing block blk (and, for a single
-// block, the tables), run by one 1024-thread workgroup.
-__device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
-  __shared__ uint32_t sel_key[kRouteTokens][kMaxTopk];
-  __shared__ int32_t sel_e[kRouteTokens][kMaxTopk];
-  __shared__ int32_t ids_s[kRouteTokens * kMaxTopk];
-  __shared__ int32_t rank_s[kRouteTokens * kMaxTopk];
-  __shared__ int32_t hist[kMaxExperts];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int t0 = blk * kRouteTokens;
-  const int nt = min(kRouteTokens, a.T - t0);
-  const int E = a.E, k = a.k;
-  const uint64_t below = (1ull << lane) - 1ull;
-
-  const int nthr = blockDim.x;   // at least E and one wave per token of the block
-  for (int e = tid; e < E; e += nthr) hist[e] = 0;
-
-  const int m = wave;                                            // this wave's token
-  if (m < nt) {
-    // every load of the token's logits (or of their K-range partials) is
-    // issued before the first use, so the wave waits for one round trip;
-    // experts past E read the last expert's entry and get key 0
-    float v[kMaxKeysPerLane];
-    size_t f[kMaxKeysPerLane];
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) f[i] = size_t(t0 + m) * E + min(lane + 64 * i, E - 1);
-    if (a.n_parts == 8) {
-      sum_parts<8>(a.logits_in, size_t(a.T) * E, f, v);
-    } else if (a.n_parts == 4) {
-      sum_parts<4>(a.logits_in, size_t(a.T) * E, f, v);
-    } else if (a.n_parts == 2) {
-      sum_parts<2>(a.logits_in, size_t(a.T) * E, f, v);
-    } else if (a.coherent) {
-#pragma unroll
-      for (int i = 0; i < kMaxKeysPerLane; ++i)
-        v[i] = __hip_atomic_load(a.logits_in + f[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kMaxKeysPerLane; ++i) {
-        v[i] = a.logits_in[f[i]];
-        for (int p = 1; p < a.n_parts; ++p) v[i] += a.logits_in[size_t(p) * a.T * E + f[i]];
-      }
-    }
-    uint32_t u[kMaxKeysPerLane];
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-      const int e = lane + 64 * i;
-      uint32_t key = 0u;
-      if (e < E) {
-        float x = v[i];
-        if (a.bias) x = x + a.bias[e];
-        x = x + 0.0f;                                            // turns -0 into +0
-        if (a.logits_out) a.logits_out[f[i]] = x;
-        key = float_order_key(x);
-      }
-      u[i] = key;
-    }
-    const uint32_t tau = kth_largest(u, k);
-    int n_gt = 0;
-    uint64_t tie[kMaxKeysPerLane];
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-      n_gt += __popcll(__ballot(u[i] > tau));
-      tie[i] = __ballot(u[i] == tau);
-    }
-    // ties at tau are taken in expert order: expert lane + 64 i ranks after
-    // every tie of a lower i and after the lower lanes' ties of the same i
-    const int need = k - n_gt;
-    int ties_before = 0;
-    int slot_base = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-      const bool is_tie = (tie[i] >> lane) & 1ull;
-      const int tie_rank = ties_before + __popcll(tie[i] & below);
-      const bool chosen = u[i] > tau || (is_tie && tie_rank < need);
-      const uint64_t cm = __ballot(chosen);
-      if (chosen) {
-        const int slot = slot_base + __popcll(cm & below);
-        sel_key[m][slot] = u[i];
-        sel_e[m][slot] = lane + 64 * i;
-      }
-      ties_before += __popcll(tie[i]);
-      slot_base += __popcll(cm);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // lane j < k: its chosen element's position in (logit desc, expert asc) order
-    int pos = 0;
-    uint32_t my_key = 0;
-    int my_e = 0;
-    if (lane < k) {
-      my_key = sel_key[m][lane];
-      my_e = sel_e[m][lane];
-#pragma unroll 8
-      for (int q = 0; q < k; ++q) {
-        const uint32_t kq = sel_key[m][q];
-        const int eq = sel_e[m][q];
-        pos += (kq > my_key || (kq == my_key && eq < my_e)) ? 1 : 0;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (lane < k) {
-      sel_key[m][pos] = my_key;
-      sel_e[m][pos] = my_e;
-    }
-    __builtin_amdgcn_wave_barrier();
-    float my_l = 0.0f;
-    if (lane < k) {
-      my_e = sel_e[m][lane];
-      my_l = float_from_order_key(sel_key[m][lane]);
-    }
-    const float l0 = float_from_order_key(sel_key[m][0]);
-    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
-    // the k terms added in rank order (lane reads, no cross-lane shuffles)
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
-    if (lane < k) {
-      const size_t f = size_t(t0 + m) * k + lane;
-      a.topk_ids[f] = my_e;
-      a.topk_w[f] = ex / sum;
-      ids_s[m * k + lane] = my_e;
-    }
-  }
-  __syncthreads();
-
-  // Histogram of the block's pairs and each pair's rank among the earlier pairs
-  // of the same expert (pair order f = t*k + j), which makes the scatter
-  // stable. Wave 0 walks the pairs 64 at a time; lanes with the same expert
-  // find each other through one ballot per expert-index bit.
-  const int npairs_all = nt * k;
-  if (wave == 0) {
-    const int npairs = npairs_all;
-    for (int c0 = 0; c0 < npairs; c0 += kWave) {
-      const int p = c0 + lane;
-      const int e = p < npairs ? ids_s[p] : kMaxExperts;   // past the end: a value no expert has
-      uint64_t same = ~0ull;
-#pragma unroll
-      for (int bit = 0; bit < 9; ++bit) {
-        const uint64_t bb = __ballot((e >> bit) & 1);
-        same &= ((e >> bit) & 1) ? bb : ~bb;
-      }
-      if (p < npairs) {
-        const int base = hist[e];
-        const int before = __popcll(same & below);
-        if (!a.finish) a.rank_in_block[size_t(t0) * k + p] = base + before;
-        rank_s[p] = base + before;
-        if (before == 0) hist[e] = base + __popcll(same);   // every lane of the group has read hist[e]
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-  __syncthreads();
-  if (!a.finish) {   // uniform: the scan and scatter kernels follow
-    for (int e = tid; e < E; e += nthr) a.block_counts[size_t(blk) * E + e] = hist[e];
-    return;
-  }
-
-  // One block holds every pair: offsets are the exclusive scan of the
-  // histogram, the block map lists ceil(count / block_rows) tiles per expert
-  // in expert order, and each pair's row is its expert's offset plus its rank.
-  __shared__ int32_t off_s[kMaxExperts];
-  __shared__ int32_t scan_tot[2 * kRouteTokens];
-  __shared__ int32_t sorted_s[kRouteTokens * kMaxTopk];
-  const int c = tid < E ? hist[tid] : 0;
-  const int ntl = ceil_div(c, a.block_rows);
-  int32_t oc = c, tc = ntl;   // inclusive scans of counts and tile counts
-  block_scan2(oc, tc, scan_tot);
-  if (tid < E) {
-    const int o = oc - c;
-    off_s[tid] = o;
-    a.counts[tid] = c;
-    a.offsets[tid] = o;
-    const int first = tc - ntl;
-    for (int i = 0; i < ntl; ++i) {
-      a.tile_map[2 * (first + i)] = tid;
-      a.tile_map[2 * (first + i) + 1] = o + i * a.block_rows;
-    }
-    if (tid == E - 1) {
-      a.offsets[E] = oc;
-      *a.num_tiles = tc;
-    }
-  }
-  __syncthreads();
-  for (int p = tid; p < npairs_all; p += nthr) {
-    const int pos = off_s[ids_s[p]] + rank_s[p];
-    a.sorted_rows[pos] = p;
-    a.row_of_pair[p] = pos;
-    sorted_s[pos] = p;
-  }
-  if (!a.tile_desc) return;   // uniform
-  __syncthreads();
-  if (tid < E && c > 0) {
-    const int o = off_s[tid];
-    const int first = tc - ntl;
-    for (int i = 0; i < ntl; ++i) {
-      const int r0 = o + i * a.block_rows;
-      const int n = min(a.block_rows, c - i * a.block_rows);
-      uint32_t tok = 0;
-      for (int j = 0; j < n && j < 8; ++j) tok |= uint32_t(sorted_s[r0 + j] / k) << (4 * j);
-      a.tile_desc[first + i] = u32x4{uint32_t(tid), uint32_t(r0), uint32_t(n), tok};
     }
   }
 }

@@ -256,12 +256,14 @@ def moe_layer_forward(x: torch.Tensor, w: MoEWeights, k: int, y: Optional[torch.
                       logits_out: Optional[torch.Tensor] = None, topk_ids_out: Optional[torch.Tensor] = None,
                       topk_w_out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, block_rows: int = 0,
-                      side_stream: Optional["torch.cuda.Stream"] = None, events=None) -> torch.Tensor:
+                      side_stream: Optional["torch.cuda.Stream"] = None, events=None,
+                      persistent_decode: bool = False) -> torch.Tensor:
     """y = MoE layer(x), bf16 [T][H]; optional outputs are filled when given.
     block_rows: routed tile height (0 = the library default, or 32, 64, 128).
     side_stream: run the shared expert on this stream (events: a (fork, join)
     pair of torch.cuda.Event already recorded once, so that they exist).
-    A gate vector in w.shared_gate gates the shared expert."""
+    A gate vector in w.shared_gate gates the shared expert. persistent_decode:
+    few-token calls run as one persistent launch (where supported)."""
     _need(x, torch.bfloat16, "x")
     dev = x.device
     T, H = x.shape
@@ -284,7 +286,7 @@ def moe_layer_forward(x: torch.Tensor, w: MoEWeights, k: int, y: Optional[torch.
     args = (_ptr(x), _ptr(w.router_w), _ptr(w.logit_bias), *[ctypes.byref(s) for s in structs], ctypes.byref(d),
             _ptr(y), _ptr(logits_out), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(workspace), workspace.numel(),
             _stream(dev))
-    if w.shared_gate is None and side_stream is None:
+    if w.shared_gate is None and side_stream is None and not persistent_decode:
         check(lib.moe_layer_forward(*args), "moe_layer_forward")
         return y
     opts = MoeLayerOptions()
@@ -297,6 +299,7 @@ def moe_layer_forward(x: torch.Tensor, w: MoEWeights, k: int, y: Optional[torch.
         opts.side_stream = side_stream.cuda_stream
         opts.fork_event = events[0].cuda_event
         opts.join_event = events[1].cuda_event
+    opts.persistent_decode = 1 if persistent_decode else 0
     check(lib.moe_layer_forward_ex(*args, ctypes.byref(opts)), "moe_layer_forward_ex")
     return y
 
@@ -329,10 +332,11 @@ class MoELayer:
     """A layer with its weights and workspace resident on one GPU."""
 
     def __init__(self, weights: MoEWeights, k: int, max_tokens: int, block_rows: int = 0,
-                 side_stream: bool = False):
+                 side_stream: bool = False, persistent_decode: bool = False):
         self.w = weights
         self.k = k
         self.block_rows = block_rows
+        self.persistent_decode = persistent_decode
         dev = weights.router_w.device
         self.side_stream = None
         self.events = None
@@ -351,4 +355,5 @@ class MoELayer:
         if x.shape[0] > self.max_tokens:
             raise ValueError("more tokens than the workspace was sized for")
         return moe_layer_forward(x, self.w, self.k, workspace=self.workspace, block_rows=self.block_rows,
-                                 side_stream=self.side_stream, events=self.events, **outs)
+                                 side_stream=self.side_stream, events=self.events,
+                                 persistent_decode=self.persistent_decode, **outs)

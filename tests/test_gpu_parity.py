@@ -563,6 +563,78 @@ def test_layer_side_stream_graph_replays(dev, T):
     check_layer(inp, g)
 
 
+def _head_ok(ws):
+    """The one-launch routing's part of the workspace head is back at zero and
+    the persistent decode kernel's status word is clear."""
+    st = int(ws[_lib.MOE_WORKSPACE_STATUS_OFFSET:_lib.MOE_WORKSPACE_STATUS_OFFSET + 4].view(torch.int32).item())
+    return int(ws[:8448].count_nonzero()) == 0 and st == 0
+
+
+@pytest.mark.parametrize("T,I,E,k,bias_mode", [(1, 512, 256, 8, "random"), (2, 512, 256, 8, "sym"),
+                                               (3, 256, 64, 4, "random"), (4, 512, 256, 8, "random"),
+                                               (5, 512, 32, 8, "random"), (6, 256, 16, 2, "random"),
+                                               (7, 512, 256, 8, "sym"), (8, 512, 256, 8, "random"),
+                                               (8, 512, 8, 8, "random"), (3, 512, 256, 1, "random")])
+def test_layer_persistent_decode_kernel(dev, T, I, E, k, bias_mode):
+    # H = 2048, T <= 8, persistent_decode: the whole layer runs as one
+    # persistent launch; it must match the oracle, and (T <= 4, where both
+    # routers sum the logits in the same order) its bits must equal the
+    # three-launch path's
+    print(f"persistent decode T={T} I={I} E={E} k={k} {bias_mode}", flush=True)
+    inp = resample_close_calls(make_layer(T, 2048, I, E, k, seed=300 + T + k, bias_mode=bias_mode))
+    w = ops.MoEWeights.from_host(inp, dev)
+    x = ops.bf16_from_bits(inp.x, dev)
+    one = ops.MoELayer(w, k, T, persistent_decode=True)
+    outs = []
+    for layer, kw in ((one, {}), (ops.MoELayer(w, k, T), {})):
+        y = torch.empty(T, 2048, dtype=torch.bfloat16, device=dev)
+        lg = torch.empty(T, E, dtype=torch.float32, device=dev)
+        ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+        wt = torch.empty(T, k, dtype=torch.float32, device=dev)
+        layer(x, y=y, logits_out=lg, topk_ids_out=ids, topk_w_out=wt)
+        torch.cuda.synchronize()
+        outs.append(dict(y=om.bf16_bits_to_f64(ops.bits_from_bf16(y)), logits=_np(lg), ids=_np(ids), w=_np(wt)))
+    assert _head_ok(one.workspace)
+    check_layer(inp, outs[0])
+    check_layer(inp, outs[1])
+    if T <= 4:
+        for key in outs[0]:
+            assert np.array_equal(outs[0][key], outs[1][key]), key
+
+
+def test_layer_persistent_decode_graph_replays(dev):
+    # the tags of one call never serve the next: a captured call replayed
+    # between eager calls of other token counts (1 .. 8) in the same workspace
+    print("persistent decode graph replays", flush=True)
+    H, I, E, k = 2048, 512, 64, 4
+    inp = make_layer(8, H, I, E, k, seed=61, bias_mode="random", gated_shared=True)
+    w = ops.MoEWeights.from_host(inp, dev)
+    layer = ops.MoELayer(w, k, 8, persistent_decode=True)
+    xs = {T: ops.bf16_from_bits(make_layer(T, H, I, E, k, seed=400 + T).x, dev) for T in range(1, 9)}
+    x = ops.bf16_from_bits(inp.x, dev)
+    y = torch.empty(8, H, dtype=torch.bfloat16, device=dev)
+    lg = torch.empty(8, E, dtype=torch.float32, device=dev)
+    ids = torch.empty(8, k, dtype=torch.int32, device=dev)
+    wt = torch.empty(8, k, dtype=torch.float32, device=dev)
+    layer(x, y=y, logits_out=lg, topk_ids_out=ids, topk_w_out=wt)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    g = dict(y=om.bf16_bits_to_f64(ops.bits_from_bf16(y_eager)), logits=_np(lg), ids=_np(ids), w=_np(wt))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer(x, y=y)
+    torch.cuda.synchronize()
+    for T in (1, 5, 8, 2, 3):
+        y.fill_(0)
+        layer(xs[T], y=torch.empty(T, H, dtype=torch.bfloat16, device=dev))
+        graph.replay()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), T
+    assert _head_ok(layer.workspace)
+    check_layer(inp, g)
+
+
 def test_layer_decode8_zipf_seeds(dev):
     print("layer decode8 zipf seeds 1, 2", flush=True)
     for seed in (1, 2):
