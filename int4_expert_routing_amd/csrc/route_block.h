@@ -10,6 +10,7 @@
 namespace moe {
 
 constexpr int kMaxKeysPerLane = kMaxExperts / kWave;
+constexpr int kMaxCand = 64;   // candidates of the fast top-k path (section in topk_block)
 
 // A token's logits from NP K-range partial planes (plane stride `plane`):
 // every load is issued before the first add, and the planes are added in
@@ -85,6 +86,8 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
   __shared__ int32_t ids_s[kRouteTokens * kMaxTopk];
   __shared__ int32_t rank_s[kRouteTokens * kMaxTopk];
   __shared__ int32_t hist[kMaxExperts];
+  __shared__ uint32_t cand_key[kRouteTokens][kMaxCand];
+  __shared__ int32_t cand_e[kRouteTokens][kMaxCand];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,6 +140,64 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
       }
       u[i] = key;
     }
+    // Fast path. Let mk be the k-th largest of the 64 lanes' largest keys: at
+    // least k keys are >= mk, so the k-th largest key is >= mk and every
+    // chosen key is among the candidates {keys >= mk}; every other key is
+    // strictly smaller than all chosen ones. The candidates (usually about k)
+    // are gathered in LDS and each one's position in (logit desc, expert asc)
+    // order is counted directly: positions 0..k-1 are the chosen experts, in
+    // order. mk itself needs one ballot per radix pass instead of four. Exact
+    // ties that leave more than kMaxCand candidates take the general path.
+    uint32_t mx = u[0];
+#pragma unroll
+    for (int i = 1; i < kMaxKeysPerLane; ++i) mx = u[i] > mx ? u[i] : mx;
+    uint32_t mk = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = mk | (1u << b);
+      mk = __popcll(__ballot(mx >= cand)) >= k ? cand : mk;
+    }
+    uint64_t cmask[kMaxKeysPerLane];
+    int n_cand = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      cmask[i] = __ballot(u[i] >= mk);
+      n_cand += __popcll(cmask[i]);
+    }
+    if (n_cand <= kMaxCand) {   // uniform
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i) {
+        if ((cmask[i] >> lane) & 1ull) {
+          const int slot = base + __popcll(cmask[i] & below);
+          cand_key[m][slot] = u[i];
+          cand_e[m][slot] = lane + 64 * i;
+        }
+        base += __popcll(cmask[i]);
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (lane < n_cand) {
+        const uint32_t my_key = cand_key[m][lane];
+        const int my_e = cand_e[m][lane];
+        int pos = 0;
+        for (int q0 = 0; q0 < n_cand; q0 += 8) {
+          uint32_t kq[8];
+          int eq[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            kq[q] = cand_key[m][min(q0 + q, n_cand - 1)];
+            eq[q] = cand_e[m][min(q0 + q, n_cand - 1)];
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            pos += int(q0 + q < n_cand) & (int(kq[q] > my_key) | (int(kq[q] == my_key) & int(eq[q] < my_e)));
+        }
+        if (pos < k) {
+          sel_key[m][pos] = my_key;
+          sel_e[m][pos] = my_e;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
     const uint32_t tau = kth_largest(u, k);
     int n_gt = 0;
     uint64_t tie[kMaxKeysPerLane];
@@ -193,7 +254,9 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
       sel_e[m][pos] = my_e;
     }
     __builtin_amdgcn_wave_barrier();
+    }
     float my_l = 0.0f;
+    int my_e = 0;
     if (lane < k) {
       my_e = sel_e[m][lane];
       my_l = float_from_order_key(sel_key[m][lane]);
