@@ -70,12 +70,14 @@ def random_weights(ops, torch, dev, E, H, I, seed):
                           sh_gate=stack(1, I, H), sh_up=stack(1, I, H), sh_down=stack(1, H, I))
 
 
-def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, reps=25, prepack=False):
+def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, reps=25, prepack=False,
+                   persistent=False):
     """Layer calls at T tokens, captured as one HIP graph of `calls` calls that
     cycle over n_sets weight sets and `calls` fresh inputs, replayed `reps`
     times; bytes per call = the distinct experts the call routes to, plus the
     shared expert, the router matrix, x and y. prepack: every set (w0
-    included) is prepacked before timing."""
+    included) is prepacked before timing. persistent: the calls ask for the
+    one-launch persistent decode kernel (moe_layer_forward_ex option)."""
     import ctypes
     E, H, I = w0.E, w0.H, w0.I
     sets = [w0] + [random_weights(ops, torch, dev, E, H, I, 1000 + i) for i in range(n_sets - 1)]
@@ -90,14 +92,17 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
     dims = _lib.MoeDims(T, H, I, E, k, 0)
     ws = torch.zeros(int(lib.moe_workspace_bytes(ctypes.byref(dims))), dtype=torch.uint8, device=dev)
 
+    opts = _lib.MoeLayerOptions()
+    opts.persistent_decode = 1 if persistent else 0
+
     def call(i):
         w = sets[i % n_sets]
-        st = lib.moe_layer_forward(
+        st = lib.moe_layer_forward_ex(
             ctypes.c_void_p(xs[i].data_ptr()), ctypes.c_void_p(w.router_w.data_ptr()), None,
             *[ctypes.byref(s) for s in structs[i % n_sets]], ctypes.byref(dims), ctypes.c_void_p(ys[i].data_ptr()),
             None, ctypes.c_void_p(ids[i].data_ptr()), None, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
-            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
-        _lib.check(st, "moe_layer_forward")
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), ctypes.byref(opts))
+        _lib.check(st, "moe_layer_forward_ex")
 
     for i in range(calls):
         call(i)

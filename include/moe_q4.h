@@ -47,7 +47,7 @@ extern "C" {
  * epoch and its tagged hand-off words): zero before the first layer call, and
  * changed by nothing else afterwards (zeroing them again between calls is
  * allowed). */
-#define MOE_WORKSPACE_HEAD_BYTES 175872
+#define MOE_WORKSPACE_HEAD_BYTES 181888
 /* Byte offset, inside that head, of a uint32 status word: nonzero after a
  * decode-sized call whose persistent kernel gave up waiting (a bounded wait
  * ran out, e.g. when other work kept its workgroups from being resident);

@@ -545,45 +545,69 @@ hipError_t launch_decode(const GemmArgs& ga, const u32x4* tile_desc, int max_row
 // small part of a decode call. Here one grid of workgroups takes work items in
 // phase order (item index = phase order):
 //   routing items (one wave per expert: the logits of every token),
-//   one top-k item (top-k, softmax and the routing tables, as in the one-block
-//     routing kernel),
 //   gate/up items (one (row tile, 16 columns of h) each; tile 0 is the shared
-//     expert, which needs no routing),
+//     expert, which needs no routing; tile i > 0 is the i-th chosen expert in
+//     ascending order, with its rows),
 //   down items (one (token, 16 output columns) each, the down projection fused
 //     with the weighted combine).
+// There is no routing hand-off item: the first gate/up or down item of a
+// routed tile that a workgroup takes reads every token's logits, runs the same
+// top-k and softmax as the routing kernels and builds the few-token tables
+// (rows sorted by expert, then by pair) in its own LDS, which serve the
+// workgroup's later items too. So a routed item waits for one global round
+// trip after the router (the logits), not three (logits, top-k, descriptors).
 // Workgroup b takes items b, b + gridDim.x, ... in increasing order, and every
 // workgroup is resident at once (the host sizes the grid from the occupancy),
 // so an item only ever waits for items of earlier phases, which their
-// workgroups reach before any later item: no wait can block the grid.
+// workgroups reach before any later item: no wait can block the grid. The
+// kernel is instantiated per token bucket (1, 2, 4, 8), which keeps it within
+// 128 VGPRs, two workgroups per CU: at T = 1 every item is resident at once.
 //
 // Hand-off without fences: every value one item passes to another (a logit, a
-// tile descriptor, a pair's expert, row and weight, a pair of bf16 of h) is
-// written as one 64-bit agent-scope atomic store tag << 32 | value, and read
-// with agent-scope atomic loads until the tag matches (AMDGPU memory model:
-// agent-scope atomics are coherent for every workgroup and become visible in
-// finite time). The tag is the call's epoch + 1: every workgroup reads the
-// epoch word when it starts, and the last workgroup to finish advances it
-// (and returns the exit counter to zero), so a later call can never take a
-// stale word for a fresh one. Every wait is bounded by the 100 MHz real-time
-// counter; a wait that gives up writes 1 to the status word (the call's
-// results are then invalid) instead of hanging the GPU.
+// pair of bf16 of h) is written as one 64-bit agent-scope atomic store
+// tag << 32 | value, and read with agent-scope atomic loads until the tag
+// matches (AMDGPU memory model: agent-scope atomics are coherent for every
+// workgroup and become visible in finite time). The tag is the call's epoch
+// + 1: every workgroup reads the epoch word when it starts, and the last
+// workgroup to finish advances it (and returns the exit counter to zero), so a
+// later call can never take a stale word for a fresh one. Every wait is
+// bounded by the 100 MHz real-time counter; a wait that gives up writes 1 to
+// the status word (the call's results are then invalid) instead of hanging
+// the GPU.
+// Waiting is cheap for the producers: a consumer first watches one counter of
+// finished producer items with one lane and a back-off, and only then reads
+// the tagged words it needs (which normally carry the tag by then; the tags,
+// not the counters, make the values safe to use, so the counters need no
+// fences either). Every polled word would otherwise draw a request from every
+// lane of every waiting workgroup, and that traffic on a few cache lines
+// delays the very stores it waits for. Adds to one word are serialised
+// (~11 ns each, measured), so no counter has many producers: the routing items
+// count into eight copies (a consumer watches the copy of its workgroup index
+// mod 8), and each gate/up tile has its own counter, which its NT column items
+// count into and the down items of its rows watch. Each counter has its own
+// cache line.
 constexpr int kFzThreads = 512;
 constexpr int kFzWaves = kFzThreads / kWave;
 constexpr int kFzMaxT = kDecodeMaxRows;
 constexpr int kFzMaxPairs = 64;                              // T * k
 constexpr int kFzMaxRows = kFzMaxPairs + kFzMaxT;            // routed + shared h rows
-constexpr int kFzMaxTiles = kFzMaxPairs / 32 + kFzMaxPairs;  // routed tiles at block rows >= 32
 constexpr int kFzMaxHalfI = 256;                             // I <= 512
+constexpr int kFzH = 2048;                                   // hidden size of the kernel
 constexpr uint64_t kFzPollTicks = 20000000;                  // 200 ms of the 100 MHz counter
+static_assert(kFzWaves >= kFzMaxT, "one wave per token in the local routing");
 // byte offsets inside the region (the workspace head after the one-launch
 // routing's part)
-constexpr size_t kFzEpoch = 0, kFzExit = 64, kFzStatus = 128, kFzNtiles = 192;
-constexpr size_t kFzSlots = 256;                                                    // [kFzMaxT][kMaxExperts]
-constexpr size_t kFzDesc = kFzSlots + size_t(kFzMaxT) * kMaxExperts * 8;           // [kFzMaxTiles][4]
-constexpr size_t kFzPairs = kFzDesc + size_t((kFzMaxTiles * 32 + 255) / 256) * 256; // [kFzMaxPairs][2]
-constexpr size_t kFzH = kFzPairs + size_t(kFzMaxPairs) * 16;                       // [kFzMaxRows][kFzMaxHalfI]
-constexpr size_t kFzBytes = kFzH + size_t(kFzMaxRows) * kFzMaxHalfI * 8;
+constexpr size_t kFzEpoch = 0, kFzExit = 64, kFzStatus = 128;
+constexpr int kFzMaxTiles = 1 + kFzMaxPairs;                 // the shared tile + one per chosen expert
+constexpr int kFzCntCopies = 8;                              // copies of the routing counter
+constexpr size_t kFzLine = 128;                              // one counter per cache line
+constexpr size_t kFzRouteCnt = 256;                                                 // [kFzCntCopies] lines
+constexpr size_t kFzTileCnt = kFzRouteCnt + kFzCntCopies * kFzLine;                 // [kFzMaxTiles] lines
+constexpr size_t kFzSlots = kFzTileCnt + kFzMaxTiles * kFzLine;                     // [kFzMaxT][kMaxExperts]
+constexpr size_t kFzHrows = kFzSlots + size_t(kFzMaxT) * kMaxExperts * 8;          // [kFzMaxRows][kFzMaxHalfI]
+constexpr size_t kFzBytes = kFzHrows + size_t(kFzMaxRows) * kFzMaxHalfI * 8;
 static_assert(kHandoffBytes + kFzBytes == MOE_WORKSPACE_HEAD_BYTES, "workspace head size in the header");
+static_assert(kFzCntCopies + kFzMaxTiles <= kFzThreads, "one thread per counter when the counters are reset");
 
 __device__ __forceinline__ uint64_t fz_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -592,279 +616,458 @@ __device__ __forceinline__ void fz_store(uint64_t* p, uint32_t tag, uint32_t v) 
   __hip_atomic_store(p, (uint64_t(tag) << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The value of *p once it carries the tag. Every lane of the wave calls this
-// (need == false: the lane waits for nothing); bounded as described above.
-__device__ __forceinline__ uint32_t fz_wait(const uint64_t* p, uint32_t tag, bool need, uint32_t* status) {
-  uint64_t v = need ? fz_load(p) : (uint64_t(tag) << 32);
-  if (__all((v >> 32) == tag)) return uint32_t(v);
-  const uint64_t t0 = wall_clock64();
-  while (true) {
-    __builtin_amdgcn_s_sleep(1);
-    if ((v >> 32) != tag) v = fz_load(p);
-    if (__all((v >> 32) == tag)) break;
-    if (wall_clock64() - t0 > kFzPollTicks) {
-      if ((v >> 32) != tag) __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
+// The values of N words once each carries the tag (need[i] == false: the lane
+// waits for nothing there). Every lane of the wave calls this: all N loads go
+// out together, and only words not yet tagged are read again; bounded as
+// described above.
+template <int N>
+__device__ __forceinline__ void fz_wait_n(const uint64_t* const (&p)[N], const bool (&need)[N], uint32_t tag,
+                                          uint32_t* status, uint32_t (&out)[N]) {
+  uint64_t v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = need[i] ? fz_load(p[i]) : (uint64_t(tag) << 32);
+  auto ready = [&]() {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ok = ok && (v[i] >> 32) == tag;
+    return ok;
+  };
+  if (!__all(ready())) {
+    const uint64_t t0 = wall_clock64();
+    while (true) {
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if ((v[i] >> 32) != tag) v[i] = fz_load(p[i]);
+      if (__all(ready())) break;
+      if (wall_clock64() - t0 > kFzPollTicks) {
+        if (!ready()) __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
     }
   }
-  return uint32_t(v);
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = uint32_t(v[i]);
 }
 
-struct FusedArgs {
-  RouteArgs ra;        // router, top-k and tables (finish mode, with tile descriptors)
-  GemmArgs g;          // gate/up (A = x in natural order, NT = N / 16)
-  DownCombineArgs d;   // down + combine
-  uint8_t* fz;         // the region described above
-  int n_route, n_gu, n_dn;
-};
-
-// Routing item: wave w computes expert (item * kFzWaves + w)'s logit of every
-// token (lane l takes every 64th 8-element chunk of H; a fixed lane tree).
-__device__ __forceinline__ void fz_route_item(const FusedArgs& f, int item, uint32_t tag) {
-  const RouteArgs& a = f.ra;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = item * kFzWaves + wave;
-  const int T = a.T, H = a.H, E = a.E, nch = H / 8;
-  float acc[kFzMaxT];
-#pragma unroll
-  for (int t = 0; t < kFzMaxT; ++t) acc[t] = 0.0f;
-  if (e < E) {
-    const uint16_t* wr = a.wr + size_t(e) * H;
-    for (int c0 = lane; c0 < nch; c0 += 2 * kWave) {
-      u32x4 wv[2], xv[2][kFzMaxT];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ch = min(c0 + i * kWave, nch - 1);
-        wv[i] = *reinterpret_cast<const u32x4*>(wr + ch * 8);
-#pragma unroll
-        for (int t = 0; t < kFzMaxT; ++t)
-          if (t < T) xv[i][t] = *reinterpret_cast<const u32x4*>(a.x + size_t(t) * H + ch * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (c0 + i * kWave >= nch) break;
-#pragma unroll
-        for (int t = 0; t < kFzMaxT; ++t) {
-          if (t < T) {
-            acc[t] = dot2(wv[i].x, xv[i][t].x, acc[t]);
-            acc[t] = dot2(wv[i].y, xv[i][t].y, acc[t]);
-            acc[t] = dot2(wv[i].z, xv[i][t].z, acc[t]);
-            acc[t] = dot2(wv[i].w, xv[i][t].w, acc[t]);
-          }
+// Lane 0 of the calling wave watches the counter until it reaches n (bounded as
+// above); returns to every lane once it does.
+__device__ __forceinline__ void fz_wait_count(const uint32_t* cnt, uint32_t n, uint32_t* status) {
+  uint32_t v = 0;
+  if ((threadIdx.x & 63) == 0) {
+    v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v < n) {
+      const uint64_t t0 = wall_clock64();
+      while (true) {
+        __builtin_amdgcn_s_sleep(4);
+        v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v >= n) break;
+        if (wall_clock64() - t0 > kFzPollTicks) {
+          __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
         }
       }
     }
   }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// This workgroup's item is done: its stores are complete (waited for by every
+// wave), then thread i < copies counts the item in counter copy i (copies
+// kFzLine bytes apart).
+__device__ __forceinline__ void fz_count_done(uint8_t* cnt, int copies) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
+  __syncthreads();
+  if (int(threadIdx.x) < copies)
+    __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(cnt + threadIdx.x * kFzLine), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct FusedArgs {
+  GemmArgs g;            // gate/up: A = x (natural order), E, N = I, K = H, NT = I / 16, shared_rows = T
+  DownCombineArgs d;     // down + combine (its table pointers are unused: the kernel's own tables)
+  const uint16_t* wr;    // router [E][H]
+  const float* bias;     // [E] or null
+  float* logits_out;     // [T][E] or null
+  int32_t* ids_out;      // [T][k] or null
+  float* w_out;          // [T][k] or null
+  uint8_t* fz;           // the region described above
+  int n_route, n_gu, n_dn;
+};
+
+// The few-token routing tables of one workgroup (LDS).
+struct FzRoute {
+  uint32_t cand_key[kFzMaxT][kMaxCand];
+  int32_t cand_e[kFzMaxT][kMaxCand];
+  uint32_t sel_key[kFzMaxT][kMaxTopk];
+  int32_t sel_e[kFzMaxT][kMaxTopk];
+  int32_t ids[kFzMaxPairs];       // pair t*k + j: expert
+  float w[kFzMaxPairs];           //   weight
+  int32_t row[kFzMaxPairs];       //   h row (expert-sorted order)
+  int32_t first[kFzMaxPairs];     //   1 if no earlier pair has its expert
+  int32_t row_tile[kFzMaxPairs];  // routed h row: its tile (1 + the index below)
+  int32_t tile_e[kFzMaxPairs];    // routed tile i (the i-th chosen expert, ascending): expert
+  int32_t tile_r0[kFzMaxPairs];   //   first h row
+  int32_t tile_n[kFzMaxPairs];    //   rows
+  uint32_t tile_tok[kFzMaxPairs]; //   token of row j at bits 4j..4j+3
+  int32_t n_tiles;
+};
+
+// Routing item: wave w computes expert (item * kFzWaves + w)'s logit of every
+// token. Lane l takes 8-element chunks l, l + 64, l + 128, l + 192 of H (added
+// in that order) and the lanes meet in a fixed tree, as in the one-launch
+// routing kernel, so both give the same bits. Every load is issued at once;
+// from 3 tokens on, x is staged in LDS by the whole workgroup.
+template <int TM>
+__device__ __forceinline__ void fz_route_item(const FusedArgs& f, int item, uint32_t tag, uint8_t* smem) {
+  constexpr int H = kFzH, NCH = H / 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = f.g.shared_rows, E = f.g.E;
+  const int e = item * kFzWaves + wave;
+  const uint16_t* wr = f.wr + size_t(min(e, E - 1)) * H;
+  const uint16_t* x = f.g.A;
+  u32x4 wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = *reinterpret_cast<const u32x4*>(wr + (lane + 64 * i) * 8);
+  float acc[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) acc[t] = 0.0f;
+  if constexpr (TM <= 2) {
+    u32x4 xv[TM][4];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[t][i] = *reinterpret_cast<const u32x4*>(x + size_t(min(t, T - 1)) * H + (lane + 64 * i) * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        acc[t] = dot2(wv[i].x, xv[t][i].x, acc[t]);
+        acc[t] = dot2(wv[i].y, xv[t][i].y, acc[t]);
+        acc[t] = dot2(wv[i].z, xv[t][i].z, acc[t]);
+        acc[t] = dot2(wv[i].w, xv[t][i].w, acc[t]);
+      }
+  } else {
+    // x [T][H] into LDS: chunk c of token t at (t * NCH + c) * 16
+    constexpr int PER = TM * NCH / kFzThreads;
+    u32x4 xs[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * kFzThreads;
+      xs[i] = *reinterpret_cast<const u32x4*>(x + size_t(min(c, T * NCH - 1)) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * kFzThreads;
+      if (c < T * NCH) *reinterpret_cast<u32x4*>(smem + c * 16) = xs[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        if (t < T) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(smem + (t * NCH + lane + 64 * i) * 16);
+          acc[t] = dot2(wv[i].x, xv.x, acc[t]);
+          acc[t] = dot2(wv[i].y, xv.y, acc[t]);
+          acc[t] = dot2(wv[i].z, xv.z, acc[t]);
+          acc[t] = dot2(wv[i].w, xv.w, acc[t]);
+        }
+      }
+  }
   float mine = 0.0f;
 #pragma unroll
-  for (int t = 0; t < kFzMaxT; ++t) {
+  for (int t = 0; t < TM; ++t) {
     const float v = wave_sum_f32(acc[t]);
     mine = lane == t ? v : mine;
   }
   if (e < E && lane < T) {
     float v = mine;
-    if (a.bias) v = v + a.bias[e];
+    if (f.bias) v = v + f.bias[e];
     v = v + 0.0f;   // turns -0 into +0
     fz_store(reinterpret_cast<uint64_t*>(f.fz + kFzSlots) + lane * E + e, tag, __float_as_uint(v));
   }
 }
 
-// Top-k item: the logits into LDS (and logits_out), the routing block, then
-// the tile descriptors, the tile count and each pair's (expert, row, weight)
-// published as tagged words.
-__device__ __forceinline__ void fz_topk_item(const FusedArgs& f, uint32_t tag, float* lg) {
-  const RouteArgs& a = f.ra;
-  const int T = a.T, E = a.E, k = a.k, tid = threadIdx.x;
+// The workgroup's routing: wave m < T waits for token m's logits, selects its
+// top-k and softmax weights (the same functions as the routing kernels, so
+// the same results); wave 0 then orders the T*k pairs by (expert, pair) into h
+// rows and lists the chosen experts in ascending order as tiles. emit: also
+// write logits, ids and weights to the caller's buffers.
+__device__ __forceinline__ void fz_local_route(const FusedArgs& f, uint32_t tag, FzRoute& rt, bool emit) {
+  const int tid = threadIdx.x, lane = tid & 63, m = tid >> 6;
+  const int T = f.g.shared_rows, E = f.g.E, k = f.d.k;
   uint32_t* status = reinterpret_cast<uint32_t*>(f.fz + kFzStatus);
   const uint64_t* slots = reinterpret_cast<const uint64_t*>(f.fz + kFzSlots);
-  for (int i0 = 0; i0 < T * E; i0 += kFzThreads) {
-    const int i = i0 + tid;
-    const float v = __uint_as_float(fz_wait(slots + min(i, T * E - 1), tag, i < T * E, status));
-    if (i < T * E) {
-      lg[i] = v;
-      a.logits_out[i] = v;
+  if (m == 0)
+    fz_wait_count(reinterpret_cast<const uint32_t*>(f.fz + kFzRouteCnt + (blockIdx.x % kFzCntCopies) * kFzLine),
+                  uint32_t(f.n_route), status);
+  __syncthreads();
+  if (m < T) {
+    const uint64_t* p[kMaxKeysPerLane];
+    bool need[kMaxKeysPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      const int e = lane + 64 * i;
+      p[i] = slots + m * E + min(e, E - 1);
+      need[i] = e < E;
+    }
+    uint32_t bits[kMaxKeysPerLane];
+    fz_wait_n<kMaxKeysPerLane>(p, need, tag, status, bits);
+    uint32_t u[kMaxKeysPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      const int e = lane + 64 * i;
+      u[i] = e < E ? float_order_key(__uint_as_float(bits[i])) : 0u;
+      if (emit && e < E && f.logits_out) f.logits_out[m * E + e] = __uint_as_float(bits[i]);
+    }
+    token_topk(u, k, rt.cand_key[m], rt.cand_e[m], rt.sel_key[m], rt.sel_e[m]);
+    int my_e;
+    float wgt;
+    token_softmax(rt.sel_key[m], rt.sel_e[m], k, my_e, wgt);
+    if (lane < k) {
+      rt.ids[m * k + lane] = my_e;
+      rt.w[m * k + lane] = wgt;
+      if (emit && f.ids_out) f.ids_out[m * k + lane] = my_e;
+      if (emit && f.w_out) f.w_out[m * k + lane] = wgt;
     }
   }
   __syncthreads();
-  RouteArgs b = a;
-  b.logits_in = lg;
-  b.coherent = 0;
-  b.n_parts = 1;
-  b.bias = nullptr;
-  b.logits_out = nullptr;
-  b.finish = 1;
-  topk_block(b, 0);
-  __syncthreads();   // this workgroup's table stores are visible to its threads
-  const int nt = *b.num_tiles;
-  uint64_t* desc = reinterpret_cast<uint64_t*>(f.fz + kFzDesc);
-  if (tid < nt) {
-    const u32x4 d = b.tile_desc[tid];
-    fz_store(desc + 4 * tid + 0, tag, d.x);
-    fz_store(desc + 4 * tid + 1, tag, d.y);
-    fz_store(desc + 4 * tid + 2, tag, d.z);
-    fz_store(desc + 4 * tid + 3, tag, d.w);
-  }
-  uint64_t* pairs = reinterpret_cast<uint64_t*>(f.fz + kFzPairs);
-  if (tid < T * k) {
-    fz_store(pairs + 2 * tid, tag, uint32_t(b.topk_ids[tid]) | (uint32_t(b.row_of_pair[tid]) << 16));
-    fz_store(pairs + 2 * tid + 1, tag, __float_as_uint(b.topk_w[tid]));
-  }
-  if (tid == 0) fz_store(reinterpret_cast<uint64_t*>(f.fz + kFzNtiles), tag, uint32_t(nt));
-}
-
-// Gate/up item: one (row tile, 16 columns of h); h goes out as tagged words.
-__device__ __forceinline__ void fz_gu_item(const FusedArgs& f, int gi, uint32_t tag, uint8_t* smem) {
-  __shared__ uint32_t desc_s[5];
-  const GemmArgs& g = f.g;
-  const int tile = gi / g.NT, cb = gi % g.NT;
-  uint32_t* status = reinterpret_cast<uint32_t*>(f.fz + kFzStatus);
-  DecTile ti;
-  if (tile == 0) {
-    ti.e = g.E;
-    ti.r0 = g.routed_rows;
-    ti.n = g.shared_rows;
-    ti.tok = 0u;
-    for (int j = 0; j < g.shared_rows; ++j) ti.tok |= uint32_t(j) << (4 * j);
-  } else {
-    const int i = tile - 1;
-    if (threadIdx.x < kWave) {
-      const int l = threadIdx.x;
-      const uint32_t nt = fz_wait(reinterpret_cast<const uint64_t*>(f.fz + kFzNtiles), tag, true, status);
-      uint32_t dv = 0;
-      if (uint32_t(i) < nt)
-        dv = fz_wait(reinterpret_cast<const uint64_t*>(f.fz + kFzDesc) + 4 * i + min(l, 3), tag, l < 4, status);
-      if (l == 0) desc_s[4] = nt;
-      if (l < 4) desc_s[l] = dv;
+  if (m == 0) {
+    // lane p: pair p (T * k <= 64)
+    // (every loop reads its entries in groups of eight, each group's loads
+    // issued together)
+    const int np = T * k, p = lane;
+    const int ep = p < np ? rt.ids[p] : 0x7FFFFFFF;
+    int less = 0, before = 0, cnt = 0;
+    for (int q0 = 0; q0 < np; q0 += 8) {
+      int eq[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) eq[q] = rt.ids[min(q0 + q, np - 1)];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int in = int(q0 + q < np);
+        less += in & int(eq[q] < ep);
+        before += in & int(eq[q] == ep) & int(q0 + q < p);
+        cnt += in & int(eq[q] == ep);
+      }
     }
-    __syncthreads();
-    if (uint32_t(i) >= min(desc_s[4], uint32_t(kFzMaxTiles))) return;   // uniform: no such tile in this call
-    // the values are checked to stay in bounds even if a wait gave up
-    ti.n = int(min(desc_s[2], uint32_t(g.shared_rows)));
-    ti.e = int(min(desc_s[0], uint32_t(g.E - 1)));
-    ti.r0 = int(min(desc_s[1], uint32_t(g.routed_rows - ti.n)));
-    ti.tok = 0u;
-    for (int j = 0; j < ti.n; ++j) ti.tok |= min((desc_s[3] >> (4 * j)) & 15u, uint32_t(g.shared_rows - 1)) << (4 * j);
+    const bool first = p < np && before == 0;
+    rt.first[p] = int(first);
+    __builtin_amdgcn_wave_barrier();
+    int tix = 0;
+    for (int q0 = 0; q0 < np; q0 += 8) {
+      int eq[8], fq[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        eq[q] = rt.ids[min(q0 + q, np - 1)];
+        fq[q] = rt.first[min(q0 + q, np - 1)];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) tix += int(q0 + q < np) & fq[q] & int(eq[q] < ep);
+    }
+    if (first) {
+      rt.tile_e[tix] = ep;
+      rt.tile_r0[tix] = less;
+      rt.tile_n[tix] = cnt;
+      rt.tile_tok[tix] = 0u;
+    }
+    const uint64_t fm = __ballot(first);
+    if (lane == 0) rt.n_tiles = int(__popcll(fm));
+    __builtin_amdgcn_wave_barrier();
+    if (p < np) {
+      rt.row[p] = less + before;
+      rt.row_tile[less + before] = 1 + tix;
+      // a tile has at most T <= 8 rows: its row j's token fits in 4 bits
+      atomicOr(&rt.tile_tok[tix], uint32_t(p / k) << (4 * before));
+    }
   }
-  uint64_t* h = reinterpret_cast<uint64_t*>(f.fz + kFzH);
+  __syncthreads();
+}
+
+template <int TM>
+__device__ __forceinline__ void fz_swiglu(const GemmArgs& g, const DecTile& ti, int cb, uint8_t* smem, uint64_t* h,
+                                          uint32_t tag) {
   switch (ti.n) {
-    case 1: swiglu_tile<1, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
-    case 2: swiglu_tile<2, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
-    case 3: swiglu_tile<3, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
-    case 4: swiglu_tile<4, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
-    case 5: swiglu_tile<5, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
-    case 6: swiglu_tile<6, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
-    case 7: swiglu_tile<7, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
-    case 8: swiglu_tile<8, 4, 4>(g, ti, cb, smem, g.shared_rows, h, tag); break;
-    default: break;   // 1..T rows per tile (a wait that gave up may leave garbage here)
+    case 1: swiglu_tile<1, 4, 4>(g, ti, cb, smem, TM, h, tag); break;
+    case 2: if constexpr (TM >= 2) swiglu_tile<2, 4, 4>(g, ti, cb, smem, TM, h, tag); break;
+    case 3: if constexpr (TM >= 4) swiglu_tile<3, 4, 4>(g, ti, cb, smem, TM, h, tag); break;
+    case 4: if constexpr (TM >= 4) swiglu_tile<4, 4, 4>(g, ti, cb, smem, TM, h, tag); break;
+    case 5: if constexpr (TM >= 8) swiglu_tile<5, 4, 4>(g, ti, cb, smem, TM, h, tag); break;
+    case 6: if constexpr (TM >= 8) swiglu_tile<6, 4, 4>(g, ti, cb, smem, TM, h, tag); break;
+    case 7: if constexpr (TM >= 8) swiglu_tile<7, 4, 4>(g, ti, cb, smem, TM, h, tag); break;
+    case 8: if constexpr (TM >= 8) swiglu_tile<8, 4, 4>(g, ti, cb, smem, TM, h, tag); break;
+    default: break;   // 1..T rows per tile
   }
 }
 
-// Down item: one (token, 16 output columns); the pairs and the h rows come
-// from tagged words.
+// Down item: one (token, 16 output columns); the pairs come from the
+// workgroup's tables and the h rows from tagged words.
 template <int DSTEPS>
-__device__ __forceinline__ void fz_dn_item(const FusedArgs& f, int di, uint32_t tag, uint8_t* smem) {
+__device__ __forceinline__ void fz_dn_item(const FusedArgs& f, int di, uint32_t tag, uint8_t* smem,
+                                           const FzRoute& rt) {
   constexpr int K = DSTEPS * 128;
   const DownCombineArgs& a = f.d;
   const int ncb = a.N / 16;
   const int t = di / ncb, col0 = (di % ncb) * 16;
   const int lane = threadIdx.x & 63;
   uint32_t* status = reinterpret_cast<uint32_t*>(f.fz + kFzStatus);
-  const uint64_t* pairs = reinterpret_cast<const uint64_t*>(f.fz + kFzPairs);
-  const uint64_t* h = reinterpret_cast<const uint64_t*>(f.fz + kFzH);
+  const uint64_t* h = reinterpret_cast<const uint64_t*>(f.fz + kFzHrows);
   auto pair = [&](int j) {
-    const uint64_t* pw = pairs + 2 * (t * a.k + j);
-    const uint32_t ir = fz_wait(pw, tag, true, status);
-    const uint32_t wb = fz_wait(pw + 1, tag, true, status);
-    // in bounds even if a wait gave up
-    return DcPair{min(int(ir & 0xFFFFu), f.ra.E - 1), min(int(ir >> 16), f.g.routed_rows - 1), __uint_as_float(wb)};
+    const int p = t * a.k + j;
+    return DcPair{rt.ids[p], rt.row[p], rt.w[p]};
   };
   auto stage_row = [&](int row, uint8_t* xs) {
+    // every column item of the row's tile is done (shared rows: tile 0)
+    const int tile = row < f.g.routed_rows ? rt.row_tile[row] : 0;
+    fz_wait_count(reinterpret_cast<const uint32_t*>(f.fz + kFzTileCnt + tile * kFzLine), uint32_t(f.g.NT), status);
     const uint64_t* hr = h + size_t(row) * (K / 2);   // row < T * k + T <= kFzMaxRows
-    for (int i0 = 0; i0 < K / 2; i0 += kWave) {
-      const uint32_t v = fz_wait(hr + i0 + lane, tag, true, status);
-      *reinterpret_cast<uint32_t*>(xs + dec_off(K, 0, 2 * (i0 + lane))) = v;
+    constexpr int N = K / 2 / kWave;
+    const uint64_t* p[N];
+    bool need[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      p[i] = hr + i * kWave + lane;
+      need[i] = true;
     }
+    uint32_t v[N];
+    fz_wait_n<N>(p, need, tag, status, v);
+#pragma unroll
+    for (int i = 0; i < N; ++i) *reinterpret_cast<uint32_t*>(xs + dec_off(K, 0, 2 * (i * kWave + lane))) = v[i];
   };
   down_combine_unit<DSTEPS>(a, t, col0, kFzWaves, smem, pair, stage_row);
 }
 
-template <int DSTEPS>
-__global__ __launch_bounds__(kFzThreads) void decode_fused_kernel(FusedArgs f) {
+template <int TM, int DSTEPS>
+__global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(TM <= 2 ? 4 : 2)))
+void decode_fused_kernel(FusedArgs f) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ float lg[kFzMaxT * kMaxExperts];
+  __shared__ FzRoute rt;
   __shared__ uint32_t tag_s;
   uint32_t* epoch = reinterpret_cast<uint32_t*>(f.fz + kFzEpoch);
   if (threadIdx.x == 0) tag_s = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   __syncthreads();
   const uint32_t tag = tag_s;
-  const int n0 = f.n_route, n1 = n0 + 1, n2 = n1 + f.n_gu, n3 = n2 + f.n_dn;
-  for (int item = blockIdx.x; item < n3; item += gridDim.x) {
-    if (item < n0)
-      fz_route_item(f, item, tag);
-    else if (item < n1)
-      fz_topk_item(f, tag, lg);
-    else if (item < n2)
-      fz_gu_item(f, item - n1, tag, smem);
-    else
-      fz_dn_item<DSTEPS>(f, item - n2, tag, smem);
+  const GemmArgs& g = f.g;
+  const int T = g.shared_rows;
+  uint64_t* h = reinterpret_cast<uint64_t*>(f.fz + kFzHrows);
+  const int n0 = f.n_route, n1 = n0 + f.n_gu, n2 = n1 + f.n_dn;
+  bool have_rt = false;   // uniform: this workgroup's tables are built
+  for (int item = blockIdx.x; item < n2; item += gridDim.x) {
+    if (item < n0) {
+      fz_route_item<TM>(f, item, tag, smem);
+      fz_count_done(f.fz + kFzRouteCnt, kFzCntCopies);
+    } else if (item < n1) {
+      const int gi = item - n0, tile = gi / g.NT, cb = gi % g.NT;
+      if (tile == 0) {
+        // the shared expert: one tile of every token's row (row routed_rows + t
+        // is token t)
+        DecTile ti{g.E, g.routed_rows, T, 0u};
+        for (int j = 0; j < T; ++j) ti.tok |= uint32_t(j) << (4 * j);
+        fz_swiglu<TM>(g, ti, cb, smem, h, tag);
+        fz_count_done(f.fz + kFzTileCnt, 1);
+      } else {
+        if (!have_rt) {
+          fz_local_route(f, tag, rt, item == n0 + g.NT);   // the first routed item writes the routing outputs
+          have_rt = true;
+        }
+        const int i = tile - 1;
+        if (i < rt.n_tiles) {   // uniform
+          const DecTile ti{rt.tile_e[i], rt.tile_r0[i], rt.tile_n[i], rt.tile_tok[i]};
+          fz_swiglu<TM>(g, ti, cb, smem, h, tag);
+          fz_count_done(f.fz + kFzTileCnt + tile * kFzLine, 1);
+        }
+      }
+    } else {
+      if (!have_rt) {
+        fz_local_route(f, tag, rt, false);
+        have_rt = true;
+      }
+      fz_dn_item<DSTEPS>(f, item - n1, tag, smem, rt);
+    }
     __syncthreads();   // LDS is reused by the next item
   }
+  __shared__ int last_s;
   if (threadIdx.x == 0) {
     uint32_t* ex = reinterpret_cast<uint32_t*>(f.fz + kFzExit);
-    if (__hip_atomic_fetch_add(ex, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
-      // every workgroup has read the epoch and finished: the next call's tag
-      __hip_atomic_store(ex, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_s = __hip_atomic_fetch_add(ex, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (last_s) {   // uniform
+    // every workgroup has read the epoch and finished: the counters back at
+    // zero, and the next call's tag
+    const int tid = threadIdx.x;
+    if (tid < kFzCntCopies + kFzMaxTiles)
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(f.fz + kFzRouteCnt + tid * kFzLine), 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(f.fz + kFzExit), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
 bool decode_fused_supported(int T, int k, int H, int I) {
-  return T >= 1 && T <= kFzMaxT && T * k <= kFzMaxPairs && H == 2048 && (I == 256 || I == 512);
+  return T >= 1 && T <= kFzMaxT && T * k <= kFzMaxPairs && H == kFzH && (I == 256 || I == 512);
 }
 
 static_assert(kHandoffBytes + kFzStatus == MOE_WORKSPACE_STATUS_OFFSET, "status word offset in the header");
 
 namespace {
 constexpr int kFzMaxDevices = 64;
-int g_fz_grid[kFzMaxDevices][2];   // resident workgroups per device for I = 256, 512 (0: not queried)
-}  // namespace
+constexpr int kFzVariants = 8;   // token bucket (1, 2, 4, 8) x I (256, 512)
+int g_fz_grid[kFzMaxDevices][kFzVariants];   // resident workgroups per device and variant (0: not queried)
 
-hipError_t launch_decode_fused(const RouteArgs& ra, const GemmArgs& g, const DownCombineArgs& d, uint8_t* fz,
-                               hipStream_t stream) {
-  const int T = ra.T, I = g.N;
-  if (!decode_fused_supported(T, ra.k, ra.H, I)) return hipErrorInvalidValue;
-  FusedArgs f{ra, g, d, fz, ceil_div(ra.E, kFzWaves), 0, 0};
-  const int max_routed = ra.T * ra.k / max(ra.block_rows, 1) + min(ra.E, ra.T * ra.k);
-  f.n_gu = (1 + max_routed) * g.NT;
-  f.n_dn = T * (d.N / 16);
-  const size_t lds_gu = size_t(dec_lds_bytes(4, 4, kFzMaxT));
-  const size_t lds_dn = size_t(kFzWaves) * dc_wave_bytes(I) + size_t(kFzWaves) * 33 * 4;
-  const size_t lds = lds_gu > lds_dn ? lds_gu : lds_dn;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kFzMaxDevices) return hipErrorInvalidDevice;
-  const int slot = I == 256 ? 0 : 1;
+template <int TM, int DSTEPS>
+hipError_t fz_launch(const FusedArgs& f, int dev, int slot, size_t lds, hipStream_t stream) {
   if (g_fz_grid[dev][slot] == 0) {
     // every workgroup of the grid must be resident at once (the items wait on
     // one another): the grid is at most the resident capacity of the device
     int per_cu = 0, cus = 0;
-    hipError_t e = I == 256 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<2>,
-                                                                           kFzThreads, lds)
-                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<4>,
-                                                                           kFzThreads, lds);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<TM, DSTEPS>,
+                                                                kFzThreads, lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
     g_fz_grid[dev][slot] = per_cu * cus;
   }
-  const int items = f.n_route + 1 + f.n_gu + f.n_dn;
+  const int items = f.n_route + f.n_gu + f.n_dn;
   const int grid = min(items, g_fz_grid[dev][slot]);
-  if (I == 256)
-    hipLaunchKernelGGL(decode_fused_kernel<2>, dim3(grid), dim3(kFzThreads), lds, stream, f);
-  else
-    hipLaunchKernelGGL(decode_fused_kernel<4>, dim3(grid), dim3(kFzThreads), lds, stream, f);
+  hipLaunchKernelGGL((decode_fused_kernel<TM, DSTEPS>), dim3(grid), dim3(kFzThreads), lds, stream, f);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_fused(const FusedLaunch& fl, hipStream_t stream) {
+  const int T = fl.g.shared_rows, I = fl.g.N, E = fl.g.E, k = fl.d.k;
+  if (!decode_fused_supported(T, k, fl.g.K, I) || fl.d.N != kFzH || fl.d.K != I || fl.g.NT != I / 16 ||
+      fl.g.routed_rows != T * k || E < k || E > kMaxExperts)
+    return hipErrorInvalidValue;
+  FusedArgs f{fl.g, fl.d, fl.wr, fl.bias, fl.logits_out, fl.ids_out, fl.w_out, fl.fz, 0, 0, 0};
+  f.n_route = ceil_div(E, kFzWaves);
+  f.n_gu = (1 + min(E, T * k)) * fl.g.NT;   // the shared tile, then one tile per chosen expert
+  f.n_dn = T * (kFzH / 16);
+  const int tm = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+  const size_t lds_gu = size_t(dec_lds_bytes(4, 4, tm));
+  const size_t lds_dn = size_t(kFzWaves) * dc_wave_bytes(I) + size_t(kFzWaves) * 33 * 4;
+  const size_t lds_rt = size_t(tm) * kFzH * 2;   // the routing items' staged x (tm >= 4)
+  size_t lds = lds_gu > lds_dn ? lds_gu : lds_dn;
+  lds = lds > lds_rt ? lds : lds_rt;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kFzMaxDevices) return hipErrorInvalidDevice;
+  const int slot = (tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3) * 2 + (I == 256 ? 0 : 1);
+  switch (slot) {
+    case 0: return fz_launch<1, 2>(f, dev, slot, lds, stream);
+    case 1: return fz_launch<1, 4>(f, dev, slot, lds, stream);
+    case 2: return fz_launch<2, 2>(f, dev, slot, lds, stream);
+    case 3: return fz_launch<2, 4>(f, dev, slot, lds, stream);
+    case 4: return fz_launch<4, 2>(f, dev, slot, lds, stream);
+    case 5: return fz_launch<4, 4>(f, dev, slot, lds, stream);
+    case 6: return fz_launch<8, 2>(f, dev, slot, lds, stream);
+    default: return fz_launch<8, 4>(f, dev, slot, lds, stream);
+  }
 }
 
 }  // namespace moe

@@ -430,32 +430,11 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
 
   // few tokens at the full hidden size: the whole layer as one persistent launch
   if (decode && !s2 && opts && opts->persistent_decode && decode_fused_supported(T, k, H, I)) {
-    RouteArgs fa{};
-    fa.x = x;
-    fa.wr = router_w;
-    fa.bias = logit_bias;
-    fa.logits_out = logits_out ? logits_out : at<float>(ws, L.logits);
-    fa.topk_ids = ids;
-    fa.topk_w = wts;
-    fa.block_counts = at<int32_t>(ws, L.block_counts);
-    fa.rank_in_block = at<int32_t>(ws, L.rank);
-    fa.T = T;
-    fa.H = H;
-    fa.E = E;
-    fa.k = k;
-    fa.finish = 1;
-    fa.block_rows = bm;
-    fa.counts = at<int32_t>(ws, L.counts);
-    fa.offsets = offsets;
-    fa.tile_map = tile_map;
-    fa.num_tiles = num_tiles;
-    fa.sorted_rows = sorted_rows;
-    fa.row_of_pair = row_of_pair;
-    fa.tile_desc = tile_desc;
     const DownCombineArgs da{h, stack_of(down), stack_of(sh_down), ids, wts, row_of_pair, T, k, H, I,
                              routed_rows, y, x, shared_gate};
-    uint8_t* fz = at<uint8_t>(ws, L.done + kHandoffBytes);
-    const hipError_t ef = launch_decode_fused(fa, g1, da, fz, s);
+    const FusedLaunch fl{g1, da, router_w, logit_bias, logits_out, topk_ids_out, topk_w_out,
+                         at<uint8_t>(ws, L.done + kHandoffBytes)};
+    const hipError_t ef = launch_decode_fused(fl, s);
     if (ef == hipSuccess) return (mark(2) && mark(3) && mark(4) && mark(5)) ? MOE_OK : MOE_ERR_HIP;
     if (ef != hipErrorInvalidConfiguration) return MOE_ERR_HIP;
     // no resident grid possible on this device: the three-launch path below

@@ -106,9 +106,18 @@ hipError_t launch_decode_down_combine(const DownCombineArgs& da, hipStream_t str
 // as work items handed over through tagged words in `fz`, the workspace head
 // after the one-launch routing's part. hipErrorInvalidConfiguration: the
 // device cannot hold a resident grid (use the three-launch path).
+struct FusedLaunch {
+  GemmArgs g;            // gate/up arguments of the decode path (A = x, NT = I / 16, shared_rows = T)
+  DownCombineArgs d;     // down + combine arguments (h, topk and row tables unused)
+  const uint16_t* wr;    // router weights [E][H]
+  const float* bias;     // logit bias [E] or null
+  float* logits_out;     // [T][E] or null
+  int32_t* ids_out;      // [T][k] or null
+  float* w_out;          // [T][k] or null
+  uint8_t* fz;
+};
 bool decode_fused_supported(int T, int k, int H, int I);
-hipError_t launch_decode_fused(const RouteArgs& ra, const GemmArgs& g, const DownCombineArgs& d, uint8_t* fz,
-                               hipStream_t stream);
+hipError_t launch_decode_fused(const FusedLaunch& fl, hipStream_t stream);
 
 // Min-max affine 4-bit quantiser: bf16 [rows][K] -> codes [rows][K/8],
 // bf16 scale and bias [rows][K/64].

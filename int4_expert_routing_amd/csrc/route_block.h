@@ -78,6 +78,149 @@ __device__ __forceinline__ void block_scan2(int32_t& a, int32_t& b, int32_t* tot
   b += pb;
 }
 
+// Top-k of one token held by one wave (keys as in kth_largest): leaves the k
+// chosen keys and experts in (logit desc, expert asc) order in sel_key[0..k-1]
+// and sel_e[0..k-1]. cand_key and cand_e are kMaxCand entries of scratch; all
+// four arrays are the wave's own LDS rows.
+__device__ __forceinline__ void token_topk(const uint32_t (&u)[kMaxKeysPerLane], int k, uint32_t* cand_key,
+                                           int32_t* cand_e, uint32_t* sel_key, int32_t* sel_e) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  // Fast path. Let mk be the k-th largest of the 64 lanes' largest keys: at
+  // least k keys are >= mk, so the k-th largest key is >= mk and every
+  // chosen key is among the candidates {keys >= mk}; every other key is
+  // strictly smaller than all chosen ones. The candidates (usually about k)
+  // are gathered in LDS and each one's position in (logit desc, expert asc)
+  // order is counted directly: positions 0..k-1 are the chosen experts, in
+  // order. mk itself needs one ballot per radix pass instead of four. Exact
+  // ties that leave more than kMaxCand candidates take the general path.
+  uint32_t mx = u[0];
+#pragma unroll
+  for (int i = 1; i < kMaxKeysPerLane; ++i) mx = u[i] > mx ? u[i] : mx;
+  uint32_t mk = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = mk | (1u << b);
+    mk = __popcll(__ballot(mx >= cand)) >= k ? cand : mk;
+  }
+  uint64_t cmask[kMaxKeysPerLane];
+  int n_cand = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) {
+    cmask[i] = __ballot(u[i] >= mk);
+    n_cand += __popcll(cmask[i]);
+  }
+  if (n_cand <= kMaxCand) {   // uniform
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      if ((cmask[i] >> lane) & 1ull) {
+        const int slot = base + __popcll(cmask[i] & below);
+        cand_key[slot] = u[i];
+        cand_e[slot] = lane + 64 * i;
+      }
+      base += __popcll(cmask[i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < n_cand) {
+      const uint32_t my_key = cand_key[lane];
+      const int my_e = cand_e[lane];
+      int pos = 0;
+      for (int q0 = 0; q0 < n_cand; q0 += 8) {
+        uint32_t kq[8];
+        int eq[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          kq[q] = cand_key[min(q0 + q, n_cand - 1)];
+          eq[q] = cand_e[min(q0 + q, n_cand - 1)];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          pos += int(q0 + q < n_cand) & (int(kq[q] > my_key) | (int(kq[q] == my_key) & int(eq[q] < my_e)));
+      }
+      if (pos < k) {
+        sel_key[pos] = my_key;
+        sel_e[pos] = my_e;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  } else {
+    const uint32_t tau = kth_largest(u, k);
+    int n_gt = 0;
+    uint64_t tie[kMaxKeysPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      n_gt += __popcll(__ballot(u[i] > tau));
+      tie[i] = __ballot(u[i] == tau);
+    }
+    // ties at tau are taken in expert order: expert lane + 64 i ranks after
+    // every tie of a lower i and after the lower lanes' ties of the same i
+    const int need = k - n_gt;
+    int ties_before = 0;
+    int slot_base = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+      const bool is_tie = (tie[i] >> lane) & 1ull;
+      const int tie_rank = ties_before + __popcll(tie[i] & below);
+      const bool chosen = u[i] > tau || (is_tie && tie_rank < need);
+      const uint64_t cm = __ballot(chosen);
+      if (chosen) {
+        const int slot = slot_base + __popcll(cm & below);
+        sel_key[slot] = u[i];
+        sel_e[slot] = lane + 64 * i;
+      }
+      ties_before += __popcll(tie[i]);
+      slot_base += __popcll(cm);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane j < k: its chosen element's position in (logit desc, expert asc)
+    // order, counted without branches over all k chosen elements (read in
+    // groups of eight, each group's loads issued together)
+    int pos = 0;
+    uint32_t my_key = 0;
+    int my_e = 0;
+    if (lane < k) {
+      my_key = sel_key[lane];
+      my_e = sel_e[lane];
+      for (int q0 = 0; q0 < k; q0 += 8) {
+        uint32_t kq[8];
+        int eq[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          kq[q] = sel_key[min(q0 + q, k - 1)];
+          eq[q] = sel_e[min(q0 + q, k - 1)];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          pos += int(q0 + q < k) & (int(kq[q] > my_key) | (int(kq[q] == my_key) & int(eq[q] < my_e)));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) {
+      sel_key[pos] = my_key;
+      sel_e[pos] = my_e;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Softmax over a token's chosen logits (sel_key in rank order): lane j < k gets
+// its expert and weight; the k terms are added in rank order.
+__device__ __forceinline__ void token_softmax(const uint32_t* sel_key, const int32_t* sel_e, int k, int& my_e,
+                                              float& wgt) {
+  const int lane = threadIdx.x & 63;
+  float my_l = 0.0f;
+  my_e = 0;
+  if (lane < k) {
+    my_e = sel_e[lane];
+    my_l = float_from_order_key(sel_key[lane]);
+  }
+  const float l0 = float_from_order_key(sel_key[0]);
+  const float ex = lane < k ? expf(my_l - l0) : 0.0f;
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+  wgt = ex / sum;
+}
+
 // Top-k, softmax, histogram and ranks of routing block blk (and, for a single
 // block, the tables), run by one 1024-thread workgroup.
 __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
@@ -140,136 +283,14 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
       }
       u[i] = key;
     }
-    // Fast path. Let mk be the k-th largest of the 64 lanes' largest keys: at
-    // least k keys are >= mk, so the k-th largest key is >= mk and every
-    // chosen key is among the candidates {keys >= mk}; every other key is
-    // strictly smaller than all chosen ones. The candidates (usually about k)
-    // are gathered in LDS and each one's position in (logit desc, expert asc)
-    // order is counted directly: positions 0..k-1 are the chosen experts, in
-    // order. mk itself needs one ballot per radix pass instead of four. Exact
-    // ties that leave more than kMaxCand candidates take the general path.
-    uint32_t mx = u[0];
-#pragma unroll
-    for (int i = 1; i < kMaxKeysPerLane; ++i) mx = u[i] > mx ? u[i] : mx;
-    uint32_t mk = 0;
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t cand = mk | (1u << b);
-      mk = __popcll(__ballot(mx >= cand)) >= k ? cand : mk;
-    }
-    uint64_t cmask[kMaxKeysPerLane];
-    int n_cand = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-      cmask[i] = __ballot(u[i] >= mk);
-      n_cand += __popcll(cmask[i]);
-    }
-    if (n_cand <= kMaxCand) {   // uniform
-      int base = 0;
-#pragma unroll
-      for (int i = 0; i < kMaxKeysPerLane; ++i) {
-        if ((cmask[i] >> lane) & 1ull) {
-          const int slot = base + __popcll(cmask[i] & below);
-          cand_key[m][slot] = u[i];
-          cand_e[m][slot] = lane + 64 * i;
-        }
-        base += __popcll(cmask[i]);
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (lane < n_cand) {
-        const uint32_t my_key = cand_key[m][lane];
-        const int my_e = cand_e[m][lane];
-        int pos = 0;
-        for (int q0 = 0; q0 < n_cand; q0 += 8) {
-          uint32_t kq[8];
-          int eq[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            kq[q] = cand_key[m][min(q0 + q, n_cand - 1)];
-            eq[q] = cand_e[m][min(q0 + q, n_cand - 1)];
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            pos += int(q0 + q < n_cand) & (int(kq[q] > my_key) | (int(kq[q] == my_key) & int(eq[q] < my_e)));
-        }
-        if (pos < k) {
-          sel_key[m][pos] = my_key;
-          sel_e[m][pos] = my_e;
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    } else {
-    const uint32_t tau = kth_largest(u, k);
-    int n_gt = 0;
-    uint64_t tie[kMaxKeysPerLane];
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-      n_gt += __popcll(__ballot(u[i] > tau));
-      tie[i] = __ballot(u[i] == tau);
-    }
-    // ties at tau are taken in expert order: expert lane + 64 i ranks after
-    // every tie of a lower i and after the lower lanes' ties of the same i
-    const int need = k - n_gt;
-    int ties_before = 0;
-    int slot_base = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-      const bool is_tie = (tie[i] >> lane) & 1ull;
-      const int tie_rank = ties_before + __popcll(tie[i] & below);
-      const bool chosen = u[i] > tau || (is_tie && tie_rank < need);
-      const uint64_t cm = __ballot(chosen);
-      if (chosen) {
-        const int slot = slot_base + __popcll(cm & below);
-        sel_key[m][slot] = u[i];
-        sel_e[m][slot] = lane + 64 * i;
-      }
-      ties_before += __popcll(tie[i]);
-      slot_base += __popcll(cm);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // lane j < k: its chosen element's position in (logit desc, expert asc)
-    // order, counted without branches over all k chosen elements (read in
-    // groups of eight, each group's loads issued together)
-    int pos = 0;
-    uint32_t my_key = 0;
-    int my_e = 0;
-    if (lane < k) {
-      my_key = sel_key[m][lane];
-      my_e = sel_e[m][lane];
-      for (int q0 = 0; q0 < k; q0 += 8) {
-        uint32_t kq[8];
-        int eq[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          kq[q] = sel_key[m][min(q0 + q, k - 1)];
-          eq[q] = sel_e[m][min(q0 + q, k - 1)];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          pos += int(q0 + q < k) & (int(kq[q] > my_key) | (int(kq[q] == my_key) & int(eq[q] < my_e)));
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (lane < k) {
-      sel_key[m][pos] = my_key;
-      sel_e[m][pos] = my_e;
-    }
-    __builtin_amdgcn_wave_barrier();
-    }
-    float my_l = 0.0f;
-    int my_e = 0;
-    if (lane < k) {
-      my_e = sel_e[m][lane];
-      my_l = float_from_order_key(sel_key[m][lane]);
-    }
-    const float l0 = float_from_order_key(sel_key[m][0]);
-    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
-    // the k terms added in rank order (lane reads, no cross-lane shuffles)
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+    token_topk(u, k, cand_key[m], cand_e[m], sel_key[m], sel_e[m]);
+    int my_e;
+    float wgt;
+    token_softmax(sel_key[m], sel_e[m], k, my_e, wgt);
     if (lane < k) {
       const size_t f = size_t(t0 + m) * k + lane;
       a.topk_ids[f] = my_e;
-      a.topk_w[f] = ex / sum;
+      a.topk_w[f] = wgt;
       ids_s[m * k + lane] = my_e;
     }
   }
