@@ -37,6 +37,26 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
+RAMP_SECONDS = 0.3
+
+
+def ramp(torch, fn, seconds=RAMP_SECONDS):
+    """Call fn (a layer call or a graph replay) until `seconds` of wall time
+    have passed, synchronising every few calls. The GPU raises its clocks under
+    sustained load and takes tens of milliseconds to settle (the first ~50
+    T=4096 layer calls ran 5-15% slower); the timed regions measure the
+    sustained state. Returns the number of calls."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def layer_flops(T, H, I, E, k):
     return T * (2 * H * E + (k + 1) * 2 * H * 3 * I)
 
@@ -119,6 +139,7 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
             call(i)
     graph.replay()
     torch.cuda.synchronize()
+    ramp(torch, graph.replay)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -141,8 +162,9 @@ def decode_measure(lib, _lib, ops, torch, dev, w0, T, k, n_sets=8, calls=16, rep
 
 def prefill_measure(lib, _lib, ops, torch, dev, w, T, k, zipf=None, steps=10, warmup=3, weight_bytes=None):
     """Layer calls at T tokens on the same layer weights (x drawn on the device,
-    N(0,1) in bf16; optional Zipf logit bias -zipf*ln(e+1)), timed with events
-    around `steps` back-to-back calls on the launch stream."""
+    N(0,1) in bf16; optional Zipf logit bias -zipf*ln(e+1)): `steps` calls
+    launched back to back and timed with events (ms_per_layer), and the same
+    calls captured in one HIP graph and replayed (graph_ms_per_layer)."""
     import ctypes
     E, H, I = w.E, w.H, w.I
     g = torch.Generator(device=dev)
@@ -164,12 +186,14 @@ def prefill_measure(lib, _lib, ops, torch, dev, w, T, k, zipf=None, steps=10, wa
             ctypes.c_void_p(bias.data_ptr()) if bias is not None else None,
             *[ctypes.byref(s) for s in structs], ctypes.byref(dims), ctypes.c_void_p(y.data_ptr()),
             None, ctypes.c_void_p(ids.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
-            ctypes.c_void_p(stream.cuda_stream))
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
         _lib.check(st, "moe_layer_forward")
 
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    ramp(torch, call)
+    y_eager = y.clone()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
@@ -177,13 +201,29 @@ def prefill_measure(lib, _lib, ops, torch, dev, w, T, k, zipf=None, steps=10, wa
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y, y_eager))
+    ramp(torch, graph.replay)   # the GPU idled during the capture
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    del graph
     counts = torch.bincount(ids.flatten().long(), minlength=E).cpu().numpy()
     flops = layer_flops(T, H, I, E, k)
     out = {"T": T, "ms_per_layer": ms, "tokens_per_s": T / (ms * 1e-3),
            "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
            "logit_bias": f"zipf{zipf}" if zipf is not None else None,
            "experts_hit": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max()),
-           "method": f"{steps} back-to-back layer calls timed with events"}
+           "graph_ms_per_layer": graph_ms, "graph_replay_matches_eager": same,
+           "method": f"{steps} back-to-back layer calls timed with events at sustained clocks; graph: the same "
+                     f"calls captured in one HIP graph and replayed"}
     if weight_bytes:
         # weights of the experts this call routed to (+ shared, + router), as HBM bytes per second
         hit = int((counts > 0).sum())
@@ -427,11 +467,32 @@ def main():
             ctypes.c_void_p(stream.cuda_stream), evp, n)
         _lib.check(st, "moe_layer_forward_timed")
 
+    def plain_step():
+        st = lib.moe_layer_forward(
+            ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.router_w.data_ptr()),
+            ctypes.c_void_p(w.logit_bias.data_ptr()) if w.logit_bias is not None else None,
+            *[ctypes.byref(s) for s in structs], ctypes.byref(dims), ctypes.c_void_p(y.data_ptr()), None, None,
+            None, ctypes.c_void_p(layer.workspace.data_ptr()), layer.workspace.numel(),
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        _lib.check(st, "moe_layer_forward")
+
     for _ in range(args.warmup):
-        step()
+        plain_step()
     torch.cuda.synchronize()
+    ramp_calls = ramp(torch, plain_step)
+    # the timed region: K back-to-back layer calls between synchronizations
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        plain_step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    y_ref = y.clone()
+
+    # the same calls with HIP events between the stages (stage times and the
+    # gate/up launch's duration for the roofline)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    for e in evs:            # create the HIP events before the timed region
+    for e in evs:            # create the HIP events before use
         for ev in e:
             ev.record(stream)
     torch.cuda.synchronize()
@@ -439,7 +500,7 @@ def main():
     for s in range(args.steps):
         step(evs[s])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    events_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     stage_ms = np.zeros(nev - 1)
     step_ms = []
     for e in evs:
@@ -447,7 +508,22 @@ def main():
             stage_ms[i] += e[i].elapsed_time(e[i + 1])
         step_ms.append(e[0].elapsed_time(e[nev - 1]))
     stage_ms /= args.steps
-    ms_per_step = wall * 1e3 / args.steps
+
+    # and captured in one HIP graph (the whole layer as one submission, as the
+    # pages' single command buffer), replayed once
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            plain_step()
+    graph.replay()   # untimed: the first replay uploads the graph
+    torch.cuda.synchronize()
+    graph_matches = bool(torch.equal(y, y_ref))
+    ramp(torch, graph.replay)   # the GPU idled during the capture
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graph
     gpu_ms = float(np.mean(step_ms))
     names = ["prep", "route", "gate_up_gemm", "down_gemm", "combine"]
     flops = layer_flops(T, H, I, E, k)
@@ -475,6 +551,13 @@ def main():
                    "weight_layout": ("prepacked (moe_prepack_q4, once before timing)" if packed
                                      else "canonical")},
         "layer_pct_mfma_peak": 100.0 * flops / (ms_per_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "timing": (f"{args.steps} back-to-back layer calls, wall clock between synchronizations, after the "
+                   f"{args.warmup} warm-up calls and {ramp_calls} more calls ({RAMP_SECONDS} s) that bring the GPU "
+                   "to its sustained clocks; graph_ms_per_step: the same calls captured in one HIP graph and "
+                   "replayed once; events_ms_per_step: with HIP events between the stages"),
+        "graph_ms_per_step": graph_ms_per_step,
+        "events_ms_per_step": events_ms_per_step,
+        "graph_replay_matches_eager": graph_matches,
         "layer_gpu_ms_events": gpu_ms,
         "stage_ms": {n: float(v) for n, v in zip(names, stage_ms)},
         "roofline": {"kernel": "gemm_q4_kernel<SwiGLU> (gate/up grouped GEMM)", "bound": "mfma",
