@@ -697,8 +697,7 @@ struct FusedArgs {
 
 // The few-token routing tables of one workgroup (LDS).
 struct FzRoute {
-  uint32_t cand_key[kFzMaxT][kMaxCand];
-  int32_t cand_e[kFzMaxT][kMaxCand];
+  uint64_t cand[kFzMaxT][kMaxCand];
   uint32_t sel_key[kFzMaxT][kMaxTopk];
   int32_t sel_e[kFzMaxT][kMaxTopk];
   int32_t ids[kFzMaxPairs];       // pair t*k + j: expert
@@ -822,7 +821,7 @@ __device__ __forceinline__ void fz_local_route(const FusedArgs& f, uint32_t tag,
       u[i] = e < E ? float_order_key(__uint_as_float(bits[i])) : 0u;
       if (emit && e < E && f.logits_out) f.logits_out[m * E + e] = __uint_as_float(bits[i]);
     }
-    token_topk(u, k, rt.cand_key[m], rt.cand_e[m], rt.sel_key[m], rt.sel_e[m]);
+    token_topk(u, k, rt.cand[m], rt.sel_key[m], rt.sel_e[m]);
     int my_e;
     float wgt;
     token_softmax(rt.sel_key[m], rt.sel_e[m], k, my_e, wgt);

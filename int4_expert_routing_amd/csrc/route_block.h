@@ -10,7 +10,7 @@
 namespace moe {
 
 constexpr int kMaxKeysPerLane = kMaxExperts / kWave;
-constexpr int kMaxCand = 64;   // candidates of the fast top-k path (section in topk_block)
+constexpr int kMaxCand = 64;   // candidates of the fast top-k path (token_topk)
 
 // A token's logits from NP K-range partial planes (plane stride `plane`):
 // every load is issued before the first add, and the planes are added in
@@ -49,21 +49,29 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&u)[kMaxKeysPerL
   return tau;
 }
 
+// Inclusive scan of one int over the 64 lanes of a wave with DPP: shifts by
+// 1, 2, 4 and 8 inside each row of 16 lanes, then the last lane of row 0
+// (and of row 2) into rows 1 (and 3), and lane 31 into rows 2 and 3. Lanes
+// with no source add 0. Only VALU operations, no LDS round trip.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Inclusive scans of two per-thread values over the whole workgroup (thread
-// order), one value pair per thread: a shuffle scan inside each wave, then each
+// order), one value pair per thread: a DPP scan inside each wave, then each
 // wave adds the totals of the waves before it. tot holds 2 x (waves) ints of
 // LDS; every thread of the workgroup must call this.
 __device__ __forceinline__ void block_scan2(int32_t& a, int32_t& b, int32_t* tot) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nw = blockDim.x >> 6;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int32_t ua = __shfl_up(a, d, kWave), ub = __shfl_up(b, d, kWave);
-    if (lane >= d) {
-      a += ua;
-      b += ub;
-    }
-  }
+  a = wave_scan_incl(a);
+  b = wave_scan_incl(b);
   if (lane == kWave - 1) {
     tot[w] = a;
     tot[nw + w] = b;
@@ -80,66 +88,62 @@ __device__ __forceinline__ void block_scan2(int32_t& a, int32_t& b, int32_t* tot
 
 // Top-k of one token held by one wave (keys as in kth_largest): leaves the k
 // chosen keys and experts in (logit desc, expert asc) order in sel_key[0..k-1]
-// and sel_e[0..k-1]. cand_key and cand_e are kMaxCand entries of scratch; all
-// four arrays are the wave's own LDS rows.
-__device__ __forceinline__ void token_topk(const uint32_t (&u)[kMaxKeysPerLane], int k, uint32_t* cand_key,
-                                           int32_t* cand_e, uint32_t* sel_key, int32_t* sel_e) {
+// and sel_e[0..k-1]; cand is kMaxCand entries of scratch. All three are the
+// wave's own LDS rows.
+__device__ __forceinline__ void token_topk(const uint32_t (&u)[kMaxKeysPerLane], int k, uint64_t* cand,
+                                           uint32_t* sel_key, int32_t* sel_e) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1ull;
   // Fast path. Let mk be the k-th largest of the 64 lanes' largest keys: at
-  // least k keys are >= mk, so the k-th largest key is >= mk and every
-  // chosen key is among the candidates {keys >= mk}; every other key is
-  // strictly smaller than all chosen ones. The candidates (usually about k)
-  // are gathered in LDS and each one's position in (logit desc, expert asc)
-  // order is counted directly: positions 0..k-1 are the chosen experts, in
-  // order. mk itself needs one ballot per radix pass instead of four. Exact
-  // ties that leave more than kMaxCand candidates take the general path.
+  // least k keys are >= mk, so the k-th largest key is >= mk and every chosen
+  // key is among the candidates {keys >= mk}; every other key is strictly
+  // smaller than all chosen ones. The threshold used is mk with its low 16
+  // bits cleared (<= mk, so the candidates still hold every chosen key; a
+  // 16-pass radix on the lane maxima' top halves finds it). The candidates
+  // (usually about k) are gathered in LDS as key << 32 | ~expert, which orders
+  // them as (logit desc, expert asc) does, and lane j counts the candidates
+  // above its own: that count is its position, and positions 0..k-1 are the
+  // chosen experts, in order. Exact ties that leave more than kMaxCand
+  // candidates take the general path.
   uint32_t mx = u[0];
 #pragma unroll
   for (int i = 1; i < kMaxKeysPerLane; ++i) mx = u[i] > mx ? u[i] : mx;
-  uint32_t mk = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = mk | (1u << b);
-    mk = __popcll(__ballot(mx >= cand)) >= k ? cand : mk;
+  const uint32_t mxh = mx >> 16;
+  uint32_t ph = 0;
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t cand = ph | (1u << b);
+    ph = __popcll(__ballot(mxh >= cand)) >= k ? cand : ph;
   }
+  const uint32_t thr = ph << 16;
   uint64_t cmask[kMaxKeysPerLane];
   int n_cand = 0;
 #pragma unroll
   for (int i = 0; i < kMaxKeysPerLane; ++i) {
-    cmask[i] = __ballot(u[i] >= mk);
+    cmask[i] = __ballot(u[i] >= thr);
     n_cand += __popcll(cmask[i]);
   }
   if (n_cand <= kMaxCand) {   // uniform
     int base = 0;
 #pragma unroll
     for (int i = 0; i < kMaxKeysPerLane; ++i) {
-      if ((cmask[i] >> lane) & 1ull) {
-        const int slot = base + __popcll(cmask[i] & below);
-        cand_key[slot] = u[i];
-        cand_e[slot] = lane + 64 * i;
-      }
+      if ((cmask[i] >> lane) & 1ull)
+        cand[base + __popcll(cmask[i] & below)] = (uint64_t(u[i]) << 32) | uint32_t(~uint32_t(lane + 64 * i));
       base += __popcll(cmask[i]);
     }
     __builtin_amdgcn_wave_barrier();
     if (lane < n_cand) {
-      const uint32_t my_key = cand_key[lane];
-      const int my_e = cand_e[lane];
+      const uint64_t mine = cand[lane];
       int pos = 0;
       for (int q0 = 0; q0 < n_cand; q0 += 8) {
-        uint32_t kq[8];
-        int eq[8];
+        uint64_t cq[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          kq[q] = cand_key[min(q0 + q, n_cand - 1)];
-          eq[q] = cand_e[min(q0 + q, n_cand - 1)];
-        }
+        for (int q = 0; q < 8; ++q) cq[q] = cand[min(q0 + q, n_cand - 1)];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          pos += int(q0 + q < n_cand) & (int(kq[q] > my_key) | (int(kq[q] == my_key) & int(eq[q] < my_e)));
+        for (int q = 0; q < 8; ++q) pos += int(q0 + q < n_cand) & int(cq[q] > mine);
       }
       if (pos < k) {
-        sel_key[pos] = my_key;
-        sel_e[pos] = my_e;
+        sel_key[pos] = uint32_t(mine >> 32);
+        sel_e[pos] = int(~uint32_t(mine));
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -221,6 +225,78 @@ __device__ __forceinline__ void token_softmax(const uint32_t* sel_key, const int
   wgt = ex / sum;
 }
 
+// The tables of a single routing block of at most 64 pairs (the few-token
+// case), built by one wave: the same results as the general path of
+// topk_block below (stable ranks, offsets, block map, scatter, descriptors),
+// with lane p holding pair p and lane l experts l, l + 64, l + 128, l + 192,
+// so that no step needs the rest of the workgroup. hist: E zeros in LDS.
+__device__ __forceinline__ void small_tables(const RouteArgs& a, const int32_t* ids_s, int32_t* hist, int np) {
+  __shared__ int32_t off_w[kMaxExperts];
+  __shared__ int32_t sorted_w[kWave];
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int E = a.E, k = a.k, bm = a.block_rows;
+  const bool live = lane < np;
+  const int e = live ? ids_s[lane] : kMaxExperts;   // past the end: a value no expert has
+  uint64_t same = ~0ull;
+#pragma unroll
+  for (int bit = 0; bit < 9; ++bit) {
+    const uint64_t bb = __ballot((e >> bit) & 1);
+    same &= ((e >> bit) & 1) ? bb : ~bb;
+  }
+  const int rank = __popcll(same & below);
+  if (live && rank == 0) hist[e] = __popcll(same);
+  __builtin_amdgcn_wave_barrier();
+  int c[kMaxKeysPerLane], o[kMaxKeysPerLane], ntl[kMaxKeysPerLane], tf[kMaxKeysPerLane];
+  int base = 0, tbase = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) {
+    const int ee = lane + 64 * i;
+    c[i] = ee < E ? hist[ee] : 0;
+    ntl[i] = ceil_div(c[i], bm);
+    const int sc = wave_scan_incl(c[i]), st = wave_scan_incl(ntl[i]);
+    o[i] = base + sc - c[i];
+    tf[i] = tbase + st - ntl[i];
+    base += __builtin_amdgcn_readlane(sc, kWave - 1);
+    tbase += __builtin_amdgcn_readlane(st, kWave - 1);
+    if (ee < E) {
+      a.counts[ee] = c[i];
+      a.offsets[ee] = o[i];
+      off_w[ee] = o[i];
+      for (int j = 0; j < ntl[i]; ++j) {
+        a.tile_map[2 * (tf[i] + j)] = ee;
+        a.tile_map[2 * (tf[i] + j) + 1] = o[i] + j * bm;
+      }
+    }
+  }
+  if (lane == 0) {
+    a.offsets[E] = base;
+    *a.num_tiles = tbase;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (live) {
+    const int pos = off_w[e] + rank;
+    a.sorted_rows[pos] = lane;
+    a.row_of_pair[lane] = pos;
+    sorted_w[pos] = lane;
+  }
+  if (!a.tile_desc) return;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) {
+    const int ee = lane + 64 * i;
+    if (ee < E) {
+      for (int j = 0; j < ntl[i]; ++j) {
+        const int r0 = o[i] + j * bm;
+        const int n = min(bm, c[i] - j * bm);
+        uint32_t tok = 0;
+        for (int q = 0; q < n && q < 8; ++q) tok |= uint32_t(sorted_w[r0 + q] / k) << (4 * q);
+        a.tile_desc[tf[i] + j] = u32x4{uint32_t(ee), uint32_t(r0), uint32_t(n), tok};
+      }
+    }
+  }
+}
+
 // Top-k, softmax, histogram and ranks of routing block blk (and, for a single
 // block, the tables), run by one 1024-thread workgroup.
 __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
@@ -229,8 +305,7 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
   __shared__ int32_t ids_s[kRouteTokens * kMaxTopk];
   __shared__ int32_t rank_s[kRouteTokens * kMaxTopk];
   __shared__ int32_t hist[kMaxExperts];
-  __shared__ uint32_t cand_key[kRouteTokens][kMaxCand];
-  __shared__ int32_t cand_e[kRouteTokens][kMaxCand];
+  __shared__ uint64_t cand[kRouteTokens][kMaxCand];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -283,7 +358,7 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
       }
       u[i] = key;
     }
-    token_topk(u, k, cand_key[m], cand_e[m], sel_key[m], sel_e[m]);
+    token_topk(u, k, cand[m], sel_key[m], sel_e[m]);
     int my_e;
     float wgt;
     token_softmax(sel_key[m], sel_e[m], k, my_e, wgt);
@@ -296,11 +371,16 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
   }
   __syncthreads();
 
+  const int npairs_all = nt * k;
+  if (a.finish && npairs_all <= kWave) {   // uniform
+    if (wave == 0) small_tables(a, ids_s, hist, npairs_all);
+    return;
+  }
+
   // Histogram of the block's pairs and each pair's rank among the earlier pairs
   // of the same expert (pair order f = t*k + j), which makes the scatter
   // stable. Wave 0 walks the pairs 64 at a time; lanes with the same expert
   // find each other through one ballot per expert-index bit.
-  const int npairs_all = nt * k;
   if (wave == 0) {
     const int npairs = npairs_all;
     for (int c0 = 0; c0 < npairs; c0 += kWave) {
