@@ -40,12 +40,13 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 RAMP_SECONDS = 0.3
 
 
-def ramp(torch, fn, seconds=RAMP_SECONDS):
+def ramp(torch, fn, seconds=None):
     """Call fn (a layer call or a graph replay) until `seconds` of wall time
     have passed, synchronising every few calls. The GPU raises its clocks under
     sustained load and takes tens of milliseconds to settle (the first ~50
     T=4096 layer calls ran 5-15% slower); the timed regions measure the
     sustained state. Returns the number of calls."""
+    seconds = RAMP_SECONDS if seconds is None else seconds
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -369,6 +370,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--ramp-seconds", type=float, default=RAMP_SECONDS,
+                   help="untimed calls before each timed region, in seconds of wall time (sustained clocks)")
     p.add_argument("--config", default="prefill4096")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -415,6 +418,8 @@ def cpu_baseline(inp, small):
 
 def main():
     args = parse()
+    global RAMP_SECONDS
+    RAMP_SECONDS = args.ramp_seconds
     if args.write_traffic_summary:
         fd, wd, cf, cw = args.write_traffic_summary
         write_traffic_summary(fd, wd, 512, cf, cw)
