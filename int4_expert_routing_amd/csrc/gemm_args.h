@@ -35,6 +35,8 @@ struct GemmArgs {
   int bm;                   // rows per routed tile (32, 64 or kBlockRows)
   int n_shared_tiles;       // the first n_shared_tiles tiles cover the shared rows, kBlockRows each
   int routed_tiles;         // 1: the routed tiles of the block map follow them; 0: shared tiles only
+  int merge_tail;           // 1 (bm == kBlockRows, a complete block map in expert order): an expert's last
+                            // tile of at most 32 rows is computed by the full tile before it
   int shared_rows;
   int N, K, NT;             // NT = column tiles per row tile
   void* out;                // f32 [rows][N], or bf16 [rows][N]

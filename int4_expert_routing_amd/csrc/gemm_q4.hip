@@ -79,11 +79,19 @@ constexpr int kSbSlotBytes = 2048;       // scale/bias words of one group pair: 
 //     (a column's codes of two groups are 64 contiguous bytes). Such a tile
 //     does too little arithmetic per group to cover a memory round trip in two
 //     steps; its activation tile is a quarter of a full one, so the same LDS
-//     holds twice the groups in flight.
-template <bool SR>
+//     holds twice the groups in flight;
+//   merged tiles (129..160 rows: an expert's last full tile together with a
+//     remainder of at most 32 rows, in the layer's tile lists): 2 slots of 160
+//     activation rows then the codes; group g issued at step g - 1. The
+//     remainder rows then share the full tile's code unpacking instead of
+//     unpacking the expert's weights again for a few rows (a tile of 1..32
+//     rows costs ~35-45% of a full one).
+enum RingMode { kRingFull = 0, kRingSmall = 1, kRingMerged = 2 };
+template <int RM>
 struct Ring {
-  static constexpr int DIST = SR ? 4 : 2;
-  static constexpr int AROWS = SR ? 32 : 128;             // activation rows per slot
+  static constexpr bool SR = RM == kRingSmall;
+  static constexpr int DIST = SR ? 4 : RM == kRingMerged ? 1 : 2;
+  static constexpr int AROWS = SR ? 32 : RM == kRingMerged ? 160 : 128;   // activation rows per slot
   static constexpr int ALOADS = AROWS / 32;               // activation loads per wave and group (8 rows each)
   static constexpr int A_RING = DIST + 1;
   static constexpr int C_RING = SR ? DIST + 2 : DIST + 1;
@@ -92,7 +100,10 @@ struct Ring {
   static constexpr int C_BASE = SR ? A_RING * A_SLOT : AROWS * 128;
   static constexpr int C_SLOT = SR ? CODES : A_SLOT;
   static constexpr int XP = SR ? C_BASE + C_RING * C_SLOT : A_RING * A_SLOT;
-  static constexpr int SB = XP + kXpSlotBytes;
+  // side-table slot of one pair: 32 B per row; merged tiles load rows
+  // 128..159 with a second load per wave (every wave writes the same bytes)
+  static constexpr int XLOADS = AROWS > 128 ? 2 : 1;
+  static constexpr int SB = XP + XLOADS * kXpSlotBytes;
   static constexpr int SBS = SR ? 3 : 2;               // pair p's words are read at step 2p, loaded at 2p - DIST
   static constexpr int END = SB + SBS * kSbSlotBytes;
   // vector-memory instructions a wave issues for one group (the waits count
@@ -101,7 +112,9 @@ struct Ring {
   static constexpr int LOADS_EVEN = ALOADS + 2 + 2;      // activations, codes, scale|bias words of both blocks
   static constexpr int LOADS_ODD = ALOADS + 2;           // activations, codes
 };
-constexpr int kLdsLoop = Ring<false>::END > Ring<true>::END ? Ring<false>::END : Ring<true>::END;
+constexpr int kLdsLoopFS = Ring<kRingFull>::END > Ring<kRingSmall>::END ? Ring<kRingFull>::END : Ring<kRingSmall>::END;
+constexpr int kLdsLoop = kLdsLoopFS > Ring<kRingMerged>::END ? kLdsLoopFS : Ring<kRingMerged>::END;
+constexpr int kMaxRows = 160;   // rows of a merged tile
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
 // s_waitcnt immediates (gfx9: vmcnt[3:0] and [15:14], expcnt[6:4],
 // lgkmcnt[11:8]); only vmcnt waits.
@@ -136,11 +149,12 @@ __device__ __forceinline__ void global_to_lds4(const uint32_t* src, uint8_t* dst
 }
 
 // LDS of one workgroup: the two rings during the K loop; afterwards the h
-// tile (SwiGLU: 128 x 128 bf16) or each wave's 128 x 32 fp32 staging block
-// (STORE_F32, row stride 36 floats).
+// tile (SwiGLU: up to 160 x 128 bf16) or each wave's 128 x 32 fp32 staging
+// block (STORE_F32, row stride 36 floats; a merged tile's last 32 rows take a
+// second round).
 constexpr int kF32StageStride = 36;
 size_t gemm_lds_bytes(int /*K*/) {
-  const size_t swiglu = size_t(kBlockRows) * 128 * 2;
+  const size_t swiglu = size_t(kMaxRows) * 128 * 2;
   const size_t f32 = size_t(kGemmWaves) * kBlockRows * kF32StageStride * 4;
   size_t m = size_t(kLdsLoop);
   m = m > swiglu ? m : swiglu;
@@ -151,9 +165,10 @@ size_t gemm_lds_bytes(int /*K*/) {
 // scale/bias pair addresses of the lane's two columns.
 struct Stream {
   __amdgpu_buffer_rsrc_t ra, rb0, rb1, rxp;
-  uint32_t va[4];    // activation chunk offsets (4 instructions; small tiles use va[0] only)
+  uint32_t va[5];    // activation chunk offsets (one per load; small tiles use va[0] only)
   uint32_t vb;       // code offset of the lane (same in both column blocks)
   uint32_t vxp;      // side-table offset of (row, half)
+  uint32_t vxp2;     // merged tiles: the same for rows 128..159
   int gstride;       // bytes between a column's codes of consecutive groups (32, or N * 32 when packed)
   int sbstride;      // u32 words between a column's scale/bias pairs of consecutive pairs (1, or N when packed)
   const uint32_t* sbp[2];  // lanes 0-31: scale pairs, lanes 32-63: bias pairs of the lane's column (blocks 0, 1)
@@ -169,9 +184,9 @@ struct SBPair {
 // (g/2) % SBS (per wave and column block: 32 scale words, then 32 bias
 // words). Every load writes LDS directly, so the compiler tracks no register
 // results of them and only the explicit waits order them.
-template <bool SR>
+template <int RM>
 __device__ __forceinline__ void issue_codes(const Stream& st, uint8_t* ring, int g, int wave) {
-  using R = Ring<SR>;
+  using R = Ring<RM>;
   uint8_t* cs = ring + R::C_BASE + (g % R::C_RING) * R::C_SLOT;
   buffer_to_lds16(st.rb0, cs + (wave * 2) * 1024, st.vb, g * st.gstride);
   buffer_to_lds16(st.rb1, cs + (wave * 2 + 1) * 1024, st.vb, g * st.gstride);
@@ -182,29 +197,31 @@ __device__ __forceinline__ void issue_codes(const Stream& st, uint8_t* ring, int
 //     pair g/2;
 //   small ring, even g: activations and codes of g, the scale/bias words of
 //     pair g/2, then the codes of g+1; odd g: activations of g.
-template <int ODD, bool SR>
+template <int ODD, int RM>
 __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave) {
-  using R = Ring<SR>;
+  using R = Ring<RM>;
+  constexpr bool SR = R::SR;
   uint8_t* slot = ring + (g % R::A_RING) * R::A_SLOT;
 #pragma unroll
   for (int i = 0; i < R::ALOADS; ++i)
     buffer_to_lds16(st.ra, slot + (wave * R::ALOADS + i) * 1024, st.va[i], g * (kGroup * 2));
-  if (!SR || !ODD) issue_codes<SR>(st, ring, g, wave);
+  if (!SR || !ODD) issue_codes<RM>(st, ring, g, wave);
   if (!ODD) {
     const int p = g >> 1;
     uint8_t* sbs = ring + R::SB + (p % R::SBS) * kSbSlotBytes + wave * 512;
     global_to_lds4(st.sbp[0] + p * st.sbstride, sbs);
     global_to_lds4(st.sbp[1] + p * st.sbstride, sbs + 256);
-    if (SR) issue_codes<SR>(st, ring, g + 1, wave);   // g + 1 < G: G is even
+    if (SR) issue_codes<RM>(st, ring, g + 1, wave);   // g + 1 < G: G is even
   }
 }
 
 // Side-table entries of group pair p (groups 2p, 2p+1; every wave loads 32
 // rows) into the side-table slot, issued at step 2p once every wave is past
 // step 2p-1, the last reader of pair p-1.
-template <bool SR>
+template <int RM>
 __device__ __forceinline__ void issue_xp(const Stream& st, uint8_t* ring, int p, int wave) {
-  buffer_to_lds16(st.rxp, ring + Ring<SR>::XP + wave * 1024, st.vxp, p * 32);
+  buffer_to_lds16(st.rxp, ring + Ring<RM>::XP + wave * 1024, st.vxp, p * 32);
+  if constexpr (Ring<RM>::XLOADS > 1) buffer_to_lds16(st.rxp, ring + Ring<RM>::XP + kXpSlotBytes, st.vxp2, p * 32);
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding.
@@ -250,11 +267,16 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 //     odd g: the side table of step g-3 (g >= 3), groups g+1, g+2 (7 + 1)
 //       while g <= G-3, the side table of step g-1, and groups g+3, g+4 (7,
 //       the activations of g+4 following at step g) while g <= G-5.
-template <int ODD, bool SR>
+template <int ODD, int RM>
 __device__ __forceinline__ void wait_group(int g, int G) {
-  using R = Ring<SR>;
+  using R = Ring<RM>;
+  constexpr bool SR = R::SR;
   constexpr int E = R::LOADS_EVEN, O = R::LOADS_ODD;
-  if constexpr (!SR) {
+  if constexpr (RM == kRingMerged) {
+    // one group ahead: every load outstanding at the top of step g is group
+    // g's or the side table issued before it
+    wait_vm<0>();
+  } else if constexpr (!SR) {
     if (g + 1 < G) {
       if (ODD)
         wait_vm<E + 1>();
@@ -297,19 +319,20 @@ __device__ __forceinline__ void wait_group(int g, int G) {
   }
 }
 
-template <int NRB, int P4, bool SR>
+template <int NRB, int P4, int RM>
 __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g, int G, int wave, int lane,
-                                          SBPair& sb, float (&U)[2], f32x16 (&acc)[4][2]) {
-  using R = Ring<SR>;
+                                          SBPair& sb, float (&U)[2], f32x16 (&acc)[5][2]) {
+  using R = Ring<RM>;
+  constexpr bool SR = R::SR;
   constexpr int ODD = P4 & 1;
   const int l32 = lane & 31, half = lane >> 5;
   // this wave's loads of group g have landed; the barrier makes it so for
   // every wave, and orders every wave's reads of the slot of group g-1
   // (previous step) before its refill
-  wait_group<ODD, SR>(g, G);
+  wait_group<ODD, RM>(g, G);
   __builtin_amdgcn_s_barrier();
-  if (!ODD) issue_xp<SR>(st, ring, g >> 1, wave);
-  if (g + R::DIST < G) issue_group<ODD, SR>(st, ring, g + R::DIST, wave);
+  if (!ODD) issue_xp<RM>(st, ring, g >> 1, wave);
+  if (g + R::DIST < G) issue_group<(ODD + R::DIST) & 1, RM>(st, ring, g + R::DIST, wave);
   const uint8_t* slot = ring + (g % R::A_RING) * R::A_SLOT;
   const uint8_t* cslot = ring + R::C_BASE + (g % R::C_RING) * R::C_SLOT;
   if (!ODD) {
@@ -324,7 +347,7 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
 
   const u32x4 w0 = *reinterpret_cast<const u32x4*>(cslot + (wave * 2) * 1024 + lane * 16);
   const u32x4 w1 = *reinterpret_cast<const u32x4*>(cslot + (wave * 2 + 1) * 1024 + lane * 16);
-  bf16x8 fa[2][4];
+  bf16x8 fa[2][NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
     fa[0][rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(rb * 32 + l32, 4 * half)));
@@ -366,7 +389,10 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
     // g-1+DIST's loads, and group g+DIST's followed it: every wave waits for
     // its part. The full ring's last step already waited for every load at
     // its top; the small ring's last steps leave side tables outstanding there.
-    if constexpr (!SR) {
+    if constexpr (RM == kRingMerged) {
+      // issued at step g-1 before group g's loads, which this step's top
+      // wait and barrier covered
+    } else if constexpr (!SR) {
       if (g + 1 < G) {
         wait_vm<R::LOADS_EVEN + R::LOADS_ODD>();
         __builtin_amdgcn_s_barrier();
@@ -404,25 +430,27 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
   }
 }
 
-// G is even (K is a multiple of 128). SR: the small-tile ring (NRB == 1).
-template <int NRB, bool SR>
+// G is even (K is a multiple of 128). RM: the ring geometry (small tiles:
+// NRB == 1; merged tiles: NRB == 5).
+template <int NRB, int RM>
 __device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, int G, int wave, int lane,
-                                          SBPair& sb, f32x16 (&acc)[4][2]) {
+                                          SBPair& sb, f32x16 (&acc)[5][2]) {
+  using R = Ring<RM>;
   // groups 0 .. DIST-1 (those that exist) before the first step
-  issue_group<0, SR>(st, ring, 0, wave);
-  issue_group<1, SR>(st, ring, 1, wave);
-  if constexpr (SR) {
-    if (2 < G) issue_group<0, SR>(st, ring, 2, wave);
-    if (3 < G) issue_group<1, SR>(st, ring, 3, wave);
+  issue_group<0, RM>(st, ring, 0, wave);
+  if constexpr (R::DIST >= 2) issue_group<1, RM>(st, ring, 1, wave);
+  if constexpr (R::SR) {
+    if (2 < G) issue_group<0, RM>(st, ring, 2, wave);
+    if (3 < G) issue_group<1, RM>(st, ring, 3, wave);
   }
   float U[2] = {1.0f, 1.0f};   // any normal value: acc is zero until the first nonzero scale
   // unrolled by 4 so the group parity and the pair parity are constants
   for (int g = 0; g < G; g += 4) {
-    loop_step<NRB, 0, SR>(st, ring, g, G, wave, lane, sb, U, acc);
-    loop_step<NRB, 1, SR>(st, ring, g + 1, G, wave, lane, sb, U, acc);
+    loop_step<NRB, 0, RM>(st, ring, g, G, wave, lane, sb, U, acc);
+    loop_step<NRB, 1, RM>(st, ring, g + 1, G, wave, lane, sb, U, acc);
     if (g + 2 < G) {
-      loop_step<NRB, 2, SR>(st, ring, g + 2, G, wave, lane, sb, U, acc);
-      loop_step<NRB, 3, SR>(st, ring, g + 3, G, wave, lane, sb, U, acc);
+      loop_step<NRB, 2, RM>(st, ring, g + 2, G, wave, lane, sb, U, acc);
+      loop_step<NRB, 3, RM>(st, ring, g + 3, G, wave, lane, sb, U, acc);
     }
   }
 #pragma unroll
@@ -511,9 +539,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
     // A = activation loads per wave (4, or 1 in the small-tile ring): row
     // m = (A w + i)*8 + lane/8 and chunk slot lane%8, which holds logical
     // chunk (lane%8) ^ swz(m)
-    const int aloads = nrb == 1 ? Ring<true>::ALOADS : Ring<false>::ALOADS;
+    const int aloads = nrb == 1 ? Ring<kRingSmall>::ALOADS : nrb == 5 ? Ring<kRingMerged>::ALOADS
+                                                                       : Ring<kRingFull>::ALOADS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 5; ++i) {
       const int m = (wave * aloads + i) * 8 + (lane >> 3);
       const int cidx = (lane & 7) ^ swz(m);
       const int r = ti.r0 + min(m, nrows - 1);     // padding rows re-read the last real row
@@ -522,6 +551,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
     // side-table load of wave w: row w*32 + lane/2, 16-byte half lane%2
     const int mx = wave * 32 + (lane >> 1);
     st.vxp = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KPx * 2) + uint32_t((lane & 1) * 16);
+    st.vxp2 = uint32_t(src_row(a, ti.r0 + min(128 + (lane >> 1), nrows - 1))) * uint32_t(KPx * 2) +
+              uint32_t((lane & 1) * 16);
   }
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -534,14 +565,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
 
   SBPair sb;
 
-  f32x16 acc[4][2];
+  f32x16 acc[5][2];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
+  for (int rb = 0; rb < 5; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
   switch (nrb) {
-    case 1: main_loop<1, true>(st, ring, G, wave, lane, sb, acc); break;
-    case 2: main_loop<2, false>(st, ring, G, wave, lane, sb, acc); break;
-    case 3: main_loop<3, false>(st, ring, G, wave, lane, sb, acc); break;
-    default: main_loop<4, false>(st, ring, G, wave, lane, sb, acc); break;
+    case 1: main_loop<1, kRingSmall>(st, ring, G, wave, lane, sb, acc); break;
+    case 2: main_loop<2, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
+    case 3: main_loop<3, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
+    case 4: main_loop<4, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
+    default: main_loop<5, kRingMerged>(st, ring, G, wave, lane, sb, acc); break;   // merged tiles only
   }
   __syncthreads();   // every wave is done with the rings
 
@@ -570,12 +602,31 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         }
       }
       __builtin_amdgcn_wave_barrier();
+      if (nrows > kBlockRows) {   // uniform: a merged tile's rows 128..159
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+          stg[m * kF32StageStride + l32] = acc[4][cb][r];
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (live[cb]) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = i * 8 + (lane >> 3), c4 = (lane & 7) * 4;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(stg + m * kF32StageStride + c4);
+            if (kBlockRows + m < nrows)
+              *reinterpret_cast<f32x4*>(out + size_t(ti.r0 + kBlockRows + m) * a.N + cbase[cb] + c4) = v;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   } else {
-    uint16_t* hs = reinterpret_cast<uint16_t*>(ring);   // [128][128] bf16
+    uint16_t* hs = reinterpret_cast<uint16_t*>(ring);   // [160][128] bf16
     const int col = wave * 32 + l32;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 5; ++rb) {
+      if (rb == 4 && nrows <= kBlockRows) break;   // uniform
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -583,13 +634,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[rb][1][r];
         hs[m * 128 + col] = uint16_t(f32_to_bf16_rne(hv));
       }
+    }
     __syncthreads();
     // unit u: row u/4, quarter u%4 = 32 columns; quarters (0,1) and (2,3) are
     // the two 64-wide groups of h this workgroup produced (units u and u^1 are
     // in adjacent lanes)
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < 3; ++it) {
+      if (it == 2 && nrows <= kBlockRows) break;   // uniform: rows 128..159 of a merged tile
       const int u = tid + it * kGemmThreads;
       const int srow = u >> 2, sq = u & 3;
       const int row = ti.r0 + srow;

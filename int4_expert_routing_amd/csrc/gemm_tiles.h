@@ -28,7 +28,15 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int tile, TileInfo&
   if (!a.routed_tiles || i >= *a.num_tiles) return false;
   ti.e = a.tile_map[2 * i];
   ti.r0 = a.tile_map[2 * i + 1];
-  ti.r1 = min(ti.r0 + a.bm, a.offsets[ti.e + 1]);
+  const int end = a.offsets[ti.e + 1];
+  ti.r1 = min(ti.r0 + a.bm, end);
+  if (a.merge_tail) {
+    // an expert's rows beyond its full tiles, at most 32 of them, join the
+    // last full tile (up to 160 rows), whose tile then covers them, and
+    // their own tile has nothing to do
+    if (ti.r1 == end && end - ti.r0 <= 32 && ti.r0 - a.offsets[ti.e] >= kBlockRows) return false;
+    if (end - ti.r0 > kBlockRows && end - ti.r0 <= kBlockRows + 32) ti.r1 = end;
+  }
   return true;
 }
 

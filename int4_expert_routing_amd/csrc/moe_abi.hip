@@ -378,6 +378,7 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   g1.bm = bm;
   g1.n_shared_tiles = decode ? 1 : n_sh;   // decode: the shared expert's T rows form one tile
   g1.routed_tiles = 1;
+  g1.merge_tail = bm == kBlockRows ? 1 : 0;   // the routing's block map is complete and in expert order
   g1.shared_rows = T;
   g1.N = I;
   g1.K = H;
