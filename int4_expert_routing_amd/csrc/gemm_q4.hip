@@ -42,19 +42,19 @@
 //   MFMA v_mfma_f32_32x32x16_bf16: per 64-wide group a wave issues one chain
 //   of 4 MFMAs per (row block, column block); one group's weight codes are
 //   unpacked once and reused by every row block.
-// Streaming: per group, the activation tile (128 rows x 64 bf16, 16-byte chunks
-//   XOR-swizzled by row) and the 256 columns' weight codes land in a 3-slot
-//   LDS ring through buffer loads that write LDS directly (no registers, one
-//   scalar offset per group), issued two groups ahead (tiles of at most 32
-//   rows: 32-row activation tiles in a 5-slot ring, four groups ahead); the
-//   scale and bias words of a group pair land in a 2-slot (3-slot) ring with
-//   the even group's loads
-//   (global loads that write LDS), and the rows' side-table entries of the
-//   current pair in a single slot, issued at its even step. No load returns
-//   to registers: a register-returning load would make the compiler wait for
-//   it with a count that ignores the LDS-writing loads issued after it, i.e.
-//   stall on the loads just issued. One s_waitcnt + s_barrier per group, one
-//   more per pair before the side table is read.
+// Streaming: per group, the activation tile (128 or 160 rows x 64 bf16,
+//   16-byte chunks XOR-swizzled by row) and the 256 columns' weight codes land
+//   in a 2-slot LDS ring through buffer loads that write LDS directly (no
+//   registers, one scalar offset per group), issued one group ahead (tiles of
+//   at most 32 rows: 32-row activation tiles in a 5-slot ring, four groups
+//   ahead); the scale and bias words of a group pair land in a 2-slot (3-slot)
+//   ring with the even group's loads (global loads that write LDS), and the
+//   rows' side-table entries of the current pair in a single slot, issued at
+//   its even step. No load returns to registers: a register-returning load
+//   would make the compiler wait for it with a count that ignores the
+//   LDS-writing loads issued after it, i.e. stall on the loads just issued.
+//   One s_waitcnt + s_barrier per group (small tiles: one more per pair
+//   before the side table is read).
 // Work mapping: each XCD takes a contiguous chunk of the tile list and runs
 // all column slices of its tiles (see the kernel), so activation rows and
 // expert weights are fetched into one XCD's L2 rather than into all eight.
@@ -70,8 +70,10 @@ constexpr int kSbSlotBytes = 2048;       // scale/bias words of one group pair: 
 // LDS ring geometry. Group g's activation tile lives in A slot g % A_RING and
 // its codes in code slot g % C_RING; groups are loaded DIST steps ahead. The
 // scale/bias words of pair p live in slot p % SBS.
-//   full tiles (33..128 rows): 3 slots, each 128 activation rows then the
-//     codes; group g issued at step g - 2 into the slot group g - 1 used;
+//   full tiles (33..128 rows): 2 slots, each 128 activation rows then the
+//     codes; group g issued at step g - 1 into the slot group g - 2 used (one
+//     step of a full tile covers the round trip: three slots, two groups
+//     ahead, measured 1% slower at T=4096 and the same at T=512);
 //   small tiles (at most 32 rows): 5 slots of 32 activation rows and 6 code
 //     slots; group g's activations issued at step g - 4, and both groups of a
 //     pair's codes at the pair's even step 2p - 4, back to back, so the second
@@ -81,8 +83,8 @@ constexpr int kSbSlotBytes = 2048;       // scale/bias words of one group pair: 
 //     steps; its activation tile is a quarter of a full one, so the same LDS
 //     holds twice the groups in flight;
 //   merged tiles (129..160 rows: an expert's last full tile together with a
-//     remainder of at most 32 rows, in the layer's tile lists): 2 slots of 160
-//     activation rows then the codes; group g issued at step g - 1. The
+//     remainder of at most 32 rows, in the layer's tile lists): the same with
+//     160 activation rows. The
 //     remainder rows then share the full tile's code unpacking instead of
 //     unpacking the expert's weights again for a few rows (a tile of 1..32
 //     rows costs ~35-45% of a full one).
@@ -90,7 +92,7 @@ enum RingMode { kRingFull = 0, kRingSmall = 1, kRingMerged = 2 };
 template <int RM>
 struct Ring {
   static constexpr bool SR = RM == kRingSmall;
-  static constexpr int DIST = SR ? 4 : RM == kRingMerged ? 1 : 2;
+  static constexpr int DIST = SR ? 4 : 1;
   static constexpr int AROWS = SR ? 32 : RM == kRingMerged ? 160 : 128;   // activation rows per slot
   static constexpr int ALOADS = AROWS / 32;               // activation loads per wave and group (8 rows each)
   static constexpr int A_RING = DIST + 1;
@@ -106,11 +108,6 @@ struct Ring {
   static constexpr int SB = XP + XLOADS * kXpSlotBytes;
   static constexpr int SBS = SR ? 3 : 2;               // pair p's words are read at step 2p, loaded at 2p - DIST
   static constexpr int END = SB + SBS * kSbSlotBytes;
-  // vector-memory instructions a wave issues for one group (the waits count
-  // them); an even step also issues the pair's side-table load ahead of its
-  // group's
-  static constexpr int LOADS_EVEN = ALOADS + 2 + 2;      // activations, codes, scale|bias words of both blocks
-  static constexpr int LOADS_ODD = ALOADS + 2;           // activations, codes
 };
 constexpr int kLdsLoopFS = Ring<kRingFull>::END > Ring<kRingSmall>::END ? Ring<kRingFull>::END : Ring<kRingSmall>::END;
 constexpr int kLdsLoop = kLdsLoopFS > Ring<kRingMerged>::END ? kLdsLoopFS : Ring<kRingMerged>::END;
@@ -258,8 +255,8 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 // step j the side table of pair j/2 (even j) followed by group j + DIST (see
 // issue_group). At most the loads issued after the last needed one may still
 // be outstanding:
-//   full ring: even g: group g+1 (4+2); odd g: the side table of step g-1 and
-//     group g+1 (4+2+2, + 1); none at the last step;
+//   full and merged rings (one group ahead): none (at step g-1 the side table
+//     was issued before group g);
 //   small ring (an even step issues 7 loads after its side table, an odd step
 //     1; G is even):
 //     even g: the codes of g+1 and the activations of g+1 (3), the side table
@@ -271,20 +268,10 @@ template <int ODD, int RM>
 __device__ __forceinline__ void wait_group(int g, int G) {
   using R = Ring<RM>;
   constexpr bool SR = R::SR;
-  constexpr int E = R::LOADS_EVEN, O = R::LOADS_ODD;
-  if constexpr (RM == kRingMerged) {
+  if constexpr (!SR) {
     // one group ahead: every load outstanding at the top of step g is group
     // g's or the side table issued before it
     wait_vm<0>();
-  } else if constexpr (!SR) {
-    if (g + 1 < G) {
-      if (ODD)
-        wait_vm<E + 1>();
-      else
-        wait_vm<O>();
-    } else {
-      wait_vm<0>();
-    }
   } else if constexpr (ODD) {
     const bool xp3 = g >= 3;
     if (g <= G - 5) {
@@ -386,18 +373,10 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
   }
   if (ODD) {
     // the side table of this pair was issued at step g-1 ahead of group
-    // g-1+DIST's loads, and group g+DIST's followed it: every wave waits for
-    // its part. The full ring's last step already waited for every load at
-    // its top; the small ring's last steps leave side tables outstanding there.
-    if constexpr (RM == kRingMerged) {
-      // issued at step g-1 before group g's loads, which this step's top
-      // wait and barrier covered
-    } else if constexpr (!SR) {
-      if (g + 1 < G) {
-        wait_vm<R::LOADS_EVEN + R::LOADS_ODD>();
-        __builtin_amdgcn_s_barrier();
-      }
-    } else {
+    // g-1+DIST's loads: every wave waits for its part. One group ahead, that
+    // is group g, which this step's top wait and barrier already covered; the
+    // small ring has later loads outstanding.
+    if constexpr (SR) {
       // issued after the side table: step g-1's group (7 loads) and step g's
       // activations (1), while g + 4 < G
       if (g + R::DIST < G)
