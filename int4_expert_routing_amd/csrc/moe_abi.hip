@@ -4,6 +4,7 @@
 #include <mutex>
 
 #include "moe_internal.h"
+#include "prep_rows.h"
 
 // Workspace of moe_layer_forward_noalloc: one array per GPU, held until the
 // process ends. Host code never uses this name as an address (in host code it
@@ -343,10 +344,16 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   const bool decode = T <= kDecodeMaxRows && decode_supported(I, H) &&
                       decode_down_combine_supported(H, I);
 
-  // 1. activations: permuted chunk order + group sums
+  // 1. activations: permuted chunk order + group sums. With several routing
+  // blocks (and no side stream, which forks after this step) they run as
+  // extra workgroups of the routing's scan launch, which leaves most of the
+  // GPU idle otherwise; else as a launch of their own here.
   uint16_t* x_perm = at<uint16_t>(ws, L.x_perm);
   uint16_t* x_part = at<uint16_t>(ws, L.x_part);
-  if ((!decode && launch_prep_rows(x, T, H, x_perm, x_part, s) != hipSuccess) || !mark(1)) return MOE_ERR_HIP;
+  const PrepArgs prep{x, T, H, x_perm, x_part};
+  const bool fold_prep = !decode && !s2 && nblk > 1;
+  if ((!decode && !fold_prep && launch_prep_rows(x, T, H, x_perm, x_part, s) != hipSuccess) || !mark(1))
+    return MOE_ERR_HIP;
 
   // gate/up arguments: routed tiles + shared-expert tiles
   const int routed_rows = T * k;
@@ -460,7 +467,10 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
   ra.tile_desc = decode ? tile_desc : nullptr;
   ra.done = at<int32_t>(ws, L.done);
   ra.slots = at<uint64_t>(ws, L.done + 256);
-  if (launch_route(ra, sa, ca, true, s) != hipSuccess || !mark(2)) return MOE_ERR_HIP;
+  bool prep_done = false;
+  if (launch_route(ra, sa, ca, true, s, fold_prep ? &prep : nullptr, &prep_done) != hipSuccess) return MOE_ERR_HIP;
+  if (fold_prep && !prep_done && launch_prep_rows(x, T, H, x_perm, x_part, s) != hipSuccess) return MOE_ERR_HIP;
+  if (!mark(2)) return MOE_ERR_HIP;
 
   // 5. gate/up grouped GEMM with SwiGLU
   const int n_tiles1 = (decode ? g1.n_shared_tiles : (s2 ? 0 : n_sh)) + max_routed;

@@ -67,8 +67,12 @@ struct ScatterArgs {
 constexpr int kRouterTileMinT = 1024;
 int router_splits(int T, int H, int E);
 
+// prep (optional): the grouped GEMM's activation preparation, run as extra
+// workgroups of the scan launch when there is one (*prep_done says whether it
+// ran; otherwise the caller launches it itself).
+struct PrepArgs;
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,
-                        hipStream_t stream);
+                        hipStream_t stream, const PrepArgs* prep = nullptr, bool* prep_done = nullptr);
 
 // Decode-shaped kernels: row tiles of at most kDecodeMaxRows rows (every tile
 // of a layer call with T <= kDecodeMaxRows tokens).

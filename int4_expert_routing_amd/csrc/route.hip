@@ -19,6 +19,7 @@
 //      the final row of each pair = offset + block base + in-block rank.
 // Ranks count only earlier pairs, so the sort is stable and the result does not
 // depend on thread timing: repeated runs give identical tables.
+#include "prep_rows.h"
 #include "route_block.h"
 
 namespace moe {
@@ -379,8 +380,17 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(RouteArgs a,
 constexpr int kScanExperts = 16;
 constexpr int kScanParts = kRouteThreads / kScanExperts;
 
-__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(ScanArgs a) {
+// Workgroups past the scan's run the activation preparation of the grouped
+// GEMM (prep_rows.h), which needs nothing from the routing: it fills the GPU
+// while the few scan workgroups and the scatter that follows run.
+static_assert(kPrepThreads == kRouteThreads, "one block size for the scan and the preparation");
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(ScanArgs a, PrepArgs prep) {
   __shared__ int32_t part[kScanParts][kScanExperts];
+  const int nscan = ceil_div(a.E, kScanExperts);
+  if (int(blockIdx.x) >= nscan) {   // uniform
+    prep_rows_block(prep, long(blockIdx.x) - nscan);
+    return;
+  }
   const int tid = threadIdx.x;
   const int el = tid % kScanExperts, p = tid / kScanExperts;
   const int e = blockIdx.x * kScanExperts + el;
@@ -478,7 +488,8 @@ int router_splits(int T, int H, int E) {
 }
 
 hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterArgs& ca, bool from_x,
-                        hipStream_t stream) {
+                        hipStream_t stream, const PrepArgs* prep, bool* prep_done) {
+  if (prep_done) *prep_done = false;
   const int nblk = ceil_div(ra.T, kRouteTokens);
   const int nrb = ceil_div(ra.T, kRouterRows);
   RouteArgs rb = ra;
@@ -534,7 +545,10 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
   hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, stream, rb);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || rb.finish) return err;
-  hipLaunchKernelGGL(route_scan_kernel, dim3(ceil_div(ra.E, kScanExperts)), dim3(kRouteThreads), 0, stream, sa);
+  const long nprep = prep ? prep_rows_blocks(prep->rows, prep->K) : 0;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(unsigned(ceil_div(ra.E, kScanExperts) + nprep)), dim3(kRouteThreads), 0,
+                     stream, sa, prep ? *prep : PrepArgs{});
+  if (prep_done) *prep_done = prep != nullptr;
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kRouteThreads), 0, stream, ca, sa);

@@ -2,47 +2,20 @@
 // order and the exact group-sum table) and the weighted combine of the experts'
 // output rows.
 #include "moe_internal.h"
+#include "prep_rows.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Activation preparation: permuted chunk order plus the group-sum table.
-// 8 lanes per group, one 16-byte chunk each; group sums in fp64, rounded once.
-__global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* A, int rows, int K, uint16_t* a_perm,
-                                                        uint16_t* a_part) {
-  const int G = K / kGroup;
-  const int KPx = xpart_cols(K);
-  const long gid = long(blockIdx.x) * blockDim.x + threadIdx.x;
-  const long team = gid >> 3;
-  const int sub = int(gid & 7);
-  const long total = long(rows) * G;
-  const bool ok = team < total;
-  const int row = ok ? int(team / G) : 0;
-  const int g = ok ? int(team % G) : 0;
-  u32x4 v = u32x4{0, 0, 0, 0};
-  if (ok) v = *reinterpret_cast<const u32x4*>(A + size_t(row) * K + g * kGroup + 8 * sub);
-  double s = chunk_sum_f64(v);
-  s += __shfl_xor(s, 1, kWave);
-  s += __shfl_xor(s, 2, kWave);
-  s += __shfl_xor(s, 4, kWave);
-  if (!ok) return;
-  *reinterpret_cast<u32x4*>(a_perm + size_t(row) * K + g * kGroup + 8 * sub) = permute_chunk(v);
-  uint16_t* xp = a_part + size_t(row) * KPx;
-  if (sub == 0) {
-    uint16_t h, m, l;
-    split3_bf16(float(s), h, m, l);
-    const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
-                     uint32_t(m) | (uint32_t(h) << 16), 0u};
-    *reinterpret_cast<u32x4*>(xp + 8 * g) = e;
-  }
-}
+// Activation preparation (prep_rows.h) as a launch of its own.
+__global__ __launch_bounds__(kPrepThreads) void prep_rows_kernel(PrepArgs p) { prep_rows_block(p, blockIdx.x); }
 
 hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm, uint16_t* a_part,
                             hipStream_t stream) {
-  const long threads = long(rows) * (K / kGroup) * 8;
-  if (threads == 0) return hipSuccess;
-  const unsigned blocks = unsigned((threads + 255) / 256);
-  hipLaunchKernelGGL(prep_rows_kernel, dim3(blocks), dim3(256), 0, stream, A, rows, K, a_perm, a_part);
+  const long blocks = prep_rows_blocks(rows, K);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(prep_rows_kernel, dim3(unsigned(blocks)), dim3(kPrepThreads), 0, stream,
+                     PrepArgs{A, rows, K, a_perm, a_part});
   return hipGetLastError();
 }
 
