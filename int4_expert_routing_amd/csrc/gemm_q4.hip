@@ -559,7 +559,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   // ---- epilogues ------------------------------------------------------------
   if constexpr (EPI == kEpiF32) {
     // each wave stages one 128 x 32 column block at a time in its own LDS area
-    // (row stride 36 floats) and writes whole 128-byte row segments
+    // (row stride 36 floats) and writes whole 128-byte row segments, with
+    // non-temporal stores (the rows are read once, by the combine; 1.5-2%
+    // faster T=4096 layer with the combine's non-temporal loads)
     float* out = reinterpret_cast<float*>(a.out);
     float* stg = reinterpret_cast<float*>(ring) + wave * (kBlockRows * kF32StageStride);
 #pragma unroll
@@ -577,7 +579,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
         for (int i = 0; i < 16; ++i) {
           const int m = i * 8 + (lane >> 3), c4 = (lane & 7) * 4;
           const f32x4 v = *reinterpret_cast<const f32x4*>(stg + m * kF32StageStride + c4);
-          if (m < nrows) *reinterpret_cast<f32x4*>(out + size_t(ti.r0 + m) * a.N + cbase[cb] + c4) = v;
+          if (m < nrows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + size_t(ti.r0 + m) * a.N + cbase[cb] + c4));
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -594,7 +596,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
             const int m = i * 8 + (lane >> 3), c4 = (lane & 7) * 4;
             const f32x4 v = *reinterpret_cast<const f32x4*>(stg + m * kF32StageStride + c4);
             if (kBlockRows + m < nrows)
-              *reinterpret_cast<f32x4*>(out + size_t(ti.r0 + kBlockRows + m) * a.N + cbase[cb] + c4) = v;
+              __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + size_t(ti.r0 + kBlockRows + m) * a.N + cbase[cb] + c4));
           }
         }
         __builtin_amdgcn_wave_barrier();

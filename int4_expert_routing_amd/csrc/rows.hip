@@ -24,7 +24,8 @@ hipError_t launch_prep_rows(const uint16_t* A, int rows, int K, uint16_t* a_perm
 // summed in that order (shared row first, then j ascending) with fp32 FMAs;
 // g[t] = 1, or the shared-expert gate of the token when a gate vector is given.
 // One workgroup per token; a thread owns 4 consecutive columns in each of the
-// H/1024 column chunks. KK > 0 fixes k at compile time, so that every row
+// H/1024 column chunks; Y is read once, with non-temporal loads. KK > 0 fixes k
+// at compile time, so that every row
 // load of the token (both column chunks at H = 2048) is issued before the
 // first FMA; KK = 0 is the generic loop.
 template <int KK>
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const floa
     for (int u = 0; u < kChunks; ++u) {
       const int c = c0 + u * 1024;
       in[u] = c < H;
-      acc[u] = in[u] ? *reinterpret_cast<const f32x4*>(Y + size_t(shared_row0 + t) * H + c) : f32x4{};
+      acc[u] = in[u] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + size_t(shared_row0 + t) * H + c)) : f32x4{};
       if (shared_gate) acc[u] *= g;
     }
     if constexpr (KK > 0) {
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const floa
       for (int j = 0; j < KK; ++j)
 #pragma unroll
         for (int u = 0; u < kChunks; ++u)
-          v[j][u] = in[u] ? *reinterpret_cast<const f32x4*>(Y + size_t(rows[j]) * H + c0 + u * 1024) : f32x4{};
+          v[j][u] = in[u] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + size_t(rows[j]) * H + c0 + u * 1024)) : f32x4{};
 #pragma unroll
       for (int j = 0; j < KK; ++j)
 #pragma unroll
