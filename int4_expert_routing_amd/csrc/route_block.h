@@ -297,6 +297,49 @@ __device__ __forceinline__ void small_tables(const RouteArgs& a, const int32_t* 
   }
 }
 
+// The tables of a routing block of one token: its k experts are distinct, so
+// every count is 0 or 1, an expert's offset is the number of chosen experts
+// below it (four ballots), and a pair's row (its tile, its rank in the
+// sorted rows) is the number of the token's other experts below its own. The
+// same results as small_tables, with no scan and no LDS round trip beyond the
+// count flags. Run by one wave; hist: E zeros in LDS.
+__device__ __forceinline__ void one_token_tables(const RouteArgs& a, const int32_t* ids_s, int32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int E = a.E, k = a.k;
+  const bool live = lane < k;
+  const int e = live ? ids_s[lane] : 0;
+  if (live) hist[e] = 1;
+  int rank = 0;
+  for (int q = 0; q < k; ++q) rank += int(__builtin_amdgcn_readlane(e, q) < e);
+  __builtin_amdgcn_wave_barrier();
+  int c[kMaxKeysPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) c[i] = lane + 64 * i < E ? hist[lane + 64 * i] : 0;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) {
+    const int ee = lane + 64 * i;
+    const uint64_t m = __ballot(c[i] != 0);
+    if (ee < E) {
+      a.counts[ee] = c[i];
+      a.offsets[ee] = base + __popcll(m & below);
+    }
+    base += __popcll(m);
+  }
+  if (lane == 0) {
+    a.offsets[E] = k;
+    *a.num_tiles = k;
+  }
+  if (live) {
+    a.row_of_pair[lane] = rank;
+    a.sorted_rows[rank] = lane;
+    a.tile_map[2 * rank] = e;
+    a.tile_map[2 * rank + 1] = rank;
+    if (a.tile_desc) a.tile_desc[rank] = u32x4{uint32_t(e), uint32_t(rank), 1u, 0u};
+  }
+}
+
 // Top-k, softmax, histogram and ranks of routing block blk (and, for a single
 // block, the tables), run by one 1024-thread workgroup.
 __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
@@ -372,6 +415,10 @@ __device__ __forceinline__ void topk_block(const RouteArgs& a, int blk) {
   __syncthreads();
 
   const int npairs_all = nt * k;
+  if (a.finish && nt == 1) {   // uniform
+    if (wave == 0) one_token_tables(a, ids_s, hist);
+    return;
+  }
   if (a.finish && npairs_all <= kWave) {   // uniform
     if (wave == 0) small_tables(a, ids_s, hist, npairs_all);
     return;

@@ -57,6 +57,9 @@ ROUTE_CASES = [
     (100, 32, 4, 64, "zeros"), (513, 256, 8, 64, "ties"), (32768, 256, 8, 64, "gauss"),
     (33, 256, 32, 1, "ties"), (257, 5, 3, 7, "gauss"),
     (3, 256, 8, 128, "neginf"), (16, 64, 8, 128, "neginf"), (1000, 256, 8, 128, "neginf"),
+    # one token: the single-token tables (every count 0 or 1)
+    (1, 8, 8, 1, "ties"), (1, 64, 32, 3, "neginf"), (1, 5, 3, 7, "gauss"), (1, 256, 32, 128, "zeros"),
+    (1, 256, 1, 64, "zipf"),
 ]
 
 
