@@ -227,12 +227,18 @@ __device__ __forceinline__ void token_softmax(const uint32_t* sel_key, const int
 
 // The tables of a single routing block of at most 64 pairs (the few-token
 // case), built by one wave: the same results as the general path of
-// topk_block below (stable ranks, offsets, block map, scatter, descriptors),
-// with lane p holding pair p and lane l experts l, l + 64, l + 128, l + 192,
-// so that no step needs the rest of the workgroup. hist: E zeros in LDS.
+// topk_block below (stable ranks, offsets, block map, scatter, descriptors).
+// Lane p holds pair p; lane l holds experts l, l + 64, l + 128, l + 192 for
+// the counts. Every count and tile count is at most 64, so an expert's count
+// and tile count and those of the expert 64 above it share one 32-bit word (8
+// bits each) and two DPP scans give every offset and first tile. Each pair
+// then finds its row and tile from its expert's offset and its rank; the
+// first pair of a tile writes the block map entry and the descriptor, whose
+// token nibbles the tile's pairs have OR-ed into LDS. hist: E zeros in LDS.
 __device__ __forceinline__ void small_tables(const RouteArgs& a, const int32_t* ids_s, int32_t* hist, int np) {
   __shared__ int32_t off_w[kMaxExperts];
-  __shared__ int32_t sorted_w[kWave];
+  __shared__ int32_t tf_w[kMaxExperts];
+  __shared__ uint32_t tok_w[kWave];
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1ull;
   const int E = a.E, k = a.k, bm = a.block_rows;
@@ -245,28 +251,51 @@ __device__ __forceinline__ void small_tables(const RouteArgs& a, const int32_t* 
     same &= ((e >> bit) & 1) ? bb : ~bb;
   }
   const int rank = __popcll(same & below);
-  if (live && rank == 0) hist[e] = __popcll(same);
+  const int cnt = __popcll(same);
+  if (live && rank == 0) hist[e] = cnt;
+  tok_w[lane] = 0u;
   __builtin_amdgcn_wave_barrier();
-  int c[kMaxKeysPerLane], o[kMaxKeysPerLane], ntl[kMaxKeysPerLane], tf[kMaxKeysPerLane];
-  int base = 0, tbase = 0;
+  static_assert(kMaxKeysPerLane == 4 && kWave <= 255, "two experts per word, 8-bit fields");
+  int c[kMaxKeysPerLane], ntl[kMaxKeysPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxKeysPerLane; ++i) {
     const int ee = lane + 64 * i;
     c[i] = ee < E ? hist[ee] : 0;
     ntl[i] = ceil_div(c[i], bm);
-    const int sc = wave_scan_incl(c[i]), st = wave_scan_incl(ntl[i]);
-    o[i] = base + sc - c[i];
-    tf[i] = tbase + st - ntl[i];
-    base += __builtin_amdgcn_readlane(sc, kWave - 1);
-    tbase += __builtin_amdgcn_readlane(st, kWave - 1);
+  }
+  const uint32_t p0 = uint32_t(c[0]) | uint32_t(ntl[0]) << 8 | uint32_t(c[1]) << 16 | uint32_t(ntl[1]) << 24;
+  const uint32_t p1 = uint32_t(c[2]) | uint32_t(ntl[2]) << 8 | uint32_t(c[3]) << 16 | uint32_t(ntl[3]) << 24;
+  const uint32_t s0 = uint32_t(wave_scan_incl(int(p0))), s1 = uint32_t(wave_scan_incl(int(p1)));
+  const uint32_t x0 = s0 - p0, x1 = s1 - p1;   // exclusive, field by field (no borrow: s >= p per field)
+  const uint32_t t0 = uint32_t(__builtin_amdgcn_readlane(int(s0), kWave - 1));
+  const uint32_t t1 = uint32_t(__builtin_amdgcn_readlane(int(s1), kWave - 1));
+  auto fld = [](uint32_t v, int f) { return int((v >> (8 * f)) & 0xFFu); };
+  int o[kMaxKeysPerLane], tf[kMaxKeysPerLane];
+  int base = 0, tbase = 0;
+  o[0] = fld(x0, 0);
+  tf[0] = fld(x0, 1);
+  base += fld(t0, 0);
+  tbase += fld(t0, 1);
+  o[1] = base + fld(x0, 2);
+  tf[1] = tbase + fld(x0, 3);
+  base += fld(t0, 2);
+  tbase += fld(t0, 3);
+  o[2] = base + fld(x1, 0);
+  tf[2] = tbase + fld(x1, 1);
+  base += fld(t1, 0);
+  tbase += fld(t1, 1);
+  o[3] = base + fld(x1, 2);
+  tf[3] = tbase + fld(x1, 3);
+  base += fld(t1, 2);
+  tbase += fld(t1, 3);
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) {
+    const int ee = lane + 64 * i;
     if (ee < E) {
       a.counts[ee] = c[i];
       a.offsets[ee] = o[i];
       off_w[ee] = o[i];
-      for (int j = 0; j < ntl[i]; ++j) {
-        a.tile_map[2 * (tf[i] + j)] = ee;
-        a.tile_map[2 * (tf[i] + j) + 1] = o[i] + j * bm;
-      }
+      tf_w[ee] = tf[i];
     }
   }
   if (lane == 0) {
@@ -274,27 +303,22 @@ __device__ __forceinline__ void small_tables(const RouteArgs& a, const int32_t* 
     *a.num_tiles = tbase;
   }
   __builtin_amdgcn_wave_barrier();
+  int pos = 0, tile = 0, rr = 0;
   if (live) {
-    const int pos = off_w[e] + rank;
+    pos = off_w[e] + rank;
+    tile = tf_w[e] + rank / bm;
+    rr = rank % bm;
     a.sorted_rows[pos] = lane;
     a.row_of_pair[lane] = pos;
-    sorted_w[pos] = lane;
+    if (rr == 0) {
+      a.tile_map[2 * tile] = e;
+      a.tile_map[2 * tile + 1] = pos;
+    }
+    if (a.tile_desc && rr < 8) atomicOr(&tok_w[tile], uint32_t(lane / k) << (4 * rr));
   }
   if (!a.tile_desc) return;
   __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int i = 0; i < kMaxKeysPerLane; ++i) {
-    const int ee = lane + 64 * i;
-    if (ee < E) {
-      for (int j = 0; j < ntl[i]; ++j) {
-        const int r0 = o[i] + j * bm;
-        const int n = min(bm, c[i] - j * bm);
-        uint32_t tok = 0;
-        for (int q = 0; q < n && q < 8; ++q) tok |= uint32_t(sorted_w[r0 + q] / k) << (4 * q);
-        a.tile_desc[tf[i] + j] = u32x4{uint32_t(ee), uint32_t(r0), uint32_t(n), tok};
-      }
-    }
-  }
+  if (live && rr == 0) a.tile_desc[tile] = u32x4{uint32_t(e), uint32_t(pos), uint32_t(min(bm, cnt - rank)), tok_w[tile]};
 }
 
 // The tables of a routing block of one token: its k experts are distinct, so

@@ -60,6 +60,9 @@ ROUTE_CASES = [
     # one token: the single-token tables (every count 0 or 1)
     (1, 8, 8, 1, "ties"), (1, 64, 32, 3, "neginf"), (1, 5, 3, 7, "gauss"), (1, 256, 32, 128, "zeros"),
     (1, 256, 1, 64, "zipf"),
+    # one routing block of at most 64 pairs: the one-wave tables (repeated experts, several tiles per expert)
+    (8, 16, 8, 3, "gauss"), (4, 8, 4, 1, "ties"), (16, 32, 4, 5, "zipf"), (2, 5, 3, 2, "gauss"),
+    (8, 256, 8, 64, "zeros"), (6, 64, 8, 2, "neginf"), (32, 256, 2, 64, "gauss"),
 ]
 
 
