@@ -47,12 +47,12 @@ extern "C" {
  * epoch and its tagged hand-off words): zero before the first layer call, and
  * changed by nothing else afterwards (zeroing them again between calls is
  * allowed). */
-#define MOE_WORKSPACE_HEAD_BYTES 181888
+#define MOE_WORKSPACE_HEAD_BYTES 190080
 /* Byte offset, inside that head, of a uint32 status word: nonzero after a
  * decode-sized call whose persistent kernel gave up waiting (a bounded wait
  * ran out, e.g. when other work kept its workgroups from being resident);
  * that call's outputs are then invalid. It stays set until the head is zeroed. */
-#define MOE_WORKSPACE_STATUS_OFFSET 8576
+#define MOE_WORKSPACE_STATUS_OFFSET 16768
 /* Largest supported expert count and top-k. */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32

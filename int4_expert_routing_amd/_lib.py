@@ -27,8 +27,8 @@ MOE_Q4_GROUP = 64
 MOE_GEMM_BLOCK_ROWS = 128
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
-MOE_WORKSPACE_HEAD_BYTES = 181888
-MOE_WORKSPACE_STATUS_OFFSET = 8576
+MOE_WORKSPACE_HEAD_BYTES = 190080
+MOE_WORKSPACE_STATUS_OFFSET = 16768
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 

@@ -13,7 +13,7 @@ constexpr int kWave = 64;
 // Head of a layer workspace that must be zero before a call and that every
 // call leaves zero: the one-launch routing's completion counter (256 bytes)
 // and its 64-bit logit slots for up to kHandoffTokens tokens x 256 experts.
-constexpr int kHandoffTokens = 4;
+constexpr int kHandoffTokens = 8;
 constexpr int kHandoffBytes = 256 + kHandoffTokens * 256 * 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -256,14 +256,18 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
 // then zeroes the slots and the counter (agent-scope atomic stores; the next
 // call's workgroups start after this kernel ends), writes the logits to
 // logits_out, and runs the top-k, softmax and tables as a single routing
-// block with its 256 threads (one wave per token). A release/acquire pair on
+// block with its threads (one wave per token). A release/acquire pair on
 // the counter instead costs a write-back of the L2 per workgroup: 12.3 us
-// against 9.9 us for this kernel at T = 1.
+// against 9.9 us for this kernel at T = 1. Up to 4 tokens a workgroup has 256
+// threads and 4 experts; at 5..8 tokens, 512 threads (8 waves for the top-k)
+// and 8 experts, one wave each.
 constexpr int kSmallThreads = 256;
-constexpr int kSmallRouteMaxT = kSmallThreads / kWave;   // one wave per token in the top-k
+constexpr int kSmallRouteMaxT = 8;                       // tokens of the one-launch routing
 constexpr int kSlotPolls = 1 << 24;                      // bound on the re-reads of one slot
-constexpr int kSmallEpw = 4;                             // experts per workgroup
+constexpr int kSmallEpw = 4;                             // experts per workgroup (up to 4 tokens)
 static_assert(kSmallRouteMaxT == kHandoffTokens && kMaxExperts <= 256, "slot layout of the workspace head");
+__host__ __device__ constexpr int small_threads(int tb) { return tb <= 4 ? kSmallThreads : 64 * tb; }
+constexpr int kSmallStageMaxH = 2048;                    // rows staged in LDS at 3..8 tokens: up to 32 KB
 
 // c + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (fp32). The pairs are
 // taken as plain 32-bit values: bit-casting a vector element expression in
@@ -279,11 +283,15 @@ __device__ __forceinline__ float bf16_dot2(uint32_t a, uint32_t b, float c) {
 constexpr int kSmallChunks = 8;
 
 template <int TB, int EPW>   // token bucket: TB >= T tokens are computed, rows past T repeat row T-1 and are not stored
-__global__ __launch_bounds__(kSmallThreads) void route_small_kernel(RouteArgs a, int32_t* done, uint64_t* slots) {
-  constexpr int TPE = kSmallThreads / EPW;                 // threads per expert
+__global__ __launch_bounds__(small_threads(TB)) void route_small_kernel(RouteArgs a, int32_t* done, uint64_t* slots) {
+  constexpr int NT = small_threads(TB);
+  constexpr int TPE = NT / EPW;                            // threads per expert
+  constexpr bool STAGE = TB >= 4;                          // rows staged in LDS
+  constexpr int CHUNKS = STAGE ? 4 : kSmallChunks;         // weight chunk loads in flight per thread
   static_assert(EPW == 1 || (TPE <= kWave && kWave % TPE == 0), "an expert's threads: the workgroup or part of one wave");
-  __shared__ float red[kSmallThreads / kWave][kSmallRouteMaxT];
-  __shared__ float lg[kSmallRouteMaxT * kMaxExperts];
+  static_assert(TB <= NT / kWave && TB <= kSmallRouteMaxT, "one wave per token in the top-k");
+  __shared__ float red[NT / kWave][TB];
+  __shared__ float lg[TB * kMaxExperts];
   __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ej = tid / TPE, q = tid % TPE;
@@ -293,22 +301,70 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(RouteArgs a,
   float acc[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
-  if (e < E) {
-    const uint16_t* wr = a.wr + size_t(e) * H;
-    for (int c0 = q; c0 < nch; c0 += kSmallChunks * TPE) {
-      // every load of up to kSmallChunks chunks is issued before the first product
-      u32x4 wv[kSmallChunks], xv[kSmallChunks][TB];
+  if constexpr (STAGE) {
+    // 3..8 tokens: the rows (rows past T repeat row T-1) are staged once in
+    // LDS (dynamic, TB * H bf16) and read there by every expert's wave; the
+    // first weight chunks' loads are issued before the staging. (With the
+    // rows in registers as below, the compiler interleaves their loads with
+    // the products at 4 and more tokens: several round trips instead of one.)
+    extern __shared__ __align__(16) u32x4 xsm[];   // [TB][nch]
+    const uint16_t* wr = a.wr + size_t(min(e, E - 1)) * H;
+    u32x4 wv[CHUNKS];
 #pragma unroll
-      for (int i = 0; i < kSmallChunks; ++i) {
+    for (int i = 0; i < CHUNKS; ++i) wv[i] = *reinterpret_cast<const u32x4*>(wr + min(q + i * TPE, nch - 1) * 8);
+    // at most XPT chunks per thread (H <= kSmallStageMaxH), all loaded before
+    // the first store: a fixed count, so no loop-carried wait on the loads
+    constexpr int XPT = TB * (kSmallStageMaxH / 8) / NT;
+    const int nx = TB * nch;
+    u32x4 v[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int ic = min(j * NT + tid, nx - 1);
+      const int r = ic / nch, ch = ic - r * nch;
+      v[j] = *reinterpret_cast<const u32x4*>(a.x + size_t(min(r, T - 1)) * H + ch * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < XPT; ++j)
+      if (j * NT + tid < nx) xsm[j * NT + tid] = v[j];
+    __syncthreads();
+    for (int c0 = q; c0 < nch; c0 += CHUNKS * TPE) {
+      if (c0 != q) {
+#pragma unroll
+        for (int i = 0; i < CHUNKS; ++i) wv[i] = *reinterpret_cast<const u32x4*>(wr + min(c0 + i * TPE, nch - 1) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < CHUNKS; ++i) {
+        if (c0 + i * TPE >= nch) wv[i] = u32x4{0u, 0u, 0u, 0u};
+        const int ch = min(c0 + i * TPE, nch - 1);
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const u32x4 xv = xsm[t * nch + ch];
+          acc[t] = bf16_dot2(wv[i].x, xv.x, acc[t]);
+          acc[t] = bf16_dot2(wv[i].y, xv.y, acc[t]);
+          acc[t] = bf16_dot2(wv[i].z, xv.z, acc[t]);
+          acc[t] = bf16_dot2(wv[i].w, xv.w, acc[t]);
+        }
+      }
+    }
+  } else if (e < E) {
+    const uint16_t* wr = a.wr + size_t(e) * H;
+    for (int c0 = q; c0 < nch; c0 += CHUNKS * TPE) {
+      // every load of up to CHUNKS chunks is issued before the first product
+      u32x4 wv[CHUNKS], xv[CHUNKS][TB];
+#pragma unroll
+      for (int i = 0; i < CHUNKS; ++i) {
         const int ch = min(c0 + i * TPE, nch - 1);
         wv[i] = *reinterpret_cast<const u32x4*>(wr + ch * 8);
 #pragma unroll
         for (int t = 0; t < TB; ++t)
           xv[i][t] = *reinterpret_cast<const u32x4*>(a.x + size_t(min(t, T - 1)) * H + ch * 8);
       }
+      // chunks past the end (their loads re-read the last chunk) enter with
+      // zero weights: no branch, so the compiler keeps every load ahead of
+      // the first product instead of one round trip per chunk
 #pragma unroll
-      for (int i = 0; i < kSmallChunks; ++i) {
-        if (c0 + i * TPE >= nch) break;
+      for (int i = 0; i < CHUNKS; ++i) {
+        if (c0 + i * TPE >= nch) wv[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
           acc[t] = bf16_dot2(wv[i].x, xv[i][t].x, acc[t]);
@@ -333,6 +389,7 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(RouteArgs a,
   if (q < T && e < E) {   // thread q of expert e stores token q's logit
     float v;
     if (EPW == 1) {
+      static_assert(EPW > 1 || NT == 4 * kWave, "one expert per workgroup: four waves");
       v = (red[0][q] + red[1][q]) + (red[2][q] + red[3][q]);
     } else {
       v = acc[0];
@@ -351,7 +408,7 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(RouteArgs a,
   if (!last) return;   // uniform
   // collect the logits (waiting for any slot not yet visible) into LDS and
   // logits_out, and zero the slots
-  for (int i = tid; i < T * E; i += kSmallThreads) {
+  for (int i = tid; i < T * E; i += NT) {
     uint64_t v = __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int n = 0; (v >> 32) == 0 && n < kSlotPolls; ++n)
       v = __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -502,9 +559,10 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
   rb.num_tiles = sa.num_tiles;
   rb.sorted_rows = ca.sorted_rows;
   rb.row_of_pair = ca.row_of_pair;
-  if (from_x && ra.T <= kSmallRouteMaxT && ra.done && ra.slots && ra.logits_out && ra.H % 8 == 0) {
+  if (from_x && ra.T <= kSmallRouteMaxT && ra.done && ra.slots && ra.logits_out && ra.H % 8 == 0 &&
+      (ra.T <= 2 || ra.H <= kSmallStageMaxH)) {
     // one launch: complete logits per expert slice, top-k by the last workgroup
-    // (measured faster than the MFMA router + top-k launches up to 4 tokens;
+    // (measured faster than the MFMA router + top-k launches up to 8 tokens;
     // its per-token cost is higher, so larger calls keep the two launches)
     constexpr int EPW = kSmallEpw;
     const dim3 grid(ceil_div(ra.E, EPW)), block(kSmallThreads);
@@ -512,8 +570,13 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
       hipLaunchKernelGGL((route_small_kernel<1, EPW>), grid, block, 0, stream, rb, ra.done, ra.slots);
     else if (ra.T <= 2)
       hipLaunchKernelGGL((route_small_kernel<2, EPW>), grid, block, 0, stream, rb, ra.done, ra.slots);
+    else if (ra.T <= 4)
+      hipLaunchKernelGGL((route_small_kernel<4, EPW>), grid, block, size_t(4) * ra.H * 2, stream, rb, ra.done,
+                         ra.slots);
     else
-      hipLaunchKernelGGL((route_small_kernel<4, EPW>), grid, block, 0, stream, rb, ra.done, ra.slots);
+      hipLaunchKernelGGL((route_small_kernel<kSmallRouteMaxT, 8>), dim3(ceil_div(ra.E, 8)),
+                         dim3(small_threads(kSmallRouteMaxT)), size_t(kSmallRouteMaxT) * ra.H * 2, stream, rb,
+                         ra.done, ra.slots);
     return hipGetLastError();
   }
   if (from_x) {

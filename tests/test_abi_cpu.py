@@ -186,8 +186,8 @@ def test_noalloc_rejects_sizes_beyond_its_array_before_any_hip_call(lib):
     assert st == _lib.MOE_ERR_SHAPE
     hdr = open(HEADER).read()
     assert "#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)" in hdr and _lib.MOE_NOALLOC_SCRATCH_BYTES == 32 << 20
-    assert "#define MOE_WORKSPACE_HEAD_BYTES 181888" in hdr and _lib.MOE_WORKSPACE_HEAD_BYTES == 181888
-    assert "#define MOE_WORKSPACE_STATUS_OFFSET 8576" in hdr and _lib.MOE_WORKSPACE_STATUS_OFFSET == 8576
+    assert "#define MOE_WORKSPACE_HEAD_BYTES 190080" in hdr and _lib.MOE_WORKSPACE_HEAD_BYTES == 190080
+    assert "#define MOE_WORKSPACE_STATUS_OFFSET 16768" in hdr and _lib.MOE_WORKSPACE_STATUS_OFFSET == 16768
 
 
 def test_quantize_validation_launches_nothing(lib):
