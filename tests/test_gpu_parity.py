@@ -454,6 +454,10 @@ def test_layer_full_shape_decode(dev, name):
     (8, 256, 256, 16, 2, "random", 4),
     (8, 256, 256, 16, 16, "random", 5),      # k = E: every expert gets all 8 rows
     (7, 512, 1024, 32, 8, "sym", 6),
+    (6, 256, 256, 5, 3, "random", 10),       # one-launch routing, 8-expert workgroups past E = 5
+    (3, 512, 256, 5, 2, "random", 11),       # rows staged in LDS (3..4 tokens), experts past E
+    (6, 4096, 256, 8, 2, "random", 12),      # H above the staged rows' limit: router + top-k launches
+    (2, 2560, 256, 8, 2, "random", 13),      # H = 2560 (not a power of two), rows in registers
     (9, 256, 256, 16, 2, "random", 7),       # above the threshold: grouped GEMM path
 ])
 def test_layer_few_tokens(dev, T, H, I, E, k, bias_mode, seed):
