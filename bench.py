@@ -529,6 +529,23 @@ def main():
     torch.cuda.synchronize()
     graph_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     del graph
+
+    # the same calls with the shared expert's GEMMs on a second stream (the
+    # moe_layer_forward_ex side-stream option), reported beside the value
+    side = ops.MoELayer(w, k, T, side_stream=True)
+    y_side = torch.empty_like(y)
+    side_call = lambda: side(x, y=y_side)
+    side_call()
+    torch.cuda.synchronize()
+    ramp(torch, side_call)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        side_call()
+    torch.cuda.synchronize()
+    side_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    side_matches = bool(torch.equal(y_side, y_ref))
+    del side
     gpu_ms = float(np.mean(step_ms))
     names = ["prep", "route", "gate_up_gemm", "down_gemm", "combine"]
     flops = layer_flops(T, H, I, E, k)
@@ -559,8 +576,11 @@ def main():
         "timing": (f"{args.steps} back-to-back layer calls, wall clock between synchronizations, after the "
                    f"{args.warmup} warm-up calls and {ramp_calls} more calls ({RAMP_SECONDS} s) that bring the GPU "
                    "to its sustained clocks; graph_ms_per_step: the same calls captured in one HIP graph and "
-                   "replayed once; events_ms_per_step: with HIP events between the stages"),
+                   "replayed once; events_ms_per_step: with HIP events between the stages; "
+                   "side_stream_ms_per_step: the same calls with the shared expert's GEMMs on a second stream"),
         "graph_ms_per_step": graph_ms_per_step,
+        "side_stream_ms_per_step": side_ms_per_step,
+        "side_stream_matches_one_stream": side_matches,
         "events_ms_per_step": events_ms_per_step,
         "graph_replay_matches_eager": graph_matches,
         "layer_gpu_ms_events": gpu_ms,
