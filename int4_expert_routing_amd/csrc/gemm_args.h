@@ -33,7 +33,8 @@ struct GemmArgs {
   const int32_t* tile_map;  // (expert, first row) of each routed tile of at most bm rows
   const int32_t* num_tiles;
   int bm;                   // rows per routed tile (32, 64 or kBlockRows)
-  int n_shared_tiles;       // the first n_shared_tiles tiles cover the shared rows, kBlockRows each
+  int n_shared_tiles;       // the first n_shared_tiles tiles cover the shared rows, sh_bm each
+  int sh_bm;                // rows per shared tile (kBlockRows, or 32 in one-column-block launches)
   int routed_tiles;         // 1: the routed tiles of the block map follow them; 0: shared tiles only
   int merge_tail;           // 1 (bm == kBlockRows, a complete block map in expert order): an expert's last
                             // tile of at most 32 rows is computed by the full tile before it
@@ -43,6 +44,10 @@ struct GemmArgs {
   uint16_t* out_part;       // group-sum table of the bf16 output (internal SwiGLU only)
 };
 
-hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream);
+// one_block: the one-column-block kernel (every tile of the launch holds at
+// most 32 rows: routed tiles of 32 rows, sh_bm == 32; NT = N / 64 for the
+// SwiGLU epilogues, N / 128 for STORE_F32)
+hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream,
+                       bool one_block = false);
 
 }  // namespace moe

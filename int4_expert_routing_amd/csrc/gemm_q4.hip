@@ -65,7 +65,7 @@ namespace moe {
 constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kXpSlotBytes = 4096;       // side table of one group pair: 128 rows x 32 B (groups 2p, 2p+1)
-constexpr int kSbSlotBytes = 2048;       // scale/bias words of one group pair: 4 waves x 2 column blocks x 64 words
+constexpr int kSbWaveBytes = 256;        // scale/bias words of one group pair, one column block: 64 words
 
 // LDS ring geometry. Group g's activation tile lives in A slot g % A_RING and
 // its codes in code slot g % C_RING; groups are loaded DIST steps ahead. The
@@ -88,8 +88,11 @@ constexpr int kSbSlotBytes = 2048;       // scale/bias words of one group pair: 
 //     remainder rows then share the full tile's code unpacking instead of
 //     unpacking the expert's weights again for a few rows (a tile of 1..32
 //     rows costs ~35-45% of a full one).
+//   one-column-block launches (NCB = 1: all tiles of at most 32 rows, each
+//     wave one 32-column block): the small geometry with half the code
+//     bytes per group, 51 KB, so that three workgroups fit per CU.
 enum RingMode { kRingFull = 0, kRingSmall = 1, kRingMerged = 2 };
-template <int RM>
+template <int RM, int NCB = 2>
 struct Ring {
   static constexpr bool SR = RM == kRingSmall;
   static constexpr int DIST = SR ? 4 : 1;
@@ -97,7 +100,7 @@ struct Ring {
   static constexpr int ALOADS = AROWS / 32;               // activation loads per wave and group (8 rows each)
   static constexpr int A_RING = DIST + 1;
   static constexpr int C_RING = SR ? DIST + 2 : DIST + 1;
-  static constexpr int CODES = 8192;                      // 4 waves x 2 column blocks x 64 lanes x 16 B
+  static constexpr int CODES = 4 * NCB * 1024;           // 4 waves x NCB column blocks x 64 lanes x 16 B
   static constexpr int A_SLOT = SR ? AROWS * 128 : AROWS * 128 + CODES;
   static constexpr int C_BASE = SR ? A_RING * A_SLOT : AROWS * 128;
   static constexpr int C_SLOT = SR ? CODES : A_SLOT;
@@ -107,7 +110,8 @@ struct Ring {
   static constexpr int XLOADS = AROWS > 128 ? 2 : 1;
   static constexpr int SB = XP + XLOADS * kXpSlotBytes;
   static constexpr int SBS = SR ? 3 : 2;               // pair p's words are read at step 2p, loaded at 2p - DIST
-  static constexpr int END = SB + SBS * kSbSlotBytes;
+  static constexpr int SB_SLOT = 4 * NCB * kSbWaveBytes;
+  static constexpr int END = SB + SBS * SB_SLOT;
 };
 constexpr int kLdsLoopFS = Ring<kRingFull>::END > Ring<kRingSmall>::END ? Ring<kRingFull>::END : Ring<kRingSmall>::END;
 constexpr int kLdsLoop = kLdsLoopFS > Ring<kRingMerged>::END ? kLdsLoopFS : Ring<kRingMerged>::END;
@@ -150,7 +154,16 @@ __device__ __forceinline__ void global_to_lds4(const uint32_t* src, uint8_t* dst
 // block (STORE_F32, row stride 36 floats; a merged tile's last 32 rows take a
 // second round).
 constexpr int kF32StageStride = 36;
-size_t gemm_lds_bytes(int /*K*/) {
+size_t gemm_lds_bytes(int /*K*/, int ncb = 2) {
+  if (ncb == 1) {
+    // the small ring, then 32 x 65 fp32 gate values + 32 x 64 bf16 h, or four
+    // 32 x 36 fp32 staging blocks
+    constexpr size_t ring = size_t(Ring<kRingSmall, 1>::END);
+    constexpr size_t epi = 32 * 65 * 4 + 32 * 64 * 2;
+    static_assert(ring <= 160 * 1024 / 3 && epi <= ring && size_t(kGemmWaves) * 32 * kF32StageStride * 4 <= ring,
+                  "three workgroups per CU");
+    return ring;
+  }
   const size_t swiglu = size_t(kMaxRows) * 128 * 2;
   const size_t f32 = size_t(kGemmWaves) * kBlockRows * kF32StageStride * 4;
   size_t m = size_t(kLdsLoop);
@@ -181,12 +194,12 @@ struct SBPair {
 // (g/2) % SBS (per wave and column block: 32 scale words, then 32 bias
 // words). Every load writes LDS directly, so the compiler tracks no register
 // results of them and only the explicit waits order them.
-template <int RM>
+template <int RM, int NCB>
 __device__ __forceinline__ void issue_codes(const Stream& st, uint8_t* ring, int g, int wave) {
-  using R = Ring<RM>;
+  using R = Ring<RM, NCB>;
   uint8_t* cs = ring + R::C_BASE + (g % R::C_RING) * R::C_SLOT;
-  buffer_to_lds16(st.rb0, cs + (wave * 2) * 1024, st.vb, g * st.gstride);
-  buffer_to_lds16(st.rb1, cs + (wave * 2 + 1) * 1024, st.vb, g * st.gstride);
+  buffer_to_lds16(st.rb0, cs + (wave * NCB) * 1024, st.vb, g * st.gstride);
+  if constexpr (NCB == 2) buffer_to_lds16(st.rb1, cs + (wave * 2 + 1) * 1024, st.vb, g * st.gstride);
 }
 
 // Loads of group g (in this order, which the waits count on):
@@ -194,31 +207,32 @@ __device__ __forceinline__ void issue_codes(const Stream& st, uint8_t* ring, int
 //     pair g/2;
 //   small ring, even g: activations and codes of g, the scale/bias words of
 //     pair g/2, then the codes of g+1; odd g: activations of g.
-template <int ODD, int RM>
+template <int ODD, int RM, int NCB>
 __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave) {
-  using R = Ring<RM>;
+  using R = Ring<RM, NCB>;
   constexpr bool SR = R::SR;
   uint8_t* slot = ring + (g % R::A_RING) * R::A_SLOT;
 #pragma unroll
   for (int i = 0; i < R::ALOADS; ++i)
     buffer_to_lds16(st.ra, slot + (wave * R::ALOADS + i) * 1024, st.va[i], g * (kGroup * 2));
-  if (!SR || !ODD) issue_codes<RM>(st, ring, g, wave);
+  if (!SR || !ODD) issue_codes<RM, NCB>(st, ring, g, wave);
   if (!ODD) {
     const int p = g >> 1;
-    uint8_t* sbs = ring + R::SB + (p % R::SBS) * kSbSlotBytes + wave * 512;
+    uint8_t* sbs = ring + R::SB + (p % R::SBS) * R::SB_SLOT + wave * (NCB * kSbWaveBytes);
     global_to_lds4(st.sbp[0] + p * st.sbstride, sbs);
-    global_to_lds4(st.sbp[1] + p * st.sbstride, sbs + 256);
-    if (SR) issue_codes<RM>(st, ring, g + 1, wave);   // g + 1 < G: G is even
+    if constexpr (NCB == 2) global_to_lds4(st.sbp[1] + p * st.sbstride, sbs + kSbWaveBytes);
+    if (SR) issue_codes<RM, NCB>(st, ring, g + 1, wave);   // g + 1 < G: G is even
   }
 }
 
 // Side-table entries of group pair p (groups 2p, 2p+1; every wave loads 32
 // rows) into the side-table slot, issued at step 2p once every wave is past
 // step 2p-1, the last reader of pair p-1.
-template <int RM>
+template <int RM, int NCB>
 __device__ __forceinline__ void issue_xp(const Stream& st, uint8_t* ring, int p, int wave) {
-  buffer_to_lds16(st.rxp, ring + Ring<RM>::XP + wave * 1024, st.vxp, p * 32);
-  if constexpr (Ring<RM>::XLOADS > 1) buffer_to_lds16(st.rxp, ring + Ring<RM>::XP + kXpSlotBytes, st.vxp2, p * 32);
+  using R = Ring<RM, NCB>;
+  buffer_to_lds16(st.rxp, ring + R::XP + wave * 1024, st.vxp, p * 32);
+  if constexpr (R::XLOADS > 1) buffer_to_lds16(st.rxp, ring + R::XP + kXpSlotBytes, st.vxp2, p * 32);
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding.
@@ -264,10 +278,14 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 //     odd g: the side table of step g-3 (g >= 3), groups g+1, g+2 (7 + 1)
 //       while g <= G-3, the side table of step g-1, and groups g+3, g+4 (7,
 //       the activations of g+4 following at step g) while g <= G-5.
-template <int ODD, int RM>
+template <int ODD, int RM, int NCB>
 __device__ __forceinline__ void wait_group(int g, int G) {
-  using R = Ring<RM>;
+  using R = Ring<RM, NCB>;
   constexpr bool SR = R::SR;
+  // small ring: an even group's issue is 1 + 3 NCB loads (activations, NCB
+  // code loads, NCB scale/bias loads, NCB code loads of the next group), an
+  // odd group's 1 (activations); with NCB = 2 the counts above
+  constexpr int EV = 1 + 3 * NCB;
   if constexpr (!SR) {
     // one group ahead: every load outstanding at the top of step g is group
     // g's or the side table issued before it
@@ -276,14 +294,14 @@ __device__ __forceinline__ void wait_group(int g, int G) {
     const bool xp3 = g >= 3;
     if (g <= G - 5) {
       if (xp3)
-        wait_vm<17>();
+        wait_vm<2 * EV + 3>();
       else
-        wait_vm<16>();
+        wait_vm<2 * EV + 2>();
     } else if (g == G - 3) {
       if (xp3)
-        wait_vm<10>();
+        wait_vm<EV + 3>();
       else
-        wait_vm<9>();
+        wait_vm<EV + 2>();
     } else {   // g == G - 1
       if (xp3)
         wait_vm<2>();
@@ -294,55 +312,56 @@ __device__ __forceinline__ void wait_group(int g, int G) {
     const bool xp2 = g >= 2;
     if (g <= G - 4) {
       if (xp2)
-        wait_vm<12>();
+        wait_vm<NCB + EV + 3>();
       else
-        wait_vm<11>();
+        wait_vm<NCB + EV + 2>();
     } else {   // g == G - 2
       if (xp2)
-        wait_vm<4>();
+        wait_vm<NCB + 2>();
       else
-        wait_vm<3>();
+        wait_vm<NCB + 1>();
     }
   }
 }
 
-template <int NRB, int P4, int RM>
+template <int NRB, int P4, int RM, int NCB>
 __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g, int G, int wave, int lane,
                                           SBPair& sb, float (&U)[2], f32x16 (&acc)[5][2]) {
-  using R = Ring<RM>;
+  using R = Ring<RM, NCB>;
   constexpr bool SR = R::SR;
   constexpr int ODD = P4 & 1;
   const int l32 = lane & 31, half = lane >> 5;
   // this wave's loads of group g have landed; the barrier makes it so for
   // every wave, and orders every wave's reads of the slot of group g-1
   // (previous step) before its refill
-  wait_group<ODD, RM>(g, G);
+  wait_group<ODD, RM, NCB>(g, G);
   __builtin_amdgcn_s_barrier();
-  if (!ODD) issue_xp<RM>(st, ring, g >> 1, wave);
-  if (g + R::DIST < G) issue_group<(ODD + R::DIST) & 1, RM>(st, ring, g + R::DIST, wave);
+  if (!ODD) issue_xp<RM, NCB>(st, ring, g >> 1, wave);
+  if (g + R::DIST < G) issue_group<(ODD + R::DIST) & 1, RM, NCB>(st, ring, g + R::DIST, wave);
   const uint8_t* slot = ring + (g % R::A_RING) * R::A_SLOT;
   const uint8_t* cslot = ring + R::C_BASE + (g % R::C_RING) * R::C_SLOT;
   if (!ODD) {
     // this pair's scale and bias words of the lane's column
-    const uint8_t* sbs = ring + R::SB + ((g >> 1) % R::SBS) * kSbSlotBytes + wave * 512;
+    const uint8_t* sbs = ring + R::SB + ((g >> 1) % R::SBS) * R::SB_SLOT + wave * (NCB * kSbWaveBytes);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      sb.s[cb] = *reinterpret_cast<const uint32_t*>(sbs + cb * 256 + l32 * 4);
-      sb.b[cb] = *reinterpret_cast<const uint32_t*>(sbs + cb * 256 + 128 + l32 * 4);
+    for (int cb = 0; cb < NCB; ++cb) {
+      sb.s[cb] = *reinterpret_cast<const uint32_t*>(sbs + cb * kSbWaveBytes + l32 * 4);
+      sb.b[cb] = *reinterpret_cast<const uint32_t*>(sbs + cb * kSbWaveBytes + 128 + l32 * 4);
     }
   }
 
-  const u32x4 w0 = *reinterpret_cast<const u32x4*>(cslot + (wave * 2) * 1024 + lane * 16);
-  const u32x4 w1 = *reinterpret_cast<const u32x4*>(cslot + (wave * 2 + 1) * 1024 + lane * 16);
+  u32x4 w[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) w[cb] = *reinterpret_cast<const u32x4*>(cslot + (wave * NCB + cb) * 1024 + lane * 16);
   bf16x8 fa[2][NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
     fa[0][rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(rb * 32 + l32, 4 * half)));
   // each column block's unit and the factor that moves acc into it
-  float r[2];
-  uint32_t nib[2], magic[2];
+  float r[NCB];
+  uint32_t nib[NCB], magic[NCB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     const float sf = 16.0f * __uint_as_float(ODD ? (sb.s[cb] & 0xFFFF0000u) : (sb.s[cb] << 16));
     const bool nz = __builtin_fabsf(sf) >= kMinUnit;
     const float Un = nz ? sf : U[cb];
@@ -359,16 +378,18 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
         fa[(l + 1) & 1][rb] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(slot + a_chunk_off(rb * 32 + l32, 4 * half + l + 1)));
     }
-    const bf16x8 bq0 = unpack_word(w0[l], nib[0], magic[0]);
-    const bf16x8 bq1 = unpack_word(w1[l], nib[1], magic[1]);
+    bf16x8 bq[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) bq[cb] = unpack_word(w[cb][l], nib[cb], magic[cb]);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       if (l == 0) {
-        scale_acc(acc[rb][0], r[0]);
-        scale_acc(acc[rb][1], r[1]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) scale_acc(acc[rb][cb], r[cb]);
       }
-      acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[l & 1][rb], bq0, acc[rb][0], 0, 0, 0);
-      acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[l & 1][rb], bq1, acc[rb][1], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[l & 1][rb], bq[cb], acc[rb][cb], 0, 0, 0);
     }
   }
   if (ODD) {
@@ -377,18 +398,18 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
     // is group g, which this step's top wait and barrier already covered; the
     // small ring has later loads outstanding.
     if constexpr (SR) {
-      // issued after the side table: step g-1's group (7 loads) and step g's
-      // activations (1), while g + 4 < G
+      // issued after the side table: step g-1's group (1 + 3 NCB loads) and
+      // step g's activations (1), while g + 4 < G
       if (g + R::DIST < G)
-        wait_vm<8>();
+        wait_vm<2 + 3 * NCB>();
       else
         wait_vm<0>();
       __builtin_amdgcn_s_barrier();
     }
     const int sh = half << 4;
-    bf16x8 bv[2];
+    bf16x8 bv[NCB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       const float sg = __uint_as_float(((sb.s[cb] >> sh) & 0xFFFFu) << 16);
       const float bg = __uint_as_float(((sb.b[cb] >> sh) & 0xFFFFu) << 16);
       const float c = (bg - 16.0f * sg) * __builtin_amdgcn_rcpf(U[cb]);
@@ -403,44 +424,129 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
     for (int rb = 0; rb < NRB; ++rb) {
       const bf16x8 xa =
           __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xps + (rb * 32 + l32) * 32 + half * 16));
-      acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv[0], acc[rb][0], 0, 0, 0);
-      acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv[1], acc[rb][1], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bv[cb], acc[rb][cb], 0, 0, 0);
     }
   }
 }
 
 // G is even (K is a multiple of 128). RM: the ring geometry (small tiles:
 // NRB == 1; merged tiles: NRB == 5).
-template <int NRB, int RM>
+template <int NRB, int RM, int NCB = 2>
 __device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, int G, int wave, int lane,
                                           SBPair& sb, f32x16 (&acc)[5][2]) {
-  using R = Ring<RM>;
+  using R = Ring<RM, NCB>;
   // groups 0 .. DIST-1 (those that exist) before the first step
-  issue_group<0, RM>(st, ring, 0, wave);
-  if constexpr (R::DIST >= 2) issue_group<1, RM>(st, ring, 1, wave);
+  issue_group<0, RM, NCB>(st, ring, 0, wave);
+  if constexpr (R::DIST >= 2) issue_group<1, RM, NCB>(st, ring, 1, wave);
   if constexpr (R::SR) {
-    if (2 < G) issue_group<0, RM>(st, ring, 2, wave);
-    if (3 < G) issue_group<1, RM>(st, ring, 3, wave);
+    if (2 < G) issue_group<0, RM, NCB>(st, ring, 2, wave);
+    if (3 < G) issue_group<1, RM, NCB>(st, ring, 3, wave);
   }
   float U[2] = {1.0f, 1.0f};   // any normal value: acc is zero until the first nonzero scale
   // unrolled by 4 so the group parity and the pair parity are constants
   for (int g = 0; g < G; g += 4) {
-    loop_step<NRB, 0, RM>(st, ring, g, G, wave, lane, sb, U, acc);
-    loop_step<NRB, 1, RM>(st, ring, g + 1, G, wave, lane, sb, U, acc);
+    loop_step<NRB, 0, RM, NCB>(st, ring, g, G, wave, lane, sb, U, acc);
+    loop_step<NRB, 1, RM, NCB>(st, ring, g + 1, G, wave, lane, sb, U, acc);
     if (g + 2 < G) {
-      loop_step<NRB, 2, RM>(st, ring, g + 2, G, wave, lane, sb, U, acc);
-      loop_step<NRB, 3, RM>(st, ring, g + 3, G, wave, lane, sb, U, acc);
+      loop_step<NRB, 2, RM, NCB>(st, ring, g + 2, G, wave, lane, sb, U, acc);
+      loop_step<NRB, 3, RM, NCB>(st, ring, g + 3, G, wave, lane, sb, U, acc);
     }
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    scale_acc(acc[rb][0], U[0]);
-    scale_acc(acc[rb][1], U[1]);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) scale_acc(acc[rb][cb], U[cb]);
   }
 }
 
+// Epilogue of a one-column-block workgroup (tile of at most 32 rows; acc is
+// the wave's 32 x 32 block). F32: each wave stages its block in LDS (row
+// stride 36 floats) and writes 128-byte row segments with non-temporal stores.
+// SwiGLU: the gate waves (0, 1) leave their fp32 values in LDS, the up waves
+// (2, 3) form h = silu(gate) * up in bf16, and one wave writes the 32 x 64 h
+// block (and, internal layout, the group-sum entry of its one 64-wide group).
 template <int EPI>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
+__device__ __forceinline__ void epilogue_ncb1(const GemmArgs& a, const TileInfo& ti, int nt, int nrows, bool live,
+                                              int cbase, int wave, int lane, const f32x16& acc, uint8_t* ring) {
+  const int l32 = lane & 31, half = lane >> 5;
+  if constexpr (EPI == kEpiF32) {
+    float* out = reinterpret_cast<float*>(a.out);
+    float* stg = reinterpret_cast<float*>(ring) + wave * (32 * kF32StageStride);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * half + (r & 3)) * kF32StageStride + l32] = acc[r];
+    __builtin_amdgcn_wave_barrier();
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = i * 8 + (lane >> 3), c4 = (lane & 7) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + m * kF32StageStride + c4);
+        if (m < nrows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + size_t(ti.r0 + m) * a.N + cbase + c4));
+      }
+    }
+  } else {
+    constexpr int kGs = 65;                                     // gate row stride (floats)
+    float* gs = reinterpret_cast<float*>(ring);                 // [32][65] gate values
+    uint16_t* hs = reinterpret_cast<uint16_t*>(ring + 32 * kGs * 4);   // [32][64] h
+    const int col = (wave & 1) * 32 + l32;
+    if (wave < 2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gs[(8 * (r >> 2) + 4 * half + (r & 3)) * kGs + col] = acc[r];
+    }
+    __syncthreads();
+    if (wave >= 2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+        const float gv = gs[m * kGs + col];
+        const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[r];
+        hs[m * 64 + col] = uint16_t(f32_to_bf16_rne(hv));
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // unit u: row u/2, half u%2 = 32 columns; the two halves of a row are
+      // the 64-wide group of h this workgroup produced (adjacent lanes)
+      const int u = threadIdx.x;
+      const int srow = u >> 1, sq = u & 1;
+      const int row = ti.r0 + srow;
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+      u32x4 ch[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ch[i] = *reinterpret_cast<const u32x4*>(hs + srow * 64 + sq * 32 + 8 * i);
+      if constexpr (EPI == kEpiSwigluInternal) {
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += chunk_sum_f64(ch[i]);
+        const float X = float(part + __shfl_xor(part, 1, kWave));
+        if (srow < nrows) {
+          uint16_t* dst = out + size_t(row) * a.N + nt * 64 + sq * 32;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = permute_chunk(ch[i]);
+          if (sq == 0) {
+            uint16_t h, m, l;
+            split3_bf16(X, h, m, l);
+            const u32x4 e = {uint32_t(h) | (uint32_t(m) << 16), uint32_t(l) | (uint32_t(h) << 16),
+                             uint32_t(m) | (uint32_t(h) << 16), 0u};
+            *reinterpret_cast<u32x4*>(a.out_part + size_t(row) * xpart_cols(a.N) + 8 * nt) = e;
+          }
+        }
+      } else {
+        if (srow < nrows && nt * 64 + sq * 32 < a.N) {
+          uint16_t* dst = out + size_t(row) * a.N + nt * 64 + sq * 32;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 8 * i) = ch[i];
+        }
+      }
+    }
+  }
+}
+
+// NCB = 2: every tile geometry, two workgroups per CU. NCB = 1: launches whose
+// tiles all hold at most 32 rows (the host guarantees it), three per CU.
+template <int EPI, int NCB>
+__global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 3 : 2) void gemm_q4_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K;
   const int G = K / kGroup;
@@ -473,12 +579,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // ---- this wave's two 32-column blocks -------------------------------------
+  // ---- this wave's 32-column blocks (two, or one with NCB = 1) -----------------
   // A block past the last column (N not a multiple of the workgroup's width)
   // streams the last 32 columns again and stores nothing.
   int cbase[2];
   const QStack* mat[2];
-  if constexpr (EPI == kEpiF32) {
+  if constexpr (NCB == 1) {
+    // F32: wave w = columns 32w..32w+31 of the workgroup's 128; SwiGLU: waves
+    // 0, 1 = gate columns 32w.. of the workgroup's 64 h columns, waves 2, 3 =
+    // the same up columns (gate and up meet in LDS after the loop)
+    if constexpr (EPI == kEpiF32) {
+      cbase[0] = nt * 128 + wave * 32;
+      mat[0] = &a.w0[stack];
+    } else {
+      cbase[0] = nt * 64 + (wave & 1) * 32;
+      mat[0] = wave < 2 ? &a.w0[stack] : &a.w1[stack];
+    }
+    cbase[1] = cbase[0];
+    mat[1] = mat[0];
+  } else if constexpr (EPI == kEpiF32) {
     cbase[0] = nt * 256 + wave * 64;
     cbase[1] = cbase[0] + 32;
     mat[0] = mat[1] = &a.w0[stack];
@@ -547,14 +666,22 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   f32x16 acc[5][2];
 #pragma unroll
   for (int rb = 0; rb < 5; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
-  switch (nrb) {
-    case 1: main_loop<1, kRingSmall>(st, ring, G, wave, lane, sb, acc); break;
-    case 2: main_loop<2, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
-    case 3: main_loop<3, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
-    case 4: main_loop<4, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
-    default: main_loop<5, kRingMerged>(st, ring, G, wave, lane, sb, acc); break;   // merged tiles only
+  if constexpr (NCB == 1) {
+    main_loop<1, kRingSmall, 1>(st, ring, G, wave, lane, sb, acc);   // every tile: at most 32 rows
+  } else {
+    switch (nrb) {
+      case 1: main_loop<1, kRingSmall>(st, ring, G, wave, lane, sb, acc); break;
+      case 2: main_loop<2, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
+      case 3: main_loop<3, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
+      case 4: main_loop<4, kRingFull>(st, ring, G, wave, lane, sb, acc); break;
+      default: main_loop<5, kRingMerged>(st, ring, G, wave, lane, sb, acc); break;   // merged tiles only
+    }
   }
   __syncthreads();   // every wave is done with the rings
+  if constexpr (NCB == 1) {
+    epilogue_ncb1<EPI>(a, ti, nt, nrows, live[0], cbase[0], wave, lane, acc[0][0], ring);
+    return;
+  }
 
   // ---- epilogues ------------------------------------------------------------
   if constexpr (EPI == kEpiF32) {
@@ -659,22 +786,24 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_q4_kernel(GemmArgs a) {
   }
 }
 
-hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream) {
+hipError_t launch_gemm(const GemmArgs& ga, int epilogue, int max_row_tiles, hipStream_t stream, bool one_block) {
   // 8 chunks of at most ceil(max_row_tiles / 8) tiles, NT column slices each
   const dim3 grid(8u * unsigned(ceil_div(max_row_tiles, 8)) * unsigned(ga.NT));
   if (grid.x == 0) return hipSuccess;
-  const size_t lds = gemm_lds_bytes(ga.K);
+  const size_t lds = gemm_lds_bytes(ga.K, one_block ? 1 : 2);
+#define MOE_GEMM_LAUNCH(E)                                                                        \
+  do {                                                                                            \
+    if (one_block)                                                                                \
+      hipLaunchKernelGGL((gemm_q4_kernel<E, 1>), grid, dim3(kGemmThreads), lds, stream, ga);      \
+    else                                                                                          \
+      hipLaunchKernelGGL((gemm_q4_kernel<E, 2>), grid, dim3(kGemmThreads), lds, stream, ga);      \
+  } while (0)
   switch (epilogue) {
-    case kEpiF32:
-      hipLaunchKernelGGL(gemm_q4_kernel<kEpiF32>, grid, dim3(kGemmThreads), lds, stream, ga);
-      break;
-    case kEpiSwigluNatural:
-      hipLaunchKernelGGL(gemm_q4_kernel<kEpiSwigluNatural>, grid, dim3(kGemmThreads), lds, stream, ga);
-      break;
-    default:
-      hipLaunchKernelGGL(gemm_q4_kernel<kEpiSwigluInternal>, grid, dim3(kGemmThreads), lds, stream, ga);
-      break;
+    case kEpiF32: MOE_GEMM_LAUNCH(kEpiF32); break;
+    case kEpiSwigluNatural: MOE_GEMM_LAUNCH(kEpiSwigluNatural); break;
+    default: MOE_GEMM_LAUNCH(kEpiSwigluInternal); break;
   }
+#undef MOE_GEMM_LAUNCH
   return hipGetLastError();
 }
 

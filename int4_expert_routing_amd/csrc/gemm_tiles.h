@@ -20,8 +20,8 @@ struct TileInfo {
 __device__ __forceinline__ bool tile_info(const GemmArgs& a, int tile, TileInfo& ti) {
   if (tile < a.n_shared_tiles) {
     ti.e = a.E;
-    ti.r0 = a.routed_rows + tile * kBlockRows;
-    ti.r1 = min(ti.r0 + kBlockRows, a.routed_rows + a.shared_rows);
+    ti.r0 = a.routed_rows + tile * a.sh_bm;
+    ti.r1 = min(ti.r0 + a.sh_bm, a.routed_rows + a.shared_rows);
     return true;
   }
   const int i = tile - a.n_shared_tiles;

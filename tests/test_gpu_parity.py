@@ -486,7 +486,8 @@ def test_layer_reduction_sizes_above_2048(dev, T, H, I):
 @pytest.mark.parametrize("bm", [32, 64, 128])
 @pytest.mark.parametrize("T,E,k", [(300, 16, 2), (700, 64, 8), (6, 16, 2)])
 def test_layer_routed_tile_heights(dev, bm, T, E, k):
-    # routed tiles of 32, 64 or 128 rows (the shared expert keeps 128-row tiles)
+    # routed tiles of 32, 64 or 128 rows (the shared expert: 32-row tiles in the
+    # one-column-block launches of bm = 32, else 128-row tiles)
     print(f"layer block_rows={bm} T={T} E={E} k={k}", flush=True)
     inp = make_layer(T, 256, 128, E, k, seed=bm + T, bias_mode="random")
     g = run_layer(dev, inp, block_rows=bm)
@@ -494,6 +495,24 @@ def test_layer_routed_tile_heights(dev, bm, T, E, k):
     if bm != 128:
         ref = run_layer(dev, inp, block_rows=128)
         assert np.array_equal(g["ids"], ref["ids"])
+
+
+# 32-row tiles run the grouped GEMMs as one-column-block launches (three
+# workgroups per CU, gate and up meeting in LDS); 128-row tiles as two-block
+# launches. Each output element is the same chain of operations either way,
+# so the two agree bit for bit, and both match the oracle: shared tiles of 32
+# rows with a ragged last one, experts spread over several 32-row tiles (Zipf),
+# reduction lengths with 2 to 32 groups.
+@pytest.mark.parametrize("T,H,I,E,k,zipf", [(300, 512, 256, 32, 4, None), (161, 256, 128, 8, 2, 1.2),
+                                            (97, 2048, 512, 64, 8, None), (40, 128, 1024, 16, 2, None)])
+def test_layer_one_block_launches_match_two_block(dev, T, H, I, E, k, zipf):
+    print(f"layer one-block vs two-block T={T} H={H} I={I} E={E} k={k} zipf={zipf}", flush=True)
+    inp = resample_close_calls(make_layer(T, H, I, E, k, seed=70 + T, bias_mode="random", zipf=zipf))
+    g32 = run_layer(dev, inp, block_rows=32)
+    g128 = run_layer(dev, inp, block_rows=128)
+    assert np.array_equal(g32["ids"], g128["ids"])
+    assert np.array_equal(g32["y"], g128["y"]), "32-row and 128-row tiles give different bits"
+    check_layer(inp, g32)
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [(64, 256, 128, 16, 2), (1, 256, 256, 16, 2), (3, 512, 256, 16, 4),
