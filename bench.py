@@ -264,7 +264,7 @@ def quantize_measure(ops, torch, dev, n=256, N=512, K=2048, reps=10):
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_q4_swiglu_prefill4096_traffic.txt")
 KERNEL_SOURCES = ("int4_expert_routing_amd/csrc/gemm_q4.hip", "int4_expert_routing_amd/csrc/gemm_tiles.h",
                   "int4_expert_routing_amd/csrc/gemm_args.h", "int4_expert_routing_amd/csrc/moe_common.h")
-GEMM_KERNEL_NAME = "gemm_q4_kernel<2>"
+GEMM_KERNEL_NAME = "gemm_q4_kernel<2, 2>"
 
 
 def kernel_source_hash():
@@ -378,6 +378,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-quantize", action="store_true")
     p.add_argument("--no-prefill-sweep", action="store_true")
+    p.add_argument("--no-side-stream", action="store_true",
+                   help="skip the timing of the calls with the shared expert on a second stream")
     p.add_argument("--layout", choices=("prepacked", "canonical"), default="prepacked",
                    help="weight layout of every timed layer (prepacked once, before timing)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -532,20 +534,22 @@ def main():
 
     # the same calls with the shared expert's GEMMs on a second stream (the
     # moe_layer_forward_ex side-stream option), reported beside the value
-    side = ops.MoELayer(w, k, T, side_stream=True)
-    y_side = torch.empty_like(y)
-    side_call = lambda: side(x, y=y_side)
-    side_call()
-    torch.cuda.synchronize()
-    ramp(torch, side_call)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
+    side_ms_per_step, side_matches = None, None
+    if not args.no_side_stream:
+        side = ops.MoELayer(w, k, T, side_stream=True)
+        y_side = torch.empty_like(y)
+        side_call = lambda: side(x, y=y_side)
         side_call()
-    torch.cuda.synchronize()
-    side_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    side_matches = bool(torch.equal(y_side, y_ref))
-    del side
+        torch.cuda.synchronize()
+        ramp(torch, side_call)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            side_call()
+        torch.cuda.synchronize()
+        side_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        side_matches = bool(torch.equal(y_side, y_ref))
+        del side
     gpu_ms = float(np.mean(step_ms))
     names = ["prep", "route", "gate_up_gemm", "down_gemm", "combine"]
     flops = layer_flops(T, H, I, E, k)
