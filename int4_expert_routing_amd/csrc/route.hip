@@ -527,6 +527,81 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(ScatterArg
   }
 }
 
+// Scan and scatter in one launch, for calls of at most kFusedScanBlocks
+// routing blocks: workgroup b < nblk sums every block's count of expert
+// e = thread (all blocks: the expert's total; blocks before b: the base of
+// block b) from the block counts, scans the totals as route_scatter_kernel
+// does, and places its block's pairs; workgroup 0 also writes counts,
+// offsets and the block map. Every workgroup reads the whole count matrix
+// (nblk x E words, from L2), which replaces the scan launch and its block
+// bases. Workgroups past nblk run the activation preparation.
+constexpr int kFusedScanBlocks = 64;
+__global__ __launch_bounds__(kRouteThreads) void route_scan_scatter_kernel(ScatterArgs a, ScanArgs sa,
+                                                                           PrepArgs prep) {
+  __shared__ int32_t off_s[kMaxExperts];
+  __shared__ int32_t base_s[kMaxExperts];
+  __shared__ int32_t scan_tot[2 * (kRouteThreads / kWave)];
+  const int blk = blockIdx.x;
+  if (blk >= sa.nblk) {   // uniform
+    prep_rows_block(prep, long(blk) - sa.nblk);
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  int c = 0, base = 0;
+  if (tid < E) {
+    // block order, so the block base is the running sum when block blk is reached
+    int b = 0;
+    for (; b + 8 <= sa.nblk; b += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = sa.block_counts[size_t(b + i) * E + tid];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        base += (b + i < blk) ? v[i] : 0;
+        c += v[i];
+      }
+    }
+    for (; b < sa.nblk; ++b) {
+      const int32_t v = sa.block_counts[size_t(b) * E + tid];
+      base += b < blk ? v : 0;
+      c += v;
+    }
+  }
+  const int ntl = ceil_div(c, sa.block_rows);
+  int32_t oc = c, tc = ntl;   // inclusive scans of counts and tile counts
+  block_scan2(oc, tc, scan_tot);
+  if (tid < E) {
+    off_s[tid] = oc - c;
+    base_s[tid] = base;
+  }
+  if (blk == 0 && tid < E) {
+    const int o = oc - c;
+    sa.counts[tid] = c;
+    sa.offsets[tid] = o;
+    const int first = tc - ntl;
+    for (int i = 0; i < ntl; ++i) {
+      sa.tile_map[2 * (first + i)] = tid;
+      sa.tile_map[2 * (first + i) + 1] = o + i * sa.block_rows;
+    }
+    if (tid == E - 1) {
+      sa.offsets[E] = oc;
+      *sa.num_tiles = tc;
+    }
+  }
+  __syncthreads();
+  const int t0 = blk * kRouteTokens;
+  const int nt = min(kRouteTokens, a.T - t0);
+  const int npairs = nt * a.k;
+  for (int p = tid; p < npairs; p += kRouteThreads) {
+    const size_t f = size_t(t0) * a.k + p;
+    const int e = a.topk_ids[f];
+    const int pos = off_s[e] + base_s[e] + a.rank_in_block[f];
+    a.sorted_rows[pos] = int32_t(f);
+    a.row_of_pair[f] = pos;
+  }
+}
+
 int router_splits(int T, int H, int E) {
   // Up to about a thousand tokens the single-wave 32 x 64 tiles are few (16 x 4
   // = 64 workgroups at T = 512), so K is split 8 ways. Above that the 64 x 128
@@ -609,9 +684,14 @@ hipError_t launch_route(const RouteArgs& ra, const ScanArgs& sa, const ScatterAr
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || rb.finish) return err;
   const long nprep = prep ? prep_rows_blocks(prep->rows, prep->K) : 0;
+  if (prep_done) *prep_done = prep != nullptr;
+  if (nblk <= kFusedScanBlocks) {
+    hipLaunchKernelGGL(route_scan_scatter_kernel, dim3(unsigned(nblk + nprep)), dim3(kRouteThreads), 0, stream, ca,
+                       sa, prep ? *prep : PrepArgs{});
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(route_scan_kernel, dim3(unsigned(ceil_div(ra.E, kScanExperts) + nprep)), dim3(kRouteThreads), 0,
                      stream, sa, prep ? *prep : PrepArgs{});
-  if (prep_done) *prep_done = prep != nullptr;
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kRouteThreads), 0, stream, ca, sa);
