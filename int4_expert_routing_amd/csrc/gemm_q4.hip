@@ -68,8 +68,8 @@ constexpr int kXpSlotBytes = 4096;       // side table of one group pair: 128 ro
 constexpr int kSbWaveBytes = 256;        // scale/bias words of one group pair, one column block: 64 words
 
 // LDS ring geometry. Group g's activation tile lives in A slot g % A_RING and
-// its codes in code slot g % C_RING; groups are loaded DIST steps ahead. The
-// scale/bias words of pair p live in slot p % SBS.
+// its codes in code slot g % C_RING; activations are loaded DA steps ahead and
+// codes DC steps ahead. The scale/bias words of pair p live in slot p % SBS.
 //   full tiles (33..128 rows): 2 slots, each 128 activation rows then the
 //     codes; group g issued at step g - 1 into the slot group g - 2 used (one
 //     step of a full tile covers the round trip: three slots, two groups
@@ -90,28 +90,34 @@ constexpr int kSbWaveBytes = 256;        // scale/bias words of one group pair, 
 //     rows costs ~35-45% of a full one).
 //   one-column-block launches (NCB = 1: all tiles of at most 32 rows, each
 //     wave one 32-column block): the small geometry with half the code
-//     bytes per group, 51 KB, so that three workgroups fit per CU.
+//     bytes per group and the activations (L2-resident: the 32 rows are read
+//     by every column slice of the tile) only two groups ahead, 40 KB, so
+//     that four workgroups fit per CU.
 enum RingMode { kRingFull = 0, kRingSmall = 1, kRingMerged = 2 };
 template <int RM, int NCB = 2>
 struct Ring {
   static constexpr bool SR = RM == kRingSmall;
-  static constexpr int DIST = SR ? 4 : 1;
+  static constexpr int DC = SR ? 4 : 1;                              // codes: groups ahead (even when SR)
+  static constexpr int DA = SR ? (NCB == 1 ? 2 : 4) : 1;             // activations: groups ahead, DA <= DC
   static constexpr int AROWS = SR ? 32 : RM == kRingMerged ? 160 : 128;   // activation rows per slot
   static constexpr int ALOADS = AROWS / 32;               // activation loads per wave and group (8 rows each)
-  static constexpr int A_RING = DIST + 1;
-  static constexpr int C_RING = SR ? DIST + 2 : DIST + 1;
+  static constexpr int A_RING = DA + 1;
+  static constexpr int C_RING = SR ? DC + 2 : DC + 1;
   static constexpr int CODES = 4 * NCB * 1024;           // 4 waves x NCB column blocks x 64 lanes x 16 B
   static constexpr int A_SLOT = SR ? AROWS * 128 : AROWS * 128 + CODES;
   static constexpr int C_BASE = SR ? A_RING * A_SLOT : AROWS * 128;
   static constexpr int C_SLOT = SR ? CODES : A_SLOT;
   static constexpr int XP = SR ? C_BASE + C_RING * C_SLOT : A_RING * A_SLOT;
-  // side-table slot of one pair: 32 B per row; merged tiles load rows
-  // 128..159 with a second load per wave (every wave writes the same bytes)
+  // side-table slot of one pair: 32 B per row. Small tiles: rows 0..31, which
+  // every wave loads into the same 1 KB (the same bytes); merged tiles load
+  // rows 128..159 with a second load per wave (again the same bytes)
   static constexpr int XLOADS = AROWS > 128 ? 2 : 1;
-  static constexpr int SB = XP + XLOADS * kXpSlotBytes;
-  static constexpr int SBS = SR ? 3 : 2;               // pair p's words are read at step 2p, loaded at 2p - DIST
+  static constexpr int XP_BYTES = SR ? 1024 : XLOADS * kXpSlotBytes;
+  static constexpr int SB = XP + XP_BYTES;
+  static constexpr int SBS = SR ? DC / 2 + 1 : 2;      // pair p's words are read at step 2p, loaded at 2p - DC
   static constexpr int SB_SLOT = 4 * NCB * kSbWaveBytes;
   static constexpr int END = SB + SBS * SB_SLOT;
+  static_assert(!SR || (DC % 2 == 0 && DA >= 1 && DA <= DC), "small ring distances");
 };
 constexpr int kLdsLoopFS = Ring<kRingFull>::END > Ring<kRingSmall>::END ? Ring<kRingFull>::END : Ring<kRingSmall>::END;
 constexpr int kLdsLoop = kLdsLoopFS > Ring<kRingMerged>::END ? kLdsLoopFS : Ring<kRingMerged>::END;
@@ -160,8 +166,8 @@ size_t gemm_lds_bytes(int /*K*/, int ncb = 2) {
     // 32 x 36 fp32 staging blocks
     constexpr size_t ring = size_t(Ring<kRingSmall, 1>::END);
     constexpr size_t epi = 32 * 65 * 4 + 32 * 64 * 2;
-    static_assert(ring <= 160 * 1024 / 3 && epi <= ring && size_t(kGemmWaves) * 32 * kF32StageStride * 4 <= ring,
-                  "three workgroups per CU");
+    static_assert(ring <= 160 * 1024 / 4 && epi <= ring && size_t(kGemmWaves) * 32 * kF32StageStride * 4 <= ring,
+                  "four workgroups per CU");
     return ring;
   }
   const size_t swiglu = size_t(kMaxRows) * 128 * 2;
@@ -202,27 +208,42 @@ __device__ __forceinline__ void issue_codes(const Stream& st, uint8_t* ring, int
   if constexpr (NCB == 2) buffer_to_lds16(st.rb1, cs + (wave * 2 + 1) * 1024, st.vb, g * st.gstride);
 }
 
-// Loads of group g (in this order, which the waits count on):
-//   full ring: activations and codes of g; for even g the scale/bias words of
-//     pair g/2;
-//   small ring, even g: activations and codes of g, the scale/bias words of
-//     pair g/2, then the codes of g+1; odd g: activations of g.
-template <int ODD, int RM, int NCB>
-__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave) {
+// Activation loads of group g (ALOADS per wave).
+template <int RM, int NCB>
+__device__ __forceinline__ void issue_act(const Stream& st, uint8_t* ring, int g, int wave) {
   using R = Ring<RM, NCB>;
-  constexpr bool SR = R::SR;
   uint8_t* slot = ring + (g % R::A_RING) * R::A_SLOT;
 #pragma unroll
   for (int i = 0; i < R::ALOADS; ++i)
     buffer_to_lds16(st.ra, slot + (wave * R::ALOADS + i) * 1024, st.va[i], g * (kGroup * 2));
-  if (!SR || !ODD) issue_codes<RM, NCB>(st, ring, g, wave);
-  if (!ODD) {
-    const int p = g >> 1;
-    uint8_t* sbs = ring + R::SB + (p % R::SBS) * R::SB_SLOT + wave * (NCB * kSbWaveBytes);
-    global_to_lds4(st.sbp[0] + p * st.sbstride, sbs);
-    if constexpr (NCB == 2) global_to_lds4(st.sbp[1] + p * st.sbstride, sbs + kSbWaveBytes);
-    if (SR) issue_codes<RM, NCB>(st, ring, g + 1, wave);   // g + 1 < G: G is even
-  }
+}
+
+// Scale/bias words of pair p (NCB loads per wave).
+template <int RM, int NCB>
+__device__ __forceinline__ void issue_sb(const Stream& st, uint8_t* ring, int p, int wave) {
+  using R = Ring<RM, NCB>;
+  uint8_t* sbs = ring + R::SB + (p % R::SBS) * R::SB_SLOT + wave * (NCB * kSbWaveBytes);
+  global_to_lds4(st.sbp[0] + p * st.sbstride, sbs);
+  if constexpr (NCB == 2) global_to_lds4(st.sbp[1] + p * st.sbstride, sbs + kSbWaveBytes);
+}
+
+// Loads of one step's lookahead, in this order (which the waits count on):
+//   full and merged rings (g = step + 1): activations and codes of g; for
+//     even g the scale/bias words of pair g/2 (issue_group);
+//   small ring (step j): activations of j + DA; at even j the codes of
+//     j + DC, the scale/bias words of pair (j + DC)/2 and the codes of
+//     j + DC + 1 (issue_codepair): both groups of a pair back to back.
+template <int ODD, int RM, int NCB>
+__device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int g, int wave) {
+  issue_act<RM, NCB>(st, ring, g, wave);
+  issue_codes<RM, NCB>(st, ring, g, wave);
+  if (!ODD) issue_sb<RM, NCB>(st, ring, g >> 1, wave);
+}
+template <int RM, int NCB>
+__device__ __forceinline__ void issue_codepair(const Stream& st, uint8_t* ring, int g, int wave) {
+  issue_codes<RM, NCB>(st, ring, g, wave);
+  issue_sb<RM, NCB>(st, ring, g >> 1, wave);
+  issue_codes<RM, NCB>(st, ring, g + 1, wave);   // g + 1 < G: G is even
 }
 
 // Side-table entries of group pair p (groups 2p, 2p+1; every wave loads 32
@@ -231,7 +252,7 @@ __device__ __forceinline__ void issue_group(const Stream& st, uint8_t* ring, int
 template <int RM, int NCB>
 __device__ __forceinline__ void issue_xp(const Stream& st, uint8_t* ring, int p, int wave) {
   using R = Ring<RM, NCB>;
-  buffer_to_lds16(st.rxp, ring + R::XP + wave * 1024, st.vxp, p * 32);
+  buffer_to_lds16(st.rxp, ring + R::XP + (R::SR ? 0 : wave * 1024), st.vxp, p * 32);
   if constexpr (R::XLOADS > 1) buffer_to_lds16(st.rxp, ring + R::XP + kXpSlotBytes, st.vxp2, p * 32);
 }
 
@@ -242,14 +263,35 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(kWaitVm0 | (N & 15) | ((N >> 4) << 14));
 }
 
+// The same with the count known only at run time (uniform): exact up to 30;
+// a larger count waits until 31 are left, which waits for more loads than
+// needed, never for fewer.
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  switch (n < 0 ? 0 : n) {
+#define MOE_WAIT_CASE(N) \
+  case N:                \
+    wait_vm<N>();        \
+    break;
+    MOE_WAIT_CASE(0) MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
+    MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10) MOE_WAIT_CASE(11)
+    MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15) MOE_WAIT_CASE(16) MOE_WAIT_CASE(17)
+    MOE_WAIT_CASE(18) MOE_WAIT_CASE(19) MOE_WAIT_CASE(20) MOE_WAIT_CASE(21) MOE_WAIT_CASE(22) MOE_WAIT_CASE(23)
+    MOE_WAIT_CASE(24) MOE_WAIT_CASE(25) MOE_WAIT_CASE(26) MOE_WAIT_CASE(27) MOE_WAIT_CASE(28) MOE_WAIT_CASE(29)
+    MOE_WAIT_CASE(30)
+#undef MOE_WAIT_CASE
+    default: wait_vm<31>(); break;
+  }
+}
+
 __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] *= r;
 }
 
 // Step g of the K loop (P4 = g % 4, a compile-time constant: group parity and
-// pair parity). Group g is in ring slot g % 3; group g+1 may still be landing;
-// group g+2 is issued into the slot that held group g-1.
+// pair parity). Group g is in activation slot g % A_RING and code slot
+// g % C_RING; the step's lookahead loads go into slots whose groups every wave
+// has finished (the barrier after the top wait orders them).
 //
 // One accumulator per (row block, column block), kept in units of U = 16 s of
 // the lane's column for the latest group with a nonzero scale: acc holds
@@ -265,63 +307,44 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float r) {
 // terms of 2^-24 relative.
 // Wait at the top of step g until this wave's loads that step g reads have
 // landed (activations and codes of group g; at even g the scale/bias words of
-// pair g/2). Issue order: the first DIST groups before the loop, then at every
-// step j the side table of pair j/2 (even j) followed by group j + DIST (see
-// issue_group). At most the loads issued after the last needed one may still
-// be outstanding:
+// pair g/2). Loads complete in issue order for the count, so at most the loads
+// issued after the last needed one may still be outstanding:
 //   full and merged rings (one group ahead): none (at step g-1 the side table
 //     was issued before group g);
-//   small ring (an even step issues 7 loads after its side table, an odd step
-//     1; G is even):
-//     even g: the codes of g+1 and the activations of g+1 (3), the side table
-//       of step g-2 (g >= 2), and groups g+2, g+3 (8) while g <= G-4;
-//     odd g: the side table of step g-3 (g >= 3), groups g+1, g+2 (7 + 1)
-//       while g <= G-3, the side table of step g-1, and groups g+3, g+4 (7,
-//       the activations of g+4 following at step g) while g <= G-5.
+//   small ring: step j issues the side table of pair j/2 (even j >= 0), the
+//     activations of j + DA and, at even j, the code pair of j + DC (3 NCB
+//     loads); the steps before the loop are j = -DC .. -1 without side
+//     tables. With DA < DC the last needed load is the activations of g
+//     (step g - DA); with DA == DC it is the pair's scale/bias words at even g
+//     (the codes of g + 1 follow them) and the activations at odd g.
+template <int RM, int NCB>
+__device__ __forceinline__ int sr_step_loads(int j, int G) {
+  using R = Ring<RM, NCB>;
+  const bool even = (j & 1) == 0;
+  return (even && j >= 0 ? 1 : 0) + (j + R::DA >= 0 && j + R::DA < G ? 1 : 0) +
+         (even && j + R::DC < G ? 3 * NCB : 0);
+}
+
+template <int RM, int NCB>
+__device__ __forceinline__ int sr_top_count(int g, int G) {
+  using R = Ring<RM, NCB>;
+  int n = 0;
+#pragma unroll
+  for (int d = R::DA - 1; d >= 1; --d) n += sr_step_loads<RM, NCB>(g - d, G);
+  if constexpr (R::DA < R::DC) {
+    if (((g - R::DA) & 1) == 0 && g - R::DA + R::DC < G) n += 3 * NCB;   // the code pair after them
+  } else {
+    if ((g & 1) == 0) n += NCB;
+  }
+  return n;
+}
+
 template <int ODD, int RM, int NCB>
 __device__ __forceinline__ void wait_group(int g, int G) {
-  using R = Ring<RM, NCB>;
-  constexpr bool SR = R::SR;
-  // small ring: an even group's issue is 1 + 3 NCB loads (activations, NCB
-  // code loads, NCB scale/bias loads, NCB code loads of the next group), an
-  // odd group's 1 (activations); with NCB = 2 the counts above
-  constexpr int EV = 1 + 3 * NCB;
-  if constexpr (!SR) {
-    // one group ahead: every load outstanding at the top of step g is group
-    // g's or the side table issued before it
+  if constexpr (!Ring<RM, NCB>::SR)
     wait_vm<0>();
-  } else if constexpr (ODD) {
-    const bool xp3 = g >= 3;
-    if (g <= G - 5) {
-      if (xp3)
-        wait_vm<2 * EV + 3>();
-      else
-        wait_vm<2 * EV + 2>();
-    } else if (g == G - 3) {
-      if (xp3)
-        wait_vm<EV + 3>();
-      else
-        wait_vm<EV + 2>();
-    } else {   // g == G - 1
-      if (xp3)
-        wait_vm<2>();
-      else
-        wait_vm<1>();
-    }
-  } else {
-    const bool xp2 = g >= 2;
-    if (g <= G - 4) {
-      if (xp2)
-        wait_vm<NCB + EV + 3>();
-      else
-        wait_vm<NCB + EV + 2>();
-    } else {   // g == G - 2
-      if (xp2)
-        wait_vm<NCB + 2>();
-      else
-        wait_vm<NCB + 1>();
-    }
-  }
+  else
+    wait_vm_dyn(sr_top_count<RM, NCB>(g, G));
 }
 
 template <int NRB, int P4, int RM, int NCB>
@@ -337,7 +360,12 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
   wait_group<ODD, RM, NCB>(g, G);
   __builtin_amdgcn_s_barrier();
   if (!ODD) issue_xp<RM, NCB>(st, ring, g >> 1, wave);
-  if (g + R::DIST < G) issue_group<(ODD + R::DIST) & 1, RM, NCB>(st, ring, g + R::DIST, wave);
+  if constexpr (SR) {
+    if (g + R::DA < G) issue_act<RM, NCB>(st, ring, g + R::DA, wave);
+    if (!ODD && g + R::DC < G) issue_codepair<RM, NCB>(st, ring, g + R::DC, wave);
+  } else if (g + R::DC < G) {
+    issue_group<(ODD + R::DC) & 1, RM, NCB>(st, ring, g + R::DC, wave);
+  }
   const uint8_t* slot = ring + (g % R::A_RING) * R::A_SLOT;
   const uint8_t* cslot = ring + R::C_BASE + (g % R::C_RING) * R::C_SLOT;
   if (!ODD) {
@@ -393,17 +421,14 @@ __device__ __forceinline__ void loop_step(const Stream& st, uint8_t* ring, int g
     }
   }
   if (ODD) {
-    // the side table of this pair was issued at step g-1 ahead of group
-    // g-1+DIST's loads: every wave waits for its part. One group ahead, that
-    // is group g, which this step's top wait and barrier already covered; the
-    // small ring has later loads outstanding.
+    // the side table of this pair was issued first at step g-1: every wave
+    // waits for its part. One group ahead, the next load was group g's, which
+    // this step's top wait and barrier already covered; the small ring has
+    // later loads outstanding.
     if constexpr (SR) {
-      // issued after the side table: step g-1's group (1 + 3 NCB loads) and
-      // step g's activations (1), while g + 4 < G
-      if (g + R::DIST < G)
-        wait_vm<2 + 3 * NCB>();
-      else
-        wait_vm<0>();
+      // issued after the side table: the rest of step g-1's loads and step
+      // g's
+      wait_vm_dyn(sr_step_loads<RM, NCB>(g - 1, G) - 1 + sr_step_loads<RM, NCB>(g, G));
       __builtin_amdgcn_s_barrier();
     }
     const int sh = half << 4;
@@ -437,12 +462,16 @@ template <int NRB, int RM, int NCB = 2>
 __device__ __forceinline__ void main_loop(const Stream& st, uint8_t* ring, int G, int wave, int lane,
                                           SBPair& sb, f32x16 (&acc)[5][2]) {
   using R = Ring<RM, NCB>;
-  // groups 0 .. DIST-1 (those that exist) before the first step
-  issue_group<0, RM, NCB>(st, ring, 0, wave);
-  if constexpr (R::DIST >= 2) issue_group<1, RM, NCB>(st, ring, 1, wave);
   if constexpr (R::SR) {
-    if (2 < G) issue_group<0, RM, NCB>(st, ring, 2, wave);
-    if (3 < G) issue_group<1, RM, NCB>(st, ring, 3, wave);
+    // steps j = -DC .. -1 issue what step j of the loop would, without side
+    // tables
+#pragma unroll
+    for (int j = -R::DC; j < 0; ++j) {
+      if (j + R::DA >= 0 && j + R::DA < G) issue_act<RM, NCB>(st, ring, j + R::DA, wave);
+      if ((j & 1) == 0 && j + R::DC < G) issue_codepair<RM, NCB>(st, ring, j + R::DC, wave);
+    }
+  } else {
+    issue_group<0, RM, NCB>(st, ring, 0, wave);   // group 0 before the first step
   }
   float U[2] = {1.0f, 1.0f};   // any normal value: acc is zero until the first nonzero scale
   // unrolled by 4 so the group parity and the pair parity are constants
@@ -544,9 +573,9 @@ __device__ __forceinline__ void epilogue_ncb1(const GemmArgs& a, const TileInfo&
 }
 
 // NCB = 2: every tile geometry, two workgroups per CU. NCB = 1: launches whose
-// tiles all hold at most 32 rows (the host guarantees it), three per CU.
+// tiles all hold at most 32 rows (the host guarantees it), four per CU.
 template <int EPI, int NCB>
-__global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 3 : 2) void gemm_q4_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 4 : 2) void gemm_q4_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K;
   const int G = K / kGroup;
@@ -647,7 +676,7 @@ __global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 3 : 2) void gemm_q4_kernel
       st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
     }
     // side-table load of wave w: row w*32 + lane/2, 16-byte half lane%2
-    const int mx = wave * 32 + (lane >> 1);
+    const int mx = (nrb == 1 ? 0 : wave * 32) + (lane >> 1);   // small tiles: rows 0..31 in every wave
     st.vxp = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KPx * 2) + uint32_t((lane & 1) * 16);
     st.vxp2 = uint32_t(src_row(a, ti.r0 + min(128 + (lane >> 1), nrows - 1))) * uint32_t(KPx * 2) +
               uint32_t((lane & 1) * 16);
