@@ -90,14 +90,16 @@ constexpr int kSbWaveBytes = 256;        // scale/bias words of one group pair, 
 //     rows costs ~35-45% of a full one).
 //   one-column-block launches (NCB = 1: all tiles of at most 32 rows, each
 //     wave one 32-column block): the small geometry with half the code
-//     bytes per group and the activations (L2-resident: the 32 rows are read
-//     by every column slice of the tile) only two groups ahead, 40 KB, so
-//     that four workgroups fit per CU.
+//     bytes per group, activations and codes two groups ahead (a code pair
+//     at every even step), 31 KB, so that five workgroups fit per CU: at this
+//     size more resident workgroups beat a deeper ring (T=512 layer, 32-row
+//     tiles: 3 per CU with 4 groups ahead ~166 us, 4 per CU with activations
+//     2 ahead ~158, 5 per CU ~151; 3 per CU with codes 6 ahead was slower).
 enum RingMode { kRingFull = 0, kRingSmall = 1, kRingMerged = 2 };
 template <int RM, int NCB = 2>
 struct Ring {
   static constexpr bool SR = RM == kRingSmall;
-  static constexpr int DC = SR ? 4 : 1;                              // codes: groups ahead (even when SR)
+  static constexpr int DC = SR ? (NCB == 1 ? 2 : 4) : 1;             // codes: groups ahead (even when SR)
   static constexpr int DA = SR ? (NCB == 1 ? 2 : 4) : 1;             // activations: groups ahead, DA <= DC
   static constexpr int AROWS = SR ? 32 : RM == kRingMerged ? 160 : 128;   // activation rows per slot
   static constexpr int ALOADS = AROWS / 32;               // activation loads per wave and group (8 rows each)
@@ -166,8 +168,8 @@ size_t gemm_lds_bytes(int /*K*/, int ncb = 2) {
     // 32 x 36 fp32 staging blocks
     constexpr size_t ring = size_t(Ring<kRingSmall, 1>::END);
     constexpr size_t epi = 32 * 65 * 4 + 32 * 64 * 2;
-    static_assert(ring <= 160 * 1024 / 4 && epi <= ring && size_t(kGemmWaves) * 32 * kF32StageStride * 4 <= ring,
-                  "four workgroups per CU");
+    static_assert(ring <= 160 * 1024 / 5 && epi <= ring && size_t(kGemmWaves) * 32 * kF32StageStride * 4 <= ring,
+                  "five workgroups per CU");
     return ring;
   }
   const size_t swiglu = size_t(kMaxRows) * 128 * 2;
@@ -573,9 +575,9 @@ __device__ __forceinline__ void epilogue_ncb1(const GemmArgs& a, const TileInfo&
 }
 
 // NCB = 2: every tile geometry, two workgroups per CU. NCB = 1: launches whose
-// tiles all hold at most 32 rows (the host guarantees it), four per CU.
+// tiles all hold at most 32 rows (the host guarantees it), five per CU.
 template <int EPI, int NCB>
-__global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 4 : 2) void gemm_q4_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 5 : 2) void gemm_q4_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K;
   const int G = K / kGroup;
