@@ -43,15 +43,16 @@ int64_t max_tiles_of(int64_t T, int64_t E, int64_t k, int64_t bm) {
 }
 
 // Routed tile height of a layer call: the caller's, else 128 rows, or 32 rows
-// when the experts average at most 24 rows (prefill calls of up to 768 tokens
+// when the experts average at most 48 rows (prefill calls of up to 1536 tokens
 // at E = 256, k = 8). With 32-row tiles every tile of the grouped GEMMs holds
 // at most 32 rows and they run as one-column-block launches (finer work items,
-// three workgroups per CU). Measured at H = 2048, I = 512, E = 256, k = 8
-// (layer µs, 32-row / 128-row tiles): T = 64 129 / 145, 256 155 / 177,
-// 512 166 / 187, 768 184 / 196, 1024 225 / 226, 1536 288 / 270.
+// five workgroups per CU). Measured at H = 2048, I = 512, E = 256, k = 8
+// (layer µs, 32-row / 128-row tiles): T = 256 149 / 192, 512 156 / 201,
+// 768 169 / 211, 1024 206 / 242, 1280 247 / 260, 1536 262 / 271,
+// 2048 316 / 295, 3072 436 / 353.
 int layer_bm(const moe_dims& d) {
   if (d.block_rows > 0) return d.block_rows;
-  if (d.T > kDecodeMaxRows && int64_t(d.T) * d.k <= int64_t(24) * d.E) return 32;
+  if (d.T > kDecodeMaxRows && int64_t(d.T) * d.k <= int64_t(48) * d.E) return 32;
   return kBlockRows;
 }
 

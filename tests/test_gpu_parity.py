@@ -497,14 +497,15 @@ def test_layer_routed_tile_heights(dev, bm, T, E, k):
         assert np.array_equal(g["ids"], ref["ids"])
 
 
-# 32-row tiles run the grouped GEMMs as one-column-block launches (three
+# 32-row tiles run the grouped GEMMs as one-column-block launches (five
 # workgroups per CU, gate and up meeting in LDS); 128-row tiles as two-block
 # launches. Each output element is the same chain of operations either way,
 # so the two agree bit for bit, and both match the oracle: shared tiles of 32
 # rows with a ragged last one, experts spread over several 32-row tiles (Zipf),
 # reduction lengths with 2 to 32 groups.
 @pytest.mark.parametrize("T,H,I,E,k,zipf", [(300, 512, 256, 32, 4, None), (161, 256, 128, 8, 2, 1.2),
-                                            (97, 2048, 512, 64, 8, None), (40, 128, 1024, 16, 2, None)])
+                                            (97, 2048, 512, 64, 8, None), (40, 128, 1024, 16, 2, None),
+                                            (1200, 2048, 512, 256, 8, None)])
 def test_layer_one_block_launches_match_two_block(dev, T, H, I, E, k, zipf):
     print(f"layer one-block vs two-block T={T} H={H} I={I} E={E} k={k} zipf={zipf}", flush=True)
     inp = resample_close_calls(make_layer(T, H, I, E, k, seed=70 + T, bias_mode="random", zipf=zipf))
