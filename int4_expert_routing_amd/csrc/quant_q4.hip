@@ -52,19 +52,35 @@ __device__ __forceinline__ void quantize_team(u32x4 v, bool ok, long team, int s
     // q = rint(fl((w - lo) / s)) without a full division per weight: t = (w - lo)
     // * rcp(s) is within 2^-18 of the correctly rounded quotient (rcp 1 ulp, one
     // rounding each; quotients are below 16), so rint(t) is the same integer
-    // unless t lies within 2^-16 of a half-integer. Those rare lanes, and
-    // scales outside [2^-100, 2^100] (reciprocal kept normal), take the IEEE
-    // division.
+    // unless t lies within 2^-16 of a half-integer. A lane with such a weight,
+    // or a scale outside [2^-100, 2^100] (reciprocal kept normal), takes the
+    // IEEE division for all 8 of its weights (for the others it gives the same
+    // integer, by the same bound).
+    // Fast path: t + 2^23 rounds t to the nearest integer, ties to even, so
+    // the low mantissa bits of the sum are rint(t); and rint(t) is in 0..15
+    // without a clamp there: d >= 0, and d <= hi - lo while s is at least
+    // (hi - lo)/15 less one bf16 rounding, so t < 15.1.
     const bool fast = sv >= 0x1p-100f && sv <= 0x1p100f;
     const float rs = __builtin_amdgcn_rcpf(sv);
+    float d[8];
+    uint32_t fw = 0;
+    bool near_half = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float d = x[i] - lo;
-      const float t = d * rs;
-      float r = __builtin_rintf(t);
-      if (!fast || __builtin_fabsf(t - __builtin_floorf(t) - 0.5f) < 0x1p-16f) r = __builtin_rintf(d / sv);
-      r = fminf(fmaxf(r, 0.0f), 15.0f);
-      word |= uint32_t(r) << (4 * i);
+      d[i] = x[i] - lo;
+      const float t = d[i] * rs;
+      const float a = t + 0x1p23f;
+      near_half |= __builtin_fabsf(t - (a - 0x1p23f)) > 0.5f - 0x1p-16f;
+      fw |= (__float_as_uint(a) & 0xFu) << (4 * i);
+    }
+    if (fast && !near_half) {
+      word = fw;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float r = fminf(fmaxf(__builtin_rintf(d[i] / sv), 0.0f), 15.0f);
+        word |= uint32_t(r) << (4 * i);
+      }
     }
   }
   if (!ok) return;
