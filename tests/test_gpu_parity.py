@@ -404,6 +404,30 @@ def test_layer_zero_tokens_is_a_noop(dev):
     assert y.shape == (0, 256)
 
 
+# Seeded random shapes across the supported range (H and I multiples of 128,
+# E from 8 to 256, k up to 8, 9 to ~1800 tokens, both bias modes, some with a
+# Zipf logit skew): the layer against the oracle, and the 32-row and 128-row
+# tile geometries (one-column-block and two-block launches) bit for bit.
+def test_layer_random_shapes(dev):
+    rng = np.random.default_rng(2024)
+    for case in range(30):
+        E = int(rng.choice([8, 16, 24, 64, 100, 256]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        H = int(rng.choice([128, 256, 384, 512, 1024, 2048]))
+        I = int(rng.choice([128, 256, 384, 512]))
+        T = int(rng.integers(9, 1800 if H * I <= 256 * 512 else 500))
+        bias_mode = str(rng.choice(["sym", "random"]))
+        zipf = None if rng.random() < 0.7 else 1.2
+        print(f"layer random case {case}: T={T} H={H} I={I} E={E} k={k} {bias_mode} zipf={zipf}", flush=True)
+        inp = resample_close_calls(make_layer(T, H, I, E, k, seed=3000 + case, bias_mode=bias_mode, zipf=zipf))
+        g = run_layer(dev, inp)
+        g32 = run_layer(dev, inp, block_rows=32)
+        g128 = run_layer(dev, inp, block_rows=128)
+        assert np.array_equal(g32["y"], g128["y"]), (case, "32-row and 128-row tiles differ")
+        assert np.array_equal(g["y"], g32["y"]), (case, "default tiles differ")
+        check_layer(inp, g)
+
+
 def test_layer_is_deterministic(dev):
     inp = make_layer(300, 256, 128, 16, 2, seed=5, bias_mode="random")
     a = run_layer(dev, inp)
