@@ -91,6 +91,20 @@ def test_route_matches_oracle_bit_exact(dev, T, E, k, bm, kind):
     assert np.array_equal(_np(out["tile_map"])[:n], tab["tile_map"])
 
 
+# Seeded random routing calls (1 to 3000 tokens, 1 to 256 experts, top-k up to
+# 32, any tile height, every logit kind, with and without a bias): the tables
+# bit for bit against the oracle, through the same checks as the cases above.
+def test_route_random_calls(dev):
+    rng = np.random.default_rng(77)
+    for case in range(60):
+        E = int(rng.integers(1, 257))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        T = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 1025)), int(rng.integers(1025, 3000))]))
+        bm = int(rng.integers(1, 129))
+        kind = str(rng.choice(["gauss", "ties", "zeros", "neginf", "zipf"]))
+        test_route_matches_oracle_bit_exact(dev, T, E, k, bm, kind)
+
+
 def test_route_is_deterministic(dev):
     l = torch.from_numpy(_logits("ties", 4096, 256, 3)).to(dev)
     a = ops.moe_route(l, 8, 64)
