@@ -259,6 +259,52 @@ def test_gemm_swiglu_matches_oracle(dev):
     assert np.mean(gotf == want) > 0.98
 
 
+# Seeded random grouped GEMM calls through the C ABI: 1 to 64 experts, 1 to
+# 700 tokens, reduction lengths 128..2048, both epilogues, both weight layouts
+# (canonical and prepacked give the same bits), against the fp64 oracle.
+def test_gemm_random_calls(dev):
+    rng = np.random.default_rng(99)
+    for case in range(24):
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 701))
+        K = 128 * int(rng.integers(1, 17))
+        swiglu = bool(rng.random() < 0.5)
+        N = 64 * int(rng.integers(1, 11)) if swiglu else 128 * int(rng.integers(1, 6))
+        bias_mode = str(rng.choice(["sym", "random"]))
+        print(f"gemm random case {case}: T={T} E={E} k={k} N={N} K={K} swiglu={swiglu} {bias_mode}", flush=True)
+        inp = make_layer(T, K, N, E, k, seed=5000 + case, bias_mode=bias_mode)
+        A = ops.bf16_from_bits(inp.x, dev)
+        Wg = ops.Q4Stack.from_host(inp.gate, dev)
+        Wu = ops.Q4Stack.from_host(inp.up, dev)
+        r = _route_for(dev, T, E, k, 6000 + case)
+        epi = ops.MOE_EPI_SWIGLU_BF16 if swiglu else ops.MOE_EPI_STORE_F32
+        outs = []
+        for packed in (False, True):
+            w0 = ops.prepack_q4(Wg) if packed else Wg
+            w1 = (ops.prepack_q4(Wu) if packed else Wu) if swiglu else None
+            out = ops.moe_grouped_gemm_q4(A, w0, r["offsets"], r["tile_map"], r["num_tiles"], epi, T * k, W1=w1,
+                                          sorted_rows=r["sorted_rows"], row_div=k)
+            torch.cuda.synchronize()
+            outs.append(out.clone())
+        assert torch.equal(outs[0], outs[1]), (case, "layouts differ")
+        srt, offs = _np(r["sorted_rows"]), _np(r["offsets"])
+        x = om.bf16_bits_to_f64(inp.x)
+        want = np.zeros((T * k, N))
+        for e in range(E):
+            rows = np.arange(offs[e], offs[e + 1])
+            if rows.size == 0:
+                continue
+            xs = x[srt[rows] // k]
+            g = xs @ om.expert_weights(inp.gate, e).T
+            want[rows] = om.round_bf16(om.silu(g) * (xs @ om.expert_weights(inp.up, e).T)) if swiglu else g
+        if swiglu:
+            assert_close_bf16(om.bf16_bits_to_f64(ops.bits_from_bf16(outs[0])), want, f"case {case} h")
+        else:
+            got = _np(outs[0]).astype(np.float64)
+            assert rel_l2(got, want) < 1e-5 and max_abs_frac(got, want) < 1e-4, case
+
+
 @pytest.mark.parametrize("I", [64, 192])
 def test_gemm_swiglu_half_column_tile(dev, I):
     # N % 128 == 64: the last 128-column slice has two live waves; the other
