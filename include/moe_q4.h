@@ -49,9 +49,10 @@ extern "C" {
  * allowed). */
 #define MOE_WORKSPACE_HEAD_BYTES 190080
 /* Byte offset, inside that head, of a uint32 status word: nonzero after a
- * decode-sized call whose persistent kernel gave up waiting (a bounded wait
- * ran out, e.g. when other work kept its workgroups from being resident);
- * that call's outputs are then invalid. It stays set until the head is zeroed. */
+ * decode-sized call whose persistent kernel, or whose one-launch routing
+ * (T <= 8), gave up waiting (a bounded wait ran out, e.g. when other work kept
+ * its workgroups from being resident); that call's outputs are then invalid.
+ * It stays set until the head is zeroed. */
 #define MOE_WORKSPACE_STATUS_OFFSET 16768
 /* Largest supported expert count and top-k. */
 #define MOE_MAX_EXPERTS 256

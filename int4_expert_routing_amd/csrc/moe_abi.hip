@@ -485,7 +485,8 @@ static int layer_forward_impl(const uint16_t* x, const uint16_t* router_w, const
               num_tiles, nblk, E, bm};
   ScatterArgs ca{ids, sa.block_base, ra.rank_in_block, sorted_rows, row_of_pair, T, E, k};
   ra.tile_desc = decode ? tile_desc : nullptr;
-  ra.done = at<int32_t>(ws, L.done);
+  ra.done = at<int32_t>(ws, L.done);   // the workspace base: the routing finds the status word from it
+  static_assert(MOE_WORKSPACE_STATUS_OFFSET + 4 <= MOE_WORKSPACE_HEAD_BYTES, "status word inside the head");
   ra.slots = at<uint64_t>(ws, L.done + 256);
   bool prep_done = false;
   if (launch_route(ra, sa, ca, true, s, fold_prep ? &prep : nullptr, &prep_done) != hipSuccess) return MOE_ERR_HIP;

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
 // and 8 experts, one wave each.
 constexpr int kSmallThreads = 256;
 constexpr int kSmallRouteMaxT = 8;                       // tokens of the one-launch routing
-constexpr int kSlotPolls = 1 << 24;                      // bound on the re-reads of one slot
+constexpr uint64_t kSlotPollTicks = 20000000;            // 200 ms of the 100 MHz counter: bound on one slot's wait
 constexpr int kSmallEpw = 4;                             // experts per workgroup (up to 4 tokens)
 static_assert(kSmallRouteMaxT == kHandoffTokens && kMaxExperts <= 256, "slot layout of the workspace head");
 __host__ __device__ constexpr int small_threads(int tb) { return tb <= 4 ? kSmallThreads : 64 * tb; }
@@ -407,11 +407,21 @@ __global__ __launch_bounds__(small_threads(TB)) void route_small_kernel(RouteArg
   __syncthreads();
   if (!last) return;   // uniform
   // collect the logits (waiting for any slot not yet visible) into LDS and
-  // logits_out, and zero the slots
+  // logits_out, and zero the slots. The wait for a slot is bounded by the
+  // real-time counter; one that runs out sets the workspace's status word
+  // (`done` is the workspace base) and the call's results are invalid.
   for (int i = tid; i < T * E; i += NT) {
     uint64_t v = __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int n = 0; (v >> 32) == 0 && n < kSlotPolls; ++n)
-      v = __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((v >> 32) == 0) {
+      const uint64_t t0 = wall_clock64();
+      do {
+        for (int n = 0; n < 64 && (v >> 32) == 0; ++n)
+          v = __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } while ((v >> 32) == 0 && wall_clock64() - t0 <= kSlotPollTicks);
+      if ((v >> 32) == 0)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(done) + MOE_WORKSPACE_STATUS_OFFSET),
+                           1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __hip_atomic_store(slots + i, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float f = __uint_as_float(uint32_t(v));
     a.logits_out[i] = f;
