@@ -488,6 +488,31 @@ def test_layer_random_shapes(dev):
         check_layer(inp, g)
 
 
+# Seeded random few-token calls (1 to 16 tokens: the one-launch routing, the
+# decode kernels and the single routing block), some with a gate vector, each
+# also through the persistent decode kernel where it applies: both against
+# the oracle.
+def test_layer_random_few_tokens(dev):
+    rng = np.random.default_rng(4242)
+    for case in range(30):
+        E = int(rng.choice([8, 16, 32, 64, 128, 256]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        H = int(rng.choice([256, 512, 1024, 2048, 2560]))
+        I = int(rng.choice([128, 256, 384, 512]))
+        T = int(rng.integers(1, 17))
+        gated = bool(rng.random() < 0.3)
+        print(f"layer random few tokens {case}: T={T} H={H} I={I} E={E} k={k} gated={gated}", flush=True)
+        inp = resample_close_calls(make_layer(T, H, I, E, k, seed=8000 + case,
+                                              bias_mode=str(rng.choice(["sym", "random"])), gated_shared=gated))
+        g = run_layer(dev, inp)
+        check_layer(inp, g)
+        w = ops.MoEWeights.from_host(inp, dev)
+        yp = ops.moe_layer_forward(ops.bf16_from_bits(inp.x, dev), w, k, persistent_decode=True)
+        torch.cuda.synchronize()
+        ref = om.moe_layer(inp, logits=g["logits"])["y"]
+        assert_close_bf16(om.bf16_bits_to_f64(ops.bits_from_bf16(yp)), ref, f"case {case} persistent")
+
+
 def test_layer_is_deterministic(dev):
     inp = make_layer(300, 256, 128, 16, 2, seed=5, bias_mode="random")
     a = run_layer(dev, inp)
