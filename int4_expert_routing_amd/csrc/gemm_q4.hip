@@ -125,6 +125,10 @@ constexpr int kLdsLoopFS = Ring<kRingFull>::END > Ring<kRingSmall>::END ? Ring<k
 constexpr int kLdsLoop = kLdsLoopFS > Ring<kRingMerged>::END ? kLdsLoopFS : Ring<kRingMerged>::END;
 constexpr int kMaxRows = 160;   // rows of a merged tile
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer descriptor flags (gfx9 family)
+// A byte offset past every buffer descriptor's range here (num_records is
+// 0x7FFFFFFF; with the per-group offsets of at most a few KB it stays below
+// 2^32): a load at it is out of range and makes no memory access.
+constexpr uint32_t kPastRange = 0x80000000u;
 // s_waitcnt immediates (gfx9: vmcnt[3:0] and [15:14], expcnt[6:4],
 // lgkmcnt[11:8]); only vmcnt waits.
 constexpr int kWaitVm0 = 0x0F70;
@@ -667,15 +671,18 @@ __global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 5 : 2) void gemm_q4_kernel
     // activation load i of wave w fills chunk positions (A w + i)*64 + lane,
     // A = activation loads per wave (4, or 1 in the small-tile ring): row
     // m = (A w + i)*8 + lane/8 and chunk slot lane%8, which holds logical
-    // chunk (lane%8) ^ swz(m)
+    // chunk (lane%8) ^ swz(m). Rows past the tile's last (the padding of its
+    // last 32-row block) get an offset past the descriptor's range: the
+    // buffer load makes no memory access for them, and their results are
+    // never stored (T=512 layer ~1% faster than re-reading the last row)
     const int aloads = nrb == 1 ? Ring<kRingSmall>::ALOADS : nrb == 5 ? Ring<kRingMerged>::ALOADS
                                                                        : Ring<kRingFull>::ALOADS;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int m = (wave * aloads + i) * 8 + (lane >> 3);
       const int cidx = (lane & 7) ^ swz(m);
-      const int r = ti.r0 + min(m, nrows - 1);     // padding rows re-read the last real row
-      st.va[i] = uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16);
+      const int r = ti.r0 + min(m, nrows - 1);
+      st.va[i] = m < nrows ? uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16) : kPastRange;
     }
     // side-table load of wave w: row w*32 + lane/2, 16-byte half lane%2
     const int mx = (nrb == 1 ? 0 : wave * 32) + (lane >> 1);   // small tiles: rows 0..31 in every wave
