@@ -674,7 +674,8 @@ __global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 5 : 2) void gemm_q4_kernel
     // chunk (lane%8) ^ swz(m). Rows past the tile's last (the padding of its
     // last 32-row block) get an offset past the descriptor's range: the
     // buffer load makes no memory access for them, and their results are
-    // never stored (T=512 layer ~1% faster than re-reading the last row)
+    // never stored (with the side table's padding rows below, the T=512
+    // layer ran ~3% faster than re-reading the last row)
     const int aloads = nrb == 1 ? Ring<kRingSmall>::ALOADS : nrb == 5 ? Ring<kRingMerged>::ALOADS
                                                                        : Ring<kRingFull>::ALOADS;
 #pragma unroll
@@ -684,11 +685,14 @@ __global__ __launch_bounds__(kGemmThreads, NCB == 1 ? 5 : 2) void gemm_q4_kernel
       const int r = ti.r0 + min(m, nrows - 1);
       st.va[i] = m < nrows ? uint32_t(src_row(a, r)) * uint32_t(K * 2) + uint32_t(cidx * 16) : kPastRange;
     }
-    // side-table load of wave w: row w*32 + lane/2, 16-byte half lane%2
+    // side-table load of wave w: row w*32 + lane/2, 16-byte half lane%2;
+    // padding rows, as above, past the range
     const int mx = (nrb == 1 ? 0 : wave * 32) + (lane >> 1);   // small tiles: rows 0..31 in every wave
-    st.vxp = uint32_t(src_row(a, ti.r0 + min(mx, nrows - 1))) * uint32_t(KPx * 2) + uint32_t((lane & 1) * 16);
-    st.vxp2 = uint32_t(src_row(a, ti.r0 + min(128 + (lane >> 1), nrows - 1))) * uint32_t(KPx * 2) +
-              uint32_t((lane & 1) * 16);
+    const int mx2 = kBlockRows + (lane >> 1);                  // merged tiles' second load
+    st.vxp = mx < nrows ? uint32_t(src_row(a, ti.r0 + mx)) * uint32_t(KPx * 2) + uint32_t((lane & 1) * 16)
+                        : kPastRange;
+    st.vxp2 = mx2 < nrows ? uint32_t(src_row(a, ti.r0 + mx2)) * uint32_t(KPx * 2) + uint32_t((lane & 1) * 16)
+                          : kPastRange;
   }
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
