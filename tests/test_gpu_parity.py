@@ -63,9 +63,10 @@ ROUTE_CASES = [
     # one routing block of at most 64 pairs: the one-wave tables (repeated experts, several tiles per expert)
     (8, 16, 8, 3, "gauss"), (4, 8, 4, 1, "ties"), (16, 32, 4, 5, "zipf"), (2, 5, 3, 2, "gauss"),
     (8, 256, 8, 64, "zeros"), (6, 64, 8, 2, "neginf"), (32, 256, 2, 64, "gauss"),
-    # the last block count whose scan and scatter share one launch (64 blocks of 16 tokens), and the first
-    # that takes the two launches
+    # scan and scatter in one launch at up to 256 routing blocks of 16 tokens (T <= 4096), as two launches
+    # above: both sides of that boundary, and of 64 blocks (T = 1024, the router kernel's switch)
     (1024, 256, 8, 32, "gauss"), (1025, 256, 8, 32, "zipf"), (1024, 200, 32, 32, "ties"),
+    (4097, 256, 8, 32, "zipf"), (4097, 200, 32, 32, "ties"), (4096, 256, 8, 128, "neginf"),
 ]
 
 
